@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks one part of the oracle against something fixed independently:
+values the pages print (tests/golden/pages_constants.json), closed forms of
+special cases, textbook or library routines (scipy, torch CPU), brute force
+on tiny shapes, or invariants of the mathematics.  Together they are chosen so
+that a dropped term, a wrong sign or index, or a transposed operand anywhere in
+the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from flow_matching_action_amd import inputs
+from oracle import pi_ae_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")
+
+TINY = inputs.ExpertConfig(num_layers=2, width=64, mlp_dim=128, num_heads=2, head_dim=16,
+                           action_dim=4, chunk_len=5, num_steps=3)
+
+
+def bits(x):
+    return inputs.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def zero_weights(cfg):
+    return {n: np.zeros(s, np.uint16) for n, s in inputs.weight_shapes(cfg)}
+
+
+def rand_weights(cfg, seed=0, std=0.2):
+    return inputs.make_weights(cfg, seed=seed, std=std, cache=False)
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------- pages' values
+def test_timesteps_match_pages():
+    g = golden()
+    ts = O.timesteps(g["euler_dt"]["num_steps"], 1.0, g["euler_dt"]["value"])
+    np.testing.assert_allclose(ts, g["timesteps"]["value"], rtol=0, atol=1e-6)
+    # dt is -1/num_steps
+    assert np.float32(g["euler_dt"]["value"]) == np.float32(-1.0 / g["euler_dt"]["num_steps"])
+
+
+def test_shapes_match_pages():
+    g = golden()["shapes"]
+    cfg = inputs.ExpertConfig()
+    shapes = dict(inputs.weight_shapes(cfg))
+    as_in_out = lambda name: list(shapes[name][::-1])  # nn.Linear [out][in] -> [in, out]
+    assert as_in_out("action_in.w") == g["action_in"]
+    assert as_in_out("action_out.w") == g["action_out"]
+    assert as_in_out("time_in.w") == g["time_mlp"] and as_in_out("time_out.w") == g["time_mlp"]
+    assert as_in_out("layers.0.attn_mod.w") == g["adarms_dense"]
+    for key, name in [("q_proj", "q"), ("k_proj", "k"), ("v_proj", "v"), ("o_proj", "o"),
+                      ("gate_proj", "gate"), ("up_proj", "up"), ("down_proj", "down")]:
+        assert as_in_out(f"layers.0.{name}.w") == g[key], key
+    assert cfg.num_layers == g["expert_layers"] and cfg.head_dim == g["head_dim"]
+    assert cfg.num_heads == g["num_heads"] and cfg.num_kv_heads == g["num_kv_heads"]
+    fused = shapes["layers.0.q.w"][0] + shapes["layers.0.k.w"][0] + shapes["layers.0.v.w"][0]
+    assert fused == golden()["fused_qkv_width"]["value"] == (cfg.num_heads + 2) * cfg.head_dim
+    assert 3 * cfg.width == golden()["style_table_width"]["value"]
+
+
+def test_rope_frequencies_match_pages():
+    g = golden()["rope"]
+    d = g["head_dim"]
+    for i in [0, 1, 17, 64, 127]:
+        x = np.zeros((1, d))
+        x[0, i] = 1.0
+        y = O.rope(x, np.array([1.0]), g["base"])[0]
+        angle = math.atan2(y[i + d // 2], y[i])
+        assert angle == pytest.approx(1.0 / g["base"] ** (2 * i / d), rel=1e-12, abs=1e-15)
+
+
+def test_mask_fill_equals_exclusion():
+    """The pages add -2.38e38 to invalid keys' scores (fp32); the oracle drops them."""
+    fill = golden()["mask_fill"]["value"]
+    rng = np.random.default_rng(5)
+    H, d, nk = 3, 8, 9
+    q = rng.standard_normal((4, H, d))
+    k = rng.standard_normal((nk, d))
+    v = rng.standard_normal((nk, d))
+    valid = np.array([1, 1, 0, 1, 0, 1, 1, 1, 0], bool)
+    ref = O.attention(q, k, v, valid, 0.25)
+    s = (np.einsum("qhd,kd->qhk", q, k) * 0.25).astype(np.float32)
+    s = s + np.where(valid, 0.0, fill).astype(np.float32)
+    p = torch.softmax(torch.from_numpy(s), dim=-1).numpy()
+    out = np.einsum("qhk,kd->qhd", p.astype(np.float64), v)
+    np.testing.assert_allclose(out, ref, rtol=1e-5, atol=1e-6)
+
+
+# --------------------------------------------------------------------- elementwise
+def test_gelu_silu_textbook():
+    assert O.gelu_tanh(np.float64(1.0)) == pytest.approx(0.841192, abs=1e-6)
+    assert O.gelu_tanh(np.float64(0.0)) == 0.0
+    x = np.linspace(-6, 6, 2001)
+    erf_gelu = 0.5 * x * (1 + scipy.special.erf(x / math.sqrt(2)))
+    assert np.max(np.abs(O.gelu_tanh(x) - erf_gelu)) < 5e-4
+    assert O.silu(np.float64(0.0)) == 0.0
+    np.testing.assert_allclose(O.silu(x), x * scipy.special.expit(x), rtol=1e-13, atol=1e-15)
+
+
+def test_adarms_textbook():
+    eps = 1e-6
+    c = -2.5
+    h = np.full((1, 32), c)
+    np.testing.assert_allclose(O.rms_normalize(h, eps), c / math.sqrt(c * c + eps), rtol=1e-14)
+    rng = np.random.default_rng(0)
+    h = rng.standard_normal((7, 48)) * 3
+    s = rng.standard_normal(48)
+    sh = rng.standard_normal(48)
+    lib = torch.nn.functional.rms_norm(torch.from_numpy(h), (48,), eps=eps).numpy()
+    # torch's CPU rms_norm rounds its reciprocal root near fp32 precision, hence 1e-6
+    np.testing.assert_allclose(O.adarms(h, s, sh, eps), lib * (1 + s) + sh, rtol=1e-6, atol=1e-6)
+    # scale invariance of the norm (exact with eps = 0)
+    np.testing.assert_allclose(O.rms_normalize(1e3 * h, 0.0), O.rms_normalize(h, 0.0), rtol=1e-13)
+
+
+def test_sinusoidal_embedding():
+    dim = 1024
+    half = dim // 2
+    e0 = O.sinusoidal_embedding(0.0, dim)
+    np.testing.assert_array_equal(e0[:half], 0.0)
+    np.testing.assert_array_equal(e0[half:], 1.0)
+    for t in [0.1, 0.55, 1.0]:
+        e = O.sinusoidal_embedding(t, dim)
+        assert np.sum(e * e) == pytest.approx(half, rel=1e-12)
+    # channel i has period 4e-3 * 1000^(i/(half-1)): a quarter period gives sin = 1
+    for i in [0, 100, 511]:
+        tau = 4e-3 * (4.0 / 4e-3) ** (i / (half - 1))
+        assert O.sinusoidal_embedding(tau / 4, dim)[i] == pytest.approx(1.0, abs=1e-12)
+
+
+def test_time_mlp_order():
+    """cond = SiLU(W_out SiLU(W_in emb + b_in) + b_out): with W_in = 0 and W_out = I
+    the condition is SiLU(SiLU(b_in) + b_out), whatever t is."""
+    cfg = TINY
+    D = cfg.width
+    wb = zero_weights(cfg)
+    rng = np.random.default_rng(1)
+    b_in = rng.standard_normal(D).astype(np.float32)
+    b_out = rng.standard_normal(D).astype(np.float32)
+    wb["time_in.b"] = bits(b_in)
+    wb["time_out.b"] = bits(b_out)
+    wb["time_out.w"] = bits(np.eye(D))
+    W = O.Weights(wb, cfg)
+    bi = O.bf16_to_float(wb["time_in.b"])
+    bo = O.bf16_to_float(wb["time_out.b"])
+    sil = lambda z: z * scipy.special.expit(z)
+    for t in [1.0, 0.3]:
+        np.testing.assert_allclose(O.time_condition(W, t), sil(sil(bi) + bo), rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------- RoPE
+def test_rope_complex_form_and_invariants():
+    rng = np.random.default_rng(2)
+    d, base = 16, 10000.0
+    x = rng.standard_normal((6, d))
+    pos = np.array([0, 1, 5, 17, 100, 4096], np.float64)
+    y = O.rope(x, pos, base)
+    half = d // 2
+    theta = base ** (-2.0 * np.arange(half) / d)
+    z = (x[:, :half] + 1j * x[:, half:]) * np.exp(1j * pos[:, None] * theta[None, :])
+    np.testing.assert_allclose(y, np.concatenate([z.real, z.imag], axis=1), rtol=1e-12, atol=1e-12)
+    # pair norms preserved, identity at position 0
+    np.testing.assert_allclose(y[:, :half] ** 2 + y[:, half:] ** 2, x[:, :half] ** 2 + x[:, half:] ** 2, rtol=1e-12)
+    np.testing.assert_array_equal(y[0], x[0])
+    # relative position: <R_p q, R_p' k> = <R_{p-p'} q, k>
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for p, pp in [(7, 3), (300, 12), (5, 9)]:
+        lhs = O.rope(q[None], np.array([p]), base)[0] @ O.rope(k[None], np.array([pp]), base)[0]
+        rhs = O.rope(q[None], np.array([p - pp]), base)[0] @ k
+        assert lhs == pytest.approx(rhs, rel=1e-10, abs=1e-12)
+
+
+# --------------------------------------------------------------------- attention
+def brute_attention(q, k, v, valid, scale):
+    nq, H, d = q.shape
+    out = np.zeros((nq, H, d))
+    keys = [j for j in range(k.shape[0]) if valid[j]]
+    for a in range(nq):
+        for h in range(H):
+            sc = []
+            for j in keys:
+                acc = 0.0
+                for c in range(d):
+                    acc += q[a, h, c] * k[j, c]
+                sc.append(acc * scale)
+            m = max(sc)
+            e = [math.exp(s - m) for s in sc]
+            z = sum(e)
+            for c in range(d):
+                out[a, h, c] = sum(e[i] * v[keys[i], c] for i in range(len(keys))) / z
+    return out
+
+
+def test_attention_brute_force_and_library():
+    rng = np.random.default_rng(3)
+    H, d = 2, 4
+    q = rng.standard_normal((2, H, d))
+    k = rng.standard_normal((5, d))
+    v = rng.standard_normal((5, d))
+    valid = np.array([True, False, True, True, True])  # 3 prefix keys (1 masked) + 2 suffix keys
+    ref = brute_attention(q, k, v, valid, 0.5)
+    np.testing.assert_allclose(O.attention(q, k, v, valid, 0.5), ref, rtol=1e-12, atol=1e-14)
+    # torch SDPA (CPU, fp64) with the single KV head repeated to H heads
+    tq = torch.from_numpy(q.transpose(1, 0, 2))[None]
+    tk = torch.from_numpy(np.repeat(k[None], H, 0))[None]
+    tv = torch.from_numpy(np.repeat(v[None], H, 0))[None]
+    mask = torch.from_numpy(valid)[None, None, None, :]
+    lib = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.5)
+    np.testing.assert_allclose(lib[0].numpy().transpose(1, 0, 2), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    H, d, nk = 3, 8, 7
+    q = rng.standard_normal((4, H, d))
+    k = rng.standard_normal((nk, d))
+    v = rng.standard_normal((nk, d))
+    valid = np.array([1, 0, 1, 1, 0, 1, 1], bool)
+    base = O.attention(q, k, v, valid, 0.3)
+    # one valid key -> its value
+    one = np.zeros(nk, bool)
+    one[3] = True
+    np.testing.assert_allclose(O.attention(q, k, v, one, 0.3), np.broadcast_to(v[3], (4, H, d)), rtol=1e-14)
+    # q = 0 -> mean of the valid values
+    np.testing.assert_allclose(O.attention(np.zeros_like(q), k, v, valid, 0.3),
+                               np.broadcast_to(v[valid].mean(0), (4, H, d)), rtol=1e-13)
+    # a common offset on every key shifts each query's scores by a constant
+    c = rng.standard_normal(d)
+    np.testing.assert_allclose(O.attention(q, k + c, v, valid, 0.3), base, rtol=1e-11, atol=1e-12)
+    # garbage in masked keys/values changes nothing
+    k2, v2 = k.copy(), v.copy()
+    k2[~valid] = 1e4
+    v2[~valid] = -1e4
+    np.testing.assert_array_equal(O.attention(q, k2, v2, valid, 0.3), base)
+    # permuting keys together with values and mask changes nothing
+    perm = rng.permutation(nk)
+    np.testing.assert_allclose(O.attention(q, k[perm], v[perm], valid[perm], 0.3), base, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------- layer closed forms
+def _layer_inputs(cfg, seed, P=6, n_valid=4):
+    rng = np.random.default_rng(seed)
+    T, D, d = cfg.chunk_len, cfg.width, cfg.head_dim
+    h = rng.standard_normal((T, D))
+    pk = O.bf16_to_float(bits(rng.standard_normal((P, d))))
+    pv = O.bf16_to_float(bits(rng.standard_normal((P, d))))
+    valid = np.zeros(P, bool)
+    valid[:n_valid] = True
+    return h, pk, pv, valid
+
+
+def test_layer_uniform_attention_closed_form():
+    """W_q = 0 makes every score 0, so attention returns the mean of the valid
+    values (prefix + suffix).  With modulation weights 0 the modulation is the
+    bias split (scale | shift | gate); a zero ffn gate switches the MLP off."""
+    cfg = TINY.replace(num_layers=1)
+    D, H, d, T = cfg.width, cfg.num_heads, cfg.head_dim, cfg.chunk_len
+    rng = np.random.default_rng(6)
+    wb = rand_weights(cfg, seed=11)
+    wb["layers.0.attn_mod.w"] = np.zeros_like(wb["layers.0.attn_mod.w"])
+    wb["layers.0.ffn_mod.w"] = np.zeros_like(wb["layers.0.ffn_mod.w"])
+    s, sh, g = rng.standard_normal(D) * 0.5, rng.standard_normal(D) * 0.3, rng.standard_normal(D)
+    wb["layers.0.attn_mod.b"] = bits(np.concatenate([s, sh, g]))
+    fb = rng.standard_normal(3 * D)
+    fb[2 * D:] = 0.0
+    wb["layers.0.ffn_mod.b"] = bits(fb)
+    wb["layers.0.q.w"] = np.zeros_like(wb["layers.0.q.w"])
+    W = O.Weights(wb, cfg)
+    h, pk, pv, valid = _layer_inputs(cfg, 7)
+    pos = valid.sum() + np.arange(T)
+    got = O.expert_layer(W, 0, h, np.zeros(D), pk, pv, valid, pos)
+    sb, shb, gb = np.split(O.bf16_to_float(wb["layers.0.attn_mod.b"]), 3)
+    u = torch.nn.functional.rms_norm(torch.from_numpy(h), (D,), eps=cfg.rms_eps).numpy() * (1 + sb) + shb
+    vs = u @ W.layer(0, "v.w").T
+    mean_v = (pv[valid].sum(0) + vs.sum(0)) / (valid.sum() + T)
+    o_row = np.tile(mean_v, H)
+    want = h + (o_row @ W.layer(0, "o.w").T)[None, :] * gb
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6)
+
+
+def test_layer_mlp_closed_form():
+    """Width = MLP dim, attention gate 0, W_gate = c I, W_up = I, W_down = a
+    permutation P: the layer adds P (GELU(c u) * u) to h, u = RMS-normalised h."""
+    cfg = TINY.replace(num_layers=1, width=16, mlp_dim=16, num_heads=2, head_dim=8)
+    D, T = cfg.width, cfg.chunk_len
+    rng = np.random.default_rng(8)
+    wb = rand_weights(cfg, seed=12)
+    wb["layers.0.attn_mod.w"] = np.zeros_like(wb["layers.0.attn_mod.w"])
+    ab = rng.standard_normal(3 * D)
+    ab[2 * D:] = 0.0
+    wb["layers.0.attn_mod.b"] = bits(ab)
+    wb["layers.0.ffn_mod.w"] = np.zeros_like(wb["layers.0.ffn_mod.w"])
+    wb["layers.0.ffn_mod.b"] = bits(np.concatenate([np.zeros(2 * D), np.ones(D)]))
+    c = 3.0
+    wb["layers.0.gate.w"] = bits(c * np.eye(D))
+    wb["layers.0.up.w"] = bits(np.eye(D))
+    perm = np.roll(np.arange(D), 3)  # not an involution
+    P = np.zeros((D, D))
+    P[np.arange(D), perm] = 1.0
+    wb["layers.0.down.w"] = bits(P)
+    W = O.Weights(wb, cfg)
+    h, pk, pv, valid = _layer_inputs(cfg, 9)
+    got = O.expert_layer(W, 0, h, np.zeros(D), pk, pv, valid, valid.sum() + np.arange(T))
+    u = torch.nn.functional.rms_norm(torch.from_numpy(h), (D,), eps=cfg.rms_eps).numpy()
+    m = 0.5 * (c * u) * (1 + scipy.special.erf(c * u / math.sqrt(2))) * u
+    want = h + m[:, perm]
+    np.testing.assert_allclose(got, want, rtol=0, atol=2e-3 * np.abs(m).max())
+
+
+def test_zero_gates_make_layers_identity():
+    cfg = TINY
+    wb = rand_weights(cfg, seed=13)
+    for l in range(cfg.num_layers):
+        for nm in ["attn_mod", "ffn_mod"]:
+            wb[f"layers.{l}.{nm}.w"] = np.zeros_like(wb[f"layers.{l}.{nm}.w"])
+            b = O.bf16_to_float(wb[f"layers.{l}.{nm}.b"])
+            b[2 * cfg.width:] = 0.0
+            wb[f"layers.{l}.{nm}.b"] = bits(b)
+    k, v = inputs.make_prefix_kv(cfg, 1, 6)
+    mask = inputs.make_pad_mask(1, 6, 4)
+    noise = inputs.make_noise(cfg, 1)
+    got = O.sample(wb, cfg, k, v, mask, noise)
+    cfg0 = cfg.replace(num_layers=0)
+    wb0 = {n: a for n, a in wb.items() if not n.startswith("layers.")}
+    want = O.sample(wb0, cfg0, k[:0], v[:0], mask, noise)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------- whole loop
+def test_zero_weights_bias_only_out_proj():
+    """Every weight 0 except b_out: gates are 0, v = b_out, x_S = x_0 + S dt b_out."""
+    for cfg, S in [(inputs.WORKLOADS["c1"].cfg, 1), (TINY.replace(num_steps=10), 10)]:
+        wb = zero_weights(cfg)
+        rng = np.random.default_rng(10)
+        wb["action_out.b"] = bits(rng.standard_normal(cfg.action_dim))
+        wb["action_in.w"] = bits(rng.standard_normal((cfg.width, cfg.action_dim)) * 0.1)
+        wb["action_in.b"] = bits(rng.standard_normal(cfg.width) * 0.1)
+        P = 7
+        k, v = inputs.make_prefix_kv(cfg, 2, P)
+        mask = inputs.make_pad_mask(2, P, 5)
+        noise = inputs.make_noise(cfg, 2)
+        x = O.sample(wb, cfg, k, v, mask, noise)
+        bout = O.bf16_to_float(wb["action_out.b"])
+        want = noise.astype(np.float64) + S * float(np.float32(cfg.dt)) * bout
+        np.testing.assert_allclose(x, want, rtol=1e-12, atol=1e-12)
+
+
+def test_euler_linear_field_closed_form():
+    """No layers and no final norm: v = x M + c is linear, so S Euler steps give
+    x_S = x_0 G^S + dt c (I + G + ... + G^(S-1)), G = I + dt M."""
+    cfg = TINY.replace(num_layers=0, final_norm=False, num_steps=7, dt=-1.0 / 7)
+    wb = rand_weights(cfg, seed=14, std=0.1)
+    W = O.Weights(wb, cfg)
+    noise = inputs.make_noise(cfg, 3)
+    x = O.sample(wb, cfg, np.zeros((0, 3, 0, cfg.head_dim), np.uint16),
+                 np.zeros((0, 3, 0, cfg.head_dim), np.uint16), np.zeros((3, 0), np.uint8), noise)
+    Win, bin_, Wout, bout = W["action_in.w"], W["action_in.b"], W["action_out.w"], W["action_out.b"]
+    M = Win.T @ Wout.T
+    c = bin_ @ Wout.T + bout
+    dt = float(np.float32(cfg.dt))
+    G = np.eye(cfg.action_dim) + dt * M
+    geo = sum(np.linalg.matrix_power(G, i) for i in range(cfg.num_steps))
+    want = noise.astype(np.float64) @ np.linalg.matrix_power(G, cfg.num_steps) + dt * c @ geo
+    np.testing.assert_allclose(x, want, rtol=1e-10, atol=1e-12)
+
+
+def test_batch_independence_and_masked_garbage():
+    cfg = TINY
+    wb = rand_weights(cfg, seed=15)
+    B, P = 3, 6
+    k, v = inputs.make_prefix_kv(cfg, B, P)
+    mask = inputs.make_pad_mask(B, P, [6, 2, 0])
+    noise = inputs.make_noise(cfg, B)
+    x = O.sample(wb, cfg, k, v, mask, noise)
+    for b in range(B):
+        xb = O.sample(wb, cfg, k[:, b:b + 1], v[:, b:b + 1], mask[b:b + 1], noise[b:b + 1])
+        np.testing.assert_allclose(x[b:b + 1], xb, rtol=1e-14, atol=1e-15)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, mask == 0] = bits(1e4)
+    v2[:, mask == 0] = bits(-1e4)
+    np.testing.assert_array_equal(O.sample(wb, cfg, k2, v2, mask, noise), x)
+
+
+def test_fold_equalities():
+    """Tabulated/fused/folded graph == unfolded model (fp64)."""
+    cfg = TINY.replace(num_steps=4, dt=-0.25)
+    wb = rand_weights(cfg, seed=16)
+    B, P = 2, 7
+    k, v = inputs.make_prefix_kv(cfg, B, P)
+    mask = inputs.make_pad_mask(B, P, [7, 3])
+    noise = inputs.make_noise(cfg, B)
+    a = O.sample(wb, cfg, k, v, mask, noise)
+    b = O.sample_folded(wb, cfg, k, v, mask, noise)
+    assert np.linalg.norm(a - b) <= 1e-10 * np.linalg.norm(a)
+    cfg2 = cfg.replace(final_norm=False)
+    a = O.sample(wb, cfg2, k, v, mask, noise)
+    b = O.sample_folded(wb, cfg2, k, v, mask, noise)
+    assert np.linalg.norm(a - b) <= 1e-10 * np.linalg.norm(a)
+
+
+def test_degenerate_sizes():
+    cfg = TINY.replace(chunk_len=1)
+    wb = rand_weights(cfg, seed=17)
+    # no prefix at all: one suffix token attends only to itself -> attention output = its value
+    k0 = np.zeros((cfg.num_layers, 1, 0, cfg.head_dim), np.uint16)
+    x = O.sample(wb, cfg, k0, k0, np.zeros((1, 0), np.uint8), inputs.make_noise(cfg, 1))
+    assert np.all(np.isfinite(x))
+    # all prefix keys masked == no prefix
+    k, v = inputs.make_prefix_kv(cfg, 1, 5)
+    x2 = O.sample(wb, cfg, k, v, np.zeros((1, 5), np.uint8), inputs.make_noise(cfg, 1))
+    np.testing.assert_allclose(x2, x, rtol=1e-14, atol=1e-15)
