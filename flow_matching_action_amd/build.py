@@ -1,0 +1,46 @@
+"""Build libpi_ae.so (gfx950) in-tree with hipcc.
+
+Usage: python -m flow_matching_action_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpi_ae.so")
+SOURCES = [os.path.join(CSRC, "pi_ae_kernels.hip"), os.path.join(CSRC, "pi_ae_runtime.cpp")]
+
+# Packed-fp32 VALU forms are kept out of generated code on purpose.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libpi_ae.so)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into flow_matching_action_amd/libpi_ae.so; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,100 @@
+// Internal interface between the host runtime and the gfx950 kernels of the
+// action-expert denoise loop.  Not part of the public C ABI (include/pi_ae.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pi_ae {
+
+// Fixed expert shape (Realtime-VLA technical blog, "LeRobot implementation":
+// Gemma-300M-shaped expert, 8 query heads x 256, one KV head, MLP 4096).
+constexpr int kD = 1024;              // width
+constexpr int kF = 4096;              // MLP dim
+constexpr int kH = 8;                 // query heads
+constexpr int kHd = 256;              // head dim
+constexpr int kA = 32;                // action dim
+constexpr int kNqkv = (kH + 2) * kHd; // fused QKV width, 2560
+constexpr int kNgu = 2 * kF;          // fused gate|up width, 8192
+constexpr int kRopeHalf = kHd / 2;    // 128 rotated pairs per head
+
+// Per-call pointers, written by the args kernel into a device block that the
+// captured graph reads, so that one graph serves every call.
+struct DevArgs {
+  const uint16_t* pk;     // prefix K [L][B][P][256]
+  const uint16_t* pv;     // prefix V [L][B][P][256]
+  const uint8_t* mask;    // [B][P] or null
+  const float* noise;     // [B][T][32]
+  float* actions;         // [B][T][32], the Euler state x
+};
+
+struct IoParams {
+  const DevArgs* da;
+  float* h;               // [Mpad][1024] fp32 residual stream
+  const uint16_t* w_in;   // action_in W [1024][32] bf16
+  const float* b_in;      // [1024]
+  const uint16_t* w_out;  // action_out W [32][1024] bf16
+  const float* fin_s1;    // final (1+scale) for the finishing step [1024] (null: no final norm)
+  const float* c_out;     // [32] shift @ W_out^T + b_out for the finishing step
+  float dt;
+  float eps;
+  int do_out;             // finish the previous step: final norm, out proj, Euler
+  int do_in;              // start a step: action_in
+  int from_noise;         // x comes from noise (first step)
+  int M;
+};
+
+struct GemmParams {
+  const uint16_t* w;      // swizzled weight fragments of this layer
+  int M;                  // valid rows
+  // A operand
+  const float* h;         // normalised-input modes: fp32 residual [Mpad][1024]
+  const float* s1;        //   (1 + scale) [1024]
+  float eps;
+  const uint16_t* a_frag; // bf16 fragment-major activations (O or m)
+  // epilogue
+  const float* bias;      // QKV / GU: shift-fold bias in the swizzled column order
+  const float* gate;      // residual modes: per-column gate [1024]
+  float* h_out;           // residual modes: fp32 residual stream
+  uint16_t* q_out;        // QKV: Q [M][8][256]
+  uint16_t* k_out;        // QKV: K_s [M][256]
+  uint16_t* v_out;        // QKV: V_s [M][256]
+  const float2* rope;     // (cos, sin) [pos][128]
+  const int* n_valid;     // [B]
+  int T;                  // chunk length (rows per episode)
+  uint16_t* m_out;        // GU: m, fragment-major [Mpad/16][128][64][8]
+};
+
+struct AttnParams {
+  const DevArgs* da;
+  size_t layer_off;       // element offset of this layer in the prefix K/V: l * B * P * 256
+  const uint16_t* q;      // [M][8][256]
+  const uint16_t* ks;     // [M][256]
+  const uint16_t* vs;     // [M][256]
+  const int* n_valid;
+  uint16_t* o;            // fragment-major [Mpad/16][64][64][8]
+  int B, T, P;
+};
+
+struct ArgsParams {
+  DevArgs* da;
+  DevArgs vals;
+  int* n_valid;
+  int B, P;
+};
+
+hipError_t launch_args(const ArgsParams& p, hipStream_t s);
+hipError_t launch_io(const IoParams& p, hipStream_t s);
+hipError_t launch_qkv(const GemmParams& p, hipStream_t s);
+hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_o(const GemmParams& p, hipStream_t s);
+hipError_t launch_gu(const GemmParams& p, hipStream_t s);
+hipError_t launch_down(const GemmParams& p, hipStream_t s);
+
+// Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
+// (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =
+// columns n in [16nb, 16nb+16), k in [32kb, 32kb+32); lane l of the fragment
+// holds W[16nb + l%16][32kb + 8(l/16) .. +8] (the B operand of
+// v_mfma_f32_16x16x32_bf16), fragments ordered nb-major.
+inline size_t frag_offset(int nb, int kb, int KB) { return (size_t(nb) * KB + kb) * 512; }
+
+}  // namespace pi_ae

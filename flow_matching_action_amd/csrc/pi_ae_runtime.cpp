@@ -1,0 +1,764 @@
+// Host runtime of libpi_ae.so: argument validation, one-time weight
+// preparation (fp64 tabulation and folding, fused and swizzled weights),
+// workspaces, the per-(batch, prefix) hipGraph cache and the C ABI.
+#include "pi_ae.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <thread>
+#include <utility>
+#include <vector>
+
+#include "pi_ae_kernels.h"
+
+using namespace pi_ae;
+
+#define PI_AE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pi_ae_status fail(pi_ae_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+struct HipError {
+  hipError_t e;
+  std::string what;
+};
+
+#define HIP_OR_THROW(call)                                                      \
+  do {                                                                          \
+    hipError_t e_ = (call);                                                     \
+    if (e_ != hipSuccess) throw HipError{e_, std::string(#call) + ": " + hipGetErrorString(e_)}; \
+  } while (0)
+
+inline double bf(uint16_t v) {
+  uint32_t u = uint32_t(v) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return double(f);
+}
+
+}  // namespace
+
+struct pi_ae_ctx {
+  pi_ae_config cfg{};
+  int device = 0;
+  bool broken = false;
+  std::vector<void*> allocs;
+  // prepared weights (device)
+  uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr, *w_in = nullptr, *w_out = nullptr;
+  float* b_in = nullptr;
+  // tables (device), kernel column order
+  float *attn_s1 = nullptr, *attn_g = nullptr, *c_qkv = nullptr, *ffn_s1 = nullptr, *ffn_g = nullptr,
+        *c_gu = nullptr, *fin_s1 = nullptr, *c_out = nullptr;
+  float2* rope = nullptr;
+  // workspaces
+  float* h = nullptr;
+  uint16_t *q = nullptr, *ks = nullptr, *vs = nullptr, *o = nullptr, *m = nullptr;
+  int* n_valid = nullptr;
+  DevArgs* da = nullptr;
+  int Mmax = 0, Mpad = 0;
+  // host copies of the tables in natural column order (debug export)
+  std::vector<float> tab[10];
+  hipStream_t cap = nullptr;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+
+  template <class T>
+  T* dalloc(size_t n) {
+    void* p = nullptr;
+    if (n == 0) n = 1;
+    hipError_t e = hipMalloc(&p, n * sizeof(T));
+    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
+    allocs.push_back(p);
+    return static_cast<T*>(p);
+  }
+  void release() {
+    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    graphs.clear();
+    for (void* p : allocs) hipFree(p);
+    allocs.clear();
+    if (cap) hipStreamDestroy(cap);
+    cap = nullptr;
+  }
+};
+
+namespace {
+
+// ------------------------------------------------------------------ validation
+pi_ae_status check_config(const pi_ae_config* c) {
+  if (c->width != kD || c->mlp_dim != kF || c->num_heads != kH || c->num_kv_heads != 1 || c->head_dim != kHd ||
+      c->action_dim != kA)
+    return fail(PI_AE_EUNSUPPORTED,
+                "kernels implement width 1024, mlp_dim 4096, 8 heads, 1 KV head, head_dim 256, action_dim 32");
+  if (c->num_layers < 1 || c->num_layers > 64) return fail(PI_AE_EINVAL, "num_layers must be in [1, 64]");
+  if (c->num_steps < 1 || c->num_steps > 64) return fail(PI_AE_EINVAL, "num_steps must be in [1, 64]");
+  if (c->chunk_len < 1 || c->chunk_len > 256) return fail(PI_AE_EINVAL, "chunk_len must be in [1, 256]");
+  if (c->max_batch < 1 || c->max_batch > 4096) return fail(PI_AE_EINVAL, "max_batch must be in [1, 4096]");
+  if (c->max_prefix_len < 0 || c->max_prefix_len > 32768)
+    return fail(PI_AE_EINVAL, "max_prefix_len must be in [0, 32768]");
+  if (!std::isfinite(c->t0) || !std::isfinite(c->dt)) return fail(PI_AE_EINVAL, "t0 and dt must be finite");
+  if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(PI_AE_EINVAL, "rope_base must be > 0");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(PI_AE_EINVAL, "rms_eps must be >= 0");
+  if (c->final_norm != 0 && c->final_norm != 1) return fail(PI_AE_EINVAL, "final_norm must be 0 or 1");
+  return PI_AE_OK;
+}
+
+pi_ae_status check_weights(const pi_ae_config* c, const pi_ae_weights* w) {
+  auto need = [](const pi_ae_linear& l, bool bias, const char* name) -> pi_ae_status {
+    if (!l.w) return fail(PI_AE_EINVAL, std::string("weight ") + name + ".w is NULL");
+    if (bias && !l.b) return fail(PI_AE_EINVAL, std::string("weight ") + name + ".b is NULL");
+    return PI_AE_OK;
+  };
+  pi_ae_status s;
+  if ((s = need(w->action_in, true, "action_in")) || (s = need(w->time_in, true, "time_in")) ||
+      (s = need(w->time_out, true, "time_out")) || (s = need(w->action_out, true, "action_out")))
+    return s;
+  if (c->final_norm && (s = need(w->final_mod, true, "final_mod"))) return s;
+  if (!w->layers) return fail(PI_AE_EINVAL, "layers is NULL");
+  for (int l = 0; l < c->num_layers; ++l) {
+    const pi_ae_layer_weights& L = w->layers[l];
+    if ((s = need(L.attn_mod, true, "attn_mod")) || (s = need(L.q, false, "q")) || (s = need(L.k, false, "k")) ||
+        (s = need(L.v, false, "v")) || (s = need(L.o, false, "o")) || (s = need(L.ffn_mod, true, "ffn_mod")) ||
+        (s = need(L.gate, false, "gate")) || (s = need(L.up, false, "up")) || (s = need(L.down, false, "down")))
+      return fail(s, g_last_error + " (layer " + std::to_string(l) + ")");
+  }
+  return PI_AE_OK;
+}
+
+// ------------------------------------------------------------------ host math (fp64)
+// Sinusoidal timestep embedding: dim/2 sines then dim/2 cosines, periods
+// geometric from 4e-3 to 4.0 (the pages name the embedding but not its
+// frequencies; this is the reading the library documents and tests).
+std::vector<double> time_embedding(double t, int dim) {
+  const int half = dim / 2;
+  std::vector<double> e(dim);
+  for (int i = 0; i < half; ++i) {
+    const double frac = double(i) / double(half - 1);
+    const double period = 4e-3 * std::pow(4.0 / 4e-3, frac);
+    const double ang = 2.0 * M_PI * t / period;
+    e[i] = std::sin(ang);
+    e[half + i] = std::cos(ang);
+  }
+  return e;
+}
+
+inline double silu(double x) { return x / (1.0 + std::exp(-x)); }
+
+// y = W x + b for a bf16 W [n][k]
+std::vector<double> matvec(const uint16_t* W, const uint16_t* b, const std::vector<double>& x, int n, int k) {
+  std::vector<double> y(n);
+  for (int i = 0; i < n; ++i) {
+    const uint16_t* row = W + size_t(i) * k;
+    double acc = b ? bf(b[i]) : 0.0;
+    for (int j = 0; j < k; ++j) acc += bf(row[j]) * x[j];
+    y[i] = acc;
+  }
+  return y;
+}
+
+// Swizzle rows `perm` of W[N][K] into MFMA B-operand fragments (see frag_offset).
+void swizzle(const uint16_t* W, int K, const std::vector<int>& perm, uint16_t* out) {
+  const int NBk = int(perm.size()) / 16, KB = K / 32;
+  for (int nb = 0; nb < NBk; ++nb)
+    for (int kb = 0; kb < KB; ++kb) {
+      uint16_t* frag = out + frag_offset(nb, kb, KB);
+      for (int lane = 0; lane < 64; ++lane) {
+        const uint16_t* src = W + size_t(perm[nb * 16 + lane % 16]) * K + kb * 32 + 8 * (lane / 16);
+        std::memcpy(frag + lane * 8, src, 16);
+      }
+    }
+}
+
+// Column order of the fused QKV GEMM: workgroup j owns n-blocks 2j, 2j+1.
+// Q head h (j = 8h + pb) and K_s (j = 64 + pb): the two blocks are head-dim
+// channels pb*16 + [0,16) and 128 + pb*16 + [0,16), so each output tile holds
+// whole RoPE pairs (i, i+128).  V_s (j = 72..79): 32 consecutive channels.
+// Natural fused index: q rows 0..2047, k rows 2048..2303, v rows 2304..2559.
+std::vector<int> qkv_perm() {
+  std::vector<int> p(kNqkv);
+  for (int j = 0; j < kNqkv / 32; ++j)
+    for (int nbi = 0; nbi < 2; ++nbi)
+      for (int c = 0; c < 16; ++c) {
+        int nat;
+        if (j < 64) nat = (j >> 3) * kHd + nbi * kRopeHalf + (j & 7) * 16 + c;
+        else if (j < 72) nat = kH * kHd + nbi * kRopeHalf + (j - 64) * 16 + c;
+        else nat = kH * kHd + kHd + (j - 72) * 32 + nbi * 16 + c;
+        p[(2 * j + nbi) * 16 + c] = nat;
+      }
+  return p;
+}
+
+// Fused gate|up: workgroup j owns gate rows 16j.. (n-block 2j) and the same
+// up rows (n-block 2j+1).  Natural fused index: gate f -> f, up f -> 4096 + f.
+std::vector<int> gu_perm() {
+  std::vector<int> p(kNgu);
+  for (int j = 0; j < kF / 16; ++j)
+    for (int c = 0; c < 16; ++c) {
+      p[(2 * j) * 16 + c] = 16 * j + c;
+      p[(2 * j + 1) * 16 + c] = kF + 16 * j + c;
+    }
+  return p;
+}
+
+template <class F>
+void parallel_for(int n, F&& fn) {
+  int nt = std::max(1, std::min<int>(n, int(std::thread::hardware_concurrency())));
+  nt = std::min(nt, 16);
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (int i = t; i < n; i += nt) fn(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+// The fp64 host half of the preparation: tables in natural column order
+// (0 attn 1+scale, 1 attn gate, 2 ffn 1+scale, 3 ffn gate, 4 final 1+scale,
+// 5 c_out, 6 c_qkv, 7 c_gu, 8 timesteps, 9 cond).
+void compute_tables(const pi_ae_config& cfg, const pi_ae_weights* w, std::vector<float>* tab) {
+  const int L = cfg.num_layers, S = cfg.num_steps;
+  // timesteps t_k = fp32(t0 + k dt), evaluated in fp64
+  std::vector<double> ts(S);
+  for (int k = 0; k < S; ++k) ts[k] = double(float(double(cfg.t0) + k * double(cfg.dt)));
+  // time MLP: cond_k = SiLU(W_out SiLU(W_in emb + b_in) + b_out)
+  std::vector<std::vector<double>> cond(S);
+  parallel_for(S, [&](int k) {
+    std::vector<double> a = matvec(w->time_in.w, w->time_in.b, time_embedding(ts[k], kD), kD, kD);
+    for (double& v : a) v = silu(v);
+    std::vector<double> c = matvec(w->time_out.w, w->time_out.b, a, kD, kD);
+    for (double& v : c) v = silu(v);
+    cond[k] = std::move(c);
+  });
+  // per (step, layer) modulation and shift-fold biases, natural order
+  auto& t_as1 = tab[0]; auto& t_ag = tab[1]; auto& t_fs1 = tab[2]; auto& t_fg = tab[3];
+  auto& t_fin = tab[4]; auto& t_cout = tab[5]; auto& t_cqkv = tab[6]; auto& t_cgu = tab[7];
+  t_as1.assign(size_t(S) * L * kD, 0.f); t_ag = t_as1; t_fs1 = t_as1; t_fg = t_as1;
+  t_cqkv.assign(size_t(S) * L * kNqkv, 0.f);
+  t_cgu.assign(size_t(S) * L * kNgu, 0.f);
+  parallel_for(L, [&](int l) {
+    const pi_ae_layer_weights& Lw = w->layers[l];
+    std::vector<std::vector<double>> sh_a(S), sh_f(S);
+    for (int k = 0; k < S; ++k) {
+      std::vector<double> ma = matvec(Lw.attn_mod.w, Lw.attn_mod.b, cond[k], 3 * kD, kD);
+      std::vector<double> mf = matvec(Lw.ffn_mod.w, Lw.ffn_mod.b, cond[k], 3 * kD, kD);
+      const size_t o = (size_t(k) * L + l) * kD;
+      for (int i = 0; i < kD; ++i) {
+        t_as1[o + i] = float(1.0 + ma[i]);
+        t_ag[o + i] = float(ma[2 * kD + i]);
+        t_fs1[o + i] = float(1.0 + mf[i]);
+        t_fg[o + i] = float(mf[2 * kD + i]);
+      }
+      sh_a[k].assign(ma.begin() + kD, ma.begin() + 2 * kD);
+      sh_f[k].assign(mf.begin() + kD, mf.begin() + 2 * kD);
+    }
+    // c = shift @ W^T for every fused output column, all steps per weight row
+    std::vector<double> row(kD);
+    auto fold = [&](const uint16_t* W, int nrows, const std::vector<std::vector<double>>& sh, std::vector<float>& dst,
+                    int width, int col0) {
+      for (int n = 0; n < nrows; ++n) {
+        for (int j = 0; j < kD; ++j) row[j] = bf(W[size_t(n) * kD + j]);
+        for (int k = 0; k < S; ++k) {
+          double acc = 0.0;
+          for (int j = 0; j < kD; ++j) acc += row[j] * sh[k][j];
+          dst[(size_t(k) * L + l) * width + col0 + n] = float(acc);
+        }
+      }
+    };
+    fold(Lw.q.w, kH * kHd, sh_a, t_cqkv, kNqkv, 0);
+    fold(Lw.k.w, kHd, sh_a, t_cqkv, kNqkv, kH * kHd);
+    fold(Lw.v.w, kHd, sh_a, t_cqkv, kNqkv, kH * kHd + kHd);
+    fold(Lw.gate.w, kF, sh_f, t_cgu, kNgu, 0);
+    fold(Lw.up.w, kF, sh_f, t_cgu, kNgu, kF);
+  });
+  // final norm table and c_out = shift_f @ W_out^T + b_out
+  t_fin.assign(size_t(S) * kD, 1.f);
+  t_cout.assign(size_t(S) * kA, 0.f);
+  for (int k = 0; k < S; ++k) {
+    std::vector<double> shf(kD, 0.0);
+    if (cfg.final_norm) {
+      std::vector<double> mfin = matvec(w->final_mod.w, w->final_mod.b, cond[k], 3 * kD, kD);
+      for (int i = 0; i < kD; ++i) t_fin[size_t(k) * kD + i] = float(1.0 + mfin[i]);
+      shf.assign(mfin.begin() + kD, mfin.begin() + 2 * kD);
+    }
+    std::vector<double> c = matvec(w->action_out.w, w->action_out.b, shf, kA, kD);
+    for (int a = 0; a < kA; ++a) t_cout[size_t(k) * kA + a] = float(c[a]);
+  }
+  tab[8].assign(ts.begin(), ts.end());
+  tab[9].resize(size_t(S) * kD);
+  for (int k = 0; k < S; ++k)
+    for (int i = 0; i < kD; ++i) tab[9][size_t(k) * kD + i] = float(cond[k][i]);
+}
+
+void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
+  const pi_ae_config& cfg = ctx->cfg;
+  const int L = cfg.num_layers, T = cfg.chunk_len;
+  compute_tables(cfg, w, ctx->tab);
+  auto& t_as1 = ctx->tab[0]; auto& t_ag = ctx->tab[1]; auto& t_fs1 = ctx->tab[2]; auto& t_fg = ctx->tab[3];
+  auto& t_fin = ctx->tab[4]; auto& t_cout = ctx->tab[5]; auto& t_cqkv = ctx->tab[6]; auto& t_cgu = ctx->tab[7];
+
+  // ---- device weights
+  const std::vector<int> pq = qkv_perm(), pg = gu_perm();
+  std::vector<int> pid(kD);
+  for (int i = 0; i < kD; ++i) pid[i] = i;
+  const size_t n_qkv = size_t(kNqkv) * kD, n_o = size_t(kD) * kH * kHd, n_gu = size_t(kNgu) * kD,
+               n_d = size_t(kD) * kF;
+  ctx->w_qkv = ctx->dalloc<uint16_t>(n_qkv * L);
+  ctx->w_o = ctx->dalloc<uint16_t>(n_o * L);
+  ctx->w_gu = ctx->dalloc<uint16_t>(n_gu * L);
+  ctx->w_d = ctx->dalloc<uint16_t>(n_d * L);
+  {
+    std::vector<uint16_t> fused(std::max(n_qkv, n_gu)), sw(std::max(std::max(n_qkv, n_gu), std::max(n_o, n_d)));
+    for (int l = 0; l < L; ++l) {
+      const pi_ae_layer_weights& Lw = w->layers[l];
+      std::memcpy(fused.data(), Lw.q.w, sizeof(uint16_t) * kH * kHd * kD);
+      std::memcpy(fused.data() + size_t(kH) * kHd * kD, Lw.k.w, sizeof(uint16_t) * kHd * kD);
+      std::memcpy(fused.data() + size_t(kH + 1) * kHd * kD, Lw.v.w, sizeof(uint16_t) * kHd * kD);
+      swizzle(fused.data(), kD, pq, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_qkv + n_qkv * l, sw.data(), n_qkv * 2, hipMemcpyHostToDevice));
+      swizzle(Lw.o.w, kH * kHd, pid, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_o + n_o * l, sw.data(), n_o * 2, hipMemcpyHostToDevice));
+      std::memcpy(fused.data(), Lw.gate.w, sizeof(uint16_t) * kF * kD);
+      std::memcpy(fused.data() + size_t(kF) * kD, Lw.up.w, sizeof(uint16_t) * kF * kD);
+      swizzle(fused.data(), kD, pg, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_gu + n_gu * l, sw.data(), n_gu * 2, hipMemcpyHostToDevice));
+      swizzle(Lw.down.w, kF, pid, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_d + n_d * l, sw.data(), n_d * 2, hipMemcpyHostToDevice));
+    }
+  }
+  ctx->w_in = ctx->dalloc<uint16_t>(size_t(kD) * kA);
+  HIP_OR_THROW(hipMemcpy(ctx->w_in, w->action_in.w, size_t(kD) * kA * 2, hipMemcpyHostToDevice));
+  ctx->w_out = ctx->dalloc<uint16_t>(size_t(kA) * kD);
+  HIP_OR_THROW(hipMemcpy(ctx->w_out, w->action_out.w, size_t(kA) * kD * 2, hipMemcpyHostToDevice));
+  {
+    std::vector<float> bin(kD);
+    for (int i = 0; i < kD; ++i) bin[i] = float(bf(w->action_in.b[i]));
+    ctx->b_in = ctx->dalloc<float>(kD);
+    HIP_OR_THROW(hipMemcpy(ctx->b_in, bin.data(), kD * 4, hipMemcpyHostToDevice));
+  }
+  // ---- device tables in kernel column order
+  auto upload = [&](const std::vector<float>& v) {
+    float* d = ctx->dalloc<float>(v.size());
+    HIP_OR_THROW(hipMemcpy(d, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+    return d;
+  };
+  auto permute = [&](const std::vector<float>& nat, int width, const std::vector<int>& perm) {
+    std::vector<float> out(nat.size());
+    for (size_t r = 0; r < nat.size() / width; ++r)
+      for (int i = 0; i < width; ++i) out[r * width + i] = nat[r * width + perm[i]];
+    return out;
+  };
+  ctx->attn_s1 = upload(t_as1);
+  ctx->attn_g = upload(t_ag);
+  ctx->ffn_s1 = upload(t_fs1);
+  ctx->ffn_g = upload(t_fg);
+  ctx->fin_s1 = upload(t_fin);
+  ctx->c_out = upload(t_cout);
+  ctx->c_qkv = upload(permute(t_cqkv, kNqkv, pq));
+  ctx->c_gu = upload(permute(t_cgu, kNgu, pg));
+  // RoPE table: angle = pos * base^(-2i/256), positions 0 .. max_prefix_len + T - 1
+  {
+    const int npos = cfg.max_prefix_len + T;
+    std::vector<float2> rt(size_t(npos) * kRopeHalf);
+    for (int pos = 0; pos < npos; ++pos)
+      for (int i = 0; i < kRopeHalf; ++i) {
+        const double inv = std::pow(double(cfg.rope_base), -2.0 * i / kHd);
+        const double a = double(pos) * inv;
+        rt[size_t(pos) * kRopeHalf + i] = make_float2(float(std::cos(a)), float(std::sin(a)));
+      }
+    ctx->rope = ctx->dalloc<float2>(rt.size());
+    HIP_OR_THROW(hipMemcpy(ctx->rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice));
+  }
+  // ---- workspaces (zeroed once; padded rows are never written)
+  ctx->Mmax = cfg.max_batch * T;
+  ctx->Mpad = (ctx->Mmax + 63) / 64 * 64;
+  const size_t Mp = size_t(ctx->Mpad);
+  ctx->h = ctx->dalloc<float>(Mp * kD);
+  ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->ks = ctx->dalloc<uint16_t>(Mp * kHd);
+  ctx->vs = ctx->dalloc<uint16_t>(Mp * kHd);
+  ctx->o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->m = ctx->dalloc<uint16_t>(Mp * kF);
+  ctx->n_valid = ctx->dalloc<int>(cfg.max_batch);
+  ctx->da = ctx->dalloc<DevArgs>(1);
+  HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kD * 4));
+  HIP_OR_THROW(hipMemset(ctx->q, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->ks, 0, Mp * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->vs, 0, Mp * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kF * 2));
+  HIP_OR_THROW(hipMemset(ctx->n_valid, 0, cfg.max_batch * 4));
+  HIP_OR_THROW(hipMemset(ctx->da, 0, sizeof(DevArgs)));
+  HIP_OR_THROW(hipStreamCreateWithFlags(&ctx->cap, hipStreamNonBlocking));
+  HIP_OR_THROW(hipDeviceSynchronize());
+}
+
+// ------------------------------------------------------------------ step sequence
+// Phases: 0 = step input (k_io), 1 = QKV, 2 = attention, 3 = O, 4 = gate/up, 5 = down.
+// stop(step, layer, phase) returns true after the named phase has been enqueued.
+struct StopAt {
+  int step = -1, layer = -1, phase = -1;
+  bool hit(int k, int l, int ph) const { return k == step && (ph == 0 ? true : l == layer) && ph == phase; }
+};
+
+// Launch one phase of one (step, layer); phase 0 is the step-boundary kernel
+// of step k (k == num_steps: the final output projection and Euler update).
+hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int l, int phase) {
+  const pi_ae_config& cfg = ctx->cfg;
+  const int L = cfg.num_layers, S = cfg.num_steps, T = cfg.chunk_len, M = B * T;
+  const size_t kl = size_t(k) * L + l;
+  switch (phase) {
+    case 0: {
+      IoParams io{};
+      io.da = ctx->da;
+      io.h = ctx->h;
+      io.w_in = ctx->w_in;
+      io.b_in = ctx->b_in;
+      io.w_out = ctx->w_out;
+      io.dt = cfg.dt;
+      io.eps = cfg.rms_eps;
+      io.M = M;
+      io.do_out = k > 0;
+      io.do_in = k < S;
+      io.from_noise = k == 0;
+      io.fin_s1 = (k > 0 && cfg.final_norm) ? ctx->fin_s1 + size_t(k - 1) * kD : nullptr;
+      io.c_out = k > 0 ? ctx->c_out + size_t(k - 1) * kA : nullptr;
+      return launch_io(io, s);
+    }
+    case 1:
+    case 4: {
+      GemmParams g{};
+      g.M = M;
+      g.eps = cfg.rms_eps;
+      g.T = T;
+      g.n_valid = ctx->n_valid;
+      g.rope = ctx->rope;
+      g.h = ctx->h;
+      if (phase == 1) {
+        g.w = ctx->w_qkv + size_t(kNqkv) * kD * l;
+        g.s1 = ctx->attn_s1 + kl * kD;
+        g.bias = ctx->c_qkv + kl * kNqkv;
+        g.q_out = ctx->q;
+        g.k_out = ctx->ks;
+        g.v_out = ctx->vs;
+        return launch_qkv(g, s);
+      }
+      g.w = ctx->w_gu + size_t(kNgu) * kD * l;
+      g.s1 = ctx->ffn_s1 + kl * kD;
+      g.bias = ctx->c_gu + kl * kNgu;
+      g.m_out = ctx->m;
+      return launch_gu(g, s);
+    }
+    case 2: {
+      AttnParams a{};
+      a.da = ctx->da;
+      a.layer_off = size_t(l) * B * P * kHd;
+      a.q = ctx->q;
+      a.ks = ctx->ks;
+      a.vs = ctx->vs;
+      a.n_valid = ctx->n_valid;
+      a.o = ctx->o;
+      a.B = B;
+      a.T = T;
+      a.P = P;
+      return launch_attn(a, s);
+    }
+    case 3:
+    case 5: {
+      GemmParams g{};
+      g.M = M;
+      g.h_out = ctx->h;
+      if (phase == 3) {
+        g.w = ctx->w_o + size_t(kD) * kH * kHd * l;
+        g.a_frag = ctx->o;
+        g.gate = ctx->attn_g + kl * kD;
+        return launch_o(g, s);
+      }
+      g.w = ctx->w_d + size_t(kD) * kF * l;
+      g.a_frag = ctx->m;
+      g.gate = ctx->ffn_g + kl * kD;
+      return launch_down(g, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& stop) {
+  const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
+  hipError_t e;
+  for (int k = 0; k <= S; ++k) {
+    if ((e = launch_phase(ctx, B, P, s, k, 0, 0)) != hipSuccess) return e;
+    if (stop.hit(k, 0, 0) || k == S) return hipSuccess;
+    for (int l = 0; l < L; ++l)
+      for (int ph = 1; ph <= 5; ++ph) {
+        if ((e = launch_phase(ctx, B, P, s, k, l, ph)) != hipSuccess) return e;
+        if (stop.hit(k, l, ph)) return hipSuccess;
+      }
+  }
+  return hipSuccess;
+}
+
+pi_ae_status check_call(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, const float* actions,
+                        int32_t batch) {
+  if (!ctx) return fail(PI_AE_EINVAL, "ctx is NULL");
+  if (ctx->broken) return fail(PI_AE_ESTATE, "context is unusable after an earlier failure");
+  if (!kv) return fail(PI_AE_EINVAL, "kv is NULL");
+  if (batch < 0 || batch > ctx->cfg.max_batch)
+    return fail(PI_AE_EINVAL, "batch " + std::to_string(batch) + " outside [0, max_batch]");
+  if (kv->prefix_len < 0 || kv->prefix_len > ctx->cfg.max_prefix_len)
+    return fail(PI_AE_EINVAL, "prefix_len " + std::to_string(kv->prefix_len) + " outside [0, max_prefix_len]");
+  if (batch == 0) return PI_AE_OK;
+  if (!noise || !actions) return fail(PI_AE_EINVAL, "noise and actions must be non-NULL");
+  if (kv->prefix_len > 0 && (!kv->k || !kv->v)) return fail(PI_AE_EINVAL, "prefix k and v must be non-NULL");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (misaligned(noise) || misaligned(actions) || misaligned(kv->k) || misaligned(kv->v))
+    return fail(PI_AE_EINVAL, "k, v, noise and actions must be 16-byte aligned");
+  return PI_AE_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+  }
+};
+
+ArgsParams args_for(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions, int batch) {
+  ArgsParams a{};
+  a.da = ctx->da;
+  a.vals.pk = static_cast<const uint16_t*>(kv->k);
+  a.vals.pv = static_cast<const uint16_t*>(kv->v);
+  a.vals.mask = kv->pad_mask;
+  a.vals.noise = noise;
+  a.vals.actions = actions;
+  a.n_valid = ctx->n_valid;
+  a.B = batch;
+  a.P = kv->prefix_len;
+  return a;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+PI_AE_API pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_ae_weights* w, pi_ae_ctx** out) {
+  if (!cfg || !w || !out) return fail(PI_AE_EINVAL, "cfg, w and out must be non-NULL");
+  pi_ae_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_weights(cfg, w))) return st;
+  pi_ae_ctx* ctx = new (std::nothrow) pi_ae_ctx();
+  if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
+  ctx->cfg = *cfg;
+  try {
+    HIP_OR_THROW(hipGetDevice(&ctx->device));
+    prepare(ctx, w);
+  } catch (const HipError& e) {
+    ctx->release();
+    delete ctx;
+    return fail(e.e == hipErrorOutOfMemory ? PI_AE_ENOMEM : PI_AE_EHIP, e.what);
+  } catch (const std::bad_alloc&) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_ENOMEM, "host allocation failed during preparation");
+  } catch (...) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_EHIP, "unexpected failure during preparation");
+  }
+  *out = ctx;
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
+                                    int32_t batch, void* stream) {
+  pi_ae_status st = check_call(ctx, kv, noise, actions, batch);
+  if (st || batch == 0) return st;
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const std::pair<int, int> key(batch, kv->prefix_len);
+  auto it = ctx->graphs.find(key);
+  if (it == ctx->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t e2 = enqueue(ctx, batch, kv->prefix_len, ctx->cap, StopAt{});
+      e = hipStreamEndCapture(ctx->cap, &graph);
+      if (e2 != hipSuccess) e = e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(key, exec).first;
+  }
+  hipError_t e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
+  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
+PI_AE_API void pi_ae_destroy(pi_ae_ctx* ctx) {
+  if (!ctx) return;
+  {
+    DeviceGuard dg(ctx->device);
+    hipDeviceSynchronize();
+    ctx->release();
+  }
+  delete ctx;
+}
+
+PI_AE_API const char* pi_ae_status_string(pi_ae_status s) {
+  switch (s) {
+    case PI_AE_OK: return "ok";
+    case PI_AE_EINVAL: return "invalid argument";
+    case PI_AE_EUNSUPPORTED: return "unsupported shape";
+    case PI_AE_ENOMEM: return "out of memory";
+    case PI_AE_EHIP: return "HIP runtime error";
+    case PI_AE_ESTATE: return "invalid context state";
+  }
+  return "unknown status";
+}
+
+PI_AE_API const char* pi_ae_last_error(void) { return g_last_error.c_str(); }
+
+PI_AE_API pi_ae_status pi_ae_debug_table(pi_ae_ctx* ctx, int32_t which, float* host_out, size_t n_floats) {
+  if (!ctx || !host_out) return fail(PI_AE_EINVAL, "ctx and host_out must be non-NULL");
+  if (which < 0 || which > 9) return fail(PI_AE_EINVAL, "table index out of range");
+  const std::vector<float>& t = ctx->tab[which];
+  if (n_floats != t.size())
+    return fail(PI_AE_EINVAL, "table " + std::to_string(which) + " has " + std::to_string(t.size()) + " floats");
+  std::memcpy(host_out, t.data(), t.size() * 4);
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_debug_host_table(const pi_ae_config* cfg, const pi_ae_weights* w, int32_t which,
+                                              float* host_out, size_t n_floats) {
+  if (!cfg || !w || !host_out) return fail(PI_AE_EINVAL, "cfg, w and host_out must be non-NULL");
+  if (which < 0 || which > 9) return fail(PI_AE_EINVAL, "table index out of range");
+  pi_ae_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_weights(cfg, w))) return st;
+  try {
+    std::vector<float> tab[10];
+    compute_tables(*cfg, w, tab);
+    if (n_floats != tab[which].size())
+      return fail(PI_AE_EINVAL, "table " + std::to_string(which) + " has " + std::to_string(tab[which].size()) + " floats");
+    std::memcpy(host_out, tab[which].data(), n_floats * 4);
+  } catch (const std::bad_alloc&) {
+    return fail(PI_AE_ENOMEM, "host allocation failed");
+  }
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise,
+                                              float* actions, int32_t batch, int32_t phase, int32_t iters,
+                                              void* stream, float* avg_us) {
+  pi_ae_status st = check_call(ctx, kv, noise, actions, batch);
+  if (st) return st;
+  if (batch < 1 || phase < 0 || phase > 5 || iters < 1 || iters > 100000 || !avg_us)
+    return fail(PI_AE_EINVAL, "time_phase: batch >= 1, phase in [0, 5], iters in [1, 100000], avg_us non-NULL");
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
+  std::vector<hipEvent_t> ev(2 * size_t(iters), nullptr);
+  hipError_t e = hipSuccess;
+  for (auto& x : ev)
+    if (e == hipSuccess) e = hipEventCreate(&x);
+  if (e == hipSuccess) e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
+  // one full pass first so every intermediate holds real values
+  if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, s, StopAt{});
+  for (int i = 0; i < iters && e == hipSuccess; ++i) {
+    const int l = i % L, k = (i / L) % S;
+    e = hipEventRecord(ev[2 * i], s);
+    if (e == hipSuccess) e = launch_phase(ctx, batch, kv->prefix_len, s, k, l, phase);
+    if (e == hipSuccess) e = hipEventRecord(ev[2 * i + 1], s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  double tot = 0.0;
+  for (int i = 0; i < iters && e == hipSuccess; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+    tot += ms;
+  }
+  for (auto& x : ev)
+    if (x) hipEventDestroy(x);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("time_phase failed: ") + hipGetErrorString(e));
+  *avg_us = float(tot * 1000.0 / iters);
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise,
+                                         int32_t batch, int32_t step, int32_t layer, int32_t phase, int32_t which,
+                                         void* host_out, size_t n_bytes) {
+  if (!ctx) return fail(PI_AE_EINVAL, "ctx is NULL");
+  float* actions = nullptr;
+  pi_ae_status st = PI_AE_OK;
+  if (batch < 1) return fail(PI_AE_EINVAL, "probe needs batch >= 1");
+  if (step < 0 || step > ctx->cfg.num_steps || layer < 0 || layer >= ctx->cfg.num_layers || phase < 0 || phase > 5)
+    return fail(PI_AE_EINVAL, "probe position out of range");
+  const int T = ctx->cfg.chunk_len, M = batch * T;
+  size_t need = 0;
+  switch (which) {
+    case 0: need = size_t(M) * kD * 4; break;
+    case 1: need = size_t(M) * kH * kHd * 2; break;
+    case 2: case 3: need = size_t(M) * kHd * 2; break;
+    case 4: need = size_t(M) * kH * kHd * 2; break;
+    case 5: need = size_t(M) * kF * 2; break;
+    case 6: need = size_t(M) * kA * 4; break;
+    default: return fail(PI_AE_EINVAL, "probe 'which' out of range");
+  }
+  if (!host_out || n_bytes != need) return fail(PI_AE_EINVAL, "probe output size must be " + std::to_string(need));
+  DeviceGuard dg(ctx->device);
+  if (hipMalloc(&actions, size_t(M) * kA * 4) != hipSuccess) return fail(PI_AE_ENOMEM, "probe scratch");
+  if ((st = check_call(ctx, kv, noise, actions, batch))) {
+    hipFree(actions);
+    return st;
+  }
+  StopAt stop;
+  stop.step = step;
+  stop.layer = layer;
+  stop.phase = phase;
+  hipError_t e = launch_args(args_for(ctx, kv, noise, actions, batch), nullptr);
+  if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, nullptr, stop);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  std::vector<uint16_t> buf;
+  if (e == hipSuccess) {
+    if (which == 0) {
+      e = hipMemcpy(host_out, ctx->h, need, hipMemcpyDeviceToHost);
+    } else if (which == 6) {
+      e = hipMemcpy(host_out, actions, need, hipMemcpyDeviceToHost);
+    } else if (which == 1 || which == 2 || which == 3) {
+      const void* src = which == 1 ? (const void*)ctx->q : which == 2 ? (const void*)ctx->ks : (const void*)ctx->vs;
+      e = hipMemcpy(host_out, src, need, hipMemcpyDeviceToHost);
+    } else {
+      // fragment-major [Mpad/16][K/32][64][8] -> natural [M][K]
+      const int K = which == 4 ? kH * kHd : kF;
+      const size_t rows = size_t((M + 15) / 16) * 16;
+      buf.resize(rows * K);
+      e = hipMemcpy(buf.data(), which == 4 ? ctx->o : ctx->m, buf.size() * 2, hipMemcpyDeviceToHost);
+      uint16_t* dst = static_cast<uint16_t*>(host_out);
+      for (int r = 0; r < M; ++r)
+        for (int k = 0; k < K; ++k) {
+          const int lane = (r & 15) + 16 * ((k & 31) >> 3);
+          dst[size_t(r) * K + k] = buf[((size_t(r >> 4) * (K / 32) + (k >> 5)) * 64 + lane) * 8 + (k & 7)];
+        }
+    }
+  }
+  hipFree(actions);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("probe failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}

@@ -1,0 +1,221 @@
+"""ctypes binding of libpi_ae.so (argument marshalling only).
+
+Every step of the denoise loop runs in the library's HIP kernels; this module
+only turns Python objects (NumPy host arrays for the weights, torch device
+tensors for the call buffers) into the C-ABI's plain pointers and sizes.  If
+the library is missing the import fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpi_ae.so")
+
+PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTATE = range(6)
+
+# symbols declared in include/pi_ae.h
+EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_status_string",
+           "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
+           "pi_ae_debug_time_phase")
+
+
+class PiAeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pi_ae status {status}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("width", ctypes.c_int32), ("mlp_dim", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("action_dim", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("num_steps", ctypes.c_int32),
+                ("t0", ctypes.c_float), ("dt", ctypes.c_float), ("max_batch", ctypes.c_int32),
+                ("max_prefix_len", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("final_norm", ctypes.c_int32)]
+
+
+class Linear(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("b", ctypes.c_void_p)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, Linear) for n in ("attn_mod", "q", "k", "v", "o", "ffn_mod", "gate", "up", "down")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("action_in", Linear), ("time_in", Linear), ("time_out", Linear), ("final_mod", Linear),
+                ("action_out", Linear), ("layers", ctypes.POINTER(LayerWeights))]
+
+
+class PrefixKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pad_mask", ctypes.c_void_p),
+                ("prefix_len", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpi_ae.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m flow_matching_action_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.pi_ae_prepare_weights.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.POINTER(ctypes.c_void_p)]
+    lib.pi_ae_prepare_weights.restype = ctypes.c_int
+    lib.pi_ae_sample.argtypes = [ctypes.c_void_p, ctypes.POINTER(PrefixKV), ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_int32, ctypes.c_void_p]
+    lib.pi_ae_sample.restype = ctypes.c_int
+    lib.pi_ae_destroy.argtypes = [ctypes.c_void_p]
+    lib.pi_ae_destroy.restype = None
+    lib.pi_ae_status_string.argtypes = [ctypes.c_int]
+    lib.pi_ae_status_string.restype = ctypes.c_char_p
+    lib.pi_ae_last_error.argtypes = []
+    lib.pi_ae_last_error.restype = ctypes.c_char_p
+    lib.pi_ae_debug_table.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t]
+    lib.pi_ae_debug_table.restype = ctypes.c_int
+    lib.pi_ae_debug_host_table.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_size_t]
+    lib.pi_ae_debug_host_table.restype = ctypes.c_int
+    lib.pi_ae_debug_probe.argtypes = [ctypes.c_void_p, ctypes.POINTER(PrefixKV), ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_size_t]
+    lib.pi_ae_debug_probe.restype = ctypes.c_int
+    lib.pi_ae_debug_time_phase.argtypes = [ctypes.c_void_p, ctypes.POINTER(PrefixKV), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_debug_time_phase.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PI_AE_OK:
+        lib = load_library()
+        raise PiAeError(status, lib.pi_ae_last_error().decode())
+
+
+def make_config(cfg, max_batch: int, max_prefix_len: int) -> Config:
+    """pi_ae_config from an :class:`inputs.ExpertConfig`-like object."""
+    return Config(cfg.num_layers, cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                  cfg.action_dim, cfg.chunk_len, cfg.num_steps, cfg.t0, cfg.dt, max_batch, max_prefix_len,
+                  cfg.rope_base, cfg.rms_eps, 1 if cfg.final_norm else 0)
+
+
+def _ptr(a):
+    """Host pointer of a NumPy array, device pointer of a torch tensor, NULL for None."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays must be C-contiguous")
+        return a.ctypes.data
+    if hasattr(a, "data_ptr"):
+        if not a.is_contiguous():
+            raise ValueError("device tensors must be contiguous")
+        return a.data_ptr()
+    return int(a)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class _MarshalledWeights:
+    """pi_ae_weights pointing into host arrays that this object keeps alive."""
+
+    def __init__(self, cfg, weights: dict):
+        self.keep = {n: np.ascontiguousarray(a, dtype=np.uint16) for n, a in weights.items()}
+
+        def lin(name, bias=True):
+            return Linear(_ptr(self.keep.get(name + ".w")), _ptr(self.keep.get(name + ".b")) if bias else None)
+
+        self.layers = (LayerWeights * max(cfg.num_layers, 1))()
+        for l in range(cfg.num_layers):
+            p = f"layers.{l}."
+            self.layers[l] = LayerWeights(lin(p + "attn_mod"), lin(p + "q", False), lin(p + "k", False),
+                                          lin(p + "v", False), lin(p + "o", False), lin(p + "ffn_mod"),
+                                          lin(p + "gate", False), lin(p + "up", False), lin(p + "down", False))
+        self.w = Weights(lin("action_in"), lin("time_in"), lin("time_out"), lin("final_mod"), lin("action_out"),
+                         ctypes.cast(self.layers, ctypes.POINTER(LayerWeights)))
+
+
+def host_table(cfg, weights: dict, which: int, n: int, max_batch: int = 1, max_prefix_len: int = 0) -> np.ndarray:
+    """pi_ae_debug_host_table: the preparation's fp64 tables, computed on the host only."""
+    lib = load_library()
+    c = make_config(cfg, max_batch, max_prefix_len)
+    mw = _MarshalledWeights(cfg, weights)
+    out = np.empty(n, np.float32)
+    _check(lib.pi_ae_debug_host_table(ctypes.byref(c), ctypes.byref(mw.w), int(which), out.ctypes.data, out.size))
+    return out
+
+
+class Context:
+    """A prepared expert (owns the library context)."""
+
+    def __init__(self, cfg, weights: dict, max_batch: int, max_prefix_len: int):
+        lib = load_library()
+        self.cfg = cfg
+        self._c = make_config(cfg, max_batch, max_prefix_len)
+        mw = _MarshalledWeights(cfg, weights)
+        handle = ctypes.c_void_p()
+        _check(lib.pi_ae_prepare_weights(ctypes.byref(self._c), ctypes.byref(mw.w), ctypes.byref(handle)))
+        self._h = handle
+        self._lib = lib
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.pi_ae_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _kv(k, v, pad_mask, prefix_len):
+        return PrefixKV(_ptr(k), _ptr(v), _ptr(pad_mask), int(prefix_len))
+
+    def sample(self, k, v, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
+        """Enqueue pi_ae_sample on `stream` (torch tensors on the device)."""
+        kv = self._kv(k, v, pad_mask, prefix_len)
+        _check(self._lib.pi_ae_sample(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
+                                      _stream_handle(stream)))
+
+    def time_phase(self, k, v, pad_mask, noise, actions, batch, prefix_len, phase, iters, stream=None) -> float:
+        """Mean per-launch duration (us) of one phase's kernel, HIP events on `stream`."""
+        kv = self._kv(k, v, pad_mask, prefix_len)
+        us = ctypes.c_float()
+        _check(self._lib.pi_ae_debug_time_phase(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
+                                                int(phase), int(iters), _stream_handle(stream), ctypes.byref(us)))
+        return float(us.value)
+
+    def table(self, which: int, n: int) -> np.ndarray:
+        out = np.empty(n, np.float32)
+        _check(self._lib.pi_ae_debug_table(self._h, int(which), out.ctypes.data, out.size))
+        return out
+
+    def probe(self, k, v, pad_mask, noise, batch, prefix_len, step, layer, phase, which):
+        T = self.cfg.chunk_len
+        M = batch * T
+        shapes = {0: ((M, 1024), np.float32), 1: ((M, 8, 256), np.uint16), 2: ((M, 256), np.uint16),
+                  3: ((M, 256), np.uint16), 4: ((M, 2048), np.uint16), 5: ((M, 4096), np.uint16),
+                  6: ((M, 32), np.float32)}
+        shape, dt = shapes[which]
+        out = np.empty(shape, dt)
+        kv = self._kv(k, v, pad_mask, prefix_len)
+        _check(self._lib.pi_ae_debug_probe(self._h, ctypes.byref(kv), _ptr(noise), int(batch), int(step), int(layer),
+                                           int(phase), int(which), out.ctypes.data, out.nbytes))
+        return out

@@ -1,0 +1,214 @@
+/*
+ * pi_ae.h -- C ABI of libpi_ae.so, the MI355X (gfx950) action-expert
+ * flow-matching denoise loop of pi0.5-style vision-language-action policies.
+ *
+ * What the library computes (Realtime-VLA technical blog, blog.w4k4.me,
+ * section "pi0.5 inference flow"): the VLM runs once and leaves a per-layer
+ * key/value cache of the prefix (images + prompt); the action expert then runs
+ * the flow-matching denoise loop against that cache.  Every denoise step
+ * projects the noisy action chunk (action_in_proj, 32 -> 1024), runs the
+ * 18-layer expert (AdaRMS-modulated attention over prefix + suffix keys and a
+ * GELU-gated MLP, both with gated residuals), projects back (action_out_proj,
+ * 1024 -> 32) to a velocity v_t and takes the Euler step x <- x + dt * v_t.
+ *
+ * The split into a one-time preparation call and a cheap per-call sample
+ * follows the blog's sections "precompute (__init__)" and "CUDA Graph"
+ * (all tables and buffers are built at initialisation; the per-call forward is
+ * "copy inputs, replay the graph").
+ *
+ * Conventions for every entry point:
+ *   - No C++ exception crosses this ABI.  Every call returns a pi_ae_status;
+ *     on failure pi_ae_last_error() gives a message for the calling thread.
+ *   - All arguments are validated before any GPU work is enqueued: a call
+ *     that returns an error has enqueued nothing.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Streams are HIP streams (hipStream_t) passed as void*; NULL is the
+ *     default stream of the current device.
+ */
+#ifndef PI_AE_H
+#define PI_AE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pi_ae_status {
+  PI_AE_OK = 0,
+  PI_AE_EINVAL = 1,        /* a NULL pointer, a size out of range, a misaligned pointer */
+  PI_AE_EUNSUPPORTED = 2,  /* a shape the kernels do not implement (see pi_ae_config) */
+  PI_AE_ENOMEM = 3,        /* device or host allocation failed */
+  PI_AE_EHIP = 4,          /* a HIP runtime call failed */
+  PI_AE_ESTATE = 5         /* the context cannot take this call (e.g. destroyed or failed) */
+} pi_ae_status;
+
+/*
+ * Model and call limits.  Shapes are those of the blog's section "LeRobot
+ * implementation" (Gemma-300M-shaped expert): the kernels implement exactly
+ *   width 1024, mlp_dim 4096, num_heads 8, num_kv_heads 1, head_dim 256,
+ *   action_dim 32, 1 <= chunk_len <= 256,
+ * and return PI_AE_EUNSUPPORTED for anything else.  num_layers >= 1,
+ * num_steps >= 1 (at most 64).  t0 and dt give the timestep schedule
+ * t_k = fp32(t0 + k * dt), k = 0 .. num_steps-1 (dt = -1/num_steps in the
+ * pages; it is a separate field so that a shortened schedule can keep dt).
+ * max_batch and max_prefix_len size the workspaces: a sample call may use any
+ * batch <= max_batch and prefix_len <= max_prefix_len.  rope_base is the RoPE
+ * base (10000), rms_eps the RMS-norm epsilon (1e-6).  final_norm = 1 adds an
+ * AdaRMS norm with its own modulation dense before action_out_proj.
+ */
+typedef struct pi_ae_config {
+  int32_t num_layers;
+  int32_t width;
+  int32_t mlp_dim;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t action_dim;
+  int32_t chunk_len;
+  int32_t num_steps;
+  float t0;
+  float dt;
+  int32_t max_batch;
+  int32_t max_prefix_len;
+  float rope_base;
+  float rms_eps;
+  int32_t final_norm;
+} pi_ae_config;
+
+/* One nn.Linear: weight [out][in] row-major, bias [out] (NULL where the layer
+ * has no bias).  Host pointers to bf16 bit patterns. */
+typedef struct pi_ae_linear {
+  const uint16_t* w;
+  const uint16_t* b;
+} pi_ae_linear;
+
+/* One expert layer.  attn_mod / ffn_mod: the AdaRMS modulation denses
+ * (width -> 3*width, with bias; output split in thirds: scale, shift, gate).
+ * q [heads*head_dim][width], k and v [head_dim][width], o [width][heads*head_dim],
+ * gate and up [mlp_dim][width], down [width][mlp_dim]; these have no bias. */
+typedef struct pi_ae_layer_weights {
+  pi_ae_linear attn_mod, q, k, v, o, ffn_mod, gate, up, down;
+} pi_ae_layer_weights;
+
+/* The unfolded expert.  action_in [width][action_dim] + b; time_in and
+ * time_out [width][width] + b (the time MLP: cond = SiLU(time_out(SiLU(
+ * time_in(emb(t)))))); final_mod [3*width][width] + b (read only when
+ * final_norm = 1); action_out [action_dim][width] + b; layers[num_layers]. */
+typedef struct pi_ae_weights {
+  pi_ae_linear action_in, time_in, time_out, final_mod, action_out;
+  const pi_ae_layer_weights* layers;
+} pi_ae_weights;
+
+/* The VLM prefix cache for one call (device memory, read only).
+ *   k, v:     bf16 [num_layers][batch][prefix_len][head_dim], contiguous,
+ *             16-byte aligned; keys already rotated by the producer's RoPE.
+ *   pad_mask: u8 [batch][prefix_len], nonzero = valid key; NULL = all valid.
+ *   prefix_len: P, 0 <= P <= max_prefix_len. */
+typedef struct pi_ae_prefix_kv {
+  const void* k;
+  const void* v;
+  const uint8_t* pad_mask;
+  int32_t prefix_len;
+} pi_ae_prefix_kv;
+
+typedef struct pi_ae_ctx pi_ae_ctx;
+
+/*
+ * One-time weight preparation (blog sections 3.2 "simplifying the
+ * computational graph" and "precompute (__init__)"):
+ *   - the time embedding and time MLP for the num_steps timesteps, and every
+ *     layer's AdaRMS scale/shift/gate (and the final norm's) are tabulated;
+ *   - each AdaRMS shift is folded into a bias of the following linear
+ *     (c = shift @ W^T), the scale stays a per-channel factor;
+ *   - Q, K and V are fused into one [(heads+2)*head_dim][width] matrix whose
+ *     RoPE is applied in the GEMM epilogue; gate and up are fused likewise;
+ *   - dt is applied to action_out_proj's output in the fp32 epilogue;
+ *   - the RoPE cos/sin table for positions 0 .. max_prefix_len+chunk_len-1.
+ * Host arithmetic is fp64; tables are stored fp32, weights stay bf16.
+ * Synchronous on the current HIP device; reads the host arrays only during the
+ * call.  The library owns everything it allocates; *out is written only on
+ * success.  Errors: EINVAL (NULL cfg/w/out/weight pointer, bad sizes),
+ * EUNSUPPORTED (shapes other than the ones above), ENOMEM, EHIP.
+ */
+pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_ae_weights* w, pi_ae_ctx** out);
+
+/*
+ * Run the denoise loop for `batch` episodes (the blog's "sample_actions"):
+ * x <- noise; for k in 0..num_steps-1: x <- x + dt * v(x, t_k); actions <- x.
+ *   kv:      the prefix cache (see pi_ae_prefix_kv).
+ *   noise:   device fp32 [batch][chunk_len][action_dim], 16-byte aligned.
+ *   actions: device fp32 [batch][chunk_len][action_dim], 16-byte aligned;
+ *            may equal noise (in place).
+ *   batch:   0 <= batch <= max_batch (0 does nothing).
+ *   stream:  hipStream_t (void*); the call is asynchronous and stream-ordered.
+ * Suffix token j of episode b sits at RoPE position n_valid[b] + j, where
+ * n_valid[b] is the number of valid prefix keys of that episode.
+ * All inputs must stay alive and unmodified until the stream has passed the
+ * call.  One call in flight per context: concurrent calls on one context (on
+ * any streams) race on its workspaces; use one context per concurrent stream.
+ * The step sequence is captured as a hipGraph per (batch, prefix_len) on first
+ * use and replayed afterwards.  Errors: EINVAL (NULL ctx/kv/noise/actions,
+ * batch or prefix_len out of range, misaligned pointers), ESTATE (ctx
+ * unusable), EHIP (a launch failed).  Device faults surface at the caller's
+ * next synchronisation.
+ */
+pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
+                          int32_t batch, void* stream);
+
+/* Synchronise the context's device, then free everything it owns.  NULL is a no-op. */
+void pi_ae_destroy(pi_ae_ctx* ctx);
+
+/* Static string for a status code. */
+const char* pi_ae_status_string(pi_ae_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pi_ae_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Test-only exports (unstable; used by the parity tests).
+ * ------------------------------------------------------------------------ */
+
+/* Copy one prepared fp32 table to host memory.  which: 0 = attn (1+scale)
+ * [S][L][width], 1 = attn gate [S][L][width], 2 = ffn (1+scale), 3 = ffn gate,
+ * 4 = final (1+scale) [S][width], 5 = c_out [S][action_dim] (shift @ W_out^T +
+ * b_out), 6 = c_qkv [S][L][(heads+2)*head_dim] (natural q|k|v column order),
+ * 7 = c_gu [S][L][2*mlp_dim] (natural gate|up order), 8 = timesteps [S],
+ * 9 = cond [S][width].  n_floats must equal the table's size.  Synchronous. */
+pi_ae_status pi_ae_debug_table(pi_ae_ctx* ctx, int32_t which, float* host_out, size_t n_floats);
+
+/* The same tables computed by the host half of pi_ae_prepare_weights alone
+ * (fp64 arithmetic, no GPU work, no allocation on the device): lets the
+ * preparation be checked on a machine without a GPU.  Same `which` codes. */
+pi_ae_status pi_ae_debug_host_table(const pi_ae_config* cfg, const pi_ae_weights* w, int32_t which,
+                                    float* host_out, size_t n_floats);
+
+/* Run the loop only up to a point and copy an intermediate to host memory.
+ * Runs steps 0..step-1 fully, then in step `step` the layers before `layer`
+ * and, in layer `layer`, the phases up to and including `phase`
+ * (0 = step input / action_in, 1 = QKV+RoPE, 2 = attention, 3 = O + gated
+ * residual, 4 = gate/up, 5 = down + gated residual).  which: 0 = h fp32
+ * [M][width], 1 = Q bf16 [M][heads][head_dim], 2 = K_s bf16 [M][head_dim],
+ * 3 = V_s bf16 [M][head_dim], 4 = O bf16 [M][heads*head_dim], 5 = m bf16
+ * [M][mlp_dim], 6 = x fp32 [M][action_dim]; M = batch*chunk_len, rows in
+ * natural order.  Synchronous; uses the null stream. */
+pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, int32_t batch,
+                               int32_t step, int32_t layer, int32_t phase, int32_t which, void* host_out,
+                               size_t n_bytes);
+
+/* Time one phase's kernel: after one full pass of the loop (so that every
+ * intermediate holds real values; its result lands in `actions`), launch the
+ * kernel of `phase` (numbering as in pi_ae_debug_probe) `iters` times on
+ * `stream`, cycling through the layers (and steps) so that each launch
+ * streams that layer's weights as it does inside the loop, with a HIP event
+ * recorded right before and right after each launch.  *avg_us = mean of the
+ * per-launch event intervals.  Synchronises `stream`.  Same argument rules as
+ * pi_ae_sample, plus batch >= 1 and 1 <= iters <= 100000. */
+pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
+                                    int32_t batch, int32_t phase, int32_t iters, void* stream, float* avg_us);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PI_AE_H */

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads and exports every symbol
+the header declares, arguments are validated (with the documented status codes)
+before any device work, and the host half of the weight preparation (fp64
+tabulation and shift folding) equals the oracle's folded tables."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from flow_matching_action_amd import inputs
+from flow_matching_action_amd import pi_ae
+from oracle import pi_ae_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pi_ae.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(pi_ae.LIB_PATH), reason="libpi_ae.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pi_ae_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(pi_ae.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(pi_ae.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {pi_ae.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (pi_ae_\w+)", out))
+    assert exported == set(header_functions())
+
+
+@needs_lib
+def test_status_strings_and_null_arguments():
+    lib = pi_ae.load_library()
+    assert lib.pi_ae_status_string(0) == b"ok"
+    assert lib.pi_ae_status_string(pi_ae.PI_AE_EUNSUPPORTED) == b"unsupported shape"
+    assert lib.pi_ae_status_string(99) == b"unknown status"
+    assert lib.pi_ae_prepare_weights(None, None, None) == pi_ae.PI_AE_EINVAL
+    assert b"non-NULL" in lib.pi_ae_last_error()
+    kv = pi_ae.PrefixKV(None, None, None, 0)
+    assert lib.pi_ae_sample(None, ctypes.byref(kv), None, None, 1, None) == pi_ae.PI_AE_EINVAL
+    assert lib.pi_ae_destroy(None) is None
+
+
+def _tiny_weights(cfg):
+    return {n: np.zeros(s, np.uint16) for n, s in inputs.weight_shapes(cfg)}
+
+
+@needs_lib
+@pytest.mark.parametrize("field,value,status", [
+    ("width", 512, pi_ae.PI_AE_EUNSUPPORTED),
+    ("num_kv_heads", 2, pi_ae.PI_AE_EUNSUPPORTED),
+    ("head_dim", 128, pi_ae.PI_AE_EUNSUPPORTED),
+    ("num_layers", 0, pi_ae.PI_AE_EINVAL),
+    ("num_steps", 0, pi_ae.PI_AE_EINVAL),
+    ("chunk_len", 0, pi_ae.PI_AE_EINVAL),
+    ("chunk_len", 257, pi_ae.PI_AE_EINVAL),
+    ("max_batch", 0, pi_ae.PI_AE_EINVAL),
+    ("max_prefix_len", -1, pi_ae.PI_AE_EINVAL),
+    ("rope_base", 0.0, pi_ae.PI_AE_EINVAL),
+    ("final_norm", 2, pi_ae.PI_AE_EINVAL),
+])
+def test_config_validation(field, value, status):
+    """Invalid configs are rejected before any allocation (no GPU needed)."""
+    cfg = inputs.WORKLOADS["c1"].cfg
+    c = pi_ae.make_config(cfg, 1, 16)
+    setattr(c, field, value)
+    mw = pi_ae._MarshalledWeights(cfg, _tiny_weights(cfg))
+    lib = pi_ae.load_library()
+    h = ctypes.c_void_p()
+    assert lib.pi_ae_prepare_weights(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == status
+    assert h.value is None
+    assert lib.pi_ae_last_error() != b""
+
+
+@needs_lib
+def test_missing_weight_pointer():
+    cfg = inputs.WORKLOADS["c1"].cfg
+    w = _tiny_weights(cfg)
+    del w["layers.1.up.w"]
+    with pytest.raises(pi_ae.PiAeError) as e:
+        pi_ae.host_table(cfg, w, 8, cfg.num_steps)
+    assert e.value.status == pi_ae.PI_AE_EINVAL and "layer 1" in str(e.value)
+    w = _tiny_weights(cfg)
+    del w["final_mod.b"]
+    with pytest.raises(pi_ae.PiAeError):
+        pi_ae.host_table(cfg, w, 8, cfg.num_steps)
+    # without the final norm its modulation is not needed
+    pi_ae.host_table(cfg.replace(final_norm=False), w, 8, cfg.num_steps)
+
+
+@needs_lib
+def test_host_tables_match_oracle():
+    """The library's fp64 preparation equals the oracle's folded tables
+    (tabulated time MLP, modulation split, shift folded into c = shift @ W^T)."""
+    cfg = inputs.WORKLOADS["c1"].cfg.replace(num_steps=3, dt=-1.0 / 3)
+    wb = inputs.make_weights(cfg, seed=3, std=0.05, cache=False)
+    W = O.Weights(wb, cfg)
+    tabs = O.folded_tables(W)
+    S, L, D = cfg.num_steps, cfg.num_layers, cfg.width
+
+    def get(which, n):
+        return pi_ae.host_table(cfg, wb, which, n).astype(np.float64)
+
+    def close(got, want, rtol=2e-6):
+        want = np.asarray(want, np.float64).ravel()
+        err = np.max(np.abs(got - want))
+        assert err <= rtol * max(1.0, np.max(np.abs(want))), err
+
+    close(get(8, S), tabs["t"])
+    close(get(9, S * D), np.concatenate(tabs["cond"]))
+    close(get(0, S * L * D), [tabs["attn"][k][l]["scale1"] for k in range(S) for l in range(L)])
+    close(get(1, S * L * D), [tabs["attn"][k][l]["gate"] for k in range(S) for l in range(L)])
+    close(get(2, S * L * D), [tabs["ffn"][k][l]["scale1"] for k in range(S) for l in range(L)])
+    close(get(3, S * L * D), [tabs["ffn"][k][l]["gate"] for k in range(S) for l in range(L)])
+    close(get(4, S * D), [tabs["final"][k]["scale1"] for k in range(S)])
+    close(get(5, S * 32), [tabs["final"][k]["c_out"] for k in range(S)])
+    close(get(6, S * L * 2560), [tabs["attn"][k][l]["c_qkv"] for k in range(S) for l in range(L)])
+    close(get(7, S * L * 8192), [tabs["ffn"][k][l]["c_gu"] for k in range(S) for l in range(L)])
+    # without the final norm, c_out is the bare output bias
+    cfg2 = cfg.replace(final_norm=False)
+    close(pi_ae.host_table(cfg2, wb, 5, S * 32).astype(np.float64),
+          np.tile(O.bf16_to_float(wb["action_out.b"]), S))

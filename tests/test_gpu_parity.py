@@ -1,0 +1,275 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Bar (per the target of this path): on the final actions, relative L2 error
+<= 1e-2 and max-abs error <= 5e-2 against the fp64 oracle, on the same
+seeded inputs; the relative L2 error of the integrated displacement
+(x_final - x_0) is checked too (<= 2e-2), because x_final is dominated by
+the noise that both sides share.  Intermediates of one step are compared
+phase by phase (bf16 storage of activations gives ~0.4% per element, so
+those use relative L2 <= 2e-2).  Invariances that hold exactly for this
+implementation (no atomics, row-independent GEMM tiles) are checked bitwise.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from flow_matching_action_amd import inputs
+from flow_matching_action_amd import pi_ae
+from oracle import pi_ae_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL_L2 = 1e-2
+TOL_MAX_ABS = 5e-2
+TOL_DELTA_REL_L2 = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    pi_ae.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def to_dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+
+
+class Run:
+    """Device copies of one workload's call inputs."""
+
+    def __init__(self, k, v, mask, noise):
+        self.k, self.v, self.mask, self.noise = k, v, mask, noise
+        self.dk, self.dv = to_dev(k), to_dev(v)
+        self.dmask = to_dev(mask)
+        self.dnoise = to_dev(noise)
+        self.B, self.P = noise.shape[0], (k.shape[2] if k is not None else 0)
+
+    def sample(self, ctx, stream=None, actions=None):
+        out = actions if actions is not None else torch.empty_like(self.dnoise)
+        ctx.sample(self.dk, self.dv, self.dmask, self.dnoise, out, self.B, self.P, stream)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+
+def check_actions(x_gpu, x_ref, noise, tag):
+    e = rel_l2(x_gpu, x_ref)
+    mx = float(np.max(np.abs(x_gpu - x_ref)))
+    d = rel_l2(x_gpu - noise, x_ref - noise)
+    log(f"[{tag}] rel_l2={e:.3e} max_abs={mx:.3e} delta_rel_l2={d:.3e}")
+    assert np.all(np.isfinite(x_gpu))
+    assert e <= TOL_REL_L2 and mx <= TOL_MAX_ABS and d <= TOL_DELTA_REL_L2, (e, mx, d)
+
+
+# ------------------------------------------------------------------ per-phase (c1)
+def oracle_step0_intermediates(wb, cfg, k, v, mask, noise):
+    """Layer-0 intermediates of step 0 for episode 0, from the oracle's pieces."""
+    W = O.Weights(wb, cfg)
+    t = O.timesteps(cfg.num_steps, cfg.t0, cfg.dt)[0]
+    cond = O.time_condition(W, t)
+    x = noise[0].astype(np.float64)
+    h0 = x @ W["action_in.w"].T + W["action_in.b"]
+    pk, pv = O.bf16_to_float(k[0, 0]), O.bf16_to_float(v[0, 0])
+    valid = mask[0] != 0
+    T, H, d = cfg.chunk_len, cfg.num_heads, cfg.head_dim
+    pos = valid.sum() + np.arange(T)
+    s, sh, g = O.modulation(W.layer(0, "attn_mod.w"), W.layer(0, "attn_mod.b"), cond)
+    u = O.adarms(h0, s, sh, cfg.rms_eps)
+    q = O.rope((u @ W.layer(0, "q.w").T).reshape(T, H, d).transpose(1, 0, 2), pos, cfg.rope_base).transpose(1, 0, 2)
+    ks = O.rope(u @ W.layer(0, "k.w").T, pos, cfg.rope_base)
+    vs = u @ W.layer(0, "v.w").T
+    keys, vals = np.concatenate([pk, ks]), np.concatenate([pv, vs])
+    o = O.attention(q, keys, vals, np.concatenate([valid, np.ones(T, bool)]), d ** -0.5).reshape(T, H * d)
+    h1 = h0 + (o @ W.layer(0, "o.w").T) * g
+    s2, sh2, g2 = O.modulation(W.layer(0, "ffn_mod.w"), W.layer(0, "ffn_mod.b"), cond)
+    u2 = O.adarms(h1, s2, sh2, cfg.rms_eps)
+    m = O.gelu_tanh(u2 @ W.layer(0, "gate.w").T) * (u2 @ W.layer(0, "up.w").T)
+    h2 = h1 + (m @ W.layer(0, "down.w").T) * g2
+    return dict(h0=h0, q=q, ks=ks, vs=vs, o=o, h1=h1, m=m, h2=h2)
+
+
+@pytest.fixture(scope="module")
+def c1_setup():
+    w = inputs.WORKLOADS["c1"]
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    ctx = pi_ae.Context(w.cfg, wb, w.batch, w.prefix_len)
+    return w, wb, Run(k, v, mask, noise), ctx
+
+
+def test_prepared_tables_match_host(c1_setup):
+    w, wb, run, ctx = c1_setup
+    S, L = w.cfg.num_steps, w.cfg.num_layers
+    for which, n in [(0, S * L * 1024), (6, S * L * 2560), (7, S * L * 8192), (5, S * 32)]:
+        np.testing.assert_array_equal(ctx.table(which, n), pi_ae.host_table(w.cfg, wb, which, n))
+
+
+def test_c1_phase_by_phase(c1_setup):
+    w, wb, run, ctx = c1_setup
+    ref = oracle_step0_intermediates(wb, w.cfg, run.k, run.v, run.mask, run.noise)
+    bf = lambda a: O.bf16_to_float(a)
+
+    def probe(phase, which):
+        log(f"probe phase={phase} which={which}")
+        return ctx.probe(run.dk, run.dv, run.dmask, run.dnoise, 1, run.P, 0, 0, phase, which)
+
+    h0 = probe(0, 0)
+    assert rel_l2(h0, ref["h0"]) < 1e-5
+    q = bf(probe(1, 1))
+    ks = bf(probe(1, 2))
+    vs = bf(probe(1, 3))
+    for name, got in [("q", q), ("ks", ks), ("vs", vs)]:
+        e = rel_l2(got, ref[name])
+        log(f"  {name}: rel_l2={e:.3e}")
+        assert e < 2e-2, name
+    o = bf(probe(2, 4))
+    e = rel_l2(o, ref["o"])
+    log(f"  o: rel_l2={e:.3e}")
+    assert e < 2e-2
+    h1 = probe(3, 0)
+    e = rel_l2(h1 - h0, ref["h1"] - ref["h0"])
+    log(f"  h1-h0: rel_l2={e:.3e}")
+    assert e < 2e-2
+    m = bf(probe(4, 5))
+    e = rel_l2(m, ref["m"])
+    log(f"  m: rel_l2={e:.3e}")
+    assert e < 2e-2
+    h2 = probe(5, 0)
+    e = rel_l2(h2 - h1, ref["h2"] - ref["h1"])
+    log(f"  h2-h1: rel_l2={e:.3e}")
+    assert e < 2e-2
+
+
+def test_c1_end_to_end(c1_setup):
+    w, wb, run, ctx = c1_setup
+    x_ref = O.sample(wb, w.cfg, run.k, run.v, run.mask, run.noise)
+    check_actions(run.sample(ctx), x_ref, run.noise, "c1")
+
+
+# ------------------------------------------------------------------ full configs
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_batch1_configs(name):
+    w = inputs.WORKLOADS[name]
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    log(f"[{name}] preparing")
+    ctx = pi_ae.Context(w.cfg, wb, w.batch, w.prefix_len)
+    run = Run(k, v, mask, noise)
+    x = run.sample(ctx)
+    t0 = time.time()
+    x_ref = O.sample(wb, w.cfg, k, v, mask, noise)
+    log(f"[{name}] oracle {time.time() - t0:.1f}s")
+    check_actions(x, x_ref, noise, name)
+    ctx.close()
+
+
+def test_c5_batched_sampled_episodes():
+    """32 episodes at once; the oracle checks three of them one by one (the
+    episodes are independent, so each alone is the exact reference)."""
+    w = inputs.WORKLOADS["c5"]
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    log("[c5] preparing")
+    ctx = pi_ae.Context(w.cfg, wb, w.batch, w.prefix_len)
+    x = Run(k, v, mask, noise).sample(ctx)
+    assert np.all(np.isfinite(x))
+    W = O.Weights(wb, w.cfg)
+    for b in [0, 13, 31]:
+        t0 = time.time()
+        x_ref = O.sample(wb, w.cfg, k[:, b:b + 1], v[:, b:b + 1], mask[b:b + 1], noise[b:b + 1], weights=W)
+        log(f"[c5] episode {b} oracle {time.time() - t0:.1f}s")
+        check_actions(x[b:b + 1], x_ref, noise[b:b + 1], f"c5[{b}]")
+    ctx.close()
+
+
+# ------------------------------------------------------------------ edge cases
+SMALL = inputs.ExpertConfig(num_layers=2, num_steps=2, dt=-0.5)
+
+
+@pytest.fixture(scope="module")
+def small_ctx():
+    wb = inputs.make_weights(SMALL, seed=5, cache=False)
+    return wb, pi_ae.Context(SMALL, wb, max_batch=4, max_prefix_len=96)
+
+
+def test_ragged_masks_and_batch(small_ctx):
+    """Per-episode masks with holes, different valid counts, and no prefix at all."""
+    wb, ctx = small_ctx
+    B, P = 3, 70
+    k, v = inputs.make_prefix_kv(SMALL, B, P, seed=7)
+    rng = np.random.default_rng(8)
+    mask = (rng.random((B, P)) < 0.7).astype(np.uint8)
+    mask[2] = 0  # an episode with every prefix key masked
+    noise = inputs.make_noise(SMALL, B, seed=9)
+    x = Run(k, v, mask, noise).sample(ctx)
+    x_ref = O.sample(wb, SMALL, k, v, mask, noise)
+    check_actions(x, x_ref, noise, "ragged")
+    # no prefix: P = 0, NULL k/v
+    k0 = np.zeros((SMALL.num_layers, 2, 0, 256), np.uint16)
+    noise2 = noise[:2].copy()
+    run0 = Run(None, None, None, noise2)
+    out = torch.empty_like(run0.dnoise)
+    ctx.sample(None, None, None, run0.dnoise, out, 2, 0)
+    torch.cuda.synchronize()
+    check_actions(out.cpu().numpy(), O.sample(wb, SMALL, k0, k0, None, noise2), noise2, "no-prefix")
+
+
+def test_masked_garbage_batch_independence_and_repeatability(small_ctx):
+    wb, ctx = small_ctx
+    B, P = 4, 96
+    k, v = inputs.make_prefix_kv(SMALL, B, P, seed=10)
+    mask = inputs.make_pad_mask(B, P, [96, 80, 33, 1])
+    noise = inputs.make_noise(SMALL, B, seed=11)
+    base = Run(k, v, mask, noise).sample(ctx)
+    # garbage (huge values, inf, nan) in masked prefix positions changes nothing
+    k2, v2 = k.copy(), v.copy()
+    k2[:, mask == 0] = inputs.f32_to_bf16_bits(np.array([3e4], np.float32))[0]
+    v2[:, mask == 0] = np.uint16(0x7FC0)  # NaN
+    np.testing.assert_array_equal(Run(k2, v2, mask, noise).sample(ctx), base)
+    # each episode alone gives bitwise the same result
+    for b in range(B):
+        alone = Run(np.ascontiguousarray(k[:, b:b + 1]), np.ascontiguousarray(v[:, b:b + 1]),
+                    mask[b:b + 1].copy(), noise[b:b + 1].copy()).sample(ctx)
+        np.testing.assert_array_equal(alone, base[b:b + 1])
+    # graph replays with eager work in between are bitwise repeatable
+    run = Run(k, v, mask, noise)
+    for _ in range(3):
+        torch.randn(1 << 20, device="cuda").sum().item()
+        np.testing.assert_array_equal(run.sample(ctx), base)
+
+
+def test_in_place_zero_batch_and_errors(small_ctx):
+    wb, ctx = small_ctx
+    B, P = 2, 40
+    k, v = inputs.make_prefix_kv(SMALL, B, P, seed=12)
+    noise = inputs.make_noise(SMALL, B, seed=13)
+    run = Run(k, v, None, noise)
+    ref = run.sample(ctx)
+    buf = run.dnoise.clone()
+    ctx.sample(run.dk, run.dv, None, buf, buf, B, P)  # actions aliases noise
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(buf.cpu().numpy(), ref)
+    ctx.sample(run.dk, run.dv, None, run.dnoise, run.dnoise, 0, P)  # batch 0: nothing happens
+    with pytest.raises(pi_ae.PiAeError) as e:
+        ctx.sample(run.dk, run.dv, None, run.dnoise, buf, 5, P)
+    assert e.value.status == pi_ae.PI_AE_EINVAL
+    with pytest.raises(pi_ae.PiAeError):
+        ctx.sample(run.dk, run.dv, None, run.dnoise, buf, B, 97)
+    with pytest.raises(ValueError):
+        ctx.sample(run.dk, run.dv, None, run.dnoise[:, :, 1:], buf, B, P)  # not contiguous -> binding refuses
+    mis = torch.empty(run.dnoise.numel() + 1, device="cuda")[1:]
+    with pytest.raises(pi_ae.PiAeError) as e:
+        ctx.sample(run.dk, run.dv, None, run.dnoise, mis, B, P)
+    assert "aligned" in str(e.value)
