@@ -1,0 +1,199 @@
+"""Benchmark of the action-expert denoise loop on one MI355X.
+
+One bench step = one pi_ae_sample call: the whole 10-step flow-matching loop of
+the 18-layer expert over one batch (inputs resident in HBM).  Prints ONE JSON
+line (rank 0).  Default workload: batch 1, 1 camera view (256 prefix keys),
+chunk 63.
+
+  python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu]
+
+Reported beside the throughput: the roofline of the dominant kernel (the
+gate/up GEMM at batch 1, algorithmic bytes = its bf16 weights per launch,
+timed live with HIP events, one event pair per launch, cycling over layers),
+and the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+
+# bf16 weight bytes streamed per launch of each phase's kernel (one layer)
+PHASE_WEIGHT_BYTES = {1: 2560 * 1024 * 2, 3: 1024 * 2048 * 2, 4: 8192 * 1024 * 2, 5: 1024 * 4096 * 2}
+PHASE_NAMES = {0: "k_io", 1: "k_gemm<qkv>", 2: "k_attn", 3: "k_gemm<o>", 4: "k_gemm<gate_up>", 5: "k_gemm<down>"}
+PMC_FILE = os.path.join(ROOT, "profiles", "gate_up_c2_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "flow_matching_action_amd", "csrc", "pi_ae_kernels.hip")
+
+
+def algorithmic_bytes_per_step(w) -> float:
+    """Weights streamed once per Euler step + each valid prefix K/V once per layer."""
+    cfg = w.cfg
+    per_layer = sum(PHASE_WEIGHT_BYTES.values())
+    io = 2 * 32 * 1024 * 2
+    kv = cfg.num_layers * w.batch * w.n_valid * 256 * 2 * 2
+    return cfg.num_layers * per_layer + io + kv
+
+
+def algorithmic_flops_per_step(w) -> float:
+    cfg = w.cfg
+    M = w.batch * cfg.chunk_len
+    gemm = 2 * M * (1024 * 2560 + 2048 * 1024 + 1024 * 8192 + 4096 * 1024) * cfg.num_layers
+    gemm += 2 * M * (32 * 1024 * 2)
+    attn = 4 * 8 * cfg.chunk_len * (w.n_valid + cfg.chunk_len) * 256 * w.batch * cfg.num_layers
+    return gemm + attn
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, wb, k, v, mask, noise, target_s: float = 12.0):
+    """The CPU oracle (fp32 mode) on a bounded sample: whole chunks of episode 0."""
+    import numpy as np
+    from oracle import pi_ae_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    W = O.Weights(wb, w.cfg, np.float32)
+    args = (k[:, :1], v[:, :1], mask[:1], noise[:1])
+    times = []
+    t_start = time.time()
+    while True:
+        t0 = time.time()
+        O.sample(wb, w.cfg, *args, dtype=np.float32, weights=W)
+        times.append(time.time() - t0)
+        if time.time() - t_start >= target_s or len(times) >= 5:
+            break
+    per_chunk = statistics.median(times)
+    return {"value": w.cfg.num_steps / per_chunk, "unit": "denoise steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} full {w.cfg.num_steps}-step chunk(s) of episode 0 of this workload, "
+                      f"NumPy fp32, median {per_chunk * 1e3:.0f} ms/chunk"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--kernel-iters", type=int, default=360)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the denoise loop on exactly one GPU; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from flow_matching_action_amd import inputs, pi_ae
+
+    w = inputs.WORKLOADS[args.workload]
+    cfg = w.cfg
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    print(f"bench: workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    ctx = pi_ae.Context(cfg, wb, w.batch, w.prefix_len)
+    dev = torch.device("cuda:0")
+    dk = torch.from_numpy(k.view(np.int16)).to(dev)
+    dv = torch.from_numpy(v.view(np.int16)).to(dev)
+    dm = torch.from_numpy(mask).to(dev)
+    dn = torch.from_numpy(noise).to(dev)
+    out = torch.empty_like(dn)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        ctx.sample(dk, dv, dm, dn, out, w.batch, w.prefix_len, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        ctx.sample(dk, dv, dm, dn, out, w.batch, w.prefix_len, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    median_us = statistics.median(per_call_ms) * 1e3
+    p99_us = float(np.percentile(per_call_ms, 99)) * 1e3
+    steps_per_s = cfg.num_steps * w.batch / (ms_per_step * 1e-3)
+    print(f"bench: {ms_per_step * 1e3:.1f} us/chunk (median {median_us:.1f}, p99 {p99_us:.1f})",
+          file=sys.stderr, flush=True)
+
+    # dominant kernel, timed live on the same stream with one event pair per launch
+    phase_us = {}
+    for ph in range(6):
+        phase_us[ph] = ctx.time_phase(dk, dv, dm, dn, out, w.batch, w.prefix_len, ph, args.kernel_iters, stream)
+    print("bench: per-launch us " + ", ".join(f"{PHASE_NAMES[p]}={t:.2f}" for p, t in phase_us.items()),
+          file=sys.stderr, flush=True)
+    bytes_step = algorithmic_bytes_per_step(w)
+    flops_step = algorithmic_flops_per_step(w)
+    chunk_s = ms_per_step * 1e-3
+    if w.batch == 1:
+        dom = 4
+        achieved = PHASE_WEIGHT_BYTES[dom] / (phase_us[dom] * 1e-6) / 1e9
+        roof = {"kernel": PHASE_NAMES[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        if os.path.exists(PMC_FILE):
+            with open(PMC_FILE) as f:
+                pmc = json.load(f)
+            if pmc.get("kernel_source_sha256_16") == kernel_source_hash() and pmc.get("workload") == w.name:
+                roof["traffic"] = pmc.get("hbm_bytes_per_launch")
+        whole_frac = bytes_step * cfg.num_steps / chunk_s / (HBM_PEAK_GBS * 1e9)
+    else:
+        dom = 4
+        flops = 2 * w.batch * cfg.chunk_len * 1024 * 8192
+        achieved = flops / (phase_us[dom] * 1e-6) / 1e12
+        roof = {"kernel": PHASE_NAMES[dom], "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": None}
+        whole_frac = flops_step * cfg.num_steps / chunk_s / (MFMA_BF16_PEAK_TFS * 1e12)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, wb, k, v, mask, noise)
+        if w.batch > 1:
+            cpu["sample"] += " (one episode; value is per-episode steps/s)"
+    ctx.close()
+    line = {
+        "metric": "denoise steps/s (10-step action chunk, 18-layer expert); us per chunk; roofline fraction",
+        "value": round(steps_per_s, 1),
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": w.batch, "chunk_len": cfg.chunk_len,
+                   "prefix_len": w.prefix_len, "valid_prefix": w.n_valid, "layers": cfg.num_layers,
+                   "euler_steps": cfg.num_steps},
+        "us_per_chunk": {"mean": round(ms_per_step * 1e3, 1), "median": round(median_us, 1), "p99": round(p99_us, 1)},
+        "whole_loop_roofline_frac": round(whole_frac, 4),
+        "per_launch_us": {PHASE_NAMES[p]: round(t, 3) for p, t in phase_us.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
