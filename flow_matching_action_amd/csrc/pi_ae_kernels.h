@@ -56,23 +56,30 @@ struct GemmParams {
   const float* gate;      // residual modes: per-column gate [1024]
   float* h_out;           // residual modes: fp32 residual stream
   uint16_t* q_out;        // QKV: Q [M][8][256]
-  uint16_t* k_out;        // QKV: K_s [M][256]
-  uint16_t* v_out;        // QKV: V_s [M][256]
-  const float2* rope;     // (cos, sin) [pos][128]
+  const float* inv_freq;  // RoPE inverse frequencies [128]
   const int* n_valid;     // [B]
   int T;                  // chunk length (rows per episode)
+  int P, nkb;             // prefix length, 32-key blocks per episode of the packed K/V
+  uint16_t* kp;           // QKV: packed K of this layer (suffix keys written here)
+  uint16_t* vp;           // QKV: packed V of this layer
   uint16_t* m_out;        // GU: m, fragment-major [Mpad/16][128][64][8]
 };
 
 struct AttnParams {
-  const DevArgs* da;
-  size_t layer_off;       // element offset of this layer in the prefix K/V: l * B * P * 256
   const uint16_t* q;      // [M][8][256]
-  const uint16_t* ks;     // [M][256]
-  const uint16_t* vs;     // [M][256]
-  const int* n_valid;
+  const uint16_t* kp;     // packed K of this layer [B][nkb][16][64][8]
+  const uint16_t* vp;     // packed V of this layer [B][nkb][16][64][8]
+  const float* kbias;     // [B][nkb*32]: 0 valid, -inf masked / padding
   uint16_t* o;            // fragment-major [Mpad/16][64][64][8]
-  int B, T, P;
+  int B, T, P, nkb;
+};
+
+struct PackParams {
+  const DevArgs* da;
+  uint16_t* kp;           // [L][B][nkb][16][64][8]
+  uint16_t* vp;
+  float* kbias;           // [B][nkb*32]
+  int B, P, T, nkb;
 };
 
 struct ArgsParams {
@@ -86,6 +93,7 @@ hipError_t launch_args(const ArgsParams& p, hipStream_t s);
 hipError_t launch_io(const IoParams& p, hipStream_t s);
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_pack(const PackParams& p, int L, hipStream_t s);
 hipError_t launch_o(const GemmParams& p, hipStream_t s);
 hipError_t launch_gu(const GemmParams& p, hipStream_t s);
 hipError_t launch_down(const GemmParams& p, hipStream_t s);

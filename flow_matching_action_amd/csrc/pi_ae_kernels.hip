@@ -50,6 +50,23 @@ __device__ __forceinline__ size_t afrag_index(int row, int k, int KB) {
   return ((size_t(row >> 4) * KB + (k >> 5)) * 64 + lane) * 8 + (k & 7);
 }
 
+// Packed per-layer K/V of one call, 32-key blocks of 16 KiB per episode:
+//   K: [b][key/32][mk = (key%32)/16][ks = d/32][lane][8] with lane = key%16 +
+//      16 ((d%32)/8): the A operand of S^T = K Q^T, one 1 KiB fragment per (mk, ks);
+//   V: [b][key/32][md = d/16][lane][8] with lane = d%16 + 16 g, where the 8
+//      values of group g are keys 4g..4g+3 and 16+4g..16+4g+3 of the block: the
+//      A operand of O^T = V^T P^T in the key order the probabilities sit in.
+__device__ __forceinline__ size_t kpack_index(int b, int key, int d, int nkb) {
+  const int w32 = key & 31;
+  const int lane = (w32 & 15) + 16 * ((d & 31) >> 3);
+  return ((size_t(b) * nkb + (key >> 5)) * 16 + (w32 >> 4) * 8 + (d >> 5)) * 512 + lane * 8 + (d & 7);
+}
+__device__ __forceinline__ size_t vpack_index(int b, int key, int d, int nkb) {
+  const int kk = key & 31, r4 = kk & 15;
+  const int lane = (d & 15) + 16 * (r4 >> 2);
+  return ((size_t(b) * nkb + (key >> 5)) * 16 + (d >> 4)) * 512 + lane * 8 + (kk >> 4) * 4 + (r4 & 3);
+}
+
 // ---------------------------------------------------------------------------
 // Per-call staging: publish the call's pointers to the graph and count each
 // episode's valid prefix keys (the suffix RoPE positions start there; the
@@ -219,6 +236,38 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   }
 #pragma unroll
   for (int kb = 0; kb < PF; ++kb) PI_AE_LOAD_A(kb, kb)
+
+  // epilogue operands that do not depend on the GEMM, in flight during it
+  constexpr int EPT = (EPI == E_RES) ? E / NT : 1;        // residual elements per thread
+  constexpr int PPT = (EPI == E_RES) ? 1 : MB * 256 / NT;  // output pairs per thread
+  static_assert(E % NT == 0 && (MB * 256) % NT == 0, "epilogue work divides evenly");
+  float eh[EPT], eg[EPT];
+  float eb0[PPT], eb1[PPT], einv[PPT];
+  int env[PPT];
+  if constexpr (EPI == E_RES) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = threadIdx.x + q * NT;
+      const int mb = e / (NB * 256), nb = (e >> 8) % NB, i = (e >> 6) & 3, ln = e & 63;
+      const int row = row0 + mb * 16 + 4 * (ln >> 4) + i;
+      const int col = (j * NB + nb) * 16 + (ln & 15);
+      eh[q] = p.h_out[size_t(row < p.M ? row : 0) * kD + col];
+      eg[q] = p.gate[col];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int pi = threadIdx.x + q * NT;
+      const int i = (pi >> 6) & 3, ln = pi & 63, mb = pi >> 8;
+      const int cc = ln & 15, rl = mb * 16 + 4 * (ln >> 4) + i, row = row0 + rl;
+      eb0[q] = p.bias[(2 * j) * 16 + cc];
+      eb1[q] = p.bias[(2 * j + 1) * 16 + cc];
+      if constexpr (EPI == E_QKV) {
+        einv[q] = p.inv_freq[(j & 7) * 16 + cc];
+        env[q] = p.n_valid[(row < p.M ? row : 0) / p.T];
+      }
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) {
@@ -278,17 +327,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   };
 
   if constexpr (EPI == E_RES) {
-    for (int e = threadIdx.x; e < E; e += NT) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = threadIdx.x + q * NT;
       float x = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) x += red[w2 * E + e];
       const int mb = e / (NB * 256), nb = (e >> 8) % NB, i = (e >> 6) & 3, ln = e & 63;
       const int row = row0 + mb * 16 + 4 * (ln >> 4) + i;
       const int col = (j * NB + nb) * 16 + (ln & 15);
-      if (row < p.M) p.h_out[size_t(row) * kD + col] += x * p.gate[col];
+      if (row < p.M) p.h_out[size_t(row) * kD + col] = eh[q] + x * eg[q];
     }
   } else {
-    for (int pi = threadIdx.x; pi < MB * 256; pi += NT) {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int pi = threadIdx.x + q * NT;
       const int mb = pi >> 8, i = (pi >> 6) & 3, ln = pi & 63;
       const int e0 = ((mb * 2 + 0) * 4 + i) * 64 + ln, e1 = ((mb * 2 + 1) * 4 + i) * 64 + ln;
       float x0 = 0.f, x1 = 0.f;
@@ -301,22 +354,29 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       const int row = row0 + rl;
       if (row >= p.M) continue;
       const float r = rstd(rl);
-      const float y0 = x0 * r + p.bias[(2 * j) * 16 + cc];
-      const float y1 = x1 * r + p.bias[(2 * j + 1) * 16 + cc];
+      const float y0 = x0 * r + eb0[q];
+      const float y1 = x1 * r + eb1[q];
       if constexpr (EPI == E_QKV) {
-        if (j < 72) {  // Q heads (j < 64) and K_s (64 <= j < 72): rotate pair (i, i+128)
-          const int pb = j & 7, ip = pb * 16 + cc;
-          const int b = row / p.T, t = row - b * p.T;
-          const float2 cs = p.rope[size_t(p.n_valid[b] + t) * kRopeHalf + ip];
-          const float o0 = y0 * cs.x - y1 * cs.y;
-          const float o1 = y1 * cs.x + y0 * cs.y;
-          uint16_t* dst = (j < 64) ? p.q_out + (size_t(row) * kH + (j >> 3)) * kHd : p.k_out + size_t(row) * kHd;
-          dst[ip] = f2bf(o0);
-          dst[kRopeHalf + ip] = f2bf(o1);
+        const int b = row / p.T, t = row - b * p.T;
+        if (j < 72) {  // Q heads (j < 64) and K_s (64 <= j < 72): rotate pair (ip, ip+128)
+          const int ip = (j & 7) * 16 + cc;
+          float sn, cs;
+          sincosf(float(env[q] + t) * einv[q], &sn, &cs);
+          const float o0 = y0 * cs - y1 * sn;
+          const float o1 = y1 * cs + y0 * sn;
+          if (j < 64) {
+            uint16_t* dst = p.q_out + (size_t(row) * kH + (j >> 3)) * kHd;
+            dst[ip] = f2bf(o0);
+            dst[kRopeHalf + ip] = f2bf(o1);
+          } else {
+            const int key = p.P + t;
+            p.kp[kpack_index(b, key, ip, p.nkb)] = f2bf(o0);
+            p.kp[kpack_index(b, key, kRopeHalf + ip, p.nkb)] = f2bf(o1);
+          }
         } else {  // V_s: no rotation
-          uint16_t* dst = p.v_out + size_t(row) * kHd + (j - 72) * 32;
-          dst[cc] = f2bf(y0);
-          dst[16 + cc] = f2bf(y1);
+          const int key = p.P + t, d0 = (j - 72) * 32 + cc;
+          p.vp[vpack_index(b, key, d0, p.nkb)] = f2bf(y0);
+          p.vp[vpack_index(b, key, d0 + 16, p.nkb)] = f2bf(y1);
         }
       } else {  // E_GELU: n-block 0 = gate columns 16j.., n-block 1 = the same up columns
         const int f = 16 * j + cc;
@@ -327,74 +387,141 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Per call, once: pack every layer's prefix K/V into the attention's operand
+// order (see kpack_index / vpack_index) and build the additive key bias of
+// each episode: 0 for valid prefix keys and for the suffix keys, -inf for
+// pad-masked prefix keys and block padding (the blog's prefix/suffix softmax
+// kernel fills invalid keys with -2.38e38; -inf gives the same exp = 0).
+// Masked and padding keys are stored as zeros so that garbage in the cache
+// cannot reach the result.  Suffix keys are written later by the QKV kernel.
+// grid (nkb, B, L), 256 threads; each workgroup packs one 32-key block.
+__global__ __launch_bounds__(256) void k_pack(PackParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t vs[32][kHd + 8];
+  const int kb = blockIdx.x, b = blockIdx.y, l = blockIdx.z, t = threadIdx.x;
+  const DevArgs* da = p.da;
+  const size_t lay = size_t(l) * p.B * p.P * kHd;
+  const uint16_t* pk = da->pk + lay + size_t(b) * p.P * kHd;
+  const uint16_t* pv = da->pv + lay + size_t(b) * p.P * kHd;
+  const uint8_t* mask = da->mask ? da->mask + size_t(b) * p.P : nullptr;
+  uint16_t* kp = p.kp + (size_t(l) * p.B + b) * p.nkb * 8192 + size_t(kb) * 8192;
+  uint16_t* vp = p.vp + (size_t(l) * p.B + b) * p.nkb * 8192 + size_t(kb) * 8192;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  // K: 1024 16-byte chunks per block, each a straight copy of part of one key row
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int chunk = t + 256 * q;         // (mk*8 + ks)*64 + lane
+    const int lane = chunk & 63, f = chunk >> 6, mk = f >> 3, ks = f & 7;
+    const int key = kb * 32 + mk * 16 + (lane & 15);
+    const bool ok = key < p.P && (!mask || mask[key] != 0);
+    reinterpret_cast<uint4*>(kp)[chunk] =
+        ok ? *reinterpret_cast<const uint4*>(pk + size_t(key) * kHd + ks * 32 + 8 * (lane >> 4)) : zero4;
+  }
+  // V: stage the 32 key rows, then gather 8 keys per 16-byte chunk
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int chunk = t + 256 * q;         // key row kk, 16-byte column dc
+    const int kk = chunk >> 5, dc = chunk & 31, key = kb * 32 + kk;
+    const bool ok = key < p.P && (!mask || mask[key] != 0);
+    *reinterpret_cast<uint4*>(&vs[kk][dc * 8]) =
+        ok ? *reinterpret_cast<const uint4*>(pv + size_t(key) * kHd + dc * 8) : zero4;
+  }
+  __syncthreads();
+  if (kb * 32 < p.P) {  // blocks made only of suffix keys / padding are written by the QKV kernel / stay zero
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int chunk = t + 256 * q;       // md*64 + lane
+      const int lane = chunk & 63, md = chunk >> 6, d = md * 16 + (lane & 15), g = lane >> 4;
+      uint16_t e[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) e[jj] = vs[(jj < 4) ? 4 * g + jj : 16 + 4 * g + (jj - 4)][d];
+      uint4 o;
+      o.x = e[0] | (uint32_t(e[1]) << 16);
+      o.y = e[2] | (uint32_t(e[3]) << 16);
+      o.z = e[4] | (uint32_t(e[5]) << 16);
+      o.w = e[6] | (uint32_t(e[7]) << 16);
+      reinterpret_cast<uint4*>(vp)[chunk] = o;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) reinterpret_cast<uint4*>(vp)[t + 256 * q] = zero4;
+  }
+  if (l == 0 && t < 32) {
+    const int key = kb * 32 + t;
+    const bool ok = key < p.P ? (!mask || mask[key] != 0) : key < p.P + p.T;
+    p.kbias[size_t(b) * p.nkb * 32 + key] = ok ? 0.f : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Attention of 8 query heads sharing one KV head over the episode's prefix
 // keys (read-only cache, pad-masked) and all of its suffix keys ("LeRobot
-// implementation": repeat_kv -> Q K^T * scaling -> softmax -> V; the
-// Realtime-VLA prefix/suffix softmax kernel masks invalid prefix keys).
-// Queries are the episode's (token, head) rows, so every query sees the same
-// key set and one K/V stream serves all heads.  Workgroup: 16 queries; its 4
-// waves split the keys (flash-decoding style, online softmax in fp32) and are
-// merged through LDS.  Scores are computed transposed (S^T = K Q^T) so that
-// the probabilities land in the B-operand lane order of O^T = V^T P^T; V
-// blocks are transposed through LDS.
-constexpr int kVtStride = 40;  // bf16 per transposed-V row: 32 keys + pad
+// implementation": repeat_kv -> Q K^T * scaling -> softmax -> V).  Queries are
+// the episode's (token, head) rows, so every query sees the same key set and
+// one K/V stream serves all heads.  Workgroup: 16 queries; its 4 waves split
+// the 32-key blocks (online softmax in fp32) and are merged through LDS.
+// Scores are computed transposed (S^T = K Q^T) so that the probabilities land
+// in the B-operand lane order of O^T = V^T P^T; K and V arrive packed in
+// operand order, so every load is one contiguous 1 KiB fragment per wave, and
+// the next block's K is in flight while the current block is processed.
 constexpr int kOStride = 260;  // floats per query row in the merge buffer
 
 __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kHd * kVtStride];
+  __shared__ __attribute__((aligned(16))) float ored[4 * 16 * kOStride + 4 * 16 * 2];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.y;
   const int nq = p.T * kH;
   const int r = blockIdx.x * 16 + c;
   const int rc = r < nq ? r : nq - 1;
-  const DevArgs* da = p.da;
 
   bf16x8 qf[8];
   const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
 
-  const int P = p.P, NK = P + p.T;
-  const uint16_t* pk = da->pk + p.layer_off + size_t(b) * P * kHd;
-  const uint16_t* pv = da->pv + p.layer_off + size_t(b) * P * kHd;
-  const uint8_t* mask = da->mask ? da->mask + size_t(b) * P : nullptr;
-  const uint16_t* sk = p.ks + size_t(b) * p.T * kHd;
-  const uint16_t* sv = p.vs + size_t(b) * p.T * kHd;
-  const int nkb = (NK + 31) / 32;
+  const int nkb = p.nkb;
   const int kb0 = w * nkb / 4, kb1 = (w + 1) * nkb / 4;
-  uint16_t* vt = smem + w * kHd * kVtStride;
+  const uint4* kp = reinterpret_cast<const uint4*>(p.kp) + size_t(b) * nkb * 1024;
+  const uint4* vp = reinterpret_cast<const uint4*>(p.vp) + size_t(b) * nkb * 1024;
+  const float* kbias = p.kbias + size_t(b) * nkb * 32;
 
   f32x4 acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
+  uint4 kf[16];
+  if (kb0 < kb1) {
+#pragma unroll
+    for (int f = 0; f < 16; ++f) kf[f] = kp[size_t(kb0) * 1024 + f * 64 + lane];
+  }
   for (int kb = kb0; kb < kb1; ++kb) {
-    // scores S^T[key][query] for 32 keys
+    uint4 vf[16];
+#pragma unroll
+    for (int md = 0; md < 16; ++md) vf[md] = vp[size_t(kb) * 1024 + md * 64 + lane];
+    const float4 bl = *reinterpret_cast<const float4*>(kbias + kb * 32 + 4 * g);
+    const float4 bh = *reinterpret_cast<const float4*>(kbias + kb * 32 + 16 + 4 * g);
+    // scores S^T[key][query] for the 32 keys of this block
     f32x4 s[2];
 #pragma unroll
     for (int mk = 0; mk < 2; ++mk) {
-      const int key = kb * 32 + mk * 16 + c;
-      const uint16_t* kr = key < P ? pk + size_t(key) * kHd : (key < NK ? sk + size_t(key - P) * kHd : nullptr);
       s[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 kv = kr ? *reinterpret_cast<const uint4*>(kr + ks * 32 + 8 * g) : zero4;
-        s[mk] = mfma(as_bf(kv), qf[ks], s[mk]);
-      }
+      for (int ks = 0; ks < 8; ++ks) s[mk] = mfma(as_bf(kf[mk * 8 + ks]), qf[ks], s[mk]);
     }
+    if (kb + 1 < kb1) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) kf[f] = kp[size_t(kb + 1) * 1024 + f * 64 + lane];
+    }
+    const float bias[2][4] = {{bl.x, bl.y, bl.z, bl.w}, {bh.x, bh.y, bh.z, bh.w}};
     float pr[2][4];
     float mloc = -INFINITY;
 #pragma unroll
     for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = kb * 32 + mk * 16 + 4 * g + i;
-        const bool ok = key < P ? (mask ? mask[key] != 0 : true) : key < NK;
-        pr[mk][i] = ok ? s[mk][i] * sc : -INFINITY;
+        pr[mk][i] = s[mk][i] * sc + bias[mk][i];
         mloc = fmaxf(mloc, pr[mk][i]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
@@ -414,44 +541,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     lsum += __shfl_xor(lsum, 32);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] *= alpha;
     const bf16x8 pf = pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]),
                             make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
-
-    // V block -> LDS, transposed to [d][key]; masked / padded keys read as 0
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int chunk = it * 64 + lane, kk = chunk >> 5, dc = chunk & 31;
-      const int key = kb * 32 + kk;
-      const bool ok = key < P ? (mask ? mask[key] != 0 : true) : key < NK;
-      const uint4 vv = ok ? *reinterpret_cast<const uint4*>((key < P ? pv + size_t(key) * kHd
-                                                                     : sv + size_t(key - P) * kHd) + dc * 8)
-                          : zero4;
-      const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(dc * 8 + 2 * e) * kVtStride + kk] = uint16_t(u[e] & 0xffffu);
-        vt[(dc * 8 + 2 * e + 1) * kVtStride + kk] = uint16_t(u[e] >> 16);
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // O^T += V^T P^T; the key order of the k dimension is the one the
-    // probabilities already sit in: group g holds keys 4g..4g+3, 16+4g..16+4g+3
-#pragma unroll
-    for (int md = 0; md < 16; ++md) {
-      const uint16_t* vr = vt + (md * 16 + c) * kVtStride;
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * g);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-      acc[md] = mfma(as_bf(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, acc[md]);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int md = 0; md < 16; ++md) acc[md] = mfma(as_bf(vf[md]), pf, acc[md] * alpha);
   }
 
   // merge the 4 key ranges
-  __syncthreads();
-  float* ored = reinterpret_cast<float*>(smem);    // [4 waves][16 queries][kOStride]
-  float* sml = ored + 4 * 16 * kOStride;           // [4][16][2]
+  float* sml = ored + 4 * 16 * kOStride;  // [4][16][2]
 #pragma unroll
   for (int md = 0; md < 16; ++md)
 #pragma unroll
@@ -484,10 +581,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float s = 0.f;
+        float sum = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) s += f[w2] * ored[(w2 * 16 + q) * kOStride + d0 + 8 * h8 + e];
-        o[e] = s * inv;
+        for (int w2 = 0; w2 < 4; ++w2) sum += f[w2] * ored[(w2 * 16 + q) * kOStride + d0 + 8 * h8 + e];
+        o[e] = sum * inv;
       }
       const uint4 packed = __builtin_bit_cast(uint4, pack8(make_float4(o[0], o[1], o[2], o[3]),
                                                             make_float4(o[4], o[5], o[6], o[7])));
@@ -526,6 +623,11 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s) {
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   k_attn<<<dim3((p.T * kH + 15) / 16, p.B), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {
+  if (p.B <= 0 || p.nkb <= 0) return hipSuccess;
+  k_pack<<<dim3(p.nkb, p.B, L), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

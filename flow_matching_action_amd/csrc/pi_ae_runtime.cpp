@@ -62,10 +62,13 @@ struct pi_ae_ctx {
   // tables (device), kernel column order
   float *attn_s1 = nullptr, *attn_g = nullptr, *c_qkv = nullptr, *ffn_s1 = nullptr, *ffn_g = nullptr,
         *c_gu = nullptr, *fin_s1 = nullptr, *c_out = nullptr;
-  float2* rope = nullptr;
+  float* inv_freq = nullptr;
   // workspaces
   float* h = nullptr;
-  uint16_t *q = nullptr, *ks = nullptr, *vs = nullptr, *o = nullptr, *m = nullptr;
+  uint16_t *q = nullptr, *o = nullptr, *m = nullptr;
+  uint16_t *kp = nullptr, *vp = nullptr;  // packed K/V of every layer, one call
+  float* kbias = nullptr;
+  int nkb_max = 0;
   int* n_valid = nullptr;
   DevArgs* da = nullptr;
   int Mmax = 0, Mpad = 0;
@@ -366,18 +369,13 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->c_out = upload(t_cout);
   ctx->c_qkv = upload(permute(t_cqkv, kNqkv, pq));
   ctx->c_gu = upload(permute(t_cgu, kNgu, pg));
-  // RoPE table: angle = pos * base^(-2i/256), positions 0 .. max_prefix_len + T - 1
+  // RoPE inverse frequencies base^(-2i/256) (fp64 -> fp32); the angle
+  // position * inv_freq is formed in the QKV epilogue
   {
-    const int npos = cfg.max_prefix_len + T;
-    std::vector<float2> rt(size_t(npos) * kRopeHalf);
-    for (int pos = 0; pos < npos; ++pos)
-      for (int i = 0; i < kRopeHalf; ++i) {
-        const double inv = std::pow(double(cfg.rope_base), -2.0 * i / kHd);
-        const double a = double(pos) * inv;
-        rt[size_t(pos) * kRopeHalf + i] = make_float2(float(std::cos(a)), float(std::sin(a)));
-      }
-    ctx->rope = ctx->dalloc<float2>(rt.size());
-    HIP_OR_THROW(hipMemcpy(ctx->rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice));
+    std::vector<float> inv(kRopeHalf);
+    for (int i = 0; i < kRopeHalf; ++i) inv[i] = float(std::pow(double(cfg.rope_base), -2.0 * i / kHd));
+    ctx->inv_freq = ctx->dalloc<float>(kRopeHalf);
+    HIP_OR_THROW(hipMemcpy(ctx->inv_freq, inv.data(), kRopeHalf * 4, hipMemcpyHostToDevice));
   }
   // ---- workspaces (zeroed once; padded rows are never written)
   ctx->Mmax = cfg.max_batch * T;
@@ -385,16 +383,19 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   const size_t Mp = size_t(ctx->Mpad);
   ctx->h = ctx->dalloc<float>(Mp * kD);
   ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
-  ctx->ks = ctx->dalloc<uint16_t>(Mp * kHd);
-  ctx->vs = ctx->dalloc<uint16_t>(Mp * kHd);
+  ctx->nkb_max = (cfg.max_prefix_len + T + 31) / 32;
+  const size_t npack = size_t(L) * cfg.max_batch * ctx->nkb_max * 8192;
+  ctx->kp = ctx->dalloc<uint16_t>(npack);
+  ctx->vp = ctx->dalloc<uint16_t>(npack);
+  ctx->kbias = ctx->dalloc<float>(size_t(cfg.max_batch) * ctx->nkb_max * 32);
   ctx->o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
   ctx->m = ctx->dalloc<uint16_t>(Mp * kF);
   ctx->n_valid = ctx->dalloc<int>(cfg.max_batch);
   ctx->da = ctx->dalloc<DevArgs>(1);
   HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kD * 4));
   HIP_OR_THROW(hipMemset(ctx->q, 0, Mp * kH * kHd * 2));
-  HIP_OR_THROW(hipMemset(ctx->ks, 0, Mp * kHd * 2));
-  HIP_OR_THROW(hipMemset(ctx->vs, 0, Mp * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->kp, 0, npack * 2));
+  HIP_OR_THROW(hipMemset(ctx->vp, 0, npack * 2));
   HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kH * kHd * 2));
   HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kF * 2));
   HIP_OR_THROW(hipMemset(ctx->n_valid, 0, cfg.max_batch * 4));
@@ -442,15 +443,18 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       g.eps = cfg.rms_eps;
       g.T = T;
       g.n_valid = ctx->n_valid;
-      g.rope = ctx->rope;
+      g.inv_freq = ctx->inv_freq;
       g.h = ctx->h;
       if (phase == 1) {
+        const int nkb = (P + T + 31) / 32;
         g.w = ctx->w_qkv + size_t(kNqkv) * kD * l;
         g.s1 = ctx->attn_s1 + kl * kD;
         g.bias = ctx->c_qkv + kl * kNqkv;
         g.q_out = ctx->q;
-        g.k_out = ctx->ks;
-        g.v_out = ctx->vs;
+        g.P = P;
+        g.nkb = nkb;
+        g.kp = ctx->kp + size_t(l) * B * nkb * 8192;
+        g.vp = ctx->vp + size_t(l) * B * nkb * 8192;
         return launch_qkv(g, s);
       }
       g.w = ctx->w_gu + size_t(kNgu) * kD * l;
@@ -461,16 +465,16 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
     }
     case 2: {
       AttnParams a{};
-      a.da = ctx->da;
-      a.layer_off = size_t(l) * B * P * kHd;
+      const int nkb = (P + T + 31) / 32;
       a.q = ctx->q;
-      a.ks = ctx->ks;
-      a.vs = ctx->vs;
-      a.n_valid = ctx->n_valid;
+      a.kp = ctx->kp + size_t(l) * B * nkb * 8192;
+      a.vp = ctx->vp + size_t(l) * B * nkb * 8192;
+      a.kbias = ctx->kbias;
       a.o = ctx->o;
       a.B = B;
       a.T = T;
       a.P = P;
+      a.nkb = nkb;
       return launch_attn(a, s);
     }
     case 3:
@@ -496,6 +500,16 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
 hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& stop) {
   const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
   hipError_t e;
+  PackParams pp{};
+  pp.da = ctx->da;
+  pp.kp = ctx->kp;
+  pp.vp = ctx->vp;
+  pp.kbias = ctx->kbias;
+  pp.B = B;
+  pp.P = P;
+  pp.T = ctx->cfg.chunk_len;
+  pp.nkb = (P + pp.T + 31) / 32;
+  if ((e = launch_pack(pp, L, s)) != hipSuccess) return e;
   for (int k = 0; k <= S; ++k) {
     if ((e = launch_phase(ctx, B, P, s, k, 0, 0)) != hipSuccess) return e;
     if (stop.hit(k, 0, 0) || k == S) return hipSuccess;
@@ -741,9 +755,30 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
       e = hipMemcpy(host_out, ctx->h, need, hipMemcpyDeviceToHost);
     } else if (which == 6) {
       e = hipMemcpy(host_out, actions, need, hipMemcpyDeviceToHost);
-    } else if (which == 1 || which == 2 || which == 3) {
-      const void* src = which == 1 ? (const void*)ctx->q : which == 2 ? (const void*)ctx->ks : (const void*)ctx->vs;
-      e = hipMemcpy(host_out, src, need, hipMemcpyDeviceToHost);
+    } else if (which == 1) {
+      e = hipMemcpy(host_out, ctx->q, need, hipMemcpyDeviceToHost);
+    } else if (which == 2 || which == 3) {
+      // suffix keys of layer `layer` from the packed K / V (see kpack_index / vpack_index)
+      const int P = kv->prefix_len, nkb = (P + T + 31) / 32;
+      const size_t n = size_t(batch) * nkb * 8192;
+      buf.resize(n);
+      const uint16_t* src = (which == 2 ? ctx->kp : ctx->vp) + size_t(layer) * batch * nkb * 8192;
+      e = hipMemcpy(buf.data(), src, n * 2, hipMemcpyDeviceToHost);
+      uint16_t* dst = static_cast<uint16_t*>(host_out);
+      for (int b = 0; b < batch; ++b)
+        for (int t = 0; t < T; ++t)
+          for (int d = 0; d < kHd; ++d) {
+            const int key = P + t, w32 = key & 31;
+            size_t idx;
+            if (which == 2) {
+              const int lane = (w32 & 15) + 16 * ((d & 31) >> 3);
+              idx = ((size_t(b) * nkb + (key >> 5)) * 16 + (w32 >> 4) * 8 + (d >> 5)) * 512 + lane * 8 + (d & 7);
+            } else {
+              const int r4 = w32 & 15, lane = (d & 15) + 16 * (r4 >> 2);
+              idx = ((size_t(b) * nkb + (key >> 5)) * 16 + (d >> 4)) * 512 + lane * 8 + (w32 >> 4) * 4 + (r4 & 3);
+            }
+            dst[(size_t(b) * T + t) * kHd + d] = buf[idx];
+          }
     } else {
       // fragment-major [Mpad/16][K/32][64][8] -> natural [M][K]
       const int K = which == 4 ? kH * kHd : kF;
