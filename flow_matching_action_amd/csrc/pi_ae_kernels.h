@@ -35,6 +35,9 @@ struct IoParams {
   const uint16_t* w_out;  // action_out W [32][1024] bf16
   const float* fin_s1;    // final (1+scale) for the finishing step [1024] (null: no final norm)
   const float* c_out;     // [32] shift @ W_out^T + b_out for the finishing step
+  const float* s1_next;   // (1 + scale) of the first layer's attention norm (do_in)
+  uint16_t* u_out;        // its operand bf16(h * (1 + scale)), fragment-major
+  float* ssq_out;         // partial sums of h^2 [Mpad][64]
   float dt;
   float eps;
   int do_out;             // finish the previous step: final norm, out proj, Euler
@@ -46,18 +49,19 @@ struct IoParams {
 struct GemmParams {
   const uint16_t* w;      // swizzled weight fragments of this layer
   int M;                  // valid rows
-  // A operand
-  const float* h;         // normalised-input modes: fp32 residual [Mpad][1024]
-  const float* s1;        //   (1 + scale) [1024]
+  // A operand: bf16 fragment-major [Mpad/16][K/32][64][8]
+  const uint16_t* a_frag; // u (QKV, GU), O or m
+  const float* ssq;       // QKV, GU: per-row partial sums of h^2 [Mpad][64]
   float eps;
-  const uint16_t* a_frag; // bf16 fragment-major activations (O or m)
   // epilogue
   const float* bias;      // QKV / GU: shift-fold bias in the swizzled column order
   const float* gate;      // residual modes: per-column gate [1024]
   float* h_out;           // residual modes: fp32 residual stream
+  const float* s1_next;   // residual modes: (1 + scale) of the next normalised GEMM, or null
+  uint16_t* u_out;        //   its operand bf16(h * (1 + scale)), fragment-major [Mpad/16][32][64][8]
+  float* ssq_out;         //   and the partial sums of h^2 [Mpad][64]
   uint16_t* q_out;        // QKV: Q [M][8][256]
-  const float* inv_freq;  // RoPE inverse frequencies [128]
-  const int* n_valid;     // [B]
+  const float2* rope_cs;  // QKV: (cos, sin) of each suffix row's position [M][128]
   int T;                  // chunk length (rows per episode)
   int P, nkb;             // prefix length, 32-key blocks per episode of the packed K/V
   uint16_t* kp;           // QKV: packed K of this layer (suffix keys written here)
@@ -76,6 +80,9 @@ struct AttnParams {
 
 struct PackParams {
   const DevArgs* da;
+  const int* n_valid;     // [B]
+  const double* inv_freq; // RoPE inverse frequencies base^(-2i/256) [128]
+  float2* rope_cs;        // out: (cos, sin) of each suffix row's position [B*T][128]
   uint16_t* kp;           // [L][B][nkb][16][64][8]
   uint16_t* vp;
   float* kbias;           // [B][nkb*32]

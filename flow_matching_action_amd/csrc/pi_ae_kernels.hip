@@ -50,6 +50,17 @@ __device__ __forceinline__ size_t afrag_index(int row, int k, int KB) {
   return ((size_t(row >> 4) * KB + (k >> 5)) * 64 + lane) * 8 + (k & 7);
 }
 
+// Raw buffer loads: the base and the uniform part of the offset live in
+// scalar registers and only the lane offset takes a vector register; reads
+// past `bytes` return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Packed per-layer K/V of one call, 32-key blocks of 16 KiB per episode:
 //   K: [b][key/32][mk = (key%32)/16][ks = d/32][lane][8] with lane = key%16 +
 //      16 ((d%32)/8): the A operand of S^T = K Q^T, one 1 KiB fragment per (mk, ks);
@@ -158,92 +169,83 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
     }
     // (su is free here: every read of it above happened before the barrier)
     __syncthreads();
-    reinterpret_cast<float4*>(p.h + size_t(row) * kD)[t] = reinterpret_cast<const float4*>(su)[t];
+    const float4 hv = reinterpret_cast<const float4*>(su)[t];
+    reinterpret_cast<float4*>(p.h + size_t(row) * kD)[t] = hv;
+    // the first layer's normalised-GEMM operand and the h^2 partial of this
+    // thread's 16-column tile (4 threads per tile)
+    const float4 s = reinterpret_cast<const float4*>(p.s1_next)[t];
+    const uint32_t lo = uint32_t(f2bf(hv.x * s.x)) | (uint32_t(f2bf(hv.y * s.y)) << 16);
+    const uint32_t hi = uint32_t(f2bf(hv.z * s.z)) | (uint32_t(f2bf(hv.w * s.w)) << 16);
+    *reinterpret_cast<uint2*>(p.u_out + afrag_index(row, 4 * t, kD / 32)) = make_uint2(lo, hi);
+    float sq = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((t & 3) == 0) p.ssq_out[size_t(row) * (kD / 16) + (t >> 2)] = sq;
   }
   if (t < kA) x[t] = sx[t];
 }
 
 // ---------------------------------------------------------------------------
 // Weight-streaming GEMM.  Workgroup tile: MB*16 rows x NB*16 columns, NW
-// waves each owning KBW consecutive 32-wide K blocks (intra-workgroup split-K).
-//   A_NORM: A = bf16(h * (1 + scale)) built from the fp32 residual stream; the
-//           RMS statistics of the full rows are reduced across the waves and
-//           1/rms is applied in the epilogue (it commutes with the GEMM).
-//   A_FRAG: A = bf16 activations stored fragment-major by their producer.
+// waves each owning KBW consecutive 32-wide K blocks (intra-workgroup
+// split-K); workgroup j hands K slice (w + j) mod NW to wave w so that the
+// workgroups do not all read the same activation lines at the same time.
+// A is bf16, fragment-major (written so by its producer).
+//   NORM (QKV, gate/up): A = bf16(h * (1 + scale)) written by the kernel that
+//     produced h, together with per-row partial sums of h^2 over 16-column
+//     tiles; 1/rms of each row is formed here from those partials (fixed
+//     order) and applied in the epilogue (it commutes with the GEMM).
 // Epilogues:
-//   E_QKV:  + shift-fold bias, RoPE on (i, i+128) pairs, scatter Q/K_s/V_s.
-//   E_GELU: + shift-fold bias, m = GELU(gate) * up, store m fragment-major.
-//   E_RES:  h += acc * gate (gated residual).
-enum { A_NORM = 0, A_FRAG = 1 };
+//   E_QKV:  * 1/rms, + shift-fold bias, RoPE on (i, i+128) pairs; Q to
+//           [M][8][256], suffix K/V into the packed per-layer buffers.
+//   E_GELU: * 1/rms, + shift-fold bias, m = GELU(gate) * up, fragment-major.
+//   E_RES:  h += acc * gate; when the next consumer is a normalised GEMM also
+//           its operand bf16(h * (1 + scale_next)) and the h^2 partials.
 enum { E_QKV = 0, E_GELU = 1, E_RES = 2 };
+constexpr int kSsqTiles = kD / 16;  // partial sums of squares per row
 
-template <int MB, int NB, int NW, int KBW, int AMODE, int EPI>
+template <int MB, int NB, int NW, int KBW, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   constexpr int KB = KBW * NW;
   constexpr int E = MB * NB * 4 * 64;  // accumulator floats per wave
   constexpr int NT = NW * 64;
-  static_assert(AMODE != A_NORM || KB * 32 == kD, "normalised input spans the full width");
+  constexpr bool NORM = EPI != E_RES;
+  static_assert(!NORM || KB * 32 == kD, "normalised input spans the full width");
   static_assert(EPI == E_RES || NB == 2, "paired epilogues take two n-blocks");
+  static_assert(!NORM || NT >= MB * 64, "one thread per (row, quarter) of the row statistics");
   __shared__ float red[NW * E];
-  __shared__ float ssq[NW * MB * 16];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
+  __shared__ float srstd[MB * 16];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = blockIdx.x;
   const int row0 = blockIdx.y * MB * 16;
+  const int ws = (w + j) % NW;  // this wave's K slice
 
-  // 1. this wave's weight fragments, all in flight before any activation load
+  // 1. activations (L2-resident), then this wave's weight fragments (HBM):
+  // all in flight before the first wait.  vmcnt retires loads in issue order,
+  // so the first MFMA waits only for the activations and its own weights.
+  constexpr int PF = (MB * KBW <= 32) ? KBW : 32 / MB;  // activation blocks issued up front
+  uint4 abuf[PF][MB];
+  const uint4* ap = reinterpret_cast<const uint4*>(p.a_frag) + size_t(row0 >> 4) * KB * 64;
+#pragma unroll
+  for (int kb = 0; kb < PF; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) abuf[kb][mb] = ap[(size_t(mb) * KB + ws * KBW + kb) * 64 + lane];
   uint4 bw[NB][KBW];
   const uint4* wp = reinterpret_cast<const uint4*>(p.w);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb)
-      bw[nb][kb] = wp[(size_t(j * NB + nb) * KB + w * KBW + kb) * 64 + lane];
+    for (int nb = 0; nb < NB; ++nb)
+      bw[nb][kb] = wp[(size_t(j * NB + nb) * KB + ws * KBW + kb) * 64 + lane];
 
-  f32x4 acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) ss[mb] = 0.f;
-
-  // 2. K loop over this wave's blocks.  Activation loads run PF blocks ahead
-  // of the MFMAs; scheduling barriers keep every weight load ahead of the
-  // first wait (vmcnt retires loads in issue order).
-  constexpr int PF = KBW < 4 ? KBW : 4;
-  constexpr int AW = (AMODE == A_NORM) ? 2 : 1;  // 16-byte loads per (row block, K block)
-  uint4 abuf[PF][MB][AW];
-  float4 sbuf[PF][AW];
-  const uint4* ap = reinterpret_cast<const uint4*>(p.a_frag);
-#define PI_AE_LOAD_A(KBI, SLOT)                                                                  \
-  {                                                                                              \
-    if constexpr (AMODE == A_NORM) {                                                             \
-      const int k_ = (w * KBW + (KBI)) * 32 + 8 * g;                                             \
-      sbuf[SLOT][0] = *reinterpret_cast<const float4*>(p.s1 + k_);                               \
-      sbuf[SLOT][AW - 1] = *reinterpret_cast<const float4*>(p.s1 + k_ + 4);                      \
-      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
-        const int row_ = row0 + mb * 16 + c;                                                     \
-        const uint4* hp_ = reinterpret_cast<const uint4*>(p.h + size_t(row_ < p.M ? row_ : 0) * kD + k_); \
-        abuf[SLOT][mb][0] = hp_[0];                                                              \
-        abuf[SLOT][mb][AW - 1] = hp_[1];                                                         \
-      }                                                                                          \
-    } else {                                                                                     \
-      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                          \
-        abuf[SLOT][mb][0] = ap[(size_t((row0 >> 4) + mb) * KB + w * KBW + (KBI)) * 64 + lane];    \
-    }                                                                                            \
-  }
-#pragma unroll
-  for (int kb = 0; kb < PF; ++kb) PI_AE_LOAD_A(kb, kb)
-
-  // epilogue operands that do not depend on the GEMM, in flight during it
+  // 3. epilogue operands that do not depend on the GEMM, in flight during it
   constexpr int EPT = (EPI == E_RES) ? E / NT : 1;        // residual elements per thread
   constexpr int PPT = (EPI == E_RES) ? 1 : MB * 256 / NT;  // output pairs per thread
   static_assert(E % NT == 0 && (MB * 256) % NT == 0, "epilogue work divides evenly");
-  float eh[EPT], eg[EPT];
-  float eb0[PPT], eb1[PPT], einv[PPT];
-  int env[PPT];
+  float eh[EPT], eg[EPT], es[EPT];
+  float eb0[PPT], eb1[PPT];
+  float2 ecs[PPT];
+  float4 ssp[4];
   if constexpr (EPI == E_RES) {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
@@ -253,8 +255,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       const int col = (j * NB + nb) * 16 + (ln & 15);
       eh[q] = p.h_out[size_t(row < p.M ? row : 0) * kD + col];
       eg[q] = p.gate[col];
+      es[q] = p.s1_next ? p.s1_next[col] : 0.f;
     }
   } else {
+    if (threadIdx.x < MB * 64) {  // row rl = t/4 sums partials 16*(t%4) .. +16
+      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(row0 + (threadIdx.x >> 2)) * kSsqTiles +
+                                                         16 * (threadIdx.x & 3));
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ssp[v] = sp[v];
+    }
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
       const int pi = threadIdx.x + q * NT;
@@ -263,68 +272,51 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       eb0[q] = p.bias[(2 * j) * 16 + cc];
       eb1[q] = p.bias[(2 * j + 1) * 16 + cc];
       if constexpr (EPI == E_QKV) {
-        einv[q] = p.inv_freq[(j & 7) * 16 + cc];
-        env[q] = p.n_valid[(row < p.M ? row : 0) / p.T];
+        // cos/sin of suffix token row at its position n_valid[b] + t, pair (j%8)*16 + cc
+        ecs[q] = (j < 72) ? p.rope_cs[size_t(row < p.M ? row : 0) * kRopeHalf + (j & 7) * 16 + cc]
+                          : make_float2(1.f, 0.f);
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) {
     const int slot = kb % PF;
-    bf16x8 af[MB];
-    if constexpr (AMODE == A_NORM) {
-      const float4 s0 = sbuf[slot][0], s1 = sbuf[slot][AW - 1];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bool live = row0 + mb * 16 + c < p.M;
-        float4 lo = __builtin_bit_cast(float4, abuf[slot][mb][0]);
-        float4 hi = __builtin_bit_cast(float4, abuf[slot][mb][AW - 1]);
-        if (!live) lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
-        ss[mb] += lo.x * lo.x + lo.y * lo.y + lo.z * lo.z + lo.w * lo.w + hi.x * hi.x + hi.y * hi.y + hi.z * hi.z +
-                  hi.w * hi.w;
-        af[mb] = pack8(make_float4(lo.x * s0.x, lo.y * s0.y, lo.z * s0.z, lo.w * s0.w),
-                       make_float4(hi.x * s1.x, hi.y * s1.y, hi.z * s1.z, hi.w * s1.w));
-      }
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) af[mb] = as_bf(abuf[slot][mb][0]);
-    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(af[mb], as_bf(bw[nb][kb]), acc[mb][nb]);
-    if (kb + PF < KBW) PI_AE_LOAD_A(kb + PF, slot)
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma(as_bf(abuf[slot][mb]), as_bf(bw[nb][kb]), acc[mb][nb]);
+    if (kb + PF < KBW) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) abuf[slot][mb] = ap[(size_t(mb) * KB + ws * KBW + kb + PF) * 64 + lane];
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-#undef PI_AE_LOAD_A
 
-  // 3. split-K partials (and row statistics) through LDS
-  if constexpr (AMODE == A_NORM) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      ss[mb] += __shfl_xor(ss[mb], 16);
-      ss[mb] += __shfl_xor(ss[mb], 32);
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) ssq[w * MB * 16 + mb * 16 + lane] = ss[mb];
-    }
-  }
+  // 4. split-K partials (and row statistics) through LDS
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w * E + ((mb * NB + nb) * 4 + i) * 64 + lane] = acc[mb][nb][i];
-  __syncthreads();
-
-  auto rstd = [&](int rl) {
-    float s = 0.f;
+  if constexpr (NORM) {
+    if (threadIdx.x < MB * 64) {
+      float s = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) s += ssq[w2 * MB * 16 + rl];
-    return 1.f / sqrtf(s * (1.f / kD) + p.eps);
-  };
+      for (int v = 0; v < 4; ++v) s += (ssp[v].x + ssp[v].y) + (ssp[v].z + ssp[v].w);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if ((threadIdx.x & 3) == 0) srstd[threadIdx.x >> 2] = 1.f / sqrtf(s * (1.f / kD) + p.eps);
+    }
+  }
+  __syncthreads();
 
   if constexpr (EPI == E_RES) {
 #pragma unroll
@@ -336,7 +328,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       const int mb = e / (NB * 256), nb = (e >> 8) % NB, i = (e >> 6) & 3, ln = e & 63;
       const int row = row0 + mb * 16 + 4 * (ln >> 4) + i;
       const int col = (j * NB + nb) * 16 + (ln & 15);
-      if (row < p.M) p.h_out[size_t(row) * kD + col] = eh[q] + x * eg[q];
+      const float hn = eh[q] + x * eg[q];
+      if (row < p.M) p.h_out[size_t(row) * kD + col] = hn;
+      if (p.s1_next) {
+        // the 16 lanes ln & 15 = 0..15 hold this row's 16 columns of the tile
+        float sq = hn * hn;
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        sq += __shfl_xor(sq, 4);
+        sq += __shfl_xor(sq, 8);
+        if (row < p.M) {
+          p.u_out[afrag_index(row, col, kD / 32)] = f2bf(hn * es[q]);
+          if ((ln & 15) == 0) p.ssq_out[size_t(row) * kSsqTiles + j * NB + nb] = sq;
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -353,15 +358,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       const int rl = mb * 16 + 4 * (ln >> 4) + i, cc = ln & 15;
       const int row = row0 + rl;
       if (row >= p.M) continue;
-      const float r = rstd(rl);
+      const float r = srstd[rl];
       const float y0 = x0 * r + eb0[q];
       const float y1 = x1 * r + eb1[q];
       if constexpr (EPI == E_QKV) {
         const int b = row / p.T, t = row - b * p.T;
         if (j < 72) {  // Q heads (j < 64) and K_s (64 <= j < 72): rotate pair (ip, ip+128)
           const int ip = (j & 7) * 16 + cc;
-          float sn, cs;
-          sincosf(float(env[q] + t) * einv[q], &sn, &cs);
+          const float cs = ecs[q].x, sn = ecs[q].y;
           const float o0 = y0 * cs - y1 * sn;
           const float o1 = y1 * cs + y0 * sn;
           if (j < 64) {
@@ -445,6 +449,14 @@ __global__ __launch_bounds__(256) void k_pack(PackParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) reinterpret_cast<uint4*>(vp)[t + 256 * q] = zero4;
   }
+  if (l == 0 && kb == 0) {  // cos/sin of this episode's suffix positions n_valid[b] + t (fp64 angle)
+    const int nv = p.n_valid[b];
+    for (int i = t; i < p.T * kRopeHalf; i += 256) {
+      const int tt = i / kRopeHalf, ip = i - tt * kRopeHalf;
+      const double a = double(nv + tt) * p.inv_freq[ip];
+      p.rope_cs[(size_t(b) * p.T + tt) * kRopeHalf + ip] = make_float2(float(cos(a)), float(sin(a)));
+    }
+  }
   if (l == 0 && t < 32) {
     const int key = kb * 32 + t;
     const bool ok = key < p.P ? (!mask || mask[key] != 0) : key < p.P + p.T;
@@ -465,9 +477,48 @@ __global__ __launch_bounds__(256) void k_pack(PackParams p) {
 // the next block's K is in flight while the current block is processed.
 constexpr int kOStride = 260;  // floats per query row in the merge buffer
 
-__global__ __launch_bounds__(256) void k_attn(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) float ored[4 * 16 * kOStride + 4 * 16 * 2];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Online-softmax update for one 32-key block: scores (S^T, two 16-key halves)
+// are scaled, biased (0 or -inf per key), folded into the running max and sum;
+// returns the block's probabilities as the B operand of O^T += V^T P^T and
+// the factor by which the running O^T must be rescaled.
+__device__ __forceinline__ bf16x8 attn_softmax(const f32x4 (&s)[2], const float4 (&bias)[2], float& m_run,
+                                               float& l_run, float& alpha) {
+  const float sc = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
+  const float bv[2][4] = {{bias[0].x, bias[0].y, bias[0].z, bias[0].w}, {bias[1].x, bias[1].y, bias[1].z, bias[1].w}};
+  float pr[2][4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[mk][i] = s[mk][i] * sc + bv[mk][i];
+      mloc = fmaxf(mloc, pr[mk][i]);
+    }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(m_run, mloc);
+  const bool none = (m_new == -INFINITY);
+  alpha = none ? 1.f : exp2f(m_run - m_new);
+  float lsum = 0.f;
+#pragma unroll
+  for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[mk][i] = none ? 0.f : exp2f(pr[mk][i] - m_new);
+      lsum += pr[mk][i];
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  return pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]), make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
+}
+
+constexpr int kAttnWaves = 8;
+
+__global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) float ored[kAttnWaves * 16 * kOStride + kAttnWaves * 16 * 2];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.y;
   const int nq = p.T * kH;
@@ -480,29 +531,33 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
 
   const int nkb = p.nkb;
-  const int kb0 = w * nkb / 4, kb1 = (w + 1) * nkb / 4;
-  const uint4* kp = reinterpret_cast<const uint4*>(p.kp) + size_t(b) * nkb * 1024;
-  const uint4* vp = reinterpret_cast<const uint4*>(p.vp) + size_t(b) * nkb * 1024;
-  const float* kbias = p.kbias + size_t(b) * nkb * 32;
+  const int kb0 = w * nkb / kAttnWaves, kb1 = (w + 1) * nkb / kAttnWaves;
+  const uint32_t ep_bytes = uint32_t(nkb) * 16384u;  // one episode's packed K (or V)
+  const rsrc_t kr = make_rsrc(p.kp + size_t(b) * nkb * 8192, ep_bytes);
+  const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
+  const rsrc_t br = make_rsrc(p.kbias + size_t(b) * nkb * 32, uint32_t(nkb) * 128u);
+  const uint32_t lo16 = uint32_t(lane) * 16u, go16 = uint32_t(g) * 16u;
 
   f32x4 acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const float sc = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
 
-  uint4 kf[16];
+  // one K / V register set per wave: block kb+1's K is issued as soon as the
+  // scores of block kb have consumed K, its V as soon as O^T has consumed V
+  uint4 kf[16], vf[16];
+  float4 bias[2];
   if (kb0 < kb1) {
 #pragma unroll
-    for (int f = 0; f < 16; ++f) kf[f] = kp[size_t(kb0) * 1024 + f * 64 + lane];
+    for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, uint32_t(kb0) * 16384u + f * 1024u);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, uint32_t(kb0) * 16384u + f * 1024u);
+    bias[0] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb0) * 128u));
+    bias[1] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb0) * 128u + 64u));
   }
   for (int kb = kb0; kb < kb1; ++kb) {
-    uint4 vf[16];
-#pragma unroll
-    for (int md = 0; md < 16; ++md) vf[md] = vp[size_t(kb) * 1024 + md * 64 + lane];
-    const float4 bl = *reinterpret_cast<const float4*>(kbias + kb * 32 + 4 * g);
-    const float4 bh = *reinterpret_cast<const float4*>(kbias + kb * 32 + 16 + 4 * g);
-    // scores S^T[key][query] for the 32 keys of this block
+    const bool more = kb + 1 < kb1;
+    const uint32_t nxt = uint32_t(kb + 1) * 16384u;
     f32x4 s[2];
 #pragma unroll
     for (int mk = 0; mk < 2; ++mk) {
@@ -510,45 +565,28 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s[mk] = mfma(as_bf(kf[mk * 8 + ks]), qf[ks], s[mk]);
     }
-    if (kb + 1 < kb1) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
 #pragma unroll
-      for (int f = 0; f < 16; ++f) kf[f] = kp[size_t(kb + 1) * 1024 + f * 64 + lane];
+      for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, nxt + f * 1024u);
     }
-    const float bias[2][4] = {{bl.x, bl.y, bl.z, bl.w}, {bh.x, bh.y, bh.z, bh.w}};
-    float pr[2][4];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[mk][i] = s[mk][i] * sc + bias[mk][i];
-        mloc = fmaxf(mloc, pr[mk][i]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const bool none = (m_new == -INFINITY);
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
-    float lsum = 0.f;
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[mk][i] = none ? 0.f : exp2f(pr[mk][i] - m_new);
-        lsum += pr[mk][i];
-      }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    const bf16x8 pf = pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]),
-                            make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
+    __builtin_amdgcn_sched_barrier(0);
+    float alpha;
+    const bf16x8 pf = attn_softmax(s, bias, m_run, l_run, alpha);
 #pragma unroll
     for (int md = 0; md < 16; ++md) acc[md] = mfma(as_bf(vf[md]), pf, acc[md] * alpha);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, nxt + f * 1024u);
+      bias[0] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb + 1) * 128u));
+      bias[1] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb + 1) * 128u + 64u));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // merge the 4 key ranges
-  float* sml = ored + 4 * 16 * kOStride;  // [4][16][2]
+  // merge the key ranges of the waves
+  float* sml = ored + kAttnWaves * 16 * kOStride;  // [waves][16][2]
 #pragma unroll
   for (int md = 0; md < 16; ++md)
 #pragma unroll
@@ -558,17 +596,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
     sml[(w * 16 + c) * 2 + 1] = l_run;
   }
   __syncthreads();
-  const int q = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 16;
-  float mw[4], f[4];
+  // 512 threads: query q = t/32, 8 head-dim values from d0 = (t%32)*8
+  const int q = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 8;
+  float mw[kAttnWaves], f[kAttnWaves];
   float mmax = -INFINITY;
 #pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) {
+  for (int w2 = 0; w2 < kAttnWaves; ++w2) {
     mw[w2] = sml[(w2 * 16 + q) * 2];
     mmax = fmaxf(mmax, mw[w2]);
   }
   float L = 0.f;
 #pragma unroll
-  for (int w2 = 0; w2 < 4; ++w2) {
+  for (int w2 = 0; w2 < kAttnWaves; ++w2) {
     f[w2] = (mw[w2] == -INFINITY) ? 0.f : exp2f(mw[w2] - mmax);
     L += f[w2] * sml[(w2 * 16 + q) * 2 + 1];
   }
@@ -576,25 +615,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams p) {
   const int rq = blockIdx.x * 16 + q;
   if (rq < nq) {
     const int trow = b * p.T + rq / kH, head = rq % kH;
+    float o[8];
 #pragma unroll
-    for (int h8 = 0; h8 < 2; ++h8) {
-      float o[8];
+    for (int e = 0; e < 8; ++e) {
+      float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) sum += f[w2] * ored[(w2 * 16 + q) * kOStride + d0 + 8 * h8 + e];
-        o[e] = sum * inv;
-      }
-      const uint4 packed = __builtin_bit_cast(uint4, pack8(make_float4(o[0], o[1], o[2], o[3]),
-                                                            make_float4(o[4], o[5], o[6], o[7])));
-      *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0 + 8 * h8, (kH * kHd) / 32)) = packed;
+      for (int w2 = 0; w2 < kAttnWaves; ++w2) sum += f[w2] * ored[(w2 * 16 + q) * kOStride + d0 + e];
+      o[e] = sum * inv;
     }
+    const uint4 packed = __builtin_bit_cast(uint4, pack8(make_float4(o[0], o[1], o[2], o[3]),
+                                                          make_float4(o[4], o[5], o[6], o[7])));
+    *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = packed;
   }
 }
 
 // ---------------------------------------------------------------------------
-static inline unsigned row_tiles(int M) { return unsigned((M + 63) / 64); }
+static inline unsigned row_tiles(int M, int rows = 64) { return unsigned((M + rows - 1) / rows); }
 
 hipError_t launch_args(const ArgsParams& p, hipStream_t s) {
   k_args<<<1, 256, 0, s>>>(p);
@@ -606,23 +642,31 @@ hipError_t launch_io(const IoParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 2, 4, 8, A_NORM, E_QKV><<<dim3(kNqkv / 32, row_tiles(p.M)), 256, 0, s>>>(p);
+  k_gemm<4, 2, 4, 8, E_QKV><<<dim3(kNqkv / 32, row_tiles(p.M)), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 2, 4, 8, A_NORM, E_GELU><<<dim3(kNgu / 32, row_tiles(p.M)), 256, 0, s>>>(p);
+  k_gemm<4, 2, 4, 8, E_GELU><<<dim3(kNgu / 32, row_tiles(p.M)), 256, 0, s>>>(p);
   return hipGetLastError();
 }
+// O and down: at small M, 32-row tiles halve each workgroup's activation
+// slice (all of it is then in flight at once) and double the CUs sharing it.
 hipError_t launch_o(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 1, 8, 8, A_FRAG, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
+  if (p.M <= 64)
+    k_gemm<2, 1, 8, 8, E_RES><<<dim3(kD / 16, row_tiles(p.M, 32)), 512, 0, s>>>(p);
+  else
+    k_gemm<4, 1, 8, 8, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 1, 8, 16, A_FRAG, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
+  if (p.M <= 64)
+    k_gemm<2, 1, 8, 16, E_RES><<<dim3(kD / 16, row_tiles(p.M, 32)), 512, 0, s>>>(p);
+  else
+    k_gemm<4, 1, 8, 16, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  k_attn<<<dim3((p.T * kH + 15) / 16, p.B), 256, 0, s>>>(p);
+  k_attn<<<dim3((p.T * kH + 15) / 16, p.B), kAttnWaves * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {

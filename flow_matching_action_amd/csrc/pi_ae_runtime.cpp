@@ -62,10 +62,12 @@ struct pi_ae_ctx {
   // tables (device), kernel column order
   float *attn_s1 = nullptr, *attn_g = nullptr, *c_qkv = nullptr, *ffn_s1 = nullptr, *ffn_g = nullptr,
         *c_gu = nullptr, *fin_s1 = nullptr, *c_out = nullptr;
-  float* inv_freq = nullptr;
+  double* inv_freq = nullptr;
+  float2* rope_cs = nullptr;
   // workspaces
   float* h = nullptr;
-  uint16_t *q = nullptr, *o = nullptr, *m = nullptr;
+  uint16_t *q = nullptr, *o = nullptr, *m = nullptr, *u = nullptr;
+  float* ssq = nullptr;
   uint16_t *kp = nullptr, *vp = nullptr;  // packed K/V of every layer, one call
   float* kbias = nullptr;
   int nkb_max = 0;
@@ -369,13 +371,13 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->c_out = upload(t_cout);
   ctx->c_qkv = upload(permute(t_cqkv, kNqkv, pq));
   ctx->c_gu = upload(permute(t_cgu, kNgu, pg));
-  // RoPE inverse frequencies base^(-2i/256) (fp64 -> fp32); the angle
-  // position * inv_freq is formed in the QKV epilogue
+  // RoPE inverse frequencies base^(-2i/256) in fp64; the pack kernel turns
+  // them into the cos/sin rows of the call's suffix positions
   {
-    std::vector<float> inv(kRopeHalf);
-    for (int i = 0; i < kRopeHalf; ++i) inv[i] = float(std::pow(double(cfg.rope_base), -2.0 * i / kHd));
-    ctx->inv_freq = ctx->dalloc<float>(kRopeHalf);
-    HIP_OR_THROW(hipMemcpy(ctx->inv_freq, inv.data(), kRopeHalf * 4, hipMemcpyHostToDevice));
+    std::vector<double> inv(kRopeHalf);
+    for (int i = 0; i < kRopeHalf; ++i) inv[i] = std::pow(double(cfg.rope_base), -2.0 * i / kHd);
+    ctx->inv_freq = ctx->dalloc<double>(kRopeHalf);
+    HIP_OR_THROW(hipMemcpy(ctx->inv_freq, inv.data(), kRopeHalf * 8, hipMemcpyHostToDevice));
   }
   // ---- workspaces (zeroed once; padded rows are never written)
   ctx->Mmax = cfg.max_batch * T;
@@ -389,6 +391,9 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->vp = ctx->dalloc<uint16_t>(npack);
   ctx->kbias = ctx->dalloc<float>(size_t(cfg.max_batch) * ctx->nkb_max * 32);
   ctx->o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->rope_cs = ctx->dalloc<float2>(Mp * kRopeHalf);
+  ctx->u = ctx->dalloc<uint16_t>(Mp * kD);
+  ctx->ssq = ctx->dalloc<float>(Mp * (kD / 16));
   ctx->m = ctx->dalloc<uint16_t>(Mp * kF);
   ctx->n_valid = ctx->dalloc<int>(cfg.max_batch);
   ctx->da = ctx->dalloc<DevArgs>(1);
@@ -397,6 +402,8 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   HIP_OR_THROW(hipMemset(ctx->kp, 0, npack * 2));
   HIP_OR_THROW(hipMemset(ctx->vp, 0, npack * 2));
   HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kD * 2));
+  HIP_OR_THROW(hipMemset(ctx->ssq, 0, Mp * (kD / 16) * 4));
   HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kF * 2));
   HIP_OR_THROW(hipMemset(ctx->n_valid, 0, cfg.max_batch * 4));
   HIP_OR_THROW(hipMemset(ctx->da, 0, sizeof(DevArgs)));
@@ -434,6 +441,9 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       io.from_noise = k == 0;
       io.fin_s1 = (k > 0 && cfg.final_norm) ? ctx->fin_s1 + size_t(k - 1) * kD : nullptr;
       io.c_out = k > 0 ? ctx->c_out + size_t(k - 1) * kA : nullptr;
+      io.s1_next = k < S ? ctx->attn_s1 + size_t(k) * L * kD : nullptr;
+      io.u_out = ctx->u;
+      io.ssq_out = ctx->ssq;
       return launch_io(io, s);
     }
     case 1:
@@ -442,13 +452,12 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       g.M = M;
       g.eps = cfg.rms_eps;
       g.T = T;
-      g.n_valid = ctx->n_valid;
-      g.inv_freq = ctx->inv_freq;
-      g.h = ctx->h;
+      g.rope_cs = ctx->rope_cs;
+      g.a_frag = ctx->u;
+      g.ssq = ctx->ssq;
       if (phase == 1) {
         const int nkb = (P + T + 31) / 32;
         g.w = ctx->w_qkv + size_t(kNqkv) * kD * l;
-        g.s1 = ctx->attn_s1 + kl * kD;
         g.bias = ctx->c_qkv + kl * kNqkv;
         g.q_out = ctx->q;
         g.P = P;
@@ -458,7 +467,6 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
         return launch_qkv(g, s);
       }
       g.w = ctx->w_gu + size_t(kNgu) * kD * l;
-      g.s1 = ctx->ffn_s1 + kl * kD;
       g.bias = ctx->c_gu + kl * kNgu;
       g.m_out = ctx->m;
       return launch_gu(g, s);
@@ -482,15 +490,20 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       GemmParams g{};
       g.M = M;
       g.h_out = ctx->h;
-      if (phase == 3) {
+      g.u_out = ctx->u;
+      g.ssq_out = ctx->ssq;
+      if (phase == 3) {  // next: this layer's gate/up
         g.w = ctx->w_o + size_t(kD) * kH * kHd * l;
         g.a_frag = ctx->o;
         g.gate = ctx->attn_g + kl * kD;
+        g.s1_next = ctx->ffn_s1 + kl * kD;
         return launch_o(g, s);
       }
+      // next: the following layer's QKV, or (last layer) the step boundary
       g.w = ctx->w_d + size_t(kD) * kF * l;
       g.a_frag = ctx->m;
       g.gate = ctx->ffn_g + kl * kD;
+      g.s1_next = (l + 1 < L) ? ctx->attn_s1 + (kl + 1) * kD : nullptr;
       return launch_down(g, s);
     }
   }
@@ -502,6 +515,9 @@ hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& st
   hipError_t e;
   PackParams pp{};
   pp.da = ctx->da;
+  pp.n_valid = ctx->n_valid;
+  pp.inv_freq = ctx->inv_freq;
+  pp.rope_cs = ctx->rope_cs;
   pp.kp = ctx->kp;
   pp.vp = ctx->vp;
   pp.kbias = ctx->kbias;
