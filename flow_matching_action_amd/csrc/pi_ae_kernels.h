@@ -27,7 +27,30 @@ struct DevArgs {
   float* actions;         // [B][T][32], the Euler state x
 };
 
+// From this many rows on the GEMMs are MFMA-bound and use 128 x 128 tiles
+// staged through LDS; below it they stream weights with one row tile.
+constexpr int kTiledMinRows = 129;
+
+// L2 warm-up of a later kernel's operands by spare workgroups appended to a
+// launch.  A workgroup's XCD (and so its L2) follows its linear block index
+// mod 8 with one fixed offset for every kernel, so a prefetching workgroup
+// whose index matches a consumer workgroup's mod 8 fills the consumer's L2.
+//   slices: the consumer's workgroup j reads bytes [j*bytes, (j+1)*bytes) of
+//           base, j < count;
+//   broadcast (count == 0): every XCD's L2 gets all `bytes` of base.
+struct Prefetch {
+  const void* base;
+  uint32_t bytes;
+  int count;
+};
+struct PrefetchSet {
+  Prefetch r[2];
+  int nwg;        // prefetching workgroups appended (multiple of 8; 0 = none)
+  uint32_t* sink; // never written in practice (keeps the loads alive)
+};
+
 struct IoParams {
+  PrefetchSet pf;
   const DevArgs* da;
   float* h;               // [Mpad][1024] fp32 residual stream
   const uint16_t* w_in;   // action_in W [1024][32] bf16
@@ -47,6 +70,7 @@ struct IoParams {
 };
 
 struct GemmParams {
+  PrefetchSet pf;
   const uint16_t* w;      // swizzled weight fragments of this layer
   int M;                  // valid rows
   // A operand: bf16 fragment-major [Mpad/16][K/32][64][8]
@@ -70,6 +94,7 @@ struct GemmParams {
 };
 
 struct AttnParams {
+  PrefetchSet pf;
   const uint16_t* q;      // [M][8][256]
   const uint16_t* kp;     // packed K of this layer [B][nkb][16][64][8]
   const uint16_t* vp;     // packed V of this layer [B][nkb][16][64][8]

@@ -22,6 +22,7 @@ namespace pi_ae {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -38,6 +39,55 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+// Workgroup barrier that orders LDS only: this wave's LDS writes are complete
+// before it arrives, while its global loads stay in flight (a full
+// __syncthreads fence would also drain them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Body of an appended prefetching workgroup (see Prefetch): pi is its index
+// among the nwg prefetchers, res = its linear block index mod 8.
+__device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int pi, int res) {
+  const int per = pf.nwg >> 3, sub = pi >> 3;
+  uint32_t acc = 0;
+  for (int d = 0; d < 2; ++d) {
+    const Prefetch& r = pf.r[d];
+    if (!r.base || r.bytes == 0) continue;
+    const u32x4* base = static_cast<const u32x4*>(r.base);
+    const uint32_t n16 = r.bytes >> 4;
+    if (r.count > 0) {  // the slices of consumer workgroups j = res (mod 8)
+      for (int j = res + 8 * sub; j < r.count; j += 8 * per) {
+        const u32x4* src = base + size_t(j) * n16;
+        for (uint32_t i = threadIdx.x; i < n16; i += 8 * blockDim.x) {
+          u32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = (i + u * blockDim.x < n16) ? src[i + u * blockDim.x] : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
+        }
+      }
+    } else {  // broadcast: this XCD's share `sub` of the region
+      const uint32_t chunk = (n16 + per - 1) / per, lo = sub * chunk, hi = min(n16, lo + chunk);
+      for (uint32_t i = lo + threadIdx.x; i < hi; i += 8 * blockDim.x) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (i + u * blockDim.x < hi) ? base[i + u * blockDim.x] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0) *pf.sink = acc;  // keeps the loads
+}
+// Prefetching workgroups are appended along x (only at blockIdx.y == 0).
+#define PI_AE_PREFETCH_GUARD(PF, MAINX)                                               \
+  if (int(blockIdx.x) >= (MAINX)) {                                                   \
+    if (blockIdx.y == 0) prefetch_body((PF), int(blockIdx.x) - (MAINX), int(blockIdx.x) & 7); \
+    return;                                                                           \
+  }
+
 // GELU, tanh approximation (the MLP activation of the Gemma-shaped expert).
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float c = 0.7978845608028654f;
@@ -110,6 +160,7 @@ __global__ __launch_bounds__(256) void k_args(ArgsParams p) {
 //           inference flow", steps 3-4; dt applied in fp32);
 //   do_in:  h = x W_in^T + b_in                          (action_in_proj).
 __global__ __launch_bounds__(256) void k_io(IoParams p) {
+  PI_AE_PREFETCH_GUARD(p.pf, p.M)
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   __shared__ float su[kD];
   __shared__ float sred[4];
@@ -206,6 +257,7 @@ constexpr int kSsqTiles = kD / 16;  // partial sums of squares per row
 
 template <int MB, int NB, int NW, int KBW, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
+  PI_AE_PREFETCH_GUARD(p.pf, int(gridDim.x) - p.pf.nwg)
   constexpr int KB = KBW * NW;
   constexpr int E = MB * NB * 4 * 64;  // accumulator floats per wave
   constexpr int NT = NW * 64;
@@ -391,6 +443,207 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Tiled GEMM for large M (many episodes per call), where the loop is bound by
+// MFMA throughput rather than by weight streaming.  Workgroup tile BM x BN,
+// WM x WN waves each owning TM x TN 16x16 output blocks.  K advances one
+// 32-wide block per iteration through a double-buffered LDS stage holding the
+// tile's A and B fragments (1 KiB each, copied contiguously from their
+// fragment-major global layouts); global loads run PD blocks ahead in
+// registers.  The fused epilogues are those of k_gemm, applied by each wave to
+// its own accumulators.
+template <int TM, int TN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K) {
+  constexpr int NW = WM * WN;
+  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per stage
+  constexpr int BM = 16 * FA;
+  constexpr int FPW = F / NW;                              // fragments copied per wave
+  constexpr int PD = 4;                                    // k-blocks in flight
+  constexpr bool NORM = EPI != E_RES;
+  static_assert(F % NW == 0, "stage fragments split evenly over the waves");
+  static_assert(EPI == E_RES || TN % 2 == 0, "paired epilogues take n-block pairs");
+  static_assert(PD % 2 == 0, "the LDS double buffer alternates within one unrolled group");
+  __shared__ __attribute__((aligned(16))) u32x4 st[2][F][64];
+  __shared__ float srstd[BM];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int KB = K >> 5;
+  const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag);
+  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w);
+
+  u32x4 pre[PD][FPW];
+#define PI_AE_TILE_LOAD(KBI, SLOT)                                                     \
+  {                                                                                    \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                  \
+      const int f = q * NW + w;                                                        \
+      const u32x4* src = (f < FA) ? ap + (size_t(mb0 + f) * KB + (KBI)) * 64 + lane    \
+                                  : wp + (size_t(nb0 + f - FA) * KB + (KBI)) * 64 + lane; \
+      pre[SLOT][q] = *src;                                                             \
+    }                                                                                  \
+  }
+  // (K is a multiple of 32 * PD for every GEMM of the expert)
+  PI_AE_TILE_LOAD(0, 0)
+  PI_AE_TILE_LOAD(1, 1)
+  PI_AE_TILE_LOAD(2, 2)
+  PI_AE_TILE_LOAD(3, 3)
+
+  if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
+    for (int r = threadIdx.x; r < BM; r += NW * 64) {
+      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSsqTiles / 4; ++v) {
+        const float4 x = sp[v];
+        sum += (x.x + x.y) + (x.z + x.w);
+      }
+      srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
+    }
+  }
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // K loop unrolled by PD with literal slot numbers, so that every register
+  // slot and LDS buffer index is a constant (the prefetch registers stay in
+  // registers) and each wait covers exactly the block it needs.
+#define PI_AE_TILE_STEP(SL)                                                              \
+  {                                                                                      \
+    const int kb = kq + (SL);                                                            \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[(SL) & 1][q * NW + w][lane] = pre[SL][q]; \
+    PI_AE_TILE_LOAD(min(kb + PD, KB - 1), SL)                                            \
+    lds_barrier();                                                                       \
+    bf16x8 a[TM], b[TN];                                                                 \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(bf16x8, st[(SL) & 1][wm * TM + i][lane]); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(bf16x8, st[(SL) & 1][FA + wn * TN + j][lane]); \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]); \
+  }
+  static_assert(PD == 4, "the unrolled K step below names four slots");
+  for (int kq = 0; kq < KB; kq += PD) {
+    // (LDS buffer SL & 1 was last read two steps ago, before the last barrier;
+    // the tail steps re-read the last block so no branch hides a load)
+    PI_AE_TILE_STEP(0)
+    PI_AE_TILE_STEP(1)
+    PI_AE_TILE_STEP(2)
+    PI_AE_TILE_STEP(3)
+  }
+#undef PI_AE_TILE_STEP
+#undef PI_AE_TILE_LOAD
+
+  // epilogue: lane holds rows 4(lane/16)+r of each 16-row block, column
+  // lane%16.  Every operand is loaded first (the stores below could alias
+  // later loads as far as the compiler knows, which would serialise them).
+  const int cc = lane & 15, rq = 4 * (lane >> 4);
+  if constexpr (EPI == E_RES) {
+    float hv[TM][4][TN], gv[TN], sv[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = (nb0 + wn * TN + j) * 16 + cc;
+      gv[j] = p.gate[col];
+      sv[j] = p.s1_next ? p.s1_next[col] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          hv[i][r][j] = p.h_out[size_t(row < p.M ? row : 0) * kD + (nb0 + wn * TN + j) * 16 + cc];
+      }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
+        const bool live = row < p.M;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int nbg = nb0 + wn * TN + j, col = nbg * 16 + cc;
+          const float hn = hv[i][r][j] + acc[i][j][r] * gv[j];
+          if (live) p.h_out[size_t(row) * kD + col] = hn;
+          if (p.s1_next) {
+            float sq = hn * hn;
+            sq += __shfl_xor(sq, 1);
+            sq += __shfl_xor(sq, 2);
+            sq += __shfl_xor(sq, 4);
+            sq += __shfl_xor(sq, 8);
+            if (live) {
+              p.u_out[afrag_index(row, col, kD / 32)] = f2bf(hn * sv[j]);
+              if (cc == 0) p.ssq_out[size_t(row) * kSsqTiles + nbg] = sq;
+            }
+          }
+        }
+      }
+  } else {
+    constexpr int NP = TN / 2;
+    float b0[NP], b1[NP];
+    float2 cs[TM][4][NP];
+#pragma unroll
+    for (int jj = 0; jj < NP; ++jj) {
+      const int jp = (nb0 + wn * TN) / 2 + jj;  // global pair index
+      b0[jj] = p.bias[(2 * jp) * 16 + cc];
+      b1[jj] = p.bias[(2 * jp + 1) * 16 + cc];
+    }
+    if constexpr (EPI == E_QKV) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
+#pragma unroll
+          for (int jj = 0; jj < NP; ++jj) {
+            const int jp = (nb0 + wn * TN) / 2 + jj;
+            cs[i][r][jj] = (jp < 72) ? p.rope_cs[size_t(row < p.M ? row : 0) * kRopeHalf + (jp & 7) * 16 + cc]
+                                     : make_float2(1.f, 0.f);
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = (wm * TM + i) * 16 + rq + r;
+        const int row = mb0 * 16 + rl;
+        if (row >= p.M) continue;
+        const float rs = srstd[rl];
+#pragma unroll
+        for (int jj = 0; jj < NP; ++jj) {
+          const int jp = (nb0 + wn * TN) / 2 + jj;
+          const float y0 = acc[i][2 * jj][r] * rs + b0[jj];
+          const float y1 = acc[i][2 * jj + 1][r] * rs + b1[jj];
+          if constexpr (EPI == E_QKV) {
+            const int b = row / p.T, t = row - b * p.T;
+            if (jp < 72) {
+              const int ip = (jp & 7) * 16 + cc;
+              const float o0 = y0 * cs[i][r][jj].x - y1 * cs[i][r][jj].y;
+              const float o1 = y1 * cs[i][r][jj].x + y0 * cs[i][r][jj].y;
+              if (jp < 64) {
+                uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
+                dst[ip] = f2bf(o0);
+                dst[kRopeHalf + ip] = f2bf(o1);
+              } else {
+                const int key = p.P + t;
+                p.kp[kpack_index(b, key, ip, p.nkb)] = f2bf(o0);
+                p.kp[kpack_index(b, key, kRopeHalf + ip, p.nkb)] = f2bf(o1);
+              }
+            } else {
+              const int key = p.P + t, d0 = (jp - 72) * 32 + cc;
+              p.vp[vpack_index(b, key, d0, p.nkb)] = f2bf(y0);
+              p.vp[vpack_index(b, key, d0 + 16, p.nkb)] = f2bf(y1);
+            }
+          } else {
+            p.m_out[afrag_index(row, 16 * jp + cc, kF / 32)] = f2bf(gelu_tanh(y0) * y1);
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per call, once: pack every layer's prefix K/V into the attention's operand
 // order (see kpack_index / vpack_index) and build the additive key bias of
 // each episode: 0 for valid prefix keys and for the suffix keys, -inf for
@@ -517,6 +770,7 @@ __device__ __forceinline__ bf16x8 attn_softmax(const f32x4 (&s)[2], const float4
 constexpr int kAttnWaves = 8;
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
+  PI_AE_PREFETCH_GUARD(p.pf, int(gridDim.x) - p.pf.nwg)
   __shared__ __attribute__((aligned(16))) float ored[kAttnWaves * 16 * kOStride + kAttnWaves * 16 * 2];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
@@ -638,35 +892,51 @@ hipError_t launch_args(const ArgsParams& p, hipStream_t s) {
 }
 hipError_t launch_io(const IoParams& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
-  k_io<<<p.M, 256, 0, s>>>(p);
+  k_io<<<p.M + p.pf.nwg, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 2, 4, 8, E_QKV><<<dim3(kNqkv / 32, row_tiles(p.M)), 256, 0, s>>>(p);
+  if (p.M >= kTiledMinRows) {
+    k_gemm_tiled<4, 4, 2, 2, E_QKV><<<dim3(kNqkv / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kD);
+    return hipGetLastError();
+  }
+  k_gemm<4, 2, 4, 8, E_QKV><<<dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s) {
-  k_gemm<4, 2, 4, 8, E_GELU><<<dim3(kNgu / 32, row_tiles(p.M)), 256, 0, s>>>(p);
+  if (p.M >= kTiledMinRows) {
+    k_gemm_tiled<4, 4, 2, 2, E_GELU><<<dim3(kNgu / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kD);
+    return hipGetLastError();
+  }
+  k_gemm<4, 2, 4, 8, E_GELU><<<dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 // O and down: at small M, 32-row tiles halve each workgroup's activation
 // slice (all of it is then in flight at once) and double the CUs sharing it.
 hipError_t launch_o(const GemmParams& p, hipStream_t s) {
+  if (p.M >= kTiledMinRows) {
+    k_gemm_tiled<4, 4, 2, 2, E_RES><<<dim3(kD / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kH * kHd);
+    return hipGetLastError();
+  }
   if (p.M <= 64)
-    k_gemm<2, 1, 8, 8, E_RES><<<dim3(kD / 16, row_tiles(p.M, 32)), 512, 0, s>>>(p);
+    k_gemm<2, 1, 8, 8, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), 512, 0, s>>>(p);
   else
-    k_gemm<4, 1, 8, 8, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
+    k_gemm<4, 1, 8, 8, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), 512, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s) {
+  if (p.M >= kTiledMinRows) {
+    k_gemm_tiled<4, 4, 2, 2, E_RES><<<dim3(kD / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kF);
+    return hipGetLastError();
+  }
   if (p.M <= 64)
-    k_gemm<2, 1, 8, 16, E_RES><<<dim3(kD / 16, row_tiles(p.M, 32)), 512, 0, s>>>(p);
+    k_gemm<2, 1, 8, 16, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), 512, 0, s>>>(p);
   else
-    k_gemm<4, 1, 8, 16, E_RES><<<dim3(kD / 16, row_tiles(p.M)), 512, 0, s>>>(p);
+    k_gemm<4, 1, 8, 16, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), 512, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  k_attn<<<dim3((p.T * kH + 15) / 16, p.B), kAttnWaves * 64, 0, s>>>(p);
+  k_attn<<<dim3((p.T * kH + 15) / 16 + p.pf.nwg, p.B), kAttnWaves * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {

@@ -73,6 +73,7 @@ struct pi_ae_ctx {
   int nkb_max = 0;
   int* n_valid = nullptr;
   DevArgs* da = nullptr;
+  uint32_t* pf_sink = nullptr;  // never written: keeps prefetch loads alive
   int Mmax = 0, Mpad = 0;
   // host copies of the tables in natural column order (debug export)
   std::vector<float> tab[10];
@@ -381,7 +382,7 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   }
   // ---- workspaces (zeroed once; padded rows are never written)
   ctx->Mmax = cfg.max_batch * T;
-  ctx->Mpad = (ctx->Mmax + 63) / 64 * 64;
+  ctx->Mpad = (ctx->Mmax + 127) / 128 * 128;  // whole 128-row tiles of the large-M GEMM
   const size_t Mp = size_t(ctx->Mpad);
   ctx->h = ctx->dalloc<float>(Mp * kD);
   ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
@@ -397,6 +398,7 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->m = ctx->dalloc<uint16_t>(Mp * kF);
   ctx->n_valid = ctx->dalloc<int>(cfg.max_batch);
   ctx->da = ctx->dalloc<DevArgs>(1);
+  ctx->pf_sink = ctx->dalloc<uint32_t>(64);
   HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kD * 4));
   HIP_OR_THROW(hipMemset(ctx->q, 0, Mp * kH * kHd * 2));
   HIP_OR_THROW(hipMemset(ctx->kp, 0, npack * 2));
@@ -419,15 +421,72 @@ struct StopAt {
   bool hit(int k, int l, int ph) const { return k == step && (ph == 0 ? true : l == layer) && ph == phase; }
 };
 
+Prefetch slices(const void* base, size_t bytes, int count) { return Prefetch{base, uint32_t(bytes), count}; }
+Prefetch broadcast(const void* base, size_t bytes) { return Prefetch{base, uint32_t(bytes), 0}; }
+
+// L2 warm-up plan of the streaming (small-M) path: the spare workgroups of
+// each kernel read what the next kernels stream, into the L2 of the XCD whose
+// workgroups will read it (see Prefetch).  Only data that no kernel of the
+// loop writes is prefetched: weights, and whole prefix blocks of packed K/V.
+//   step input     -> layer 0 QKV weights
+//   QKV(l)         -> layer l prefix K and V (batch 1)
+//   attention(l)   -> layer l O and gate/up weights
+//   O(l)           -> layer l down weights
+//   down(l)        -> layer l+1 QKV weights
+PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phase) {
+  const pi_ae_config& cfg = ctx->cfg;
+  const int L = cfg.num_layers, T = cfg.chunk_len;
+  PrefetchSet pf{};
+  pf.sink = ctx->pf_sink;
+  if (B * T >= kTiledMinRows) return pf;
+  const size_t qkv_slice = size_t(32) * kD * 2, qkv_layer = size_t(kNqkv) * kD;
+  switch (phase) {
+    case 0:
+      if (k < cfg.num_steps) {
+        pf.r[0] = slices(ctx->w_qkv, qkv_slice, kNqkv / 32);
+        pf.nwg = 80;
+      }
+      break;
+    case 1: {
+      const int nkb = (P + T + 31) / 32, full = P / 32;
+      if (B == 1 && full > 0) {
+        const size_t off = size_t(l) * nkb * 8192;
+        pf.r[0] = broadcast(ctx->kp + off, size_t(full) * 8192 * 2);
+        pf.r[1] = broadcast(ctx->vp + off, size_t(full) * 8192 * 2);
+        pf.nwg = 64;
+      }
+      break;
+    }
+    case 2:
+      pf.r[0] = slices(ctx->w_o + size_t(kD) * kH * kHd * l, size_t(16) * kH * kHd * 2, kD / 16);
+      pf.r[1] = slices(ctx->w_gu + size_t(kNgu) * kD * l, size_t(32) * kD * 2, kNgu / 32);
+      pf.nwg = 160;
+      break;
+    case 3:
+      pf.r[0] = slices(ctx->w_d + size_t(kD) * kF * l, size_t(16) * kF * 2, kD / 16);
+      pf.nwg = 64;
+      break;
+    case 5:
+      if (l + 1 < L) {
+        pf.r[0] = slices(ctx->w_qkv + qkv_layer * (l + 1), qkv_slice, kNqkv / 32);
+        pf.nwg = 80;
+      }
+      break;
+  }
+  return pf;
+}
+
 // Launch one phase of one (step, layer); phase 0 is the step-boundary kernel
 // of step k (k == num_steps: the final output projection and Euler update).
 hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int l, int phase) {
   const pi_ae_config& cfg = ctx->cfg;
   const int L = cfg.num_layers, S = cfg.num_steps, T = cfg.chunk_len, M = B * T;
   const size_t kl = size_t(k) * L + l;
+  const PrefetchSet pf = warm_plan(ctx, B, P, k, l, phase);
   switch (phase) {
     case 0: {
       IoParams io{};
+      io.pf = pf;
       io.da = ctx->da;
       io.h = ctx->h;
       io.w_in = ctx->w_in;
@@ -449,6 +508,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
     case 1:
     case 4: {
       GemmParams g{};
+      g.pf = pf;
       g.M = M;
       g.eps = cfg.rms_eps;
       g.T = T;
@@ -473,6 +533,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
     }
     case 2: {
       AttnParams a{};
+      a.pf = pf;
       const int nkb = (P + T + 31) / 32;
       a.q = ctx->q;
       a.kp = ctx->kp + size_t(l) * B * nkb * 8192;
@@ -488,6 +549,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
     case 3:
     case 5: {
       GemmParams g{};
+      g.pf = pf;
       g.M = M;
       g.h_out = ctx->h;
       g.u_out = ctx->u;
@@ -704,30 +766,39 @@ PI_AE_API pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
-  std::vector<hipEvent_t> ev(2 * size_t(iters), nullptr);
-  hipError_t e = hipSuccess;
-  for (auto& x : ev)
-    if (e == hipSuccess) e = hipEventCreate(&x);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
   if (e == hipSuccess) e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
   // one full pass first so every intermediate holds real values
   if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, s, StopAt{});
-  for (int i = 0; i < iters && e == hipSuccess; ++i) {
-    const int l = i % L, k = (i / L) % S;
-    e = hipEventRecord(ev[2 * i], s);
-    if (e == hipSuccess) e = launch_phase(ctx, batch, kv->prefix_len, s, k, l, phase);
-    if (e == hipSuccess) e = hipEventRecord(ev[2 * i + 1], s);
-  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  double tot = 0.0;
-  for (int i = 0; i < iters && e == hipSuccess; ++i) {
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
-    tot += ms;
+  // the phase's kernel, `iters` times back to back as one graph (layers and
+  // steps cycled, so every launch streams that layer's weights)
+  if (e == hipSuccess) e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t e2 = hipSuccess;
+    for (int i = 0; i < iters && e2 == hipSuccess; ++i)
+      e2 = launch_phase(ctx, batch, kv->prefix_len, ctx->cap, (i / L) % S, i % L, phase);
+    e = hipStreamEndCapture(ctx->cap, &graph);
+    if (e2 != hipSuccess) e = e2;
   }
-  for (auto& x : ev)
-    if (x) hipEventDestroy(x);
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, s);  // warm
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (exec) hipGraphExecDestroy(exec);
+  if (graph) hipGraphDestroy(graph);
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("time_phase failed: ") + hipGetErrorString(e));
-  *avg_us = float(tot * 1000.0 / iters);
+  *avg_us = ms * 1000.f / float(iters);
   return PI_AE_OK;
 }
 

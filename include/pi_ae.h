@@ -198,13 +198,14 @@ pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const 
                                size_t n_bytes);
 
 /* Time one phase's kernel: after one full pass of the loop (so that every
- * intermediate holds real values; its result lands in `actions`), launch the
- * kernel of `phase` (numbering as in pi_ae_debug_probe) `iters` times on
- * `stream`, cycling through the layers (and steps) so that each launch
- * streams that layer's weights as it does inside the loop, with a HIP event
- * recorded right before and right after each launch.  *avg_us = mean of the
- * per-launch event intervals.  Synchronises `stream`.  Same argument rules as
- * pi_ae_sample, plus batch >= 1 and 1 <= iters <= 100000. */
+ * intermediate holds real values; its result lands in `actions`), capture
+ * `iters` back-to-back launches of the kernel of `phase` (numbering as in
+ * pi_ae_debug_probe) as one hipGraph, cycling through the layers (and steps)
+ * so that each launch streams that layer's weights as it does inside the
+ * loop, and replay it between two HIP events on `stream`.  *avg_us = elapsed
+ * time / iters (the per-launch duration as inside the loop's own graph).
+ * Synchronises `stream`.  Same argument rules as pi_ae_sample, plus
+ * batch >= 1 and 1 <= iters <= 100000. */
 pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
                                     int32_t batch, int32_t phase, int32_t iters, void* stream, float* avg_us);
 
