@@ -8,9 +8,10 @@ chunk 63.
   python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu]
 
 Reported beside the throughput: the roofline of the dominant kernel (the
-gate/up GEMM at batch 1, algorithmic bytes = its bf16 weights per launch,
-timed live with HIP events, one event pair per launch, cycling over layers),
-and the CPU oracle timed on this host on a bounded sample.
+gate/up GEMM: at batch 1 its algorithmic bytes = its bf16 weights per launch;
+at batch 32 its flops), its duration timed live inside the loop with a HIP
+event pair bound to each of its launches, and the CPU oracle timed on this
+host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -91,7 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--kernel-iters", type=int, default=360)
+    ap.add_argument("--kernel-chunks", type=int, default=2,
+                    help="whole loop passes over which each kernel's in-loop duration is averaged")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the denoise loop on exactly one GPU; --gpus must be 1", file=sys.stderr)
@@ -135,10 +137,11 @@ def main():
     print(f"bench: {ms_per_step * 1e3:.1f} us/chunk (median {median_us:.1f}, p99 {p99_us:.1f})",
           file=sys.stderr, flush=True)
 
-    # dominant kernel, timed live on the same stream with one event pair per launch
+    # per-kernel durations inside the loop: HIP events bound to each launch of
+    # one phase's kernel, over whole passes of the loop on the same stream
     phase_us = {}
     for ph in range(6):
-        phase_us[ph] = ctx.time_phase(dk, dv, dm, dn, out, w.batch, w.prefix_len, ph, args.kernel_iters, stream)
+        phase_us[ph] = ctx.time_phase(dk, dv, dm, dn, out, w.batch, w.prefix_len, ph, args.kernel_chunks, stream)
     print("bench: per-launch us " + ", ".join(f"{PHASE_NAMES[p]}={t:.2f}" for p, t in phase_us.items()),
           file=sys.stderr, flush=True)
     bytes_step = algorithmic_bytes_per_step(w)

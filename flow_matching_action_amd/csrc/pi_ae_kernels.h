@@ -45,7 +45,7 @@ struct Prefetch {
 };
 struct PrefetchSet {
   Prefetch r[2];
-  int nwg;        // prefetching workgroups appended (multiple of 8; 0 = none)
+  int nwg;        // columns of prefetching workgroups appended (multiple of 8; 0 = none)
   uint32_t* sink; // never written in practice (keeps the loads alive)
 };
 
@@ -121,14 +121,20 @@ struct ArgsParams {
   int B, P;
 };
 
+// Optional per-launch timing: events recorded at the kernel's own start and
+// end (used to time one kernel inside the real loop).
+struct KernelTiming {
+  hipEvent_t start, stop;
+};
+
 hipError_t launch_args(const ArgsParams& p, hipStream_t s);
-hipError_t launch_io(const IoParams& p, hipStream_t s);
-hipError_t launch_qkv(const GemmParams& p, hipStream_t s);
-hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s);
-hipError_t launch_o(const GemmParams& p, hipStream_t s);
-hipError_t launch_gu(const GemmParams& p, hipStream_t s);
-hipError_t launch_down(const GemmParams& p, hipStream_t s);
+hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

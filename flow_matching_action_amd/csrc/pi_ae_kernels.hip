@@ -15,6 +15,8 @@
 // the fused epilogue runs.  Activations stay L2-resident between kernels.
 #include "pi_ae_kernels.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 
 namespace pi_ae {
@@ -47,45 +49,47 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// Body of an appended prefetching workgroup (see Prefetch): pi is its index
-// among the nwg prefetchers, res = its linear block index mod 8.
-__device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int pi, int res) {
-  const int per = pf.nwg >> 3, sub = pi >> 3;
+// Body of an appended prefetching workgroup (see Prefetch).  The `per`
+// prefetchers that share XCD residue `res` split that XCD's bytes evenly;
+// this one is number `sub` of them.  Loads are batched 8 deep per thread.
+__device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, int per, int res) {
   uint32_t acc = 0;
   for (int d = 0; d < 2; ++d) {
     const Prefetch& r = pf.r[d];
-    if (!r.base || r.bytes == 0) continue;
+    if (!r.base || r.bytes < 16) continue;
     const u32x4* base = static_cast<const u32x4*>(r.base);
     const uint32_t n16 = r.bytes >> 4;
-    if (r.count > 0) {  // the slices of consumer workgroups j = res (mod 8)
-      for (int j = res + 8 * sub; j < r.count; j += 8 * per) {
-        const u32x4* src = base + size_t(j) * n16;
-        for (uint32_t i = threadIdx.x; i < n16; i += 8 * blockDim.x) {
-          u32x4 v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = (i + u * blockDim.x < n16) ? src[i + u * blockDim.x] : u32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
-        }
-      }
-    } else {  // broadcast: this XCD's share `sub` of the region
-      const uint32_t chunk = (n16 + per - 1) / per, lo = sub * chunk, hi = min(n16, lo + chunk);
-      for (uint32_t i = lo + threadIdx.x; i < hi; i += 8 * blockDim.x) {
+    // broadcast: one "slice", the whole region; slices: j = res, res+8, ...
+    const uint32_t nsl = r.count > 0 ? (r.count > res ? uint32_t(r.count - res + 7) / 8u : 0u) : 1u;
+    const uint64_t total = uint64_t(nsl) * n16;
+    uint32_t u = uint32_t(total * sub / per);
+    const uint32_t hi = uint32_t(total * (sub + 1) / per);
+    while (u < hi) {  // this prefetcher's units, one slice at a time
+      const uint32_t sl = u / n16, off = u - sl * n16, n = min(hi, (sl + 1) * n16) - u;
+      const u32x4* src = base + (r.count > 0 ? size_t(res + 8 * sl) * n16 : size_t(0)) + off;
+      for (uint32_t i = threadIdx.x; i < n; i += 8 * blockDim.x) {
         u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (i + u * blockDim.x < hi) ? base[i + u * blockDim.x] : u32x4{0, 0, 0, 0};
+        for (int k = 0; k < 8; ++k) v[k] = (i + k * blockDim.x < n) ? src[i + k * blockDim.x] : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].w;
+        for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].w;
       }
+      u += n;
     }
   }
   if (acc == 0x9E3779B9u && threadIdx.x == 0) *pf.sink = acc;  // keeps the loads
 }
-// Prefetching workgroups are appended along x (only at blockIdx.y == 0).
-#define PI_AE_PREFETCH_GUARD(PF, MAINX)                                               \
-  if (int(blockIdx.x) >= (MAINX)) {                                                   \
-    if (blockIdx.y == 0) prefetch_body((PF), int(blockIdx.x) - (MAINX), int(blockIdx.x) & 7); \
-    return;                                                                           \
+// Prefetching workgroups are the columns appended along x (a multiple of 8),
+// in every row of the grid when the grid's width is a multiple of 8 (then
+// the XCD residue of a block is its x mod 8 in every row), else in row 0.
+#define PI_AE_PREFETCH_GUARD(PF, MAINX)                                                       \
+  if (int(blockIdx.x) >= (MAINX)) {                                                           \
+    const int cols_ = (int(gridDim.x) - (MAINX)) >> 3;                                        \
+    const int rows_ = (gridDim.x & 7u) ? 1 : int(gridDim.y);                                  \
+    if (int(blockIdx.y) < rows_)                                                              \
+      prefetch_body((PF), ((int(blockIdx.x) - (MAINX)) >> 3) + int(blockIdx.y) * cols_, cols_ * rows_, \
+                    int(blockIdx.x) & 7);                                                     \
+    return;                                                                                   \
   }
 
 // GELU, tanh approximation (the MLP activation of the Gemma-shaped expert).
@@ -886,58 +890,53 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 // ---------------------------------------------------------------------------
 static inline unsigned row_tiles(int M, int rows = 64) { return unsigned((M + rows - 1) / rows); }
 
+// One launch; with a KernelTiming the start/stop events bracket this kernel's
+// own execution (hipExtLaunchKernel), so their elapsed time is its duration.
+template <class... A, class... B>
+static hipError_t go(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t s, const KernelTiming* t, B... args) {
+  if (t)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, t->start, t->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
+
 hipError_t launch_args(const ArgsParams& p, hipStream_t s) {
   k_args<<<1, 256, 0, s>>>(p);
   return hipGetLastError();
 }
-hipError_t launch_io(const IoParams& p, hipStream_t s) {
+hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M <= 0) return hipSuccess;
-  k_io<<<p.M + p.pf.nwg, 256, 0, s>>>(p);
-  return hipGetLastError();
+  return go(k_io, dim3(p.M + p.pf.nwg), dim3(256), s, t, p);
 }
-hipError_t launch_qkv(const GemmParams& p, hipStream_t s) {
-  if (p.M >= kTiledMinRows) {
-    k_gemm_tiled<4, 4, 2, 2, E_QKV><<<dim3(kNqkv / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kD);
-    return hipGetLastError();
-  }
-  k_gemm<4, 2, 4, 8, E_QKV><<<dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), 256, 0, s>>>(p);
-  return hipGetLastError();
+hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M >= kTiledMinRows)
+    return go(k_gemm_tiled<4, 4, 2, 2, E_QKV>, dim3(kNqkv / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+  return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
-hipError_t launch_gu(const GemmParams& p, hipStream_t s) {
-  if (p.M >= kTiledMinRows) {
-    k_gemm_tiled<4, 4, 2, 2, E_GELU><<<dim3(kNgu / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kD);
-    return hipGetLastError();
-  }
-  k_gemm<4, 2, 4, 8, E_GELU><<<dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), 256, 0, s>>>(p);
-  return hipGetLastError();
+hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M >= kTiledMinRows)
+    return go(k_gemm_tiled<4, 4, 2, 2, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+  return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 // O and down: at small M, 32-row tiles halve each workgroup's activation
 // slice (all of it is then in flight at once) and double the CUs sharing it.
-hipError_t launch_o(const GemmParams& p, hipStream_t s) {
-  if (p.M >= kTiledMinRows) {
-    k_gemm_tiled<4, 4, 2, 2, E_RES><<<dim3(kD / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kH * kHd);
-    return hipGetLastError();
-  }
+hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M >= kTiledMinRows)
+    return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
   if (p.M <= 64)
-    k_gemm<2, 1, 8, 8, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), 512, 0, s>>>(p);
-  else
-    k_gemm<4, 1, 8, 8, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), 512, 0, s>>>(p);
-  return hipGetLastError();
+    return go(k_gemm<2, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), dim3(512), s, t, p);
+  return go(k_gemm<4, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
-hipError_t launch_down(const GemmParams& p, hipStream_t s) {
-  if (p.M >= kTiledMinRows) {
-    k_gemm_tiled<4, 4, 2, 2, E_RES><<<dim3(kD / 128, row_tiles(p.M, 128)), 256, 0, s>>>(p, kF);
-    return hipGetLastError();
-  }
+hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M >= kTiledMinRows)
+    return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
   if (p.M <= 64)
-    k_gemm<2, 1, 8, 16, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), 512, 0, s>>>(p);
-  else
-    k_gemm<4, 1, 8, 16, E_RES><<<dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), 512, 0, s>>>(p);
-  return hipGetLastError();
+    return go(k_gemm<2, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), dim3(512), s, t, p);
+  return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
-hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  k_attn<<<dim3((p.T * kH + 15) / 16 + p.pf.nwg, p.B), kAttnWaves * 64, 0, s>>>(p);
-  return hipGetLastError();
+hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
+  return go(k_attn, dim3((p.T * kH + 15) / 16 + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {
   if (p.B <= 0 || p.nkb <= 0) return hipSuccess;

@@ -478,7 +478,8 @@ PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phas
 
 // Launch one phase of one (step, layer); phase 0 is the step-boundary kernel
 // of step k (k == num_steps: the final output projection and Euler update).
-hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int l, int phase) {
+hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int l, int phase,
+                        const KernelTiming* t = nullptr) {
   const pi_ae_config& cfg = ctx->cfg;
   const int L = cfg.num_layers, S = cfg.num_steps, T = cfg.chunk_len, M = B * T;
   const size_t kl = size_t(k) * L + l;
@@ -503,7 +504,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       io.s1_next = k < S ? ctx->attn_s1 + size_t(k) * L * kD : nullptr;
       io.u_out = ctx->u;
       io.ssq_out = ctx->ssq;
-      return launch_io(io, s);
+      return launch_io(io, s, t);
     }
     case 1:
     case 4: {
@@ -524,12 +525,12 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
         g.nkb = nkb;
         g.kp = ctx->kp + size_t(l) * B * nkb * 8192;
         g.vp = ctx->vp + size_t(l) * B * nkb * 8192;
-        return launch_qkv(g, s);
+        return launch_qkv(g, s, t);
       }
       g.w = ctx->w_gu + size_t(kNgu) * kD * l;
       g.bias = ctx->c_gu + kl * kNgu;
       g.m_out = ctx->m;
-      return launch_gu(g, s);
+      return launch_gu(g, s, t);
     }
     case 2: {
       AttnParams a{};
@@ -544,7 +545,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       a.T = T;
       a.P = P;
       a.nkb = nkb;
-      return launch_attn(a, s);
+      return launch_attn(a, s, t);
     }
     case 3:
     case 5: {
@@ -559,20 +560,22 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
         g.a_frag = ctx->o;
         g.gate = ctx->attn_g + kl * kD;
         g.s1_next = ctx->ffn_s1 + kl * kD;
-        return launch_o(g, s);
+        return launch_o(g, s, t);
       }
       // next: the following layer's QKV, or (last layer) the step boundary
       g.w = ctx->w_d + size_t(kD) * kF * l;
       g.a_frag = ctx->m;
       g.gate = ctx->ffn_g + kl * kD;
       g.s1_next = (l + 1 < L) ? ctx->attn_s1 + (kl + 1) * kD : nullptr;
-      return launch_down(g, s);
+      return launch_down(g, s, t);
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& stop) {
+// timed_phase / timing: launch i of that phase (in loop order) gets timing[i].
+hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& stop, int timed_phase = -1,
+                   const KernelTiming* timing = nullptr) {
   const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
   hipError_t e;
   PackParams pp{};
@@ -588,12 +591,14 @@ hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& st
   pp.T = ctx->cfg.chunk_len;
   pp.nkb = (P + pp.T + 31) / 32;
   if ((e = launch_pack(pp, L, s)) != hipSuccess) return e;
+  int n_timed = 0;
+  auto tm = [&](int ph) { return (timing && ph == timed_phase) ? &timing[n_timed++] : nullptr; };
   for (int k = 0; k <= S; ++k) {
-    if ((e = launch_phase(ctx, B, P, s, k, 0, 0)) != hipSuccess) return e;
+    if ((e = launch_phase(ctx, B, P, s, k, 0, 0, tm(0))) != hipSuccess) return e;
     if (stop.hit(k, 0, 0) || k == S) return hipSuccess;
     for (int l = 0; l < L; ++l)
       for (int ph = 1; ph <= 5; ++ph) {
-        if ((e = launch_phase(ctx, B, P, s, k, l, ph)) != hipSuccess) return e;
+        if ((e = launch_phase(ctx, B, P, s, k, l, ph, tm(ph))) != hipSuccess) return e;
         if (stop.hit(k, l, ph)) return hipSuccess;
       }
   }
@@ -757,48 +762,39 @@ PI_AE_API pi_ae_status pi_ae_debug_host_table(const pi_ae_config* cfg, const pi_
 }
 
 PI_AE_API pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise,
-                                              float* actions, int32_t batch, int32_t phase, int32_t iters,
+                                              float* actions, int32_t batch, int32_t phase, int32_t chunks,
                                               void* stream, float* avg_us) {
   pi_ae_status st = check_call(ctx, kv, noise, actions, batch);
   if (st) return st;
-  if (batch < 1 || phase < 0 || phase > 5 || iters < 1 || iters > 100000 || !avg_us)
-    return fail(PI_AE_EINVAL, "time_phase: batch >= 1, phase in [0, 5], iters in [1, 100000], avg_us non-NULL");
+  if (batch < 1 || phase < 0 || phase > 5 || chunks < 1 || chunks > 1000 || !avg_us)
+    return fail(PI_AE_EINVAL, "time_phase: batch >= 1, phase in [0, 5], chunks in [1, 1000], avg_us non-NULL");
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-  hipError_t e = hipEventCreate(&e0);
-  if (e == hipSuccess) e = hipEventCreate(&e1);
-  if (e == hipSuccess) e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
-  // one full pass first so every intermediate holds real values
-  if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, s, StopAt{});
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  // the phase's kernel, `iters` times back to back as one graph (layers and
-  // steps cycled, so every launch streams that layer's weights)
-  if (e == hipSuccess) e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
-  if (e == hipSuccess) {
-    hipError_t e2 = hipSuccess;
-    for (int i = 0; i < iters && e2 == hipSuccess; ++i)
-      e2 = launch_phase(ctx, batch, kv->prefix_len, ctx->cap, (i / L) % S, i % L, phase);
-    e = hipStreamEndCapture(ctx->cap, &graph);
-    if (e2 != hipSuccess) e = e2;
+  const int per_chunk = phase == 0 ? S + 1 : S * L;
+  std::vector<KernelTiming> tv(size_t(per_chunk) * chunks, KernelTiming{nullptr, nullptr});
+  hipError_t e = hipSuccess;
+  for (auto& t : tv) {
+    if (e == hipSuccess) e = hipEventCreate(&t.start);
+    if (e == hipSuccess) e = hipEventCreate(&t.stop);
   }
-  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (e == hipSuccess) e = hipGraphLaunch(exec, s);  // warm
-  if (e == hipSuccess) e = hipEventRecord(e0, s);
-  if (e == hipSuccess) e = hipGraphLaunch(exec, s);
-  if (e == hipSuccess) e = hipEventRecord(e1, s);
-  if (e == hipSuccess) e = hipEventSynchronize(e1);
-  float ms = 0.f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
-  if (exec) hipGraphExecDestroy(exec);
-  if (graph) hipGraphDestroy(graph);
-  if (e0) hipEventDestroy(e0);
-  if (e1) hipEventDestroy(e1);
+  for (int c = 0; c < chunks && e == hipSuccess; ++c) {
+    e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
+    if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, s, StopAt{}, phase, &tv[size_t(c) * per_chunk]);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  double sum_ms = 0.0;
+  for (auto& t : tv) {
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    sum_ms += ms;
+  }
+  for (auto& t : tv) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("time_phase failed: ") + hipGetErrorString(e));
-  *avg_us = ms * 1000.f / float(iters);
+  *avg_us = float(sum_ms * 1000.0 / double(tv.size()));
   return PI_AE_OK;
 }
 

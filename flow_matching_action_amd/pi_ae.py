@@ -194,12 +194,13 @@ class Context:
         _check(self._lib.pi_ae_sample(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
                                       _stream_handle(stream)))
 
-    def time_phase(self, k, v, pad_mask, noise, actions, batch, prefix_len, phase, iters, stream=None) -> float:
-        """Mean per-launch duration (us) of one phase's kernel, HIP events on `stream`."""
+    def time_phase(self, k, v, pad_mask, noise, actions, batch, prefix_len, phase, chunks, stream=None) -> float:
+        """Mean duration (us) of one phase's kernel inside the loop: `chunks` whole
+        passes on `stream`, a HIP event pair bound to each launch of that kernel."""
         kv = self._kv(k, v, pad_mask, prefix_len)
         us = ctypes.c_float()
         _check(self._lib.pi_ae_debug_time_phase(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
-                                                int(phase), int(iters), _stream_handle(stream), ctypes.byref(us)))
+                                                int(phase), int(chunks), _stream_handle(stream), ctypes.byref(us)))
         return float(us.value)
 
     def table(self, which: int, n: int) -> np.ndarray:

@@ -125,7 +125,8 @@ typedef struct pi_ae_ctx pi_ae_ctx;
  *   - Q, K and V are fused into one [(heads+2)*head_dim][width] matrix whose
  *     RoPE is applied in the GEMM epilogue; gate and up are fused likewise;
  *   - dt is applied to action_out_proj's output in the fp32 epilogue;
- *   - the RoPE cos/sin table for positions 0 .. max_prefix_len+chunk_len-1.
+ *   - the RoPE inverse frequencies base^(-2i/head_dim) in fp64 (each call
+ *     turns them into the cos/sin rows of its own suffix positions).
  * Host arithmetic is fp64; tables are stored fp32, weights stay bf16.
  * Synchronous on the current HIP device; reads the host arrays only during the
  * call.  The library owns everything it allocates; *out is written only on
@@ -197,17 +198,17 @@ pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const 
                                int32_t step, int32_t layer, int32_t phase, int32_t which, void* host_out,
                                size_t n_bytes);
 
-/* Time one phase's kernel: after one full pass of the loop (so that every
- * intermediate holds real values; its result lands in `actions`), capture
- * `iters` back-to-back launches of the kernel of `phase` (numbering as in
- * pi_ae_debug_probe) as one hipGraph, cycling through the layers (and steps)
- * so that each launch streams that layer's weights as it does inside the
- * loop, and replay it between two HIP events on `stream`.  *avg_us = elapsed
- * time / iters (the per-launch duration as inside the loop's own graph).
- * Synchronises `stream`.  Same argument rules as pi_ae_sample, plus
- * batch >= 1 and 1 <= iters <= 100000. */
+/* Time one phase's kernel inside the real loop: run the whole loop `chunks`
+ * times on `stream`, launched kernel by kernel (the same kernels, order and
+ * arguments as the captured graph), with a pair of HIP events bound to each
+ * launch of the kernel of `phase` (numbering as in pi_ae_debug_probe): the
+ * events are taken at that kernel's own start and end, so each pair's
+ * elapsed time is one launch's duration in the loop's context.  *avg_us =
+ * mean over all timed launches.  The result of the last pass lands in
+ * `actions`.  Synchronises `stream`.  Same argument rules as pi_ae_sample,
+ * plus batch >= 1 and 1 <= chunks <= 1000. */
 pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
-                                    int32_t batch, int32_t phase, int32_t iters, void* stream, float* avg_us);
+                                    int32_t batch, int32_t phase, int32_t chunks, void* stream, float* avg_us);
 
 #ifdef __cplusplus
 }
