@@ -44,7 +44,7 @@ struct Prefetch {
   int count;
 };
 struct PrefetchSet {
-  Prefetch r[2];
+  Prefetch r[3];
   int nwg;        // columns of prefetching workgroups appended (multiple of 8; 0 = none)
   uint32_t* sink; // never written in practice (keeps the loads alive)
 };

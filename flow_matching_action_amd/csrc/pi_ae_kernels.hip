@@ -54,7 +54,7 @@ __device__ __forceinline__ void lds_barrier() {
 // this one is number `sub` of them.  Loads are batched 8 deep per thread.
 __device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, int per, int res) {
   uint32_t acc = 0;
-  for (int d = 0; d < 2; ++d) {
+  for (int d = 0; d < 3; ++d) {
     const Prefetch& r = pf.r[d];
     if (!r.base || r.bytes < 16) continue;
     const u32x4* base = static_cast<const u32x4*>(r.base);
@@ -295,9 +295,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
       bw[nb][kb] = wp[(size_t(j * NB + nb) * KB + ws * KBW + kb) * 64 + lane];
 
   // 3. epilogue operands that do not depend on the GEMM, in flight during it
-  constexpr int EPT = (EPI == E_RES) ? E / NT : 1;        // residual elements per thread
+  constexpr int EPT = (EPI == E_RES) ? (E + NT - 1) / NT : 1;  // residual elements per thread
   constexpr int PPT = (EPI == E_RES) ? 1 : MB * 256 / NT;  // output pairs per thread
-  static_assert(E % NT == 0 && (MB * 256) % NT == 0, "epilogue work divides evenly");
+  static_assert((E % NT == 0 || NT % E == 0) && (EPI == E_RES || (MB * 256) % NT == 0),
+                "epilogue work divides evenly (or leaves whole waves idle)");
   float eh[EPT], eg[EPT], es[EPT];
   float eb0[PPT], eb1[PPT];
   float2 ecs[PPT];
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   if constexpr (EPI == E_RES) {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-      const int e = threadIdx.x + q * NT;
+      const int e = min(int(threadIdx.x) + q * NT, E - 1);  // threads past E: a harmless duplicate
       const int mb = e / (NB * 256), nb = (e >> 8) % NB, i = (e >> 6) & 3, ln = e & 63;
       const int row = row0 + mb * 16 + 4 * (ln >> 4) + i;
       const int col = (j * NB + nb) * 16 + (ln & 15);
@@ -378,6 +379,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
       const int e = threadIdx.x + q * NT;
+      if (E < NT && e >= E) break;  // whole waves idle when the tile is smaller than the workgroup
       float x = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) x += red[w2 * E + e];
@@ -912,6 +914,8 @@ hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
     return go(k_gemm_tiled<4, 4, 2, 2, E_QKV>, dim3(kNqkv / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+  if (p.M <= 64)  // 32-row tiles: half the activation bytes per workgroup, twice the CUs
+    return go(k_gemm<2, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M, 32)), dim3(256), s, t, p);
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
@@ -919,20 +923,20 @@ hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) 
     return go(k_gemm_tiled<4, 4, 2, 2, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
-// O and down: at small M, 32-row tiles halve each workgroup's activation
-// slice (all of it is then in flight at once) and double the CUs sharing it.
+// O and down: at small M, 16-row tiles quarter each workgroup's activation
+// slice and spread the launch over four times the CUs.
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
     return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
   if (p.M <= 64)
-    return go(k_gemm<2, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), dim3(512), s, t, p);
+    return go(k_gemm<1, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
     return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
   if (p.M <= 64)
-    return go(k_gemm<2, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 32)), dim3(512), s, t, p);
+    return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {

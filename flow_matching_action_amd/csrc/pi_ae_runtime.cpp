@@ -424,22 +424,23 @@ struct StopAt {
 Prefetch slices(const void* base, size_t bytes, int count) { return Prefetch{base, uint32_t(bytes), count}; }
 Prefetch broadcast(const void* base, size_t bytes) { return Prefetch{base, uint32_t(bytes), 0}; }
 
-// L2 warm-up plan of the streaming (small-M) path: the spare workgroups of
-// each kernel read what the next kernels stream, into the L2 of the XCD whose
-// workgroups will read it (see Prefetch).  Only data that no kernel of the
-// loop writes is prefetched: weights, and whole prefix blocks of packed K/V.
+// L2 warm-up plan of the streaming (small-M) path: spare workgroups of a
+// kernel read what a later kernel streams, into the L2 of the XCD whose
+// workgroups will read it (see Prefetch).  Only kernels that leave CUs idle
+// host warm-ups (a prefetching workgroup that shares a CU with a main one
+// slows it more than the warm-up saves): the step input, QKV (80 or 160
+// workgroups) and attention (32 per episode).  Only data that no kernel of
+// the loop writes is prefetched: weights, and whole prefix blocks of K/V.
 //   step input     -> layer 0 QKV weights
 //   QKV(l)         -> layer l prefix K and V (batch 1)
 //   attention(l)   -> layer l O and gate/up weights
-//   O(l)           -> layer l down weights
-//   down(l)        -> layer l+1 QKV weights
 PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phase) {
   const pi_ae_config& cfg = ctx->cfg;
-  const int L = cfg.num_layers, T = cfg.chunk_len;
+  const int T = cfg.chunk_len;
   PrefetchSet pf{};
   pf.sink = ctx->pf_sink;
   if (B * T >= kTiledMinRows) return pf;
-  const size_t qkv_slice = size_t(32) * kD * 2, qkv_layer = size_t(kNqkv) * kD;
+  const size_t qkv_slice = size_t(32) * kD * 2;
   switch (phase) {
     case 0:
       if (k < cfg.num_steps) {
@@ -453,7 +454,7 @@ PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phas
         const size_t off = size_t(l) * nkb * 8192;
         pf.r[0] = broadcast(ctx->kp + off, size_t(full) * 8192 * 2);
         pf.r[1] = broadcast(ctx->vp + off, size_t(full) * 8192 * 2);
-        pf.nwg = 64;
+        pf.nwg = 32;
       }
       break;
     }
@@ -461,16 +462,6 @@ PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phas
       pf.r[0] = slices(ctx->w_o + size_t(kD) * kH * kHd * l, size_t(16) * kH * kHd * 2, kD / 16);
       pf.r[1] = slices(ctx->w_gu + size_t(kNgu) * kD * l, size_t(32) * kD * 2, kNgu / 32);
       pf.nwg = 160;
-      break;
-    case 3:
-      pf.r[0] = slices(ctx->w_d + size_t(kD) * kF * l, size_t(16) * kF * 2, kD / 16);
-      pf.nwg = 64;
-      break;
-    case 5:
-      if (l + 1 < L) {
-        pf.r[0] = slices(ctx->w_qkv + qkv_layer * (l + 1), qkv_slice, kNqkv / 32);
-        pf.nwg = 80;
-      }
       break;
   }
   return pf;
