@@ -85,6 +85,22 @@ def cpu_baseline(w, wb, k, v, mask, noise, target_s: float = 12.0):
                       f"NumPy fp32, median {per_chunk * 1e3:.0f} ms/chunk"}
 
 
+COPY_BYTES = 256 << 20  # fp32 source read once and destination written once per launch
+
+
+def calibrate_copy(torch):
+    """A plain elementwise copy (dst = src * 1) of COPY_BYTES each way, 3 launches:
+    the reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": True, "read_bytes": COPY_BYTES, "write_bytes": COPY_BYTES, "launches": 3}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-chunks", type=int, default=2,
                     help="whole loop passes over which each kernel's in-loop duration is averaged")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain elementwise copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs the denoise loop on exactly one GPU; --gpus must be 1", file=sys.stderr)
@@ -101,6 +119,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     from flow_matching_action_amd import inputs, pi_ae
 
@@ -167,6 +189,26 @@ def main():
                 "traffic": None}
         whole_frac = flops_step * cfg.num_steps / chunk_s / (MFMA_BF16_PEAK_TFS * 1e12)
 
+    # every phase kernel against the same roofline: algorithmic bytes per
+    # launch (weights; valid prefix K/V for attention) over its in-loop duration
+    launches = {0: cfg.num_steps + 1, **{ph: cfg.num_steps * cfg.num_layers for ph in range(1, 6)}}
+    alg_bytes = dict(PHASE_WEIGHT_BYTES)
+    alg_bytes[0] = 2 * 32 * 1024 * 2
+    alg_bytes[2] = w.batch * w.n_valid * 256 * 2 * 2
+    M = w.batch * cfg.chunk_len
+    alg_flops = {0: 2 * M * 32 * 1024 * 2, 1: 2 * M * 1024 * 2560, 3: 2 * M * 2048 * 1024, 4: 2 * M * 1024 * 8192,
+                 5: 2 * M * 4096 * 1024, 2: 4 * 8 * cfg.chunk_len * (w.n_valid + cfg.chunk_len) * 256 * w.batch}
+    by_kernel = {}
+    for ph in range(6):
+        sec = phase_us[ph] * 1e-6
+        gbs = alg_bytes[ph] / sec / 1e9
+        tfs = alg_flops[ph] / sec / 1e12
+        by_kernel[PHASE_NAMES[ph]] = {
+            "us": round(phase_us[ph], 3), "alg_bytes": alg_bytes[ph], "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "alg_flops": alg_flops[ph], "TFLOP/s": round(tfs, 2),
+            "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "time_share": round(phase_us[ph] * launches[ph] / (ms_per_step * 1e3), 4)}
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, wb, k, v, mask, noise)
@@ -193,6 +235,7 @@ def main():
         "whole_loop_roofline_frac": round(whole_frac, 4),
         "per_launch_us": {PHASE_NAMES[p]: round(t, 3) for p, t in phase_us.items()},
         "roofline": roof,
+        "roofline_by_kernel": by_kernel,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
