@@ -773,6 +773,44 @@ __device__ __forceinline__ bf16x8 attn_softmax(const f32x4 (&s)[2], const float4
   return pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]), make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
 }
 
+// The same online-softmax update over two key blocks at once (64 keys):
+// s[0..1] / bias[0..1] belong to the first block, s[2..3] / bias[2..3] to the
+// second; pa and pb are their probabilities in PV operand order.
+__device__ __forceinline__ void attn_softmax2(const f32x4 (&s)[4], const float4 (&bias)[4], float& m_run,
+                                              float& l_run, float& alpha, bf16x8& pa, bf16x8& pb) {
+  const float sc = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
+  float pr[4][4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int mk = 0; mk < 4; ++mk) {
+    const float bv[4] = {bias[mk].x, bias[mk].y, bias[mk].z, bias[mk].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[mk][i] = s[mk][i] * sc + bv[i];
+      mloc = fmaxf(mloc, pr[mk][i]);
+    }
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(m_run, mloc);
+  const bool none = (m_new == -INFINITY);
+  alpha = none ? 1.f : exp2f(m_run - m_new);
+  float lsum = 0.f;
+#pragma unroll
+  for (int mk = 0; mk < 4; ++mk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[mk][i] = none ? 0.f : exp2f(pr[mk][i] - m_new);
+      lsum += pr[mk][i];
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  l_run = l_run * alpha + lsum;
+  m_run = m_new;
+  pa = pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]), make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
+  pb = pack8(make_float4(pr[2][0], pr[2][1], pr[2][2], pr[2][3]), make_float4(pr[3][0], pr[3][1], pr[3][2], pr[3][3]));
+}
+
 constexpr int kAttnWaves = 8;
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
@@ -889,6 +927,177 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   }
 }
 
+// Attention for many episodes (the batch alone fills the GPU): a workgroup
+// owns 16 * NWQ query rows of one episode (wave w: rows 16w .. 16w+15, i.e.
+// two suffix tokens x 8 heads) and walks all of the episode's key blocks,
+// two at a time.  Each pair of packed K/V blocks (64 KB, plus 64 key biases)
+// is read once per workgroup into LDS and shared by its waves; each wave
+// keeps its own online-softmax state, so no cross-wave merge is needed.  Two
+// blocks per step give every wave four independent score chains and one
+// softmax reduction per 64 keys, which is what bounds a step (one barrier per
+// step).  The only global loads in the key loop are these pair fetches,
+// kAttnRowStages steps ahead of the math (register stages, two LDS buffers),
+// issued identically by every wave, so the in-order waits count exactly the
+// steps in flight.  Each pair's K fragments are all read from LDS before its
+// score MFMAs and its V fragments before the softmax (explicit batches: left
+// to itself the scheduler serialises one LDS read per MFMA).
+// The grid is 1-D and XCD-aware: block i runs on XCD (i + c) mod 8, and all
+// workgroups of episode e use i = e mod 8 (mod 8), so an episode's K/V is
+// fetched from HBM into one XCD's L2 once and re-read from there.
+constexpr int kAttnRowWaves = 4;
+constexpr int kAttnRowStages = 1;
+// 16-row query blocks (all episodes) from which the LDS-sharing kernel is used
+constexpr int kAttnRowsMinBlocks = 256;
+
+template <int NWQ>
+__global__ __launch_bounds__(NWQ * 64) void k_attn_rows(AttnParams p) {
+  constexpr int FPW = 64 / NWQ;  // fragments of a block pair copied per wave
+  constexpr int NST = kAttnRowStages;
+  static_assert(64 % NWQ == 0 && FPW >= 2, "a pair's 64 fragments split evenly over the waves");
+  // [buffer][block of the pair][16 K + 16 V fragments][lane], then
+  // [buffer][64] key biases; the front is reused for the output transpose
+  constexpr int kKvFloats = 2 * 2 * 32 * 64 * 4, kOutFloats = NWQ * 16 * kOStride;
+  constexpr int kFront = kKvFloats > kOutFloats ? kKvFloats : kOutFloats;
+  __shared__ __attribute__((aligned(16))) float lds[kFront + 2 * 64];
+  u32x4 (*kv)[2][32][64] = reinterpret_cast<u32x4 (*)[2][32][64]>(lds);
+  float* kbl = lds + kFront;  // [2][64]
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int nq = p.T * kH;
+  const int per_ep = (nq + 16 * NWQ - 1) / (16 * NWQ);  // workgroups per episode
+  const int xr = int(blockIdx.x) & 7, j = int(blockIdx.x) >> 3;
+  const int b = xr + 8 * (j / per_ep), qw = j % per_ep;
+  if (b >= p.B) return;  // padding of the XCD-aware grid (uniform per workgroup)
+  const int r = (qw * NWQ + w) * 16 + c;
+  const int rc = r < nq ? r : nq - 1;
+
+  bf16x8 qf[8];
+  const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
+  // Q lands before any K/V fetch is issued, so no wait inside the key loop
+  // (loads retire in order) has to cover it
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  const int nkb = p.nkb, npair = (nkb + 1) / 2;
+  const uint32_t ep_bytes = uint32_t(nkb) * 16384u;
+  const rsrc_t kr = make_rsrc(p.kp + size_t(b) * nkb * 8192, ep_bytes);
+  const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
+  const rsrc_t br = make_rsrc(p.kbias + size_t(b) * nkb * 32, uint32_t(nkb) * 128u);
+  const uint32_t lo16 = uint32_t(lane) * 16u, bo16 = uint32_t(lane & 7) * 16u;
+
+  // fragment q*NWQ + w of a pair: block (f / 32), K fragments f%32 < 16, V
+  // otherwise; plus both blocks' biases (lane l: bytes 16(l%8).. of each;
+  // every wave stores the same values to the same place, branch-free).
+  // Blocks past the last re-read block 0 (in bounds; masked or never used).
+  u32x4 st[NST][FPW], sb[NST][2];
+#define PI_AE_KV_FETCH(SLOT, PR)                                                      \
+  {                                                                                   \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
+      const int f = q * NWQ + w, blk = 2 * (PR) + (f >> 5);                           \
+      const uint32_t kb_ = uint32_t(blk < nkb ? blk : 0);                             \
+      st[SLOT][q] = __builtin_bit_cast(u32x4, bload16((f & 31) < 16 ? kr : vr, lo16, kb_ * 16384u + uint32_t(f & 15) * 1024u)); \
+    }                                                                                 \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
+      const int blk = 2 * (PR) + h;                                                   \
+      sb[SLOT][h] = __builtin_bit_cast(u32x4, bload16(br, bo16, uint32_t(blk < nkb ? blk : 0) * 128u)); \
+    }                                                                                 \
+  }
+#define PI_AE_KV_STORE(SLOT, BUF)                                                     \
+  {                                                                                   \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
+      const int f = q * NWQ + w;                                                      \
+      kv[BUF][f >> 5][f & 31][lane] = st[SLOT][q];                                    \
+    }                                                                                 \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
+      *reinterpret_cast<u32x4*>(kbl + (BUF) * 64 + h * 32 + (lane & 7) * 4) = sb[SLOT][h]; \
+  }
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // the math of one pair from LDS buffer BUF; the second block of the last
+  // pair of an odd count is masked out
+#define PI_AE_KV_PAIR(BUF, PR)                                                         \
+  {                                                                                    \
+    const bool second = 2 * (PR) + 1 < nkb;                                            \
+    float4 bias[4];                                                                    \
+    _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) {                                 \
+      bias[mk] = *reinterpret_cast<const float4*>(kbl + (BUF) * 64 + (mk >> 1) * 32 + (mk & 1) * 16 + 4 * g); \
+      if (mk >= 2 && !second) bias[mk] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); \
+    }                                                                                  \
+    /* every K fragment of the pair in flight at once, then 4 interleaved chains */   \
+    u32x4 fr[32];                                                                      \
+    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks)                                   \
+      _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) fr[ks * 4 + mk] = kv[BUF][mk >> 1][(mk & 1) * 8 + ks][lane]; \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    f32x4 sc[4];                                                                       \
+    _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) sc[mk] = f32x4{0.f, 0.f, 0.f, 0.f}; \
+    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks)                                   \
+      _Pragma("unroll") for (int mk = 0; mk < 4; ++mk)                                 \
+        sc[mk] = mfma(__builtin_bit_cast(bf16x8, fr[ks * 4 + mk]), qf[ks], sc[mk]);    \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    /* V fragments issued before the softmax, so their reads overlap it */            \
+    _Pragma("unroll") for (int md = 0; md < 16; ++md) {                                \
+      fr[2 * md] = kv[BUF][0][16 + md][lane];                                          \
+      fr[2 * md + 1] = kv[BUF][1][16 + md][lane];                                      \
+    }                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    float alpha;                                                                       \
+    bf16x8 pa, pb;                                                                     \
+    attn_softmax2(sc, bias, m_run, l_run, alpha, pa, pb);                              \
+    _Pragma("unroll") for (int md = 0; md < 16; ++md) {                                \
+      acc[md] = mfma(__builtin_bit_cast(bf16x8, fr[2 * md]), pa, acc[md] * alpha);     \
+      acc[md] = mfma(__builtin_bit_cast(bf16x8, fr[2 * md + 1]), pb, acc[md]);         \
+    }                                                                                  \
+  }
+
+#pragma unroll
+  for (int s2 = 0; s2 < NST; ++s2) PI_AE_KV_FETCH(s2, s2)
+  PI_AE_KV_STORE(0, 0)
+  // step pr (stage s = pr mod NST, buffer pr mod 2): pair pr is in LDS after
+  // the barrier; st[s] is free again and fetches pair pr+NST; pair pr+1
+  // (fetched NST-1 steps ago) goes to the other buffer after the math.
+  for (int p0 = 0; p0 < npair; p0 += NST) {
+#pragma unroll
+    for (int s2 = 0; s2 < NST; ++s2) {
+      const int pr = p0 + s2, buf = pr & 1;
+      PI_AE_KV_FETCH(s2, pr + NST)
+      lds_barrier();  // pair pr is in buffer buf; buffer buf^1 is no longer read
+      if (pr < npair) PI_AE_KV_PAIR(buf, pr)
+      PI_AE_KV_STORE((s2 + 1) % NST, buf ^ 1)
+    }
+  }
+#undef PI_AE_KV_PAIR
+#undef PI_AE_KV_STORE
+#undef PI_AE_KV_FETCH
+
+  // normalise and write O: through LDS so that each lane stores 8
+  // consecutive head-dim values of one row (16 bytes)
+  __syncthreads();
+  float* ob = lds + w * 16 * kOStride;  // this wave's 16 rows
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int md = 0; md < 16; ++md)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ob[c * kOStride + md * 16 + 4 * g + i] = acc[md][i] * inv;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only its own rows
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int idx = pass * 64 + lane, q = idx >> 5, d0 = (idx & 31) * 8;
+    const int rq = (qw * NWQ + w) * 16 + q;
+    const float4 a0 = *reinterpret_cast<const float4*>(&ob[q * kOStride + d0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&ob[q * kOStride + d0 + 4]);
+    if (rq < nq) {
+      const int trow = b * p.T + rq / kH, head = rq % kH;
+      *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) =
+          __builtin_bit_cast(uint4, pack8(a0, a1));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 static inline unsigned row_tiles(int M, int rows = 64) { return unsigned((M + rows - 1) / rows); }
 
@@ -940,7 +1149,13 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
-  return go(k_attn, dim3((p.T * kH + 15) / 16 + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
+  const int nqb = (p.T * kH + 15) / 16;
+  if (p.B * nqb >= kAttnRowsMinBlocks && p.pf.nwg == 0) {  // many episodes: K/V shared through LDS
+    const int per_ep = (nqb + kAttnRowWaves - 1) / kAttnRowWaves;
+    const int groups = (p.B + 7) / 8;  // 8 episodes (one per XCD residue) per group
+    return go(k_attn_rows<kAttnRowWaves>, dim3(8 * groups * per_ep), dim3(kAttnRowWaves * 64), s, t, p);
+  }
+  return go(k_attn, dim3(nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {
   if (p.B <= 0 || p.nkb <= 0) return hipSuccess;

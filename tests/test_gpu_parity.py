@@ -226,6 +226,39 @@ def test_ragged_masks_and_batch(small_ctx):
     check_actions(out.cpu().numpy(), O.sample(wb, SMALL, k0, k0, None, noise2), noise2, "no-prefix")
 
 
+def test_many_episodes_ragged_masks():
+    """Nine episodes (288 query blocks of 16 rows): the attention kernel that
+    shares each K/V block through LDS across the waves of a workgroup, with
+    ragged masks (holes, a fully masked prefix), masked garbage, and the
+    tiled GEMMs; every episode against the oracle."""
+    wb = inputs.make_weights(SMALL, seed=5, cache=False)
+    ctx = pi_ae.Context(SMALL, wb, max_batch=9, max_prefix_len=100)
+    B, P = 9, 100
+    k, v = inputs.make_prefix_kv(SMALL, B, P, seed=21)
+    rng = np.random.default_rng(22)
+    mask = (rng.random((B, P)) < 0.6).astype(np.uint8)
+    mask[3] = 0
+    mask[5, :] = 1
+    noise = inputs.make_noise(SMALL, B, seed=23)
+    x = Run(k, v, mask, noise).sample(ctx)
+    x_ref = O.sample(wb, SMALL, k, v, mask, noise)
+    for b in range(B):
+        check_actions(x[b:b + 1], x_ref[b:b + 1], noise[b:b + 1], f"many[{b}]")
+    k2, v2 = k.copy(), v.copy()
+    k2[:, mask == 0] = inputs.f32_to_bf16_bits(np.array([3e4], np.float32))[0]
+    v2[:, mask == 0] = np.uint16(0x7FC0)  # NaN
+    np.testing.assert_array_equal(Run(k2, v2, mask, noise).sample(ctx), x)
+    # an odd number of 32-key blocks (70 prefix + 63 suffix keys: 5 blocks)
+    P2 = 70
+    k3, v3 = np.ascontiguousarray(k[:, :, :P2]), np.ascontiguousarray(v[:, :, :P2])
+    mask3 = np.ascontiguousarray(mask[:, :P2])
+    x3 = Run(k3, v3, mask3, noise).sample(ctx)
+    x3_ref = O.sample(wb, SMALL, k3, v3, mask3, noise)
+    for b in (0, 3, 8):
+        check_actions(x3[b:b + 1], x3_ref[b:b + 1], noise[b:b + 1], f"many-odd[{b}]")
+    ctx.close()
+
+
 def test_masked_garbage_batch_independence_and_repeatability(small_ctx):
     """Exact invariances.  Up to 128 rows (2 episodes here) the weight-streaming
     GEMMs run; above that the tiled GEMMs, whose K accumulation order differs,
