@@ -460,39 +460,44 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 template <int TM, int TN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K) {
   constexpr int NW = WM * WN;
-  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per stage
+  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per k-block
+  constexpr int KS = 2;                                    // k-blocks per stage (one barrier each)
+  constexpr int FS = F * KS;                               // fragments per stage
   constexpr int BM = 16 * FA;
-  constexpr int FPW = F / NW;                              // fragments copied per wave
-  constexpr int PD = 4;                                    // k-blocks in flight
+  constexpr int FPW = FS / NW;                             // fragments copied per wave and stage
   constexpr bool NORM = EPI != E_RES;
-  static_assert(F % NW == 0, "stage fragments split evenly over the waves");
+  static_assert(FS % NW == 0, "stage fragments split evenly over the waves");
   static_assert(EPI == E_RES || TN % 2 == 0, "paired epilogues take n-block pairs");
-  static_assert(PD % 2 == 0, "the LDS double buffer alternates within one unrolled group");
-  __shared__ __attribute__((aligned(16))) u32x4 st[2][F][64];
+  constexpr int BN = 16 * FB;
+  constexpr int CS = BN + 4;  // floats per row of the output tile in LDS (pad: conflict-free writes)
+  constexpr int kStFloats = 2 * FS * 64 * 4, kCtFloats = BM * CS;
+  __shared__ __attribute__((aligned(16))) float lds_raw[kStFloats > kCtFloats ? kStFloats : kCtFloats];
+  u32x4 (*st)[FS][64] = reinterpret_cast<u32x4 (*)[FS][64]>(lds_raw);
   __shared__ float srstd[BM];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WN, wn = w % WN;
-  const int KB = K >> 5;
+  const int KB = K >> 5, NS = KB / KS;  // (K is a multiple of 64 for every GEMM of the expert)
   const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
   const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag);
   const u32x4* wp = reinterpret_cast<const u32x4*>(p.w);
 
-  u32x4 pre[PD][FPW];
-#define PI_AE_TILE_LOAD(KBI, SLOT)                                                     \
-  {                                                                                    \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                  \
-      const int f = q * NW + w;                                                        \
-      const u32x4* src = (f < FA) ? ap + (size_t(mb0 + f) * KB + (KBI)) * 64 + lane    \
-                                  : wp + (size_t(nb0 + f - FA) * KB + (KBI)) * 64 + lane; \
-      pre[SLOT][q] = *src;                                                             \
-    }                                                                                  \
+  // stage fragment fi = kk * F + f: A fragment f < FA of k-block kk, else B
+  // fragment f - FA; wave w copies fi = q * NW + w.  Past the last stage the
+  // copy re-reads stage 0 (in bounds, never used).
+  u32x4 pre[FPW];
+#define PI_AE_TILE_LOAD(STAGE)                                                          \
+  {                                                                                     \
+    const int sg_ = (STAGE) < NS ? (STAGE) : 0;                                         \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                   \
+      const int fi = q * NW + w, kk = fi / F, f = fi % F, kb = sg_ * KS + kk;           \
+      pre[q] = (f < FA) ? ap[(size_t(mb0 + f) * KB + kb) * 64 + lane]                   \
+                        : wp[(size_t(nb0 + f - FA) * KB + kb) * 64 + lane];             \
+    }                                                                                   \
   }
-  // (K is a multiple of 32 * PD for every GEMM of the expert)
-  PI_AE_TILE_LOAD(0, 0)
-  PI_AE_TILE_LOAD(1, 1)
-  PI_AE_TILE_LOAD(2, 2)
-  PI_AE_TILE_LOAD(3, 3)
+#define PI_AE_TILE_STORE(BUF) \
+  _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[BUF][q * NW + w][lane] = pre[q];
 
+  PI_AE_TILE_LOAD(0)
   if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
     for (int r = threadIdx.x; r < BM; r += NW * 64) {
       const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
@@ -505,6 +510,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K
       srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
     }
   }
+  PI_AE_TILE_STORE(0)
+  PI_AE_TILE_LOAD(1)
+  lds_barrier();
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -512,140 +520,151 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K loop unrolled by PD with literal slot numbers, so that every register
-  // slot and LDS buffer index is a constant (the prefetch registers stay in
-  // registers) and each wait covers exactly the block it needs.
-#define PI_AE_TILE_STEP(SL)                                                              \
-  {                                                                                      \
-    const int kb = kq + (SL);                                                            \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[(SL) & 1][q * NW + w][lane] = pre[SL][q]; \
-    PI_AE_TILE_LOAD(min(kb + PD, KB - 1), SL)                                            \
-    lds_barrier();                                                                       \
-    bf16x8 a[TM], b[TN];                                                                 \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(bf16x8, st[(SL) & 1][wm * TM + i][lane]); \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(bf16x8, st[(SL) & 1][FA + wn * TN + j][lane]); \
-    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]); \
-  }
-  static_assert(PD == 4, "the unrolled K step below names four slots");
-  for (int kq = 0; kq < KB; kq += PD) {
-    // (LDS buffer SL & 1 was last read two steps ago, before the last barrier;
-    // the tail steps re-read the last block so no branch hides a load)
-    PI_AE_TILE_STEP(0)
-    PI_AE_TILE_STEP(1)
-    PI_AE_TILE_STEP(2)
-    PI_AE_TILE_STEP(3)
-  }
-#undef PI_AE_TILE_STEP
-#undef PI_AE_TILE_LOAD
-
-  // epilogue: lane holds rows 4(lane/16)+r of each 16-row block, column
-  // lane%16.  Every operand is loaded first (the stores below could alias
-  // later loads as far as the compiler knows, which would serialise them).
-  const int cc = lane & 15, rq = 4 * (lane >> 4);
-  if constexpr (EPI == E_RES) {
-    float hv[TM][4][TN], gv[TN], sv[TN];
+  // stage sg: read every fragment this wave needs from LDS buffer sg&1 (all
+  // in flight at once), the MFMAs, then stage sg+1 (loaded during this
+  // stage's math) goes to the other buffer and stage sg+2 is requested.
+  for (int sg = 0; sg < NS; ++sg) {
+    const int buf = sg & 1;
+    u32x4 a[KS][TM], b[KS][TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = (nb0 + wn * TN + j) * 16 + cc;
-      gv[j] = p.gate[col];
-      sv[j] = p.s1_next ? p.s1_next[col] : 0.f;
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[kk][i] = st[buf][kk * F + wm * TM + i][lane];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[kk][j] = st[buf][kk * F + FA + wn * TN + j][lane];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          hv[i][r][j] = p.h_out[size_t(row < p.M ? row : 0) * kD + (nb0 + wn * TN + j) * 16 + cc];
-      }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
-        const bool live = row < p.M;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int nbg = nb0 + wn * TN + j, col = nbg * 16 + cc;
-          const float hn = hv[i][r][j] + acc[i][j][r] * gv[j];
-          if (live) p.h_out[size_t(row) * kD + col] = hn;
-          if (p.s1_next) {
-            float sq = hn * hn;
-            sq += __shfl_xor(sq, 1);
-            sq += __shfl_xor(sq, 2);
-            sq += __shfl_xor(sq, 4);
-            sq += __shfl_xor(sq, 8);
-            if (live) {
-              p.u_out[afrag_index(row, col, kD / 32)] = f2bf(hn * sv[j]);
-              if (cc == 0) p.ssq_out[size_t(row) * kSsqTiles + nbg] = sq;
-            }
-          }
-        }
-      }
-  } else {
-    constexpr int NP = TN / 2;
-    float b0[NP], b1[NP];
-    float2 cs[TM][4][NP];
-#pragma unroll
-    for (int jj = 0; jj < NP; ++jj) {
-      const int jp = (nb0 + wn * TN) / 2 + jj;  // global pair index
-      b0[jj] = p.bias[(2 * jp) * 16 + cc];
-      b1[jj] = p.bias[(2 * jp + 1) * 16 + cc];
-    }
-    if constexpr (EPI == E_QKV) {
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = mb0 * 16 + (wm * TM + i) * 16 + rq + r;
-#pragma unroll
-          for (int jj = 0; jj < NP; ++jj) {
-            const int jp = (nb0 + wn * TN) / 2 + jj;
-            cs[i][r][jj] = (jp < 72) ? p.rope_cs[size_t(row < p.M ? row : 0) * kRopeHalf + (jp & 7) * 16 + cc]
-                                     : make_float2(1.f, 0.f);
-          }
-        }
-    }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma(__builtin_bit_cast(bf16x8, a[kk][i]), __builtin_bit_cast(bf16x8, b[kk][j]), acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    PI_AE_TILE_STORE(buf ^ 1)
+    PI_AE_TILE_LOAD(sg + 2)
+    lds_barrier();
+  }
+#undef PI_AE_TILE_STORE
+#undef PI_AE_TILE_LOAD
+
+  // epilogue through LDS: the tile's fp32 results go to LDS in the MFMA
+  // layout (lane: rows 4(lane/16)+r of a 16-row block, column lane%16), then
+  // each thread takes 8 consecutive columns of one row per pass, so that
+  // every global access is 16 or 32 contiguous bytes.
+  __syncthreads();  // every wave is done with the staging buffers
+  float* ct = lds_raw;
+  {
+    const int cc = lane & 15, rq = 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = (wm * TM + i) * 16 + rq + r;
-        const int row = mb0 * 16 + rl;
-        if (row >= p.M) continue;
-        const float rs = srstd[rl];
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int jj = 0; jj < NP; ++jj) {
-          const int jp = (nb0 + wn * TN) / 2 + jj;
-          const float y0 = acc[i][2 * jj][r] * rs + b0[jj];
-          const float y1 = acc[i][2 * jj + 1][r] * rs + b1[jj];
-          if constexpr (EPI == E_QKV) {
-            const int b = row / p.T, t = row - b * p.T;
-            if (jp < 72) {
-              const int ip = (jp & 7) * 16 + cc;
-              const float o0 = y0 * cs[i][r][jj].x - y1 * cs[i][r][jj].y;
-              const float o1 = y1 * cs[i][r][jj].x + y0 * cs[i][r][jj].y;
-              if (jp < 64) {
-                uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
-                dst[ip] = f2bf(o0);
-                dst[kRopeHalf + ip] = f2bf(o1);
-              } else {
-                const int key = p.P + t;
-                p.kp[kpack_index(b, key, ip, p.nkb)] = f2bf(o0);
-                p.kp[kpack_index(b, key, kRopeHalf + ip, p.nkb)] = f2bf(o1);
-              }
-            } else {
-              const int key = p.P + t, d0 = (jp - 72) * 32 + cc;
-              p.vp[vpack_index(b, key, d0, p.nkb)] = f2bf(y0);
-              p.vp[vpack_index(b, key, d0 + 16, p.nkb)] = f2bf(y1);
-            }
+        for (int r = 0; r < 4; ++r) ct[((wm * TM + i) * 16 + rq + r) * CS + (wn * TN + j) * 16 + cc] = acc[i][j][r];
+  }
+  __syncthreads();
+  constexpr int NT = NW * 64;
+  if constexpr (EPI == E_RES) {
+    // chunk = (row, 8 columns); 16-column tiles' h^2 sums pair adjacent chunks
+    constexpr int CPR = BN / 8;
+    static_assert((BM * CPR) % NT == 0 && CPR % 2 == 0, "whole passes, chunk pairs within a wave");
+#pragma unroll 2
+    for (int pass = 0; pass < BM * CPR / NT; ++pass) {
+      const int ci = pass * NT + threadIdx.x, rl = ci / CPR, c8 = ci % CPR;
+      const int row = mb0 * 16 + rl, col = nb0 * 16 + c8 * 8;
+      const bool live = row < p.M;
+      const size_t hoff = size_t(live ? row : 0) * kD + col;
+      const float4 h0 = *reinterpret_cast<const float4*>(p.h_out + hoff);
+      const float4 h1 = *reinterpret_cast<const float4*>(p.h_out + hoff + 4);
+      const float4 g0 = *reinterpret_cast<const float4*>(p.gate + col);
+      const float4 g1 = *reinterpret_cast<const float4*>(p.gate + col + 4);
+      const float4 x0 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8 + 4]);
+      const float4 n0 = make_float4(h0.x + x0.x * g0.x, h0.y + x0.y * g0.y, h0.z + x0.z * g0.z, h0.w + x0.w * g0.w);
+      const float4 n1 = make_float4(h1.x + x1.x * g1.x, h1.y + x1.y * g1.y, h1.z + x1.z * g1.z, h1.w + x1.w * g1.w);
+      if (live) {
+        *reinterpret_cast<float4*>(p.h_out + hoff) = n0;
+        *reinterpret_cast<float4*>(p.h_out + hoff + 4) = n1;
+      }
+      if (p.s1_next) {
+        const float4 s0 = *reinterpret_cast<const float4*>(p.s1_next + col);
+        const float4 s1 = *reinterpret_cast<const float4*>(p.s1_next + col + 4);
+        float sq = (n0.x * n0.x + n0.y * n0.y) + (n0.z * n0.z + n0.w * n0.w) + (n1.x * n1.x + n1.y * n1.y) +
+                   (n1.z * n1.z + n1.w * n1.w);
+        sq += __shfl_xor(sq, 1);  // the other half of this 16-column tile
+        if (live) {
+          *reinterpret_cast<uint4*>(p.u_out + afrag_index(row, col, kD / 32)) = __builtin_bit_cast(
+              uint4, pack8(make_float4(n0.x * s0.x, n0.y * s0.y, n0.z * s0.z, n0.w * s0.w),
+                           make_float4(n1.x * s1.x, n1.y * s1.y, n1.z * s1.z, n1.w * s1.w)));
+          if ((c8 & 1) == 0) p.ssq_out[size_t(row) * kSsqTiles + col / 16] = sq;
+        }
+      }
+    }
+  } else {
+    // chunk = (row, pair pp of n-blocks 2pp / 2pp+1, half hf: columns 8hf..8hf+7 of each)
+    constexpr int CPR = FB;  // pairs per tile row (FB / 2) x 2 halves
+    static_assert((BM * CPR) % NT == 0, "whole passes");
+#pragma unroll 2
+    for (int pass = 0; pass < BM * CPR / NT; ++pass) {
+      const int ci = pass * NT + threadIdx.x, rl = ci / CPR, c = ci % CPR, pp = c >> 1, hf = c & 1;
+      const int row = mb0 * 16 + rl;
+      const int jp = nb0 / 2 + pp;  // global pair index
+      const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;  // bias columns
+      const float rs = srstd[rl];
+      const float4 b00 = *reinterpret_cast<const float4*>(p.bias + c0), b01 = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
+      const float4 b10 = *reinterpret_cast<const float4*>(p.bias + c1), b11 = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
+      const float4 a0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf + 4]);
+      const float4 u0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf]);
+      const float4 u1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf + 4]);
+      float y0[8] = {a0.x * rs + b00.x, a0.y * rs + b00.y, a0.z * rs + b00.z, a0.w * rs + b00.w,
+                     a1.x * rs + b01.x, a1.y * rs + b01.y, a1.z * rs + b01.z, a1.w * rs + b01.w};
+      float y1[8] = {u0.x * rs + b10.x, u0.y * rs + b10.y, u0.z * rs + b10.z, u0.w * rs + b10.w,
+                     u1.x * rs + b11.x, u1.y * rs + b11.y, u1.z * rs + b11.z, u1.w * rs + b11.w};
+      if (row >= p.M) continue;
+      if constexpr (EPI == E_GELU) {  // gate columns 16jp + 8hf.. and the same up columns
+        float mv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(y0[e]) * y1[e];
+        *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, kF / 32)) = __builtin_bit_cast(
+            uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
+      } else {  // E_QKV
+        const int b = row / p.T, t = row - b * p.T;
+        if (jp < 72) {  // Q heads and K_s: rotate pairs (ip, ip+128), ip = (jp%8)*16 + 8hf + e
+          const int ip = (jp & 7) * 16 + 8 * hf;
+          const float4* csp = reinterpret_cast<const float4*>(p.rope_cs + size_t(row) * kRopeHalf + ip);
+          float o0[8], o1[8];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 cs2 = csp[e2];  // (cos, sin) of pairs ip+2e2, ip+2e2+1
+            o0[2 * e2] = y0[2 * e2] * cs2.x - y1[2 * e2] * cs2.y;
+            o1[2 * e2] = y1[2 * e2] * cs2.x + y0[2 * e2] * cs2.y;
+            o0[2 * e2 + 1] = y0[2 * e2 + 1] * cs2.z - y1[2 * e2 + 1] * cs2.w;
+            o1[2 * e2 + 1] = y1[2 * e2 + 1] * cs2.z + y0[2 * e2 + 1] * cs2.w;
+          }
+          const uint4 w0 = __builtin_bit_cast(uint4, pack8(make_float4(o0[0], o0[1], o0[2], o0[3]), make_float4(o0[4], o0[5], o0[6], o0[7])));
+          const uint4 w1 = __builtin_bit_cast(uint4, pack8(make_float4(o1[0], o1[1], o1[2], o1[3]), make_float4(o1[4], o1[5], o1[6], o1[7])));
+          if (jp < 64) {
+            uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
+            *reinterpret_cast<uint4*>(dst + ip) = w0;
+            *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
           } else {
-            p.m_out[afrag_index(row, 16 * jp + cc, kF / 32)] = f2bf(gelu_tanh(y0) * y1);
+            const int key = p.P + t;
+            *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
+            *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
+          }
+        } else {  // V_s: head-dim (jp-72)*32 + 8hf + e and +16, no rotation
+          const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
+            p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
           }
         }
       }
+    }
   }
 }
 
