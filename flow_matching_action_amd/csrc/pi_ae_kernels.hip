@@ -457,115 +457,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 // fragment-major global layouts); global loads run PD blocks ahead in
 // registers.  The fused epilogues are those of k_gemm, applied by each wave to
 // its own accumulators.
-template <int TM, int TN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K) {
-  constexpr int NW = WM * WN;
-  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per k-block
-  constexpr int KS = 2;                                    // k-blocks per stage (one barrier each)
-  constexpr int FS = F * KS;                               // fragments per stage
-  constexpr int BM = 16 * FA;
-  constexpr int FPW = FS / NW;                             // fragments copied per wave and stage
-  constexpr bool NORM = EPI != E_RES;
-  static_assert(FS % NW == 0, "stage fragments split evenly over the waves");
-  static_assert(EPI == E_RES || TN % 2 == 0, "paired epilogues take n-block pairs");
-  constexpr int BN = 16 * FB;
-  constexpr int CS = BN + 4;  // floats per row of the output tile in LDS (pad: conflict-free writes)
-  constexpr int kStFloats = 2 * FS * 64 * 4, kCtFloats = BM * CS;
-  __shared__ __attribute__((aligned(16))) float lds_raw[kStFloats > kCtFloats ? kStFloats : kCtFloats];
-  u32x4 (*st)[FS][64] = reinterpret_cast<u32x4 (*)[FS][64]>(lds_raw);
-  __shared__ float srstd[BM];
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w / WN, wn = w % WN;
-  const int KB = K >> 5, NS = KB / KS;  // (K is a multiple of 64 for every GEMM of the expert)
-  const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
-  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag);
-  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w);
-
-  // stage fragment fi = kk * F + f: A fragment f < FA of k-block kk, else B
-  // fragment f - FA; wave w copies fi = q * NW + w.  Past the last stage the
-  // copy re-reads stage 0 (in bounds, never used).
-  u32x4 pre[FPW];
-#define PI_AE_TILE_LOAD(STAGE)                                                          \
-  {                                                                                     \
-    const int sg_ = (STAGE) < NS ? (STAGE) : 0;                                         \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                   \
-      const int fi = q * NW + w, kk = fi / F, f = fi % F, kb = sg_ * KS + kk;           \
-      pre[q] = (f < FA) ? ap[(size_t(mb0 + f) * KB + kb) * 64 + lane]                   \
-                        : wp[(size_t(nb0 + f - FA) * KB + kb) * 64 + lane];             \
-    }                                                                                   \
-  }
-#define PI_AE_TILE_STORE(BUF) \
-  _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[BUF][q * NW + w][lane] = pre[q];
-
-  PI_AE_TILE_LOAD(0)
-  if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
-    for (int r = threadIdx.x; r < BM; r += NW * 64) {
-      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
-      float sum = 0.f;
-#pragma unroll
-      for (int v = 0; v < kSsqTiles / 4; ++v) {
-        const float4 x = sp[v];
-        sum += (x.x + x.y) + (x.z + x.w);
-      }
-      srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
-    }
-  }
-  PI_AE_TILE_STORE(0)
-  PI_AE_TILE_LOAD(1)
-  lds_barrier();
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // stage sg: read every fragment this wave needs from LDS buffer sg&1 (all
-  // in flight at once), the MFMAs, then stage sg+1 (loaded during this
-  // stage's math) goes to the other buffer and stage sg+2 is requested.
-  for (int sg = 0; sg < NS; ++sg) {
-    const int buf = sg & 1;
-    u32x4 a[KS][TM], b[KS][TN];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) a[kk][i] = st[buf][kk * F + wm * TM + i][lane];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) b[kk][j] = st[buf][kk * F + FA + wn * TN + j][lane];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma(__builtin_bit_cast(bf16x8, a[kk][i]), __builtin_bit_cast(bf16x8, b[kk][j]), acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-    PI_AE_TILE_STORE(buf ^ 1)
-    PI_AE_TILE_LOAD(sg + 2)
-    lds_barrier();
-  }
-#undef PI_AE_TILE_STORE
-#undef PI_AE_TILE_LOAD
-
-  // epilogue through LDS: the tile's fp32 results go to LDS in the MFMA
-  // layout (lane: rows 4(lane/16)+r of a 16-row block, column lane%16), then
-  // each thread takes 8 consecutive columns of one row per pass, so that
-  // every global access is 16 or 32 contiguous bytes.
-  __syncthreads();  // every wave is done with the staging buffers
-  float* ct = lds_raw;
-  {
-    const int cc = lane & 15, rq = 4 * (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ct[((wm * TM + i) * 16 + rq + r) * CS + (wn * TN + j) * 16 + cc] = acc[i][j][r];
-  }
-  __syncthreads();
-  constexpr int NT = NW * 64;
+// Epilogue of the large-M GEMMs, after the BM x BN fp32 tile has been placed
+// in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
+// inputs): each of the NT threads takes 8 consecutive columns of one row per
+// pass, so that every global access is 16 or 32 contiguous bytes.
+template <int BM, int BN, int CS, int NT, int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* ct, const float* srstd, int mb0,
+                                              int nb0) {
+  constexpr int FB = BN / 16;
   if constexpr (EPI == E_RES) {
     // chunk = (row, 8 columns); 16-column tiles' h^2 sums pair adjacent chunks
     constexpr int CPR = BN / 8;
@@ -666,6 +565,115 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K
       }
     }
   }
+}
+
+template <int TM, int TN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K) {
+  constexpr int NW = WM * WN;
+  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per k-block
+  constexpr int KS = 2;                                    // k-blocks per stage (one barrier each)
+  constexpr int FS = F * KS;                               // fragments per stage
+  constexpr int BM = 16 * FA;
+  constexpr int FPW = FS / NW;                             // fragments copied per wave and stage
+  constexpr bool NORM = EPI != E_RES;
+  static_assert(FS % NW == 0, "stage fragments split evenly over the waves");
+  static_assert(EPI == E_RES || TN % 2 == 0, "paired epilogues take n-block pairs");
+  constexpr int BN = 16 * FB;
+  constexpr int CS = BN + 4;  // floats per row of the output tile in LDS (pad: conflict-free writes)
+  constexpr int kStFloats = 2 * FS * 64 * 4, kCtFloats = BM * CS;
+  __shared__ __attribute__((aligned(16))) float lds_raw[kStFloats > kCtFloats ? kStFloats : kCtFloats];
+  u32x4 (*st)[FS][64] = reinterpret_cast<u32x4 (*)[FS][64]>(lds_raw);
+  __shared__ float srstd[BM];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int KB = K >> 5, NS = KB / KS;  // (K is a multiple of 64 for every GEMM of the expert)
+  const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag);
+  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w);
+
+  // stage fragment fi = kk * F + f: A fragment f < FA of k-block kk, else B
+  // fragment f - FA; wave w copies fi = q * NW + w.  Past the last stage the
+  // copy re-reads stage 0 (in bounds, never used).
+  u32x4 pre[FPW];
+#define PI_AE_TILE_LOAD(STAGE)                                                          \
+  {                                                                                     \
+    const int sg_ = (STAGE) < NS ? (STAGE) : 0;                                         \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                   \
+      const int fi = q * NW + w, kk = fi / F, f = fi % F, kb = sg_ * KS + kk;           \
+      pre[q] = (f < FA) ? ap[(size_t(mb0 + f) * KB + kb) * 64 + lane]                   \
+                        : wp[(size_t(nb0 + f - FA) * KB + kb) * 64 + lane];             \
+    }                                                                                   \
+  }
+#define PI_AE_TILE_STORE(BUF) \
+  _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[BUF][q * NW + w][lane] = pre[q];
+
+  PI_AE_TILE_LOAD(0)
+  if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
+    for (int r = threadIdx.x; r < BM; r += NW * 64) {
+      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kSsqTiles / 4; ++v) {
+        const float4 x = sp[v];
+        sum += (x.x + x.y) + (x.z + x.w);
+      }
+      srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
+    }
+  }
+  PI_AE_TILE_STORE(0)
+  PI_AE_TILE_LOAD(1)
+  lds_barrier();
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // stage sg: read every fragment this wave needs from LDS buffer sg&1 (all
+  // in flight at once), the MFMAs, then stage sg+1 (loaded during this
+  // stage's math) goes to the other buffer and stage sg+2 is requested.
+  for (int sg = 0; sg < NS; ++sg) {
+    const int buf = sg & 1;
+    u32x4 a[KS][TM], b[KS][TN];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[kk][i] = st[buf][kk * F + wm * TM + i][lane];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[kk][j] = st[buf][kk * F + FA + wn * TN + j][lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma(__builtin_bit_cast(bf16x8, a[kk][i]), __builtin_bit_cast(bf16x8, b[kk][j]), acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    PI_AE_TILE_STORE(buf ^ 1)
+    PI_AE_TILE_LOAD(sg + 2)
+    lds_barrier();
+  }
+#undef PI_AE_TILE_STORE
+#undef PI_AE_TILE_LOAD
+
+  // epilogue: the tile's fp32 results go to LDS in the MFMA layout (lane:
+  // rows 4(lane/16)+r of a 16-row block, column lane%16), then tile_epilogue
+  __syncthreads();  // every wave is done with the staging buffers
+  float* ct = lds_raw;
+  {
+    const int cc = lane & 15, rq = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ct[((wm * TM + i) * 16 + rq + r) * CS + (wn * TN + j) * 16 + cc] = acc[i][j][r];
+  }
+  __syncthreads();
+  tile_epilogue<BM, BN, CS, NW * 64, EPI>(p, ct, srstd, mb0, nb0);
 }
 
 // ---------------------------------------------------------------------------
