@@ -32,6 +32,18 @@ __device__ __forceinline__ bf16x8 as_bf(uint4 v) { return __builtin_bit_cast(bf1
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// D (32x32) += A (32x16) B (16x32), bf16 in, fp32 accumulate.  Lane l holds
+// A[l%32][8(l/32)+j], B[8(l/32)+j][l%32] (j < 8) and D[8(i/4)+4(l/32)+i%4][l%32]
+// (i < 16).  On gfx950 this form runs at twice the rate of the 16x16x32 one.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// A 32x16 (or 16x32) operand read out of the 16x16x32 fragment-major layout:
+// rows 32r'.. of k-half h of k-block kb come from fragments 2r' and 2r'+1
+// (lanes l%32 < 16 and >= 16), at lane l%16 + 16(2h + l/32) of the fragment.
+__device__ __forceinline__ int frag32_lane(int lane, int h) { return (lane & 15) + 16 * (2 * h + (lane >> 5)); }
+__device__ __forceinline__ int frag32_sub(int lane) { return (lane >> 4) & 1; }
 __device__ __forceinline__ bf16x8 pack8(float4 lo, float4 hi) {
   f32x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   return __builtin_convertvector(v, bf16x8);
@@ -93,9 +105,13 @@ __device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, in
   }
 
 // GELU, tanh approximation (the MLP activation of the Gemma-shaped expert).
+// tanh through one exp2 and one reciprocal: tanh(z) = 1 - 2 / (e^(2z) + 1),
+// exact at both tails (e^(2z) -> inf gives 1, -> 0 gives -1); relative error
+// a few ulp, far below the bf16 rounding of its result.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float c = 0.7978845608028654f;
-  return 0.5f * x * (1.f + tanhf(c * (x + 0.044715f * x * x * x)));
+  const float z = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  const float e = exp2f(z * 2.8853900817779268f);  // e^(2z)
+  return 0.5f * x * (2.f - 2.f / (e + 1.f));
 }
 // Offset (in bf16 elements) of activation (row, k) in the fragment-major
 // layout [rows/16][K/32][64 lanes][8] that the GEMM A operand loads directly.
@@ -465,101 +481,130 @@ template <int BM, int BN, int CS, int NT, int EPI>
 __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* ct, const float* srstd, int mb0,
                                               int nb0) {
   constexpr int FB = BN / 16;
+  // A thread's column chunk is the same in every pass (NT is a multiple of the
+  // chunks per row), so per-column operands are loaded once; per-row operands
+  // of a batch of passes are all loaded before any of them is used.
   if constexpr (EPI == E_RES) {
     // chunk = (row, 8 columns); 16-column tiles' h^2 sums pair adjacent chunks
-    constexpr int CPR = BN / 8;
-    static_assert((BM * CPR) % NT == 0 && CPR % 2 == 0, "whole passes, chunk pairs within a wave");
-#pragma unroll 2
-    for (int pass = 0; pass < BM * CPR / NT; ++pass) {
-      const int ci = pass * NT + threadIdx.x, rl = ci / CPR, c8 = ci % CPR;
-      const int row = mb0 * 16 + rl, col = nb0 * 16 + c8 * 8;
-      const bool live = row < p.M;
-      const size_t hoff = size_t(live ? row : 0) * kD + col;
-      const float4 h0 = *reinterpret_cast<const float4*>(p.h_out + hoff);
-      const float4 h1 = *reinterpret_cast<const float4*>(p.h_out + hoff + 4);
-      const float4 g0 = *reinterpret_cast<const float4*>(p.gate + col);
-      const float4 g1 = *reinterpret_cast<const float4*>(p.gate + col + 4);
-      const float4 x0 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8 + 4]);
-      const float4 n0 = make_float4(h0.x + x0.x * g0.x, h0.y + x0.y * g0.y, h0.z + x0.z * g0.z, h0.w + x0.w * g0.w);
-      const float4 n1 = make_float4(h1.x + x1.x * g1.x, h1.y + x1.y * g1.y, h1.z + x1.z * g1.z, h1.w + x1.w * g1.w);
-      if (live) {
-        *reinterpret_cast<float4*>(p.h_out + hoff) = n0;
-        *reinterpret_cast<float4*>(p.h_out + hoff + 4) = n1;
+    constexpr int CPR = BN / 8, NP = BM * CPR / NT, PB = NP < 8 ? NP : 8;
+    static_assert(NT % CPR == 0 && NP % PB == 0 && CPR % 2 == 0, "pass-invariant columns, chunk pairs in a wave");
+    const int c8 = threadIdx.x % CPR, col = nb0 * 16 + c8 * 8;
+    const float4 g0 = *reinterpret_cast<const float4*>(p.gate + col);
+    const float4 g1 = *reinterpret_cast<const float4*>(p.gate + col + 4);
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+    if (p.s1_next) {
+      s0 = *reinterpret_cast<const float4*>(p.s1_next + col);
+      s1 = *reinterpret_cast<const float4*>(p.s1_next + col + 4);
+    }
+    for (int pb = 0; pb < NP; pb += PB) {
+      float4 h0[PB], h1[PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int row = mb0 * 16 + (pb + q) * (NT / CPR) + threadIdx.x / CPR;
+        const size_t hoff = size_t(row < p.M ? row : 0) * kD + col;
+        h0[q] = *reinterpret_cast<const float4*>(p.h_out + hoff);
+        h1[q] = *reinterpret_cast<const float4*>(p.h_out + hoff + 4);
       }
-      if (p.s1_next) {
-        const float4 s0 = *reinterpret_cast<const float4*>(p.s1_next + col);
-        const float4 s1 = *reinterpret_cast<const float4*>(p.s1_next + col + 4);
-        float sq = (n0.x * n0.x + n0.y * n0.y) + (n0.z * n0.z + n0.w * n0.w) + (n1.x * n1.x + n1.y * n1.y) +
-                   (n1.z * n1.z + n1.w * n1.w);
-        sq += __shfl_xor(sq, 1);  // the other half of this 16-column tile
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int rl = (pb + q) * (NT / CPR) + threadIdx.x / CPR, row = mb0 * 16 + rl;
+        const bool live = row < p.M;
+        const float4 x0 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8 + 4]);
+        const float4 n0 = make_float4(h0[q].x + x0.x * g0.x, h0[q].y + x0.y * g0.y, h0[q].z + x0.z * g0.z,
+                                      h0[q].w + x0.w * g0.w);
+        const float4 n1 = make_float4(h1[q].x + x1.x * g1.x, h1[q].y + x1.y * g1.y, h1[q].z + x1.z * g1.z,
+                                      h1[q].w + x1.w * g1.w);
+        const size_t hoff = size_t(live ? row : 0) * kD + col;
         if (live) {
-          *reinterpret_cast<uint4*>(p.u_out + afrag_index(row, col, kD / 32)) = __builtin_bit_cast(
-              uint4, pack8(make_float4(n0.x * s0.x, n0.y * s0.y, n0.z * s0.z, n0.w * s0.w),
-                           make_float4(n1.x * s1.x, n1.y * s1.y, n1.z * s1.z, n1.w * s1.w)));
-          if ((c8 & 1) == 0) p.ssq_out[size_t(row) * kSsqTiles + col / 16] = sq;
+          *reinterpret_cast<float4*>(p.h_out + hoff) = n0;
+          *reinterpret_cast<float4*>(p.h_out + hoff + 4) = n1;
+        }
+        if (p.s1_next) {
+          float sq = (n0.x * n0.x + n0.y * n0.y) + (n0.z * n0.z + n0.w * n0.w) + (n1.x * n1.x + n1.y * n1.y) +
+                     (n1.z * n1.z + n1.w * n1.w);
+          sq += __shfl_xor(sq, 1);  // the other half of this 16-column tile
+          if (live) {
+            *reinterpret_cast<uint4*>(p.u_out + afrag_index(row, col, kD / 32)) = __builtin_bit_cast(
+                uint4, pack8(make_float4(n0.x * s0.x, n0.y * s0.y, n0.z * s0.z, n0.w * s0.w),
+                             make_float4(n1.x * s1.x, n1.y * s1.y, n1.z * s1.z, n1.w * s1.w)));
+            if ((c8 & 1) == 0) p.ssq_out[size_t(row) * kSsqTiles + col / 16] = sq;
+          }
         }
       }
     }
   } else {
     // chunk = (row, pair pp of n-blocks 2pp / 2pp+1, half hf: columns 8hf..8hf+7 of each)
-    constexpr int CPR = FB;  // pairs per tile row (FB / 2) x 2 halves
-    static_assert((BM * CPR) % NT == 0, "whole passes");
-#pragma unroll 2
-    for (int pass = 0; pass < BM * CPR / NT; ++pass) {
-      const int ci = pass * NT + threadIdx.x, rl = ci / CPR, c = ci % CPR, pp = c >> 1, hf = c & 1;
-      const int row = mb0 * 16 + rl;
-      const int jp = nb0 / 2 + pp;  // global pair index
-      const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;  // bias columns
-      const float rs = srstd[rl];
-      const float4 b00 = *reinterpret_cast<const float4*>(p.bias + c0), b01 = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
-      const float4 b10 = *reinterpret_cast<const float4*>(p.bias + c1), b11 = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
-      const float4 a0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf + 4]);
-      const float4 u0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf]);
-      const float4 u1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf + 4]);
-      float y0[8] = {a0.x * rs + b00.x, a0.y * rs + b00.y, a0.z * rs + b00.z, a0.w * rs + b00.w,
-                     a1.x * rs + b01.x, a1.y * rs + b01.y, a1.z * rs + b01.z, a1.w * rs + b01.w};
-      float y1[8] = {u0.x * rs + b10.x, u0.y * rs + b10.y, u0.z * rs + b10.z, u0.w * rs + b10.w,
-                     u1.x * rs + b11.x, u1.y * rs + b11.y, u1.z * rs + b11.z, u1.w * rs + b11.w};
-      if (row >= p.M) continue;
-      if constexpr (EPI == E_GELU) {  // gate columns 16jp + 8hf.. and the same up columns
-        float mv[8];
+    constexpr int CPR = FB, NP = BM * CPR / NT, PB = NP < 4 ? NP : 4;  // pairs per tile row (FB / 2) x 2 halves
+    static_assert(NT % CPR == 0 && NP % PB == 0, "pass-invariant columns, whole batches");
+    const int c = threadIdx.x % CPR, pp = c >> 1, hf = c & 1;
+    const int jp = nb0 / 2 + pp;  // global pair index
+    const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;  // bias columns
+    const float4 b00 = *reinterpret_cast<const float4*>(p.bias + c0), b01 = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
+    const float4 b10 = *reinterpret_cast<const float4*>(p.bias + c1), b11 = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
+    const int ip = (jp & 7) * 16 + 8 * hf;  // RoPE pair of Q / K_s columns
+    for (int pb = 0; pb < NP; pb += PB) {
+      float4 cs[PB][4];
+      if constexpr (EPI == E_QKV) {
+        if (jp < 72) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(y0[e]) * y1[e];
-        *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, kF / 32)) = __builtin_bit_cast(
-            uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
-      } else {  // E_QKV
-        const int b = row / p.T, t = row - b * p.T;
-        if (jp < 72) {  // Q heads and K_s: rotate pairs (ip, ip+128), ip = (jp%8)*16 + 8hf + e
-          const int ip = (jp & 7) * 16 + 8 * hf;
-          const float4* csp = reinterpret_cast<const float4*>(p.rope_cs + size_t(row) * kRopeHalf + ip);
-          float o0[8], o1[8];
+          for (int q = 0; q < PB; ++q) {
+            const int row = mb0 * 16 + (pb + q) * (NT / CPR) + threadIdx.x / CPR;
+            const float4* csp = reinterpret_cast<const float4*>(p.rope_cs + size_t(row < p.M ? row : 0) * kRopeHalf + ip);
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float4 cs2 = csp[e2];  // (cos, sin) of pairs ip+2e2, ip+2e2+1
-            o0[2 * e2] = y0[2 * e2] * cs2.x - y1[2 * e2] * cs2.y;
-            o1[2 * e2] = y1[2 * e2] * cs2.x + y0[2 * e2] * cs2.y;
-            o0[2 * e2 + 1] = y0[2 * e2 + 1] * cs2.z - y1[2 * e2 + 1] * cs2.w;
-            o1[2 * e2 + 1] = y1[2 * e2 + 1] * cs2.z + y0[2 * e2 + 1] * cs2.w;
+            for (int e2 = 0; e2 < 4; ++e2) cs[q][e2] = csp[e2];  // (cos, sin) of pairs ip+2e2, ip+2e2+1
           }
-          const uint4 w0 = __builtin_bit_cast(uint4, pack8(make_float4(o0[0], o0[1], o0[2], o0[3]), make_float4(o0[4], o0[5], o0[6], o0[7])));
-          const uint4 w1 = __builtin_bit_cast(uint4, pack8(make_float4(o1[0], o1[1], o1[2], o1[3]), make_float4(o1[4], o1[5], o1[6], o1[7])));
-          if (jp < 64) {
-            uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
-            *reinterpret_cast<uint4*>(dst + ip) = w0;
-            *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
-          } else {
-            const int key = p.P + t;
-            *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
-            *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
-          }
-        } else {  // V_s: head-dim (jp-72)*32 + 8hf + e and +16, no rotation
-          const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
+        }
+      }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
-            p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
+      for (int q = 0; q < PB; ++q) {
+        const int rl = (pb + q) * (NT / CPR) + threadIdx.x / CPR, row = mb0 * 16 + rl;
+        const float rs = srstd[rl];
+        const float4 a0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 8 * hf + 4]);
+        const float4 u0 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&ct[rl * CS + pp * 32 + 16 + 8 * hf + 4]);
+        float y0[8] = {a0.x * rs + b00.x, a0.y * rs + b00.y, a0.z * rs + b00.z, a0.w * rs + b00.w,
+                       a1.x * rs + b01.x, a1.y * rs + b01.y, a1.z * rs + b01.z, a1.w * rs + b01.w};
+        float y1[8] = {u0.x * rs + b10.x, u0.y * rs + b10.y, u0.z * rs + b10.z, u0.w * rs + b10.w,
+                       u1.x * rs + b11.x, u1.y * rs + b11.y, u1.z * rs + b11.z, u1.w * rs + b11.w};
+        if (row >= p.M) continue;
+        if constexpr (EPI == E_GELU) {  // gate columns 16jp + 8hf.. and the same up columns
+          float mv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(y0[e]) * y1[e];
+          *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, kF / 32)) = __builtin_bit_cast(
+              uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
+        } else {  // E_QKV
+          const int b = row / p.T, t = row - b * p.T;
+          if (jp < 72) {  // Q heads and K_s: rotate pairs (ip, ip+128), ip = (jp%8)*16 + 8hf + e
+            float o0[8], o1[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const float4 cs2 = cs[q][e2];
+              o0[2 * e2] = y0[2 * e2] * cs2.x - y1[2 * e2] * cs2.y;
+              o1[2 * e2] = y1[2 * e2] * cs2.x + y0[2 * e2] * cs2.y;
+              o0[2 * e2 + 1] = y0[2 * e2 + 1] * cs2.z - y1[2 * e2 + 1] * cs2.w;
+              o1[2 * e2 + 1] = y1[2 * e2 + 1] * cs2.z + y0[2 * e2 + 1] * cs2.w;
+            }
+            const uint4 w0 = __builtin_bit_cast(uint4, pack8(make_float4(o0[0], o0[1], o0[2], o0[3]), make_float4(o0[4], o0[5], o0[6], o0[7])));
+            const uint4 w1 = __builtin_bit_cast(uint4, pack8(make_float4(o1[0], o1[1], o1[2], o1[3]), make_float4(o1[4], o1[5], o1[6], o1[7])));
+            if (jp < 64) {
+              uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
+              *reinterpret_cast<uint4*>(dst + ip) = w0;
+              *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
+            } else {
+              const int key = p.P + t;
+              *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
+              *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
+            }
+          } else {  // V_s: head-dim (jp-72)*32 + 8hf + e and +16, no rotation
+            const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
+              p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
+            }
           }
         }
       }
@@ -567,47 +612,85 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
   }
 }
 
-template <int TM, int TN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K) {
-  constexpr int NW = WM * WN;
-  constexpr int FA = TM * WM, FB = TN * WN, F = FA + FB;  // fragments per k-block
-  constexpr int KS = 2;                                    // k-blocks per stage (one barrier each)
-  constexpr int FS = F * KS;                               // fragments per stage
-  constexpr int BM = 16 * FA;
-  constexpr int FPW = FS / NW;                             // fragments copied per wave and stage
+// Large-M GEMM (many rows: the batched loop) on 32x32x16 MFMAs, the form that
+// reaches the chip's bf16 peak.  The WM waves of a workgroup are stacked
+// along M (wave w: TR row tiles of 32, all TC column tiles of 32), so each
+// wave streams its own A operands straight from memory into registers and
+// only the weight operands, which every wave needs, are shared through LDS
+// (half the LDS traffic per MFMA of sharing both).  Operands stay in the
+// 16x16x32 fragment-major layout; each 32x16 operand is gathered per lane
+// from two fragments (frag32_lane).  K runs in stages of two 32-k blocks:
+// loads run NP-1 stages ahead in register slots (literal slot indices), the
+// weights of the next stage go to the other of two LDS buffers, one barrier
+// per stage, and the memory instructions of a stage are interleaved with its
+// MFMAs (sched_group_barrier) so that a single wave per SIMD keeps both busy.
+// The interleaving of one stage: the first k-half's weight operands, then
+// one MFMA with each remaining LDS read, global load and LDS store, then the
+// remaining MFMAs.  (Counts for the instantiated shapes; the scheduler treats
+// a pattern as a preference.)
+#define PI_AE_B32_SCHED                                                                \
+  {                                                                                    \
+    constexpr int NM = TR * TC * 2 * KS, NDR = KS * TC * 2, NVM = KS * TR * 2 + BPW;   \
+    __builtin_amdgcn_sched_group_barrier(0x100, TC, 0);                                \
+    _Pragma("unroll") for (int i_ = 0; i_ < NDR - TC; ++i_) {                          \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                               \
+    }                                                                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < NVM; ++i_) {                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                               \
+    }                                                                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                               \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                               \
+    }                                                                                  \
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);                                \
+  }
+template <int WM, int TR, int TC, int EPI>
+__global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
+  constexpr int NW = WM, KS = 2;
+  constexpr int NP = 4;                          // stages of loads in flight (register slots)
+  constexpr int FA = 2 * TR * WM, FB = 2 * TC;  // 16-row / 16-column fragments of the tile
+  constexpr int BM = 16 * FA, BN = 16 * FB;
+  constexpr int FBS = FB * KS;                  // B fragments per stage
+  constexpr int BPW = FBS / NW;                 // B fragments copied per wave and stage
   constexpr bool NORM = EPI != E_RES;
-  static_assert(FS % NW == 0, "stage fragments split evenly over the waves");
-  static_assert(EPI == E_RES || TN % 2 == 0, "paired epilogues take n-block pairs");
-  constexpr int BN = 16 * FB;
-  constexpr int CS = BN + 4;  // floats per row of the output tile in LDS (pad: conflict-free writes)
-  constexpr int kStFloats = 2 * FS * 64 * 4, kCtFloats = BM * CS;
+  static_assert(FBS % NW == 0, "stage B fragments split evenly over the waves");
+  constexpr int CS = BN + 4;
+  constexpr int kStFloats = 2 * FBS * 64 * 4, kCtFloats = BM * CS;
   __shared__ __attribute__((aligned(16))) float lds_raw[kStFloats > kCtFloats ? kStFloats : kCtFloats];
-  u32x4 (*st)[FS][64] = reinterpret_cast<u32x4 (*)[FS][64]>(lds_raw);
+  u32x4 (*st)[FBS][64] = reinterpret_cast<u32x4 (*)[FBS][64]>(lds_raw);
   __shared__ float srstd[BM];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w / WN, wn = w % WN;
-  const int KB = K >> 5, NS = KB / KS;  // (K is a multiple of 64 for every GEMM of the expert)
+  const int KB = K >> 5, NS = KB / KS;  // NS is a multiple of NP: K is a multiple of 256 for every GEMM of the expert
   const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
-  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag);
-  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w);
+  const int sub = frag32_sub(lane);
+  // this lane's A rows: fragments mb0 + 2(w*TR + r) + sub
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 2 * w * TR + sub) * KB * 64;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w) + size_t(nb0) * KB * 64 + lane;
+  const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
 
-  // stage fragment fi = kk * F + f: A fragment f < FA of k-block kk, else B
-  // fragment f - FA; wave w copies fi = q * NW + w.  Past the last stage the
-  // copy re-reads stage 0 (in bounds, never used).
-  u32x4 pre[FPW];
-#define PI_AE_TILE_LOAD(STAGE)                                                          \
-  {                                                                                     \
-    const int sg_ = (STAGE) < NS ? (STAGE) : 0;                                         \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                   \
-      const int fi = q * NW + w, kk = fi / F, f = fi % F, kb = sg_ * KS + kk;           \
-      pre[q] = (f < FA) ? ap[(size_t(mb0 + f) * KB + kb) * 64 + lane]                   \
-                        : wp[(size_t(nb0 + f - FA) * KB + kb) * 64 + lane];             \
-    }                                                                                   \
+  // register slot SL holds stage s = SL (mod NP): its A operands and its B
+  // fragments (to be copied to LDS one stage before use).  Loads past the
+  // last stage re-read stage 0 (in bounds, never used).
+  u32x4 av[NP][KS][TR][2], pb[NP][BPW];
+#define PI_AE_B32_LOAD(SL, STAGE)                                                      \
+  {                                                                                    \
+    const int sg_ = (STAGE) < NS ? (STAGE) : 0;                                        \
+    _Pragma("unroll") for (int kk = 0; kk < KS; ++kk)                                  \
+      _Pragma("unroll") for (int r = 0; r < TR; ++r)                                   \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h)                                  \
+          av[SL][kk][r][h] = ap[(size_t(2 * r) * KB + sg_ * KS + kk) * 64 + al[h]];   \
+    _Pragma("unroll") for (int q = 0; q < BPW; ++q) {                                  \
+      const int fi = q * NW + w, kk = fi / FB, j = fi % FB;                            \
+      pb[SL][q] = wp[(size_t(j) * KB + sg_ * KS + kk) * 64];                           \
+    }                                                                                  \
   }
-#define PI_AE_TILE_STORE(BUF) \
-  _Pragma("unroll") for (int q = 0; q < FPW; ++q) st[BUF][q * NW + w][lane] = pre[q];
+#define PI_AE_B32_STORE_B(SL, BUF) \
+  _Pragma("unroll") for (int q = 0; q < BPW; ++q) st[BUF][q * NW + w][lane] = pb[SL][q];
 
-  PI_AE_TILE_LOAD(0)
+#pragma unroll
+  for (int sl = 0; sl < NP - 1; ++sl) PI_AE_B32_LOAD(sl, sl)
   if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
     for (int r = threadIdx.x; r < BM; r += NW * 64) {
       const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
@@ -620,61 +703,63 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_tiled(GemmParams p, int K
       srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
     }
   }
-  PI_AE_TILE_STORE(0)
-  PI_AE_TILE_LOAD(1)
+  PI_AE_B32_STORE_B(0, 0)
   lds_barrier();
 
-  f32x4 acc[TM][TN];
+  f32x16 acc[TR][TC];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
 
-  // stage sg: read every fragment this wave needs from LDS buffer sg&1 (all
-  // in flight at once), the MFMAs, then stage sg+1 (loaded during this
-  // stage's math) goes to the other buffer and stage sg+2 is requested.
-  for (int sg = 0; sg < NS; ++sg) {
-    const int buf = sg & 1;
-    u32x4 a[KS][TM], b[KS][TN];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) a[kk][i] = st[buf][kk * F + wm * TM + i][lane];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) b[kk][j] = st[buf][kk * F + FA + wn * TN + j][lane];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = mfma(__builtin_bit_cast(bf16x8, a[kk][i]), __builtin_bit_cast(bf16x8, b[kk][j]), acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
-    PI_AE_TILE_STORE(buf ^ 1)
-    PI_AE_TILE_LOAD(sg + 2)
-    lds_barrier();
+  // stage SG (slot SL = SG mod NP): B of stage SG from LDS buffer SG&1 (all
+  // reads in flight at once), the MFMAs with the slot's A, then B of stage
+  // SG+1 to the other buffer, slot SL reloaded with stage SG+NP, barrier.
+#define PI_AE_B32_STEP(SL, SG)                                                         \
+  {                                                                                    \
+    u32x4 b[KS][TC][2];                                                                \
+    _Pragma("unroll") for (int kk = 0; kk < KS; ++kk)                                  \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                    \
+        _Pragma("unroll") for (int c = 0; c < TC; ++c)                                 \
+          b[kk][c][h] = st[(SG) & 1][kk * FB + 2 * c + sub][al[h]];                    \
+    _Pragma("unroll") for (int kk = 0; kk < KS; ++kk)                                  \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                    \
+        _Pragma("unroll") for (int r = 0; r < TR; ++r)                                 \
+          _Pragma("unroll") for (int c = 0; c < TC; ++c)                               \
+            acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, av[SL][kk][r][h]), __builtin_bit_cast(bf16x8, b[kk][c][h]), acc[r][c]); \
+    PI_AE_B32_STORE_B(((SL) + 1) % NP, ((SG) + 1) & 1)                                 \
+    PI_AE_B32_LOAD(((SL) + NP - 1) % NP, (SG) + NP - 1)                                \
+    PI_AE_B32_SCHED                                                                    \
+    lds_barrier();                                                                     \
   }
-#undef PI_AE_TILE_STORE
-#undef PI_AE_TILE_LOAD
+  static_assert(NP == 4, "the unrolled stage loop names four slots");
+  for (int sg = 0; sg < NS; sg += NP) {
+    PI_AE_B32_STEP(0, sg)
+    PI_AE_B32_STEP(1, sg + 1)
+    PI_AE_B32_STEP(2, sg + 2)
+    PI_AE_B32_STEP(3, sg + 3)
+  }
+#undef PI_AE_B32_STEP
+#undef PI_AE_B32_STORE_B
+#undef PI_AE_B32_LOAD
 
-  // epilogue: the tile's fp32 results go to LDS in the MFMA layout (lane:
-  // rows 4(lane/16)+r of a 16-row block, column lane%16), then tile_epilogue
-  __syncthreads();  // every wave is done with the staging buffers
+  // epilogue: D layout to LDS (row 8(i/4) + 4(l/32) + i%4, column l%32 of each 32x32 tile)
+  __syncthreads();
   float* ct = lds_raw;
-  {
-    const int cc = lane & 15, rq = 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int r = 0; r < TR; ++r)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int c = 0; c < TC; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ct[((wm * TM + i) * 16 + rq + r) * CS + (wn * TN + j) * 16 + cc] = acc[i][j][r];
-  }
+      for (int i = 0; i < 16; ++i)
+        ct[((w * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
   __syncthreads();
   tile_epilogue<BM, BN, CS, NW * 64, EPI>(p, ct, srstd, mb0, nb0);
 }
+#undef PI_AE_B32_SCHED
+
 
 // ---------------------------------------------------------------------------
 // Per call, once: pack every layer's prefix K/V into the attention's operand
@@ -1149,28 +1234,28 @@ hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_tiled<4, 4, 2, 2, E_QKV>, dim3(kNqkv / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+    return go(k_gemm_big32<4, 1, 4, E_QKV>, dim3(kNqkv / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
   if (p.M <= 64)  // 32-row tiles: half the activation bytes per workgroup, twice the CUs
     return go(k_gemm<2, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M, 32)), dim3(256), s, t, p);
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_tiled<4, 4, 2, 2, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+    return go(k_gemm_big32<4, 1, 4, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 // O and down: at small M, 16-row tiles quarter each workgroup's activation
 // slice and spread the launch over four times the CUs.
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+    return go(k_gemm_big32<4, 1, 4, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_tiled<4, 4, 2, 2, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
+    return go(k_gemm_big32<4, 1, 4, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
