@@ -15,9 +15,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpi_ae.so")
 SOURCES = [os.path.join(CSRC, "pi_ae_kernels.hip"), os.path.join(CSRC, "pi_ae_runtime.cpp")]
 
-# Packed-fp32 VALU forms are kept out of generated code on purpose.
+# Packed-fp32 VALU forms are kept out of generated code on purpose.  MFMA
+# results go to ordinary VGPRs: the attention kernels rescale their
+# accumulators with VALU code, which on accumulation registers costs a copy of
+# every accumulator out and back each step.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -885,44 +885,6 @@ __device__ __forceinline__ bf16x8 attn_softmax(const f32x4 (&s)[2], const float4
   return pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]), make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
 }
 
-// The same online-softmax update over two key blocks at once (64 keys):
-// s[0..1] / bias[0..1] belong to the first block, s[2..3] / bias[2..3] to the
-// second; pa and pb are their probabilities in PV operand order.
-__device__ __forceinline__ void attn_softmax2(const f32x4 (&s)[4], const float4 (&bias)[4], float& m_run,
-                                              float& l_run, float& alpha, bf16x8& pa, bf16x8& pb) {
-  const float sc = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
-  float pr[4][4];
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int mk = 0; mk < 4; ++mk) {
-    const float bv[4] = {bias[mk].x, bias[mk].y, bias[mk].z, bias[mk].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[mk][i] = s[mk][i] * sc + bv[i];
-      mloc = fmaxf(mloc, pr[mk][i]);
-    }
-  }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(m_run, mloc);
-  const bool none = (m_new == -INFINITY);
-  alpha = none ? 1.f : exp2f(m_run - m_new);
-  float lsum = 0.f;
-#pragma unroll
-  for (int mk = 0; mk < 4; ++mk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pr[mk][i] = none ? 0.f : exp2f(pr[mk][i] - m_new);
-      lsum += pr[mk][i];
-    }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  l_run = l_run * alpha + lsum;
-  m_run = m_new;
-  pa = pack8(make_float4(pr[0][0], pr[0][1], pr[0][2], pr[0][3]), make_float4(pr[1][0], pr[1][1], pr[1][2], pr[1][3]));
-  pb = pack8(make_float4(pr[2][0], pr[2][1], pr[2][2], pr[2][3]), make_float4(pr[3][0], pr[3][1], pr[3][2], pr[3][3]));
-}
-
 constexpr int kAttnWaves = 8;
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
@@ -1039,173 +1001,221 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   }
 }
 
-// Attention for many episodes (the batch alone fills the GPU): a workgroup
-// owns 16 * NWQ query rows of one episode (wave w: rows 16w .. 16w+15, i.e.
-// two suffix tokens x 8 heads) and walks all of the episode's key blocks,
-// two at a time.  Each pair of packed K/V blocks (64 KB, plus 64 key biases)
-// is read once per workgroup into LDS and shared by its waves; each wave
-// keeps its own online-softmax state, so no cross-wave merge is needed.  Two
-// blocks per step give every wave four independent score chains and one
-// softmax reduction per 64 keys, which is what bounds a step (one barrier per
-// step).  The only global loads in the key loop are these pair fetches,
-// kAttnRowStages steps ahead of the math (register stages, two LDS buffers),
-// issued identically by every wave, so the in-order waits count exactly the
-// steps in flight.  Each pair's K fragments are all read from LDS before its
-// score MFMAs and its V fragments before the softmax (explicit batches: left
-// to itself the scheduler serialises one LDS read per MFMA).
+// Attention for many episodes (the batch alone fills the GPU), on 32x32x16
+// MFMAs, the full-rate form.  Each workgroup owns 32 * NWQ query rows of one
+// episode and walks all of its key blocks, two at a time; each pair of packed
+// K/V blocks is read once per workgroup into LDS and shared by its waves.  A
+// wave owns 32 query rows: their Q is the B operand of S^T = K Q^T (lane l:
+// row l%32, head-dim 16s + 8(l/32) + j), so S^T of a 32-key block is one 32x32
+// accumulator in which lane l holds 16 keys of row l%32.  Those 16
+// probabilities are, unchanged, the lane's B operand of O^T += V^T P^T when
+// the block's keys are contracted in the order k -> 16t + 8((k%8)/4) +
+// 4(k/8) + k%4 (t: which half of the block); V^T is read in that order from
+// the packed V (two 16-byte LDS reads give a d-tile's operands for both
+// halves), K through the 32x32 gather of the packed K fragments.  NWQ 32-row
+// query groups share a workgroup, and two waves work on each group: wave kh
+// takes block kh of every pair, and the two halves are merged through LDS at
+// the end.  Pairs of K/V blocks are copied straight from memory into LDS
+// (buffer loads that write LDS, no registers), one pair ahead of the math,
+// into two LDS buffers that are separate objects so that the compiler's
+// wait counting keeps the copy into one buffer in flight while the other is
+// read.  The running max moves only when a block's max exceeds it by more
+// than 8 (log2 units, i.e. probabilities up to 256; FlashAttention-4's
+// conditional rescaling): O / l is the same for any reference max, and the
+// wave skips the accumulator rescale in the common case.
 // The grid is 1-D and XCD-aware: block i runs on XCD (i + c) mod 8, and all
 // workgroups of episode e use i = e mod 8 (mod 8), so an episode's K/V is
 // fetched from HBM into one XCD's L2 once and re-read from there.
-constexpr int kAttnRowWaves = 4;
-constexpr int kAttnRowStages = 1;
-// 16-row query blocks (all episodes) from which the LDS-sharing kernel is used
+constexpr int kAttn32Groups = 2;  // 32-row query groups per workgroup (two waves each)
+// 16-row query blocks (all episodes) from which this kernel is used
 constexpr int kAttnRowsMinBlocks = 256;
 
+// max and sum across lanes l and l^32 (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int NWQ>
-__global__ __launch_bounds__(NWQ * 64) void k_attn_rows(AttnParams p) {
-  constexpr int FPW = 64 / NWQ;  // fragments of a block pair copied per wave
-  constexpr int NST = kAttnRowStages;
-  static_assert(64 % NWQ == 0 && FPW >= 2, "a pair's 64 fragments split evenly over the waves");
-  // [buffer][block of the pair][16 K + 16 V fragments][lane], then
-  // [buffer][64] key biases; the front is reused for the output transpose
-  constexpr int kKvFloats = 2 * 2 * 32 * 64 * 4, kOutFloats = NWQ * 16 * kOStride;
-  constexpr int kFront = kKvFloats > kOutFloats ? kKvFloats : kOutFloats;
-  __shared__ __attribute__((aligned(16))) float lds[kFront + 2 * 64];
-  u32x4 (*kv)[2][32][64] = reinterpret_cast<u32x4 (*)[2][32][64]>(lds);
-  float* kbl = lds + kFront;  // [2][64]
+__global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
+  constexpr int NW = NWQ * 2;
+  constexpr int FPW = 64 / NW;  // fragments of a block pair copied per wave
+  static_assert(64 % NW == 0, "a pair's 64 fragments split evenly over the waves");
+  // one LDS buffer: [block of the pair][16 K + 16 V fragments][lane] (64 KiB)
+  // and the pair's 64 key biases.  After the key loop, buffer g holds query
+  // group g's merge area (the second half's accumulators in register order,
+  // its max and sum: 130 x 64 floats) and then its output rows as bf16.
+  constexpr int kMrgFloats = 130 * 64, kORow = kHd + 8;  // bf16 per output row (16-byte aligned, staggered banks)
+  static_assert(NWQ <= 2, "one LDS buffer per query group after the loop");
+  static_assert(kMrgFloats * 4 + 32 * kORow * 2 <= 65536, "merge + output rows fit one buffer");
+  __shared__ __attribute__((aligned(16))) u32x4 kva[2][32][64];
+  __shared__ __attribute__((aligned(16))) u32x4 kvb[2][32][64];
+  __shared__ __attribute__((aligned(16))) float kba[64];
+  __shared__ __attribute__((aligned(16))) float kbb[64];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, c = lane & 15;
+  const int rg = w % NWQ, kh = w / NWQ;  // query group, key half
+  const int hh = lane >> 5, l32 = lane & 31, sub = (lane >> 4) & 1;
   const int nq = p.T * kH;
-  const int per_ep = (nq + 16 * NWQ - 1) / (16 * NWQ);  // workgroups per episode
+  const int per_ep = (nq + 32 * NWQ - 1) / (32 * NWQ);
   const int xr = int(blockIdx.x) & 7, j = int(blockIdx.x) >> 3;
   const int b = xr + 8 * (j / per_ep), qw = j % per_ep;
   if (b >= p.B) return;  // padding of the XCD-aware grid (uniform per workgroup)
-  const int r = (qw * NWQ + w) * 16 + c;
+  const int r = (qw * NWQ + rg) * 32 + l32;
   const int rc = r < nq ? r : nq - 1;
 
-  bf16x8 qf[8];
-  const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd;
+  bf16x8 qf[16];
+  const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd + 8 * hh;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
-  // Q lands before any K/V fetch is issued, so no wait inside the key loop
-  // (loads retire in order) has to cover it
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  for (int s = 0; s < 16; ++s) qf[s] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * s));
 
   const int nkb = p.nkb, npair = (nkb + 1) / 2;
   const uint32_t ep_bytes = uint32_t(nkb) * 16384u;
   const rsrc_t kr = make_rsrc(p.kp + size_t(b) * nkb * 8192, ep_bytes);
   const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
   const rsrc_t br = make_rsrc(p.kbias + size_t(b) * nkb * 32, uint32_t(nkb) * 128u);
-  const uint32_t lo16 = uint32_t(lane) * 16u, bo16 = uint32_t(lane & 7) * 16u;
 
-  // fragment q*NWQ + w of a pair: block (f / 32), K fragments f%32 < 16, V
-  // otherwise; plus both blocks' biases (lane l: bytes 16(l%8).. of each;
-  // every wave stores the same values to the same place, branch-free).
-  // Blocks past the last re-read block 0 (in bounds; masked or never used).
-  u32x4 st[NST][FPW], sb[NST][2];
-#define PI_AE_KV_FETCH(SLOT, PR)                                                      \
+  // fragment q*NW + w of pair PR (block f/32; K if f%32 < 16, else V) into
+  // buffer KV, and the pair's 64 biases into KB (every wave copies the same
+  // biases to the same place, which keeps the wait counts uniform).  A
+  // missing second block re-reads block 0 (in bounds; masked).
+#define PI_AE_KV32_COPY(KV, KB, PR)                                                   \
   {                                                                                   \
     _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
-      const int f = q * NWQ + w, blk = 2 * (PR) + (f >> 5);                           \
+      const int f = q * NW + w, blk = 2 * (PR) + (f >> 5);                            \
       const uint32_t kb_ = uint32_t(blk < nkb ? blk : 0);                             \
-      st[SLOT][q] = __builtin_bit_cast(u32x4, bload16((f & 31) < 16 ? kr : vr, lo16, kb_ * 16384u + uint32_t(f & 15) * 1024u)); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((f & 31) < 16 ? kr : vr, (lds_ptr_t)&KV[f >> 5][f & 31][0], 16, \
+                                               uint32_t(lane) * 16u, kb_ * 16384u + uint32_t(f & 15) * 1024u, 0, 0); \
     }                                                                                 \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
-      const int blk = 2 * (PR) + h;                                                   \
-      sb[SLOT][h] = __builtin_bit_cast(u32x4, bload16(br, bo16, uint32_t(blk < nkb ? blk : 0) * 128u)); \
-    }                                                                                 \
-  }
-#define PI_AE_KV_STORE(SLOT, BUF)                                                     \
-  {                                                                                   \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
-      const int f = q * NWQ + w;                                                      \
-      kv[BUF][f >> 5][f & 31][lane] = st[SLOT][q];                                    \
-    }                                                                                 \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
-      *reinterpret_cast<u32x4*>(kbl + (BUF) * 64 + h * 32 + (lane & 7) * 4) = sb[SLOT][h]; \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)&KB[0], 4, uint32_t(lane) * 4u, uint32_t(PR) * 256u, 0, 0); \
   }
 
-  f32x4 acc[16];
+  f32x16 acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;  // l_part: this lane's keys only
+  const int kl0 = frag32_lane(lane, 0), kl1 = frag32_lane(lane, 1);
+  const int vl0 = (lane & 15) + 16 * hh, vl1 = vl0 + 32;
 
-  // the math of one pair from LDS buffer BUF; the second block of the last
-  // pair of an odd count is masked out
-#define PI_AE_KV_PAIR(BUF, PR)                                                         \
+  // the math of block kh of the pair in buffer KV
+#define PI_AE_KV32_MATH(KV, KB, PR)                                                    \
   {                                                                                    \
-    const bool second = 2 * (PR) + 1 < nkb;                                            \
+    u32x4 fr[16];                                                                      \
+    _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KV[kh][sub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    f32x16 sc;                                                                         \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) sc[i] = 0.f;                        \
+    _Pragma("unroll") for (int s = 0; s < 16; ++s) sc = mfma32(__builtin_bit_cast(bf16x8, fr[s]), qf[s], sc); \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    /* V operands of d-tile dt (both halves of the block) and the biases */           \
+    _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
+      fr[2 * dt] = KV[kh][16 + 2 * dt + sub][vl0];                                     \
+      fr[2 * dt + 1] = KV[kh][16 + 2 * dt + sub][vl1];                                 \
+    }                                                                                  \
     float4 bias[4];                                                                    \
-    _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) {                                 \
-      bias[mk] = *reinterpret_cast<const float4*>(kbl + (BUF) * 64 + (mk >> 1) * 32 + (mk & 1) * 16 + 4 * g); \
-      if (mk >= 2 && !second) bias[mk] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY); \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                      \
+      bias[q] = *reinterpret_cast<const float4*>(&KB[kh * 32 + 8 * q + 4 * hh]);       \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    const bool valid = 2 * (PR) + kh < nkb;                                            \
+    const float scl = 0.0625f * 1.4426950408889634f; /* 1/sqrt(256) * log2(e) */       \
+    float mloc = -INFINITY;                                                            \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                   \
+      const float4 bq = bias[i >> 2];                                                  \
+      const float bv = (i & 3) == 0 ? bq.x : (i & 3) == 1 ? bq.y : (i & 3) == 2 ? bq.z : bq.w; \
+      sc[i] = valid ? sc[i] * scl + bv : -INFINITY;                                    \
+      mloc = fmaxf(mloc, sc[i]);                                                       \
     }                                                                                  \
-    /* every K fragment of the pair in flight at once, then 4 interleaved chains */   \
-    u32x4 fr[32];                                                                      \
-    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks)                                   \
-      _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) fr[ks * 4 + mk] = kv[BUF][mk >> 1][(mk & 1) * 8 + ks][lane]; \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
-    f32x4 sc[4];                                                                       \
-    _Pragma("unroll") for (int mk = 0; mk < 4; ++mk) sc[mk] = f32x4{0.f, 0.f, 0.f, 0.f}; \
-    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks)                                   \
-      _Pragma("unroll") for (int mk = 0; mk < 4; ++mk)                                 \
-        sc[mk] = mfma(__builtin_bit_cast(bf16x8, fr[ks * 4 + mk]), qf[ks], sc[mk]);    \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
-    /* V fragments issued before the softmax, so their reads overlap it */            \
-    _Pragma("unroll") for (int md = 0; md < 16; ++md) {                                \
-      fr[2 * md] = kv[BUF][0][16 + md][lane];                                          \
-      fr[2 * md + 1] = kv[BUF][1][16 + md][lane];                                      \
+    mloc = xor32_max(mloc);                                                            \
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.f)) {                             \
+      const float m_new = fmaxf(m_run, mloc);                                          \
+      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);             \
+      l_part *= alpha;                                                                 \
+      _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;               \
+      m_run = m_new;                                                                   \
     }                                                                                  \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
-    float alpha;                                                                       \
-    bf16x8 pa, pb;                                                                     \
-    attn_softmax2(sc, bias, m_run, l_run, alpha, pa, pb);                              \
-    _Pragma("unroll") for (int md = 0; md < 16; ++md) {                                \
-      acc[md] = mfma(__builtin_bit_cast(bf16x8, fr[2 * md]), pa, acc[md] * alpha);     \
-      acc[md] = mfma(__builtin_bit_cast(bf16x8, fr[2 * md + 1]), pb, acc[md]);         \
+    const bool none = m_run == -INFINITY;                                              \
+    float pv[16];                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                   \
+      pv[i] = none ? 0.f : exp2f(sc[i] - m_run);                                       \
+      l_part += pv[i];                                                                 \
+    }                                                                                  \
+    const bf16x8 p0 = pack8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7])); \
+    const bf16x8 p1 = pack8(make_float4(pv[8], pv[9], pv[10], pv[11]), make_float4(pv[12], pv[13], pv[14], pv[15])); \
+    _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
+      const u32x4 a0 = fr[2 * dt], a1 = fr[2 * dt + 1];                                \
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), p0, acc[dt]); \
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.z, a0.w, a1.z, a1.w}), p1, acc[dt]); \
     }                                                                                  \
   }
-
-#pragma unroll
-  for (int s2 = 0; s2 < NST; ++s2) PI_AE_KV_FETCH(s2, s2)
-  PI_AE_KV_STORE(0, 0)
-  // step pr (stage s = pr mod NST, buffer pr mod 2): pair pr is in LDS after
-  // the barrier; st[s] is free again and fetches pair pr+NST; pair pr+1
-  // (fetched NST-1 steps ago) goes to the other buffer after the math.
-  for (int p0 = 0; p0 < npair; p0 += NST) {
-#pragma unroll
-    for (int s2 = 0; s2 < NST; ++s2) {
-      const int pr = p0 + s2, buf = pr & 1;
-      PI_AE_KV_FETCH(s2, pr + NST)
-      lds_barrier();  // pair pr is in buffer buf; buffer buf^1 is no longer read
-      if (pr < npair) PI_AE_KV_PAIR(buf, pr)
-      PI_AE_KV_STORE((s2 + 1) % NST, buf ^ 1)
-    }
+  // step PR: this wave's copies of pair PR (into KV) have landed, the barrier
+  // makes every wave's visible and retires all reads of the other buffer, then
+  // pair PR+1 is copied there while pair PR is processed
+#define PI_AE_KV32_STEP(KV, KB, KV2, KB2, PR)                                          \
+  {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0) */                                 \
+    lds_barrier();                                                                     \
+    if ((PR) + 1 < npair) PI_AE_KV32_COPY(KV2, KB2, (PR) + 1)                          \
+    PI_AE_KV32_MATH(KV, KB, PR)                                                        \
   }
-#undef PI_AE_KV_PAIR
-#undef PI_AE_KV_STORE
-#undef PI_AE_KV_FETCH
 
-  // normalise and write O: through LDS so that each lane stores 8
-  // consecutive head-dim values of one row (16 bytes)
+  PI_AE_KV32_COPY(kva, kba, 0)
+  for (int pr = 0; pr < npair; pr += 2) {
+    PI_AE_KV32_STEP(kva, kba, kvb, kbb, pr)
+    if (pr + 1 < npair) PI_AE_KV32_STEP(kvb, kbb, kva, kba, pr + 1)
+  }
+#undef PI_AE_KV32_STEP
+#undef PI_AE_KV32_MATH
+#undef PI_AE_KV32_COPY
+
+  // merge the key halves, normalise, and write O through LDS so that each
+  // lane stores 8 consecutive head-dim values of one row (16 bytes)
+  __syncthreads();  // every copy has landed and every read of the buffers is done
+  float* mg = reinterpret_cast<float*>(rg == 0 ? &kva[0][0][0] : &kvb[0][0][0]);
+  uint16_t* orow = reinterpret_cast<uint16_t*>(mg + kMrgFloats);  // [32][kORow]
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * 64 + lane] = acc[dt][i];
+    mg[128 * 64 + lane] = m_run;
+    mg[129 * 64 + lane] = xor32_sum(l_part);
+  }
   __syncthreads();
-  float* ob = lds + w * 16 * kOStride;  // this wave's 16 rows
-  const float inv = 1.f / l_run;
+  if (kh == 0) {
+    const float m1 = mg[128 * 64 + lane], l1 = mg[129 * 64 + lane];
+    const float m = fmaxf(m_run, m1);  // finite: every row has its own suffix keys
+    const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - m), a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - m);
+    const float inv = 1.f / (a0 * xor32_sum(l_part) + a1 * l1);
+    const float f0 = a0 * inv, f1 = a1 * inv;
 #pragma unroll
-  for (int md = 0; md < 16; ++md)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ob[c * kOStride + md * 16 + 4 * g + i] = acc[md][i] * inv;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back only its own rows
+      for (int q = 0; q < 4; ++q) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = acc[dt][4 * q + e] * f0 + mg[(dt * 16 + 4 * q + e) * 64 + lane] * f1;
+        const uint32_t lo = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
+        const uint32_t hi = uint32_t(f2bf(o[2])) | (uint32_t(f2bf(o[3])) << 16);
+        *reinterpret_cast<uint2*>(&orow[l32 * kORow + dt * 32 + 8 * q + 4 * hh]) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+  // the two waves of a group store its 32 rows x 32 chunks of 8 values
+  const int tg = kh * 64 + lane;
 #pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
-    const int idx = pass * 64 + lane, q = idx >> 5, d0 = (idx & 31) * 8;
-    const int rq = (qw * NWQ + w) * 16 + q;
-    const float4 a0 = *reinterpret_cast<const float4*>(&ob[q * kOStride + d0]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&ob[q * kOStride + d0 + 4]);
+    const int idx = pass * 128 + tg, q = idx >> 5, d0 = (idx & 31) * 8;
+    const int rq = (qw * NWQ + rg) * 32 + q;
+    const uint4 v = *reinterpret_cast<const uint4*>(&orow[q * kORow + d0]);
     if (rq < nq) {
       const int trow = b * p.T + rq / kH, head = rq % kH;
-      *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) =
-          __builtin_bit_cast(uint4, pack8(a0, a1));
+      *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = v;
     }
   }
 }
@@ -1263,9 +1273,9 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t
 hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
   const int nqb = (p.T * kH + 15) / 16;
   if (p.B * nqb >= kAttnRowsMinBlocks && p.pf.nwg == 0) {  // many episodes: K/V shared through LDS
-    const int per_ep = (nqb + kAttnRowWaves - 1) / kAttnRowWaves;
+    const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
     const int groups = (p.B + 7) / 8;  // 8 episodes (one per XCD residue) per group
-    return go(k_attn_rows<kAttnRowWaves>, dim3(8 * groups * per_ep), dim3(kAttnRowWaves * 64), s, t, p);
+    return go(k_attn_rows32<kAttn32Groups>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
   }
   return go(k_attn, dim3(nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
