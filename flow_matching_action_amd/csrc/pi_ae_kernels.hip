@@ -1244,7 +1244,7 @@ hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 4, E_QKV>, dim3(kNqkv / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+    return go(k_gemm_big32<4, 1, 2, E_QKV>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
   if (p.M <= 64)  // 32-row tiles: half the activation bytes per workgroup, twice the CUs
     return go(k_gemm<2, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M, 32)), dim3(256), s, t, p);
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
@@ -1258,14 +1258,14 @@ hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) 
 // slice and spread the launch over four times the CUs.
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 4, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 4, E_RES>, dim3(kD / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
