@@ -46,7 +46,6 @@ struct Prefetch {
 struct PrefetchSet {
   Prefetch r[3];
   int nwg;        // columns of prefetching workgroups appended (multiple of 8; 0 = none)
-  uint32_t* sink; // never written in practice (keeps the loads alive)
 };
 
 struct IoParams {
@@ -91,6 +90,11 @@ struct GemmParams {
   uint16_t* kp;           // QKV: packed K of this layer (suffix keys written here)
   uint16_t* vp;           // QKV: packed V of this layer
   uint16_t* m_out;        // GU: m, fragment-major [Mpad/16][128][64][8]
+  // O with the attention split over two key ranges (small M): a_frag and
+  // a_frag2 hold the two normalised partial outputs, astat [M][8][4] each
+  // query row's (max, sum) of both; the A operand is their weighted mean
+  const uint16_t* a_frag2;
+  const float* astat;
 };
 
 struct AttnParams {
@@ -100,8 +104,19 @@ struct AttnParams {
   const uint16_t* vp;     // packed V of this layer [B][nkb][16][64][8]
   const float* kbias;     // [B][nkb*32]: 0 valid, -inf masked / padding
   uint16_t* o;            // fragment-major [Mpad/16][64][64][8]
+  // o2 != null: each query block's keys are split over two workgroups; key
+  // range s writes its normalised partial output to (s ? o2 : o) and its
+  // (max, sum) to the row statistics fp32 [M * 8][4] (elements 2s, 2s+1),
+  // which follow the second output: attn_row_stats(o2, B * T).
+  // (Kept at 120 bytes: a larger argument block measurably slows this kernel.)
+  uint16_t* o2;
   int B, T, P, nkb;
 };
+// Where the attention row statistics live: right after the second partial
+// output, whose fragment-major rows are padded to a multiple of 16.
+inline __host__ __device__ float* attn_row_stats(uint16_t* o2, int M) {
+  return reinterpret_cast<float*>(o2 + size_t((M + 15) / 16) * 16 * kH * kHd);
+}
 
 struct PackParams {
   const DevArgs* da;

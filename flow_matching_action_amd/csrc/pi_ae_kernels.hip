@@ -64,6 +64,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Body of an appended prefetching workgroup (see Prefetch).  The `per`
 // prefetchers that share XCD residue `res` split that XCD's bytes evenly;
 // this one is number `sub` of them.  Loads are batched 8 deep per thread.
+// Written only if the XOR of everything a prefetcher loaded hits a magic
+// value: keeps the loads from being removed.
+__device__ uint32_t g_pf_sink;
 __device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, int per, int res) {
   uint32_t acc = 0;
   for (int d = 0; d < 3; ++d) {
@@ -89,7 +92,7 @@ __device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, in
       u += n;
     }
   }
-  if (acc == 0x9E3779B9u && threadIdx.x == 0) *pf.sink = acc;  // keeps the loads
+  if (acc == 0x9E3779B9u && threadIdx.x == 0) g_pf_sink = acc;  // keeps the loads
 }
 // Prefetching workgroups are the columns appended along x (a multiple of 8),
 // in every row of the grid when the grid's width is a multiple of 8 (then
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
 enum { E_QKV = 0, E_GELU = 1, E_RES = 2 };
 constexpr int kSsqTiles = kD / 16;  // partial sums of squares per row
 
-template <int MB, int NB, int NW, int KBW, int EPI>
+template <int MB, int NB, int NW, int KBW, int EPI, bool AM = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   PI_AE_PREFETCH_GUARD(p.pf, int(gridDim.x) - p.pf.nwg)
   constexpr int KB = KBW * NW;
@@ -302,6 +305,23 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
   for (int kb = 0; kb < PF; ++kb)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) abuf[kb][mb] = ap[(size_t(mb) * KB + ws * KBW + kb) * 64 + lane];
+  // AM: the second partial attention output and the weights of both, for
+  // this wave's head (its K slice is one head: ws)
+  static_assert(!AM || (PF == KBW && KBW * 32 == kHd && EPI == E_RES), "merged A: one head per wave, all up front");
+  uint4 abuf2[AM ? PF : 1][MB];
+  float4 ast[MB];
+  if constexpr (AM) {
+    const uint4* ap2 = reinterpret_cast<const uint4*>(p.a_frag2) + size_t(row0 >> 4) * KB * 64;
+#pragma unroll
+    for (int kb = 0; kb < PF; ++kb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) abuf2[kb][mb] = ap2[(size_t(mb) * KB + ws * KBW + kb) * 64 + lane];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = row0 + mb * 16 + (lane & 15);
+      ast[mb] = *reinterpret_cast<const float4*>(p.astat + (size_t(row < p.M ? row : 0) * kH + ws) * 4);
+    }
+  }
   uint4 bw[NB][KBW];
   const uint4* wp = reinterpret_cast<const uint4*>(p.w);
 #pragma unroll
@@ -352,6 +372,33 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (AM) {
+    // O = (a0 l0 O0 + a1 l1 O1) / (a0 l0 + a1 l1), a_s = 2^(m_s - max): the
+    // online-softmax merge of the two key ranges (weights in fp32, one bf16
+    // rounding of the result)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float4 st = ast[mb];
+      const float mx = fmaxf(st.x, st.z);
+      const float a0 = st.x == -INFINITY ? 0.f : exp2f(st.x - mx) * st.y;
+      const float a1 = st.z == -INFINITY ? 0.f : exp2f(st.z - mx) * st.w;
+      const float inv = 1.f / (a0 + a1);
+      const float w0 = a0 * inv, w1 = a1 * inv;
+#pragma unroll
+      for (int kb = 0; kb < PF; ++kb) {
+        const uint4 x = abuf[kb][mb], y = abuf2[kb][mb];
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf2f(xs[e] & 0xffffu) * w0 + bf2f(ys[e] & 0xffffu) * w1;
+          v[2 * e + 1] = bf2f(xs[e] >> 16) * w0 + bf2f(ys[e] >> 16) * w1;
+        }
+        abuf[kb][mb] = __builtin_bit_cast(uint4, pack8(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7])));
+      }
+    }
+  }
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -840,12 +887,18 @@ __global__ __launch_bounds__(256) void k_pack(PackParams p) {
 // keys (read-only cache, pad-masked) and all of its suffix keys ("LeRobot
 // implementation": repeat_kv -> Q K^T * scaling -> softmax -> V).  Queries are
 // the episode's (token, head) rows, so every query sees the same key set and
-// one K/V stream serves all heads.  Workgroup: 16 queries; its 4 waves split
+// one K/V stream serves all heads.  Workgroup: 16 queries; its 8 waves split
 // the 32-key blocks (online softmax in fp32) and are merged through LDS.
 // Scores are computed transposed (S^T = K Q^T) so that the probabilities land
 // in the B-operand lane order of O^T = V^T P^T; K and V arrive packed in
 // operand order, so every load is one contiguous 1 KiB fragment per wave, and
 // the next block's K is in flight while the current block is processed.
+// A workgroup's loads all pass through one CU's load path (about 64 bytes a
+// clock), and with few episodes the whole K/V stream of every query block
+// would go through it.  So at small batch and long key sequences (KS = 2)
+// the keys of each query block are split over two workgroups, each writing
+// its normalised partial output and (max, sum); the O projection merges the
+// two as it loads its A operand (the usual online-softmax combination).
 constexpr int kOStride = 260;  // floats per query row in the merge buffer
 
 // Online-softmax update for one 32-key block: scores (S^T, two 16-key halves)
@@ -887,6 +940,7 @@ __device__ __forceinline__ bf16x8 attn_softmax(const f32x4 (&s)[2], const float4
 
 constexpr int kAttnWaves = 8;
 
+template <int KS>
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   PI_AE_PREFETCH_GUARD(p.pf, int(gridDim.x) - p.pf.nwg)
   __shared__ __attribute__((aligned(16))) float ored[kAttnWaves * 16 * kOStride + kAttnWaves * 16 * 2];
@@ -894,7 +948,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.y;
   const int nq = p.T * kH;
-  const int r = blockIdx.x * 16 + c;
+  // with the key split, workgroups 2i and 2i+1 take the two key ranges of
+  // query block i
+  const int split = KS == 2 ? int(blockIdx.x) & 1 : 0;  // (KS = 2 iff p.o2 is set)
+  const int qb = KS == 2 ? int(blockIdx.x) >> 1 : int(blockIdx.x);
+  const int r = qb * 16 + c;
   const int rc = r < nq ? r : nq - 1;
 
   bf16x8 qf[8];
@@ -903,7 +961,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
 
   const int nkb = p.nkb;
-  const int kb0 = w * nkb / kAttnWaves, kb1 = (w + 1) * nkb / kAttnWaves;
+  const int kbs = split * nkb / KS, nks = (split + 1) * nkb / KS - kbs;
+  const int kb0 = kbs + w * nks / kAttnWaves, kb1 = kbs + (w + 1) * nks / kAttnWaves;
   const uint32_t ep_bytes = uint32_t(nkb) * 16384u;  // one episode's packed K (or V)
   const rsrc_t kr = make_rsrc(p.kp + size_t(b) * nkb * 8192, ep_bytes);
   const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
@@ -983,8 +1042,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
     f[w2] = (mw[w2] == -INFINITY) ? 0.f : exp2f(mw[w2] - mmax);
     L += f[w2] * sml[(w2 * 16 + q) * 2 + 1];
   }
-  const float inv = 1.f / L;
-  const int rq = blockIdx.x * 16 + q;
+  const float inv = L > 0.f ? 1.f / L : 0.f;  // L = 0: a key range with no valid key
+  const int rq = qb * 16 + q;
   if (rq < nq) {
     const int trow = b * p.T + rq / kH, head = rq % kH;
     float o[8];
@@ -997,7 +1056,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
     }
     const uint4 packed = __builtin_bit_cast(uint4, pack8(make_float4(o[0], o[1], o[2], o[3]),
                                                           make_float4(o[4], o[5], o[6], o[7])));
-    *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = packed;
+    *reinterpret_cast<uint4*>((split ? p.o2 : p.o) + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = packed;
+    if (KS == 2 && (threadIdx.x & 31) == 0)
+      *reinterpret_cast<float2*>(attn_row_stats(p.o2, p.B * p.T) + (size_t(b) * nq + rq) * 4 + 2 * split) =
+          make_float2(mmax, L);
   }
 }
 
@@ -1048,7 +1110,7 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   static_assert(64 % NW == 0, "a pair's 64 fragments split evenly over the waves");
   // one LDS buffer: [block of the pair][16 K + 16 V fragments][lane] (64 KiB)
   // and the pair's 64 key biases.  After the key loop, buffer g holds query
-  // group g's merge area (the second half's accumulators in register order,
+  // group g's merge area (the second half's accumulators, four per lane and 16-byte access,
   // its max and sum: 130 x 64 floats) and then its output rows as bf16.
   constexpr int kMrgFloats = 130 * 64, kORow = kHd + 8;  // bf16 per output row (16-byte aligned, staggered banks)
   static_assert(NWQ <= 2, "one LDS buffer per query group after the loop");
@@ -1153,23 +1215,39 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
       acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.z, a0.w, a1.z, a1.w}), p1, acc[dt]); \
     }                                                                                  \
   }
-  // step PR: this wave's copies of pair PR (into KV) have landed, the barrier
-  // makes every wave's visible and retires all reads of the other buffer, then
-  // pair PR+1 is copied there while pair PR is processed
+  // L2 warm-up of pair PR: one dword load per lane touches one 128-byte line;
+  // a workgroup's waves cover half of the pair's 512 lines (K: waves 0-1, V:
+  // waves 2-3; which half alternates with the workgroup), the episode's other
+  // workgroups the rest.  Past the last block the loads read as zeros.  The
+  // loaded words go to an LDS scratch word per lane that nothing reads (a
+  // load that writes LDS needs no register, so nothing waits for it).
+  __shared__ uint32_t warm_sink[64];
+  const uint32_t warm_off = uint32_t((qw & 1) * 128 + (w & 1) * 64 + lane) * 128u;
+#define PI_AE_KV32_WARM(PR) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(w < 2 ? kr : vr, (lds_ptr_t)&warm_sink[0], 4, warm_off, uint32_t(PR) * 32768u, 0, 0);
+
+  // step PR: this wave's copies of pair PR (into KV) have landed (only the
+  // warm-up load issued after them may be outstanding), the barrier makes
+  // every wave's visible and retires all reads of the other buffer, then pair
+  // PR+1 is copied there and pair PR+2 warmed up in L2 while pair PR is
+  // processed
 #define PI_AE_KV32_STEP(KV, KB, KV2, KB2, PR)                                          \
   {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0) */                                 \
+    __builtin_amdgcn_s_waitcnt(0x0f71); /* vmcnt(1) */                                 \
     lds_barrier();                                                                     \
     if ((PR) + 1 < npair) PI_AE_KV32_COPY(KV2, KB2, (PR) + 1)                          \
+    PI_AE_KV32_WARM((PR) + 2)                                                          \
     PI_AE_KV32_MATH(KV, KB, PR)                                                        \
   }
 
   PI_AE_KV32_COPY(kva, kba, 0)
+  PI_AE_KV32_WARM(1)
   for (int pr = 0; pr < npair; pr += 2) {
     PI_AE_KV32_STEP(kva, kba, kvb, kbb, pr)
     if (pr + 1 < npair) PI_AE_KV32_STEP(kvb, kbb, kva, kba, pr + 1)
   }
 #undef PI_AE_KV32_STEP
+#undef PI_AE_KV32_WARM
 #undef PI_AE_KV32_MATH
 #undef PI_AE_KV32_COPY
 
@@ -1178,11 +1256,13 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   __syncthreads();  // every copy has landed and every read of the buffers is done
   float* mg = reinterpret_cast<float*>(rg == 0 ? &kva[0][0][0] : &kvb[0][0][0]);
   uint16_t* orow = reinterpret_cast<uint16_t*>(mg + kMrgFloats);  // [32][kORow]
+  float4* mg4 = reinterpret_cast<float4*>(mg);  // [dt][q][lane]: accumulator values 4q .. 4q+3
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mg[(dt * 16 + i) * 64 + lane] = acc[dt][i];
+      for (int q = 0; q < 4; ++q)
+        mg4[(dt * 4 + q) * 64 + lane] = make_float4(acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]);
     mg[128 * 64 + lane] = m_run;
     mg[129 * 64 + lane] = xor32_sum(l_part);
   }
@@ -1193,26 +1273,39 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
     const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - m), a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - m);
     const float inv = 1.f / (a0 * xor32_sum(l_part) + a1 * l1);
     const float f0 = a0 * inv, f1 = a1 * inv;
+    // two batches of four d-tiles: all reads of a batch are issued before its
+    // writes (which the compiler may not reorder across, both being LDS)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int half = 0; half < 2; ++half) {
+      float4 x[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float o[4];
+      for (int k = 0; k < 16; ++k) x[k] = mg4[(half * 16 + k) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = acc[dt][4 * q + e] * f0 + mg[(dt * 16 + 4 * q + e) * 64 + lane] * f1;
-        const uint32_t lo = uint32_t(f2bf(o[0])) | (uint32_t(f2bf(o[1])) << 16);
-        const uint32_t hi = uint32_t(f2bf(o[2])) | (uint32_t(f2bf(o[3])) << 16);
+      for (int k = 0; k < 16; ++k) {
+        const int dt = half * 4 + (k >> 2), q = k & 3;
+        const float o0 = acc[dt][4 * q] * f0 + x[k].x * f1, o1 = acc[dt][4 * q + 1] * f0 + x[k].y * f1;
+        const float o2 = acc[dt][4 * q + 2] * f0 + x[k].z * f1, o3 = acc[dt][4 * q + 3] * f0 + x[k].w * f1;
+        const uint32_t lo = uint32_t(f2bf(o0)) | (uint32_t(f2bf(o1)) << 16);
+        const uint32_t hi = uint32_t(f2bf(o2)) | (uint32_t(f2bf(o3)) << 16);
         *reinterpret_cast<uint2*>(&orow[l32 * kORow + dt * 32 + 8 * q + 4 * hh]) = make_uint2(lo, hi);
       }
+    }
   }
   __syncthreads();
   // the two waves of a group store its 32 rows x 32 chunks of 8 values
   const int tg = kh * 64 + lane;
+  uint4 ov[8];
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {
+    const int idx = pass * 128 + tg, q = idx >> 5, d0 = (idx & 31) * 8;
+    ov[pass] = *reinterpret_cast<const uint4*>(&orow[q * kORow + d0]);
+  }
 #pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
     const int idx = pass * 128 + tg, q = idx >> 5, d0 = (idx & 31) * 8;
     const int rq = (qw * NWQ + rg) * 32 + q;
-    const uint4 v = *reinterpret_cast<const uint4*>(&orow[q * kORow + d0]);
+    const uint4 v = ov[pass];
     if (rq < nq) {
       const int trow = b * p.T + rq / kH, head = rq % kH;
       *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = v;
@@ -1257,8 +1350,15 @@ hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) 
 // O and down: at small M, 16-row tiles quarter each workgroup's activation
 // slice and spread the launch over four times the CUs.
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  if (p.M >= kTiledMinRows)
+  if (p.M >= kTiledMinRows) {
+    if (p.a_frag2) return hipErrorInvalidValue;  // the key split is only taken at small M
     return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+  }
+  if (p.a_frag2) {
+    if (p.M <= 64)
+      return go(k_gemm<1, 1, 8, 8, E_RES, true>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
+    return go(k_gemm<4, 1, 8, 8, E_RES, true>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
+  }
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 8, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
@@ -1272,12 +1372,13 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
   const int nqb = (p.T * kH + 15) / 16;
-  if (p.B * nqb >= kAttnRowsMinBlocks && p.pf.nwg == 0) {  // many episodes: K/V shared through LDS
+  if (!p.o2 && p.B * nqb >= kAttnRowsMinBlocks && p.pf.nwg == 0) {  // many episodes: K/V shared through LDS
     const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
     const int groups = (p.B + 7) / 8;  // 8 episodes (one per XCD residue) per group
     return go(k_attn_rows32<kAttn32Groups>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
   }
-  return go(k_attn, dim3(nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
+  if (p.o2) return go(k_attn<2>, dim3(2 * nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
+  return go(k_attn<1>, dim3(nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {
   if (p.B <= 0 || p.nkb <= 0) return hipSuccess;

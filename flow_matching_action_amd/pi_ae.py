@@ -213,7 +213,7 @@ class Context:
         M = batch * T
         shapes = {0: ((M, 1024), np.float32), 1: ((M, 8, 256), np.uint16), 2: ((M, 256), np.uint16),
                   3: ((M, 256), np.uint16), 4: ((M, 2048), np.uint16), 5: ((M, 4096), np.uint16),
-                  6: ((M, 32), np.float32)}
+                  6: ((M, 32), np.float32), 7: ((M, 2048), np.uint16), 8: ((M, 8, 4), np.float32)}
         shape, dt = shapes[which]
         out = np.empty(shape, dt)
         kv = self._kv(k, v, pad_mask, prefix_len)

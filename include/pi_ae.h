@@ -192,8 +192,18 @@ pi_ae_status pi_ae_debug_host_table(const pi_ae_config* cfg, const pi_ae_weights
  * residual, 4 = gate/up, 5 = down + gated residual).  which: 0 = h fp32
  * [M][width], 1 = Q bf16 [M][heads][head_dim], 2 = K_s bf16 [M][head_dim],
  * 3 = V_s bf16 [M][head_dim], 4 = O bf16 [M][heads*head_dim], 5 = m bf16
- * [M][mlp_dim], 6 = x fp32 [M][action_dim]; M = batch*chunk_len, rows in
- * natural order.  Synchronous; uses the null stream. */
+ * [M][mlp_dim], 6 = x fp32 [M][action_dim], 7 = second partial O bf16
+ * [M][heads*head_dim], 8 = attention row statistics fp32 [M][heads][4];
+ * M = batch*chunk_len, rows in natural order.  At M < 129 with at least 16
+ * key blocks of 32 (nkb = ceil((prefix_len + chunk_len) / 32) >= 16) the
+ * attention splits each query's keys into two ranges (blocks [0, nkb/2) and
+ * [nkb/2, nkb)): 4 and 7 are then the two ranges' normalised outputs and 8
+ * holds (max_0, sum_0, max_1, sum_1) per query, max in units of log2 after
+ * the 1/sqrt(head_dim) scaling; the attention output is
+ * (a_0 sum_0 O_0 + a_1 sum_1 O_1) / (a_0 sum_0 + a_1 sum_1), a_s =
+ * 2^(max_s - max(max_0, max_1)) (a_s = 0 where max_s = -inf).  Otherwise 4
+ * is the attention output and 7 / 8 are unused.  Synchronous; uses the null
+ * stream. */
 pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, int32_t batch,
                                int32_t step, int32_t layer, int32_t phase, int32_t which, void* host_out,
                                size_t n_bytes);
