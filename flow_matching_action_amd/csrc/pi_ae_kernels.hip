@@ -978,10 +978,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   const int r = qb * 16 + c;
   const int rc = r < nq ? r : nq - 1;
 
-  bf16x8 qf[8];
-  const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(*reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g));
+  // the workgroup's 16 query rows are loaded once (one 16-byte piece per
+  // thread) and shared through LDS: a workgroup is bound by the bytes its CU
+  // pulls in, and per-wave copies of Q were a sixth of them.  Rows are padded
+  // to 33 pieces so that the fragment reads hit distinct banks.
+  static_assert(kAttnWaves * 64 == 16 * 32, "one 16-byte piece of Q per thread");
+  __shared__ uint4 qs[16 * 33];
+  const int qpr = int(threadIdx.x) >> 5, qpc = int(threadIdx.x) & 31;
+  const uint4 qpiece = *reinterpret_cast<const uint4*>(
+      p.q + (size_t(b) * nq + min(qb * 16 + qpr, nq - 1)) * kHd + qpc * 8);
+  (void)rc;
 
   const int nkb = p.nkb;
   const int kbs = split * nkb / KS, nks = (split + 1) * nkb / KS - kbs;
@@ -999,16 +1005,25 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 
   // one K / V register set per wave: block kb+1's K is issued as soon as the
   // scores of block kb have consumed K, its V as soon as O^T has consumed V
+  // (unconditional, so that every wait count is exact: a wave without a
+  // block reads block 0, in bounds and unused)
   uint4 kf[16], vf[16];
   float4 bias[2];
-  if (kb0 < kb1) {
+  {
+    const uint32_t kbl = uint32_t(kb0 < kb1 ? kb0 : 0);
 #pragma unroll
-    for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, uint32_t(kb0) * 16384u + f * 1024u);
+    for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, kbl * 16384u + f * 1024u);
 #pragma unroll
-    for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, uint32_t(kb0) * 16384u + f * 1024u);
-    bias[0] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb0) * 128u));
-    bias[1] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb0) * 128u + 64u));
+    for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, kbl * 16384u + f * 1024u);
+    bias[0] = __builtin_bit_cast(float4, bload16(br, go16, kbl * 128u));
+    bias[1] = __builtin_bit_cast(float4, bload16(br, go16, kbl * 128u + 64u));
   }
+  // the Q piece lands in LDS while the K/V loads are in flight
+  qs[qpr * 33 + qpc] = qpiece;
+  lds_barrier();
+  bf16x8 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(qs[c * 33 + ks * 4 + g]);
   for (int kb = kb0; kb < kb1; ++kb) {
     const bool more = kb + 1 < kb1;
     const uint32_t nxt = uint32_t(kb + 1) * 16384u;
