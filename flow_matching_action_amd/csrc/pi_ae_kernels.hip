@@ -176,24 +176,25 @@ __device__ __forceinline__ size_t vpack_index(int b, int key, int d, int nkb) {
 // episode's valid prefix keys (the suffix RoPE positions start there; the
 // blog's prefix/suffix softmax kernel likewise reads the prefix valid length
 // dynamically).
+// One workgroup per episode (grid max(B, 1)); workgroup 0 also publishes the
+// pointers.
 __global__ __launch_bounds__(256) void k_args(ArgsParams p) {
-  __shared__ int cnt;
-  if (threadIdx.x == 0) *p.da = p.vals;
-  for (int b = 0; b < p.B; ++b) {
-    if (threadIdx.x == 0) cnt = 0;
-    __syncthreads();
-    int c = 0;
-    if (p.vals.mask) {
-      const uint8_t* mrow = p.vals.mask + size_t(b) * p.P;
-      for (int i = threadIdx.x; i < p.P; i += blockDim.x) c += mrow[i] != 0;
-    } else if (threadIdx.x == 0) {
-      c = p.P;
-    }
-    if (c) atomicAdd(&cnt, c);
-    __syncthreads();
-    if (threadIdx.x == 0) p.n_valid[b] = cnt;
-    __syncthreads();
+  __shared__ int part[4];
+  const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) *p.da = p.vals;
+  if (b >= p.B) return;  // (uniform per workgroup)
+  int c = 0;
+  if (p.vals.mask) {
+    const uint8_t* mrow = p.vals.mask + size_t(b) * p.P;
+    for (int i = threadIdx.x; i < p.P; i += blockDim.x) c += mrow[i] != 0;
+  } else if (threadIdx.x == 0) {
+    c = p.P;
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) p.n_valid[b] = part[0] + part[1] + part[2] + part[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -1366,7 +1367,7 @@ static hipError_t go(void (*kern)(A...), dim3 grid, dim3 block, hipStream_t s, c
 }
 
 hipError_t launch_args(const ArgsParams& p, hipStream_t s) {
-  k_args<<<1, 256, 0, s>>>(p);
+  k_args<<<p.B > 0 ? p.B : 1, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
