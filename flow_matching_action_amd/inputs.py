@@ -16,6 +16,11 @@ Draw recipe (stated here so that any reader can regenerate it):
     rounded to bf16 (round-to-nearest-even).  Order: action_in, time_in,
     time_out, final_mod, action_out (weight then bias each), then for each layer
     attn_mod (w, b), q, k, v, o, ffn_mod (w, b), gate, up, down.
+  * the pi0 variant (``variant = 1``: action-time encoder, RMSNorm scales
+    instead of AdaRMS; "Running VLAs at Real-time Speed" notes, section How):
+    order action_in, action_time_in, action_time_out, final_norm, action_out,
+    then per layer attn_norm, q, k, v, o, ffn_norm, gate, up, down; the norm
+    scales are 1 + standard_normal * 0.02 (the others as above).
   * prefix K/V cache: seed 1, drawn per layer as K[l] then V[l], each of shape
     [batch][prefix_len][head_dim], N(0, 1) rounded to bf16.
   * noise: seed 2, [batch][chunk][action_dim] N(0, 1) in fp32 (not rounded).
@@ -54,6 +59,7 @@ class ExpertConfig:
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     final_norm: bool = True
+    variant: int = 0          # 0: pi0.5 (AdaRMS); 1: pi0 (action-time encoder, RMSNorm scales)
 
     def replace(self, **kw) -> "ExpertConfig":
         return dataclasses.replace(self, **kw)
@@ -86,6 +92,11 @@ WORKLOADS = {
                    "18 layers x 10 steps, batch 1, 3 views + 48 prompt tokens, last 16 padded"),
     "c5": Workload("c5", _FULL.replace(chunk_len=50), 32, 712, 712,
                    "18 layers x 10 steps, 32 episodes x 50 tokens, 2 views + 200 prompt tokens each"),
+    # the pi0 variant of the expert (action-time encoder, RMSNorm scales)
+    "c1pi0": Workload("c1pi0", _FULL.replace(num_layers=2, num_steps=1, variant=1), 1, 256, 256,
+                      "pi0 variant: reduced expert, 2 layers, 1 Euler step, 1 view (256 prefix keys)"),
+    "c2pi0": Workload("c2pi0", _FULL.replace(variant=1), 1, 256, 256,
+                      "pi0 variant: 18 layers x 10 steps, batch 1, 1 view (256 prefix keys)"),
 }
 
 
@@ -111,6 +122,23 @@ def weight_shapes(cfg: ExpertConfig):
     """(name, shape) in draw order; nn.Linear layout [out][in]."""
     D, F, H, d, A = cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.head_dim, cfg.action_dim
     kv = cfg.num_kv_heads * d
+    if cfg.variant == 1:
+        out = [("action_in.w", (D, A)), ("action_in.b", (D,)),
+               ("action_time_in.w", (D, 2 * D)), ("action_time_in.b", (D,)),
+               ("action_time_out.w", (D, D)), ("action_time_out.b", (D,))]
+        if cfg.final_norm:
+            out += [("final_norm.w", (D,))]
+        out += [("action_out.w", (A, D)), ("action_out.b", (A,))]
+        for l in range(cfg.num_layers):
+            p = f"layers.{l}."
+            out += [
+                (p + "attn_norm.w", (D,)),
+                (p + "q.w", (H * d, D)), (p + "k.w", (kv, D)), (p + "v.w", (kv, D)),
+                (p + "o.w", (D, H * d)),
+                (p + "ffn_norm.w", (D,)),
+                (p + "gate.w", (F, D)), (p + "up.w", (F, D)), (p + "down.w", (D, F)),
+            ]
+        return out
     out = [
         ("action_in.w", (D, A)), ("action_in.b", (D,)),
         ("time_in.w", (D, D)), ("time_in.b", (D,)),
@@ -136,6 +164,8 @@ def _weights_uncached(cfg: ExpertConfig, seed: int, std: float) -> dict:
     for name, shape in weight_shapes(cfg):
         x = rng.standard_normal(shape, dtype=np.float32)
         x *= np.float32(std)
+        if name.endswith("norm.w"):  # a norm's scale: around 1
+            x += np.float32(1.0)
         out[name] = f32_to_bf16_bits(x)
     return out
 

@@ -47,6 +47,16 @@ design notes of the repository):
     the gate is used as is (no activation);
   * timestep k is t_k = fp32(t0 + k * dt), evaluated in fp64.
 
+The pi0 variant (``cfg.variant == 1``) follows the "Running VLAs at Real-time
+Speed" notes (knowledgebase summary, section How) and the Realtime-VLA blog's
+section 3.2: the expert layers use plain RMS norms with a learnable scale
+gamma (x_norm * gamma, which the pages fold into the next linear) and plain
+residuals; the step input is the action-time encoder, whose two linear layers
+the pages fold, tabulating the per-timestep part into the bias before the SiLU.
+Readings: the encoder is Linear(2048 -> 1024) on the concatenation
+[action_in_proj(x) | emb(t)], then SiLU, then Linear(1024 -> 1024); a final RMS
+norm with its own scale precedes action_out_proj (flag ``final_norm``).
+
 Every function states the passage it follows.  Parity of the trained model's
 behaviour is unpinned: there are no trained weights on the pages.
 """
@@ -219,16 +229,63 @@ def expert_layer(W: Weights, l: int, h, cond, prefix_k, prefix_v, key_valid, pos
     return h
 
 
+def encoder_pi0(W: Weights, x, t) -> np.ndarray:
+    """pi0 step input: Linear(SiLU(Linear([action_in_proj(x) | emb(t)]))).
+
+    ("Running VLAs at Real-time Speed" notes, section How: the action-time
+    encoder has two linear layers with a SiLU between them; its input joins the
+    projected action chunk with the timestep embedding.)  x: [T][A] -> [T][D].
+    """
+    D = W.cfg.width
+    a = x @ W["action_in.w"].T + W["action_in.b"]
+    emb = sinusoidal_embedding(t, D, dtype=W.dtype)
+    cat = np.concatenate([a, np.broadcast_to(emb, a.shape)], axis=1)
+    z = silu(cat @ W["action_time_in.w"].T + W["action_time_in.b"])
+    return z @ W["action_time_out.w"].T + W["action_time_out.b"]
+
+
+def expert_layer_pi0(W: Weights, l: int, h, prefix_k, prefix_v, key_valid, positions):
+    """One pi0 expert layer: RMS norm with scale gamma, attention, residual,
+    RMS norm with scale gamma, GELU-gated MLP, residual (Realtime-VLA blog,
+    section 3.2: the norm's learnable scale multiplies the normalised
+    activation)."""
+    cfg = W.cfg
+    T = h.shape[0]
+    H, d = cfg.num_heads, cfg.head_dim
+    eps = cfg.rms_eps
+    u = rms_normalize(h, eps) * W.layer(l, "attn_norm.w")
+    q = (u @ W.layer(l, "q.w").T).reshape(T, H, d)
+    ks = u @ W.layer(l, "k.w").T
+    vs = u @ W.layer(l, "v.w").T
+    q = rope(q.transpose(1, 0, 2), positions, cfg.rope_base).transpose(1, 0, 2)
+    ks = rope(ks, positions, cfg.rope_base)
+    keys = np.concatenate([prefix_k, ks], axis=0)
+    vals = np.concatenate([prefix_v, vs], axis=0)
+    valid = np.concatenate([key_valid, np.ones(T, dtype=bool)])
+    o = attention(q, keys, vals, valid, 1.0 / math.sqrt(d)).reshape(T, H * d)
+    h = h + o @ W.layer(l, "o.w").T
+    u2 = rms_normalize(h, eps) * W.layer(l, "ffn_norm.w")
+    m = gelu_tanh(u2 @ W.layer(l, "gate.w").T) * (u2 @ W.layer(l, "up.w").T)
+    return h + m @ W.layer(l, "down.w").T
+
+
 def velocity(W: Weights, x, t, prefix_k, prefix_v, key_valid):
     """v_t for one episode: x [T][A] -> [T][A] ("pi0.5 inference flow", steps 1-3).
 
     prefix_k/v: [L][P][d] (values); key_valid: bool [P].
     """
     cfg = W.cfg
-    cond = time_condition(W, t)
-    h = x @ W["action_in.w"].T + W["action_in.b"]
     n_valid = int(np.count_nonzero(key_valid))
     positions = n_valid + np.arange(x.shape[0])
+    if cfg.variant == 1:
+        h = encoder_pi0(W, x, t)
+        for l in range(cfg.num_layers):
+            h = expert_layer_pi0(W, l, h, prefix_k[l], prefix_v[l], key_valid, positions)
+        if cfg.final_norm:
+            h = rms_normalize(h, cfg.rms_eps) * W["final_norm.w"]
+        return h @ W["action_out.w"].T + W["action_out.b"]
+    cond = time_condition(W, t)
+    h = x @ W["action_in.w"].T + W["action_in.b"]
     for l in range(cfg.num_layers):
         h = expert_layer(W, l, h, cond, prefix_k[l], prefix_v[l], key_valid, positions)
     if cfg.final_norm:
@@ -291,6 +348,8 @@ def folded_tables(W: Weights):
     ts = timesteps(cfg.num_steps, cfg.t0, cfg.dt)
     L = cfg.num_layers
     tabs = {"t": ts, "cond": [], "attn": [], "ffn": [], "final": []}
+    if cfg.variant == 1:
+        return _folded_tables_pi0(W, ts, tabs)
     for t in ts:
         cond = time_condition(W, t)
         tabs["cond"].append(cond)
@@ -308,6 +367,36 @@ def folded_tables(W: Weights):
             sf, shf, _ = modulation(W["final_mod.w"], W["final_mod.b"], cond)
             c_out = W["action_out.w"] @ shf + W["action_out.b"]
             tabs["final"].append({"scale1": 1.0 + sf, "shift": shf, "c_out": c_out})
+        else:
+            tabs["final"].append({"scale1": None, "shift": None, "c_out": W["action_out.b"].copy()})
+    return tabs
+
+
+def _folded_tables_pi0(W: Weights, ts, tabs):
+    """pi0: the encoder's two linear layers folded ("Running VLAs at Real-time
+    Speed" notes, section How: the per-timestep part becomes a tabulated bias
+    before the SiLU): W_fold = W_ti[:, :D] @ W_in and, per step k, c_k =
+    W_ti[:, :D] @ b_in + W_ti[:, D:] @ emb(t_k) + b_ti; the layers' norm scales
+    become the (1 + scale) factors (shift 0, gate 1)."""
+    cfg = W.cfg
+    D, L = cfg.width, cfg.num_layers
+    wti = W["action_time_in.w"]
+    tabs["w_fold"] = wti[:, :D] @ W["action_in.w"]
+    for t in ts:
+        emb = sinusoidal_embedding(t, D, dtype=np.float64)
+        tabs["cond"].append(wti[:, :D] @ W["action_in.b"] + wti[:, D:] @ emb + W["action_time_in.b"])
+        attn_k, ffn_k = [], []
+        for l in range(L):
+            zq = np.zeros(cfg.num_heads * cfg.head_dim + 2 * cfg.head_dim)
+            attn_k.append({"scale1": W.layer(l, "attn_norm.w").copy(), "shift": np.zeros(D),
+                           "gate": np.ones(D), "c_qkv": zq})
+            ffn_k.append({"scale1": W.layer(l, "ffn_norm.w").copy(), "shift": np.zeros(D),
+                          "gate": np.ones(D), "c_gu": np.zeros(2 * cfg.mlp_dim)})
+        tabs["attn"].append(attn_k)
+        tabs["ffn"].append(ffn_k)
+        if cfg.final_norm:
+            tabs["final"].append({"scale1": W["final_norm.w"].copy(), "shift": np.zeros(D),
+                                  "c_out": W["action_out.b"].copy()})
         else:
             tabs["final"].append({"scale1": None, "shift": None, "c_out": W["action_out.b"].copy()})
     return tabs
@@ -338,7 +427,11 @@ def sample_folded(weight_bits: dict, cfg, prefix_k_bits, prefix_v_bits, pad_mask
         n_valid = int(np.count_nonzero(valid))
         pos = n_valid + np.arange(T)
         for k in range(cfg.num_steps):
-            h = x @ W["action_in.w"].T + W["action_in.b"]
+            if cfg.variant == 1:
+                z = silu(x @ tabs["w_fold"].T + tabs["cond"][k])
+                h = z @ W["action_time_out.w"].T + W["action_time_out.b"]
+            else:
+                h = x @ W["action_in.w"].T + W["action_in.b"]
             for l in range(L):
                 ta = tabs["attn"][k][l]
                 wqkv = np.concatenate([W.layer(l, "q.w"), W.layer(l, "k.w"), W.layer(l, "v.w")], axis=0)

@@ -421,3 +421,75 @@ def test_degenerate_sizes():
     k, v = inputs.make_prefix_kv(cfg, 1, 5)
     x2 = O.sample(wb, cfg, k, v, np.zeros((1, 5), np.uint8), inputs.make_noise(cfg, 1))
     np.testing.assert_allclose(x2, x, rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------- pi0 variant
+TINY_PI0 = TINY.replace(variant=1)
+
+
+def test_pi0_layer_equals_adarms_layer_with_scale_gamma():
+    """A pi0 layer (RMS norm scale gamma, plain residuals) is the AdaRMS layer
+    whose modulation is the constant (scale, shift, gate) = (gamma - 1, 0, 1):
+    pins the pi0 layer to the already-pinned AdaRMS layer."""
+    cfg = TINY_PI0
+    D = cfg.width
+    wb0 = rand_weights(cfg, seed=21)
+    W0 = O.Weights(wb0, cfg)
+    # the same layer weights in the pi0.5 layout, modulation dense = 0, bias = (gamma - 1 | 0 | 1)
+    cfg5 = cfg.replace(variant=0)
+    wb5 = zero_weights(cfg5)
+    l = 1
+    for name in ("q.w", "k.w", "v.w", "o.w", "gate.w", "up.w", "down.w"):
+        wb5[f"layers.{l}.{name}"] = wb0[f"layers.{l}.{name}"]
+    for mod, norm in (("attn_mod", "attn_norm"), ("ffn_mod", "ffn_norm")):
+        gamma = O.bf16_to_float(wb0[f"layers.{l}.{norm}.w"])
+        wb5[f"layers.{l}.{mod}.b"] = bits(np.concatenate([gamma - 1.0, np.zeros(D), np.ones(D)]))
+    W5 = O.Weights(wb5, cfg5)
+    # (gamma - 1 is exact in bf16 here only to rounding: compare against the rounded value)
+    for norm in ("attn_norm", "ffn_norm"):
+        g = O.bf16_to_float(wb0[f"layers.{l}.{norm}.w"])
+        W0.w[f"layers.{l}.{norm}.w"] = 1.0 + O.bf16_to_float(bits(g - 1.0))
+    h, pk, pv, valid = _layer_inputs(cfg, 22)
+    pos = 4 + np.arange(cfg.chunk_len)
+    a = O.expert_layer_pi0(W0, l, h, pk, pv, valid, pos)
+    b = O.expert_layer(W5, l, h, np.zeros(D), pk, pv, valid, pos)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_pi0_encoder_closed_forms():
+    """Encoder with identity blocks: [I | 0] keeps only the projected action,
+    [0 | I] only the timestep embedding; W_out = I, zero biases."""
+    cfg = TINY_PI0
+    D, A, T = cfg.width, cfg.action_dim, cfg.chunk_len
+    wb = rand_weights(cfg, seed=23)
+    eye = np.eye(D)
+    wb["action_time_out.w"] = bits(eye)
+    wb["action_time_out.b"] = bits(np.zeros(D))
+    wb["action_time_in.b"] = bits(np.zeros(D))
+    x = np.random.default_rng(24).standard_normal((T, A))
+    t = 0.7
+    wb["action_time_in.w"] = bits(np.concatenate([eye, np.zeros((D, D))], axis=1))
+    W = O.Weights(wb, cfg)
+    proj = x @ W["action_in.w"].T + W["action_in.b"]
+    np.testing.assert_allclose(O.encoder_pi0(W, x, t), proj / (1.0 + np.exp(-proj)), rtol=1e-13, atol=1e-14)
+    wb["action_time_in.w"] = bits(np.concatenate([np.zeros((D, D)), eye], axis=1))
+    W = O.Weights(wb, cfg)
+    e = O.sinusoidal_embedding(t, D)
+    want = np.broadcast_to(e / (1.0 + np.exp(-e)), (T, D))
+    np.testing.assert_allclose(O.encoder_pi0(W, x, t), want, rtol=1e-13, atol=1e-14)
+
+
+def test_pi0_fold_equalities():
+    """pi0: the folded encoder (W_ti[:, :D] @ W_in and the tabulated per-step
+    bias before the SiLU) and the norm scales as tables == unfolded (fp64)."""
+    cfg = TINY_PI0.replace(num_steps=4, dt=-0.25)
+    wb = rand_weights(cfg, seed=25)
+    B, P = 2, 7
+    k, v = inputs.make_prefix_kv(cfg, B, P)
+    mask = inputs.make_pad_mask(B, P, [7, 3])
+    noise = inputs.make_noise(cfg, B)
+    for c in (cfg, cfg.replace(final_norm=False)):
+        wbc = inputs.make_weights(c, seed=25, std=0.2, cache=False)
+        a = O.sample(wbc, c, k, v, mask, noise)
+        b = O.sample_folded(wbc, c, k, v, mask, noise)
+        assert np.linalg.norm(a - b) <= 1e-10 * np.linalg.norm(a)
