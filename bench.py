@@ -41,6 +41,8 @@ def algorithmic_bytes_per_step(w) -> float:
     cfg = w.cfg
     per_layer = sum(PHASE_WEIGHT_BYTES.values())
     io = 2 * 32 * 1024 * 2
+    if getattr(cfg, "variant", 0) == 1:  # pi0: the action-time encoder's output layer
+        io += 1024 * 1024 * 2
     kv = cfg.num_layers * w.batch * w.n_valid * 256 * 2 * 2
     return cfg.num_layers * per_layer + io + kv
 
@@ -50,6 +52,8 @@ def algorithmic_flops_per_step(w) -> float:
     M = w.batch * cfg.chunk_len
     gemm = 2 * M * (1024 * 2560 + 2048 * 1024 + 1024 * 8192 + 4096 * 1024) * cfg.num_layers
     gemm += 2 * M * (32 * 1024 * 2)
+    if getattr(cfg, "variant", 0) == 1:
+        gemm += 2 * M * 1024 * 1024
     attn = 4 * 8 * cfg.chunk_len * (w.n_valid + cfg.chunk_len) * 256 * w.batch * cfg.num_layers
     return gemm + attn
 
@@ -106,7 +110,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-chunks", type=int, default=2,
                     help="whole loop passes over which each kernel's in-loop duration is averaged")

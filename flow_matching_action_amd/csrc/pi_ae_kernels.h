@@ -66,6 +66,12 @@ struct IoParams {
   int do_in;              // start a step: action_in
   int from_noise;         // x comes from noise (first step)
   int M;
+  // pi0 action-time encoder (enc = 1): do_in computes z = SiLU(x W_in^T + b_in)
+  // (W_in, b_in: the folded encoder input and this step's bias) into u_out as
+  // the operand of the encoder's output GEMM [Mpad/16][32][64][8], and sets
+  // h = h_init (that GEMM's bias, to which it adds); no u / h^2 partials
+  const float* h_init;
+  int enc;
 };
 
 struct GemmParams {
@@ -150,6 +156,9 @@ hipError_t launch_pack(const PackParams& p, int L, hipStream_t s);
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+// h += acc * gate with K = 1024 (the pi0 encoder's output layer), the same
+// residual epilogue as O and down
+hipError_t launch_enc(const GemmParams& p, hipStream_t s);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

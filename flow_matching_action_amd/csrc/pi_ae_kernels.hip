@@ -261,11 +261,19 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
           acc += sx[8 * v4 + 2 * e + 1] * bf2f(ww[e] >> 16);
         }
       }
-      su[n] = acc;
+      su[n] = p.enc ? acc / (1.f + __expf(-acc)) : acc;  // pi0 encoder: SiLU
     }
     // (su is free here: every read of it above happened before the barrier)
     __syncthreads();
     const float4 hv = reinterpret_cast<const float4*>(su)[t];
+    if (p.enc) {  // the encoder's hidden activation for its output GEMM, which adds into h = h_init
+      reinterpret_cast<float4*>(p.h + size_t(row) * kD)[t] = reinterpret_cast<const float4*>(p.h_init)[t];
+      const uint32_t lo = uint32_t(f2bf(hv.x)) | (uint32_t(f2bf(hv.y)) << 16);
+      const uint32_t hi = uint32_t(f2bf(hv.z)) | (uint32_t(f2bf(hv.w)) << 16);
+      *reinterpret_cast<uint2*>(p.u_out + afrag_index(row, 4 * t, kD / 32)) = make_uint2(lo, hi);
+      if (t < kA) x[t] = sx[t];
+      return;
+    }
     reinterpret_cast<float4*>(p.h + size_t(row) * kD)[t] = hv;
     // the first layer's normalised-GEMM operand and the h^2 partial of this
     // thread's 16-column tile (4 threads per tile)
@@ -1408,6 +1416,13 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
+}
+hipError_t launch_enc(const GemmParams& p, hipStream_t s) {
+  if (p.M >= kTiledMinRows)
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, nullptr, p, kD);
+  if (p.M <= 64)
+    return go(k_gemm<1, 1, 8, 4, E_RES>, dim3(kD / 16, row_tiles(p.M, 16)), dim3(512), s, nullptr, p);
+  return go(k_gemm<4, 1, 8, 4, E_RES>, dim3(kD / 16, row_tiles(p.M)), dim3(512), s, nullptr, p);
 }
 hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
   const int nqb = (p.T * kH + 15) / 16;

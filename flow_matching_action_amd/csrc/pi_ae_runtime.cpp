@@ -48,6 +48,15 @@ inline double bf(uint16_t v) {
   std::memcpy(&f, &u, 4);
   return double(f);
 }
+// fp64 -> bf16 bits, round to nearest even (through fp32, also RNE)
+inline uint16_t bf16_of(double x) {
+  const float f = float(x);
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return uint16_t(u >> 16);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
 
 }  // namespace
 
@@ -59,6 +68,10 @@ struct pi_ae_ctx {
   // prepared weights (device)
   uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr, *w_in = nullptr, *w_out = nullptr;
   float* b_in = nullptr;
+  // pi0 variant: the encoder's output layer (swizzled), its bias, the encoder's
+  // per-step input bias [S][1024] and a gate of ones
+  uint16_t* w_to = nullptr;
+  float *b_to = nullptr, *enc_bias = nullptr, *ones = nullptr;
   // tables (device), kernel column order
   float *attn_s1 = nullptr, *attn_g = nullptr, *c_qkv = nullptr, *ffn_s1 = nullptr, *ffn_g = nullptr,
         *c_gu = nullptr, *fin_s1 = nullptr, *c_out = nullptr;
@@ -117,6 +130,7 @@ pi_ae_status check_config(const pi_ae_config* c) {
   if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(PI_AE_EINVAL, "rope_base must be > 0");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(PI_AE_EINVAL, "rms_eps must be >= 0");
   if (c->final_norm != 0 && c->final_norm != 1) return fail(PI_AE_EINVAL, "final_norm must be 0 or 1");
+  if (c->variant != 0 && c->variant != 1) return fail(PI_AE_EINVAL, "variant must be 0 (pi0.5) or 1 (pi0)");
   return PI_AE_OK;
 }
 
@@ -127,6 +141,23 @@ pi_ae_status check_weights(const pi_ae_config* c, const pi_ae_weights* w) {
     return PI_AE_OK;
   };
   pi_ae_status s;
+  if (c->variant == 1) {
+    if ((s = need(w->action_in, true, "action_in")) || (s = need(w->action_time_in, true, "action_time_in")) ||
+        (s = need(w->action_time_out, true, "action_time_out")) || (s = need(w->action_out, true, "action_out")))
+      return s;
+    if (c->final_norm && !w->final_norm) return fail(PI_AE_EINVAL, "final_norm (gamma) is NULL");
+    if (!w->layers) return fail(PI_AE_EINVAL, "layers is NULL");
+    for (int l = 0; l < c->num_layers; ++l) {
+      const pi_ae_layer_weights& L = w->layers[l];
+      if (!L.attn_norm || !L.ffn_norm)
+        return fail(PI_AE_EINVAL, "attn_norm / ffn_norm is NULL (layer " + std::to_string(l) + ")");
+      if ((s = need(L.q, false, "q")) || (s = need(L.k, false, "k")) || (s = need(L.v, false, "v")) ||
+          (s = need(L.o, false, "o")) || (s = need(L.gate, false, "gate")) || (s = need(L.up, false, "up")) ||
+          (s = need(L.down, false, "down")))
+        return fail(s, g_last_error + " (layer " + std::to_string(l) + ")");
+    }
+    return PI_AE_OK;
+  }
   if ((s = need(w->action_in, true, "action_in")) || (s = need(w->time_in, true, "time_in")) ||
       (s = need(w->time_out, true, "time_out")) || (s = need(w->action_out, true, "action_out")))
     return s;
@@ -232,11 +263,51 @@ void parallel_for(int n, F&& fn) {
 // The fp64 host half of the preparation: tables in natural column order
 // (0 attn 1+scale, 1 attn gate, 2 ffn 1+scale, 3 ffn gate, 4 final 1+scale,
 // 5 c_out, 6 c_qkv, 7 c_gu, 8 timesteps, 9 cond).
+// pi0 ("Running VLAs at Real-time Speed" notes, section How; blog section
+// 3.2): the norm scales gamma as the (1 + scale) tables (gates 1, shifts 0, so
+// c_qkv = c_gu = 0 and c_out = b_out), and the action-time encoder's
+// per-step bias before its SiLU, W_ti[:, :D] b_in + W_ti[:, D:] emb(t_k) + b_ti.
+void compute_tables_pi0(const pi_ae_config& cfg, const pi_ae_weights* w, const std::vector<double>& ts,
+                        std::vector<float>* tab) {
+  const int L = cfg.num_layers, S = cfg.num_steps;
+  tab[0].assign(size_t(S) * L * kD, 0.f); tab[1].assign(size_t(S) * L * kD, 1.f);
+  tab[2].assign(size_t(S) * L * kD, 0.f); tab[3].assign(size_t(S) * L * kD, 1.f);
+  for (int k = 0; k < S; ++k)
+    for (int l = 0; l < L; ++l)
+      for (int i = 0; i < kD; ++i) {
+        tab[0][(size_t(k) * L + l) * kD + i] = float(bf(w->layers[l].attn_norm[i]));
+        tab[2][(size_t(k) * L + l) * kD + i] = float(bf(w->layers[l].ffn_norm[i]));
+      }
+  tab[4].assign(size_t(S) * kD, 1.f);
+  if (cfg.final_norm)
+    for (int k = 0; k < S; ++k)
+      for (int i = 0; i < kD; ++i) tab[4][size_t(k) * kD + i] = float(bf(w->final_norm[i]));
+  tab[5].resize(size_t(S) * kA);
+  for (int k = 0; k < S; ++k)
+    for (int a = 0; a < kA; ++a) tab[5][size_t(k) * kA + a] = float(bf(w->action_out.b[a]));
+  tab[6].assign(size_t(S) * L * kNqkv, 0.f);
+  tab[7].assign(size_t(S) * L * kNgu, 0.f);
+  tab[8].assign(ts.begin(), ts.end());
+  tab[9].resize(size_t(S) * kD);
+  std::vector<double> bin(kD);
+  for (int j = 0; j < kD; ++j) bin[j] = bf(w->action_in.b[j]);
+  parallel_for(S, [&](int k) {
+    const std::vector<double> emb = time_embedding(ts[k], kD);
+    for (int i = 0; i < kD; ++i) {
+      const uint16_t* row = w->action_time_in.w + size_t(i) * 2 * kD;
+      double acc = bf(w->action_time_in.b[i]);
+      for (int j = 0; j < kD; ++j) acc += bf(row[j]) * bin[j] + bf(row[kD + j]) * emb[j];
+      tab[9][size_t(k) * kD + i] = float(acc);
+    }
+  });
+}
+
 void compute_tables(const pi_ae_config& cfg, const pi_ae_weights* w, std::vector<float>* tab) {
   const int L = cfg.num_layers, S = cfg.num_steps;
   // timesteps t_k = fp32(t0 + k dt), evaluated in fp64
   std::vector<double> ts(S);
   for (int k = 0; k < S; ++k) ts[k] = double(float(double(cfg.t0) + k * double(cfg.dt)));
+  if (cfg.variant == 1) return compute_tables_pi0(cfg, w, ts, tab);
   // time MLP: cond_k = SiLU(W_out SiLU(W_in emb + b_in) + b_out)
   std::vector<std::vector<double>> cond(S);
   parallel_for(S, [&](int k) {
@@ -343,7 +414,32 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
     }
   }
   ctx->w_in = ctx->dalloc<uint16_t>(size_t(kD) * kA);
-  HIP_OR_THROW(hipMemcpy(ctx->w_in, w->action_in.w, size_t(kD) * kA * 2, hipMemcpyHostToDevice));
+  if (cfg.variant == 1) {
+    // the encoder's input layer folded with action_in_proj: W_ti[:, :D] W_in
+    // (fp64, rounded to bf16 once); its output layer swizzled like W_o
+    std::vector<uint16_t> wf(size_t(kD) * kA);
+    parallel_for(kD, [&](int i) {
+      const uint16_t* row = w->action_time_in.w + size_t(i) * 2 * kD;
+      for (int a = 0; a < kA; ++a) {
+        double acc = 0.0;
+        for (int j = 0; j < kD; ++j) acc += bf(row[j]) * bf(w->action_in.w[size_t(j) * kA + a]);
+        wf[size_t(i) * kA + a] = bf16_of(acc);
+      }
+    });
+    HIP_OR_THROW(hipMemcpy(ctx->w_in, wf.data(), wf.size() * 2, hipMemcpyHostToDevice));
+    std::vector<uint16_t> sw(size_t(kD) * kD);
+    swizzle(w->action_time_out.w, kD, pid, sw.data());
+    ctx->w_to = ctx->dalloc<uint16_t>(sw.size());
+    HIP_OR_THROW(hipMemcpy(ctx->w_to, sw.data(), sw.size() * 2, hipMemcpyHostToDevice));
+    std::vector<float> bto(kD), ones(kD, 1.f);
+    for (int i = 0; i < kD; ++i) bto[i] = float(bf(w->action_time_out.b[i]));
+    ctx->b_to = ctx->dalloc<float>(kD);
+    HIP_OR_THROW(hipMemcpy(ctx->b_to, bto.data(), kD * 4, hipMemcpyHostToDevice));
+    ctx->ones = ctx->dalloc<float>(kD);
+    HIP_OR_THROW(hipMemcpy(ctx->ones, ones.data(), kD * 4, hipMemcpyHostToDevice));
+  } else {
+    HIP_OR_THROW(hipMemcpy(ctx->w_in, w->action_in.w, size_t(kD) * kA * 2, hipMemcpyHostToDevice));
+  }
   ctx->w_out = ctx->dalloc<uint16_t>(size_t(kA) * kD);
   HIP_OR_THROW(hipMemcpy(ctx->w_out, w->action_out.w, size_t(kA) * kD * 2, hipMemcpyHostToDevice));
   {
@@ -372,6 +468,7 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->c_out = upload(t_cout);
   ctx->c_qkv = upload(permute(t_cqkv, kNqkv, pq));
   ctx->c_gu = upload(permute(t_cgu, kNgu, pg));
+  if (cfg.variant == 1) ctx->enc_bias = upload(ctx->tab[9]);
   // RoPE inverse frequencies base^(-2i/256) in fp64; the pack kernel turns
   // them into the cos/sin rows of the call's suffix positions
   {
@@ -503,6 +600,24 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       io.s1_next = k < S ? ctx->attn_s1 + size_t(k) * L * kD : nullptr;
       io.u_out = ctx->u;
       io.ssq_out = ctx->ssq;
+      if (cfg.variant == 1) {  // pi0: the action-time encoder, then its output layer
+        io.enc = 1;
+        io.h_init = ctx->b_to;
+        io.u_out = ctx->o;
+        io.b_in = k < S ? ctx->enc_bias + size_t(k) * kD : ctx->b_to;
+        hipError_t e = launch_io(io, s, t);
+        if (e != hipSuccess || k >= S) return e;
+        GemmParams g{};
+        g.M = M;
+        g.w = ctx->w_to;
+        g.a_frag = ctx->o;
+        g.gate = ctx->ones;
+        g.h_out = ctx->h;
+        g.s1_next = ctx->attn_s1 + size_t(k) * L * kD;
+        g.u_out = ctx->u;
+        g.ssq_out = ctx->ssq;
+        return launch_enc(g, s);
+      }
       return launch_io(io, s, t);
     }
     case 1:

@@ -35,7 +35,7 @@ class Config(ctypes.Structure):
                 ("action_dim", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("num_steps", ctypes.c_int32),
                 ("t0", ctypes.c_float), ("dt", ctypes.c_float), ("max_batch", ctypes.c_int32),
                 ("max_prefix_len", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("final_norm", ctypes.c_int32)]
+                ("final_norm", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class Linear(ctypes.Structure):
@@ -43,12 +43,14 @@ class Linear(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, Linear) for n in ("attn_mod", "q", "k", "v", "o", "ffn_mod", "gate", "up", "down")]
+    _fields_ = [(n, Linear) for n in ("attn_mod", "q", "k", "v", "o", "ffn_mod", "gate", "up", "down")] + \
+               [("attn_norm", ctypes.c_void_p), ("ffn_norm", ctypes.c_void_p)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [("action_in", Linear), ("time_in", Linear), ("time_out", Linear), ("final_mod", Linear),
-                ("action_out", Linear), ("layers", ctypes.POINTER(LayerWeights))]
+                ("action_out", Linear), ("layers", ctypes.POINTER(LayerWeights)),
+                ("action_time_in", Linear), ("action_time_out", Linear), ("final_norm", ctypes.c_void_p)]
 
 
 class PrefixKV(ctypes.Structure):
@@ -105,7 +107,7 @@ def make_config(cfg, max_batch: int, max_prefix_len: int) -> Config:
     """pi_ae_config from an :class:`inputs.ExpertConfig`-like object."""
     return Config(cfg.num_layers, cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                   cfg.action_dim, cfg.chunk_len, cfg.num_steps, cfg.t0, cfg.dt, max_batch, max_prefix_len,
-                  cfg.rope_base, cfg.rms_eps, 1 if cfg.final_norm else 0)
+                  cfg.rope_base, cfg.rms_eps, 1 if cfg.final_norm else 0, int(getattr(cfg, "variant", 0)))
 
 
 def _ptr(a):
@@ -145,9 +147,11 @@ class _MarshalledWeights:
             p = f"layers.{l}."
             self.layers[l] = LayerWeights(lin(p + "attn_mod"), lin(p + "q", False), lin(p + "k", False),
                                           lin(p + "v", False), lin(p + "o", False), lin(p + "ffn_mod"),
-                                          lin(p + "gate", False), lin(p + "up", False), lin(p + "down", False))
+                                          lin(p + "gate", False), lin(p + "up", False), lin(p + "down", False),
+                                          _ptr(self.keep.get(p + "attn_norm.w")), _ptr(self.keep.get(p + "ffn_norm.w")))
         self.w = Weights(lin("action_in"), lin("time_in"), lin("time_out"), lin("final_mod"), lin("action_out"),
-                         ctypes.cast(self.layers, ctypes.POINTER(LayerWeights)))
+                         ctypes.cast(self.layers, ctypes.POINTER(LayerWeights)),
+                         lin("action_time_in"), lin("action_time_out"), _ptr(self.keep.get("final_norm.w")))
 
 
 def host_table(cfg, weights: dict, which: int, n: int, max_batch: int = 1, max_prefix_len: int = 0) -> np.ndarray:

@@ -57,6 +57,14 @@ typedef enum pi_ae_status {
  * batch <= max_batch and prefix_len <= max_prefix_len.  rope_base is the RoPE
  * base (10000), rms_eps the RMS-norm epsilon (1e-6).  final_norm = 1 adds an
  * AdaRMS norm with its own modulation dense before action_out_proj.
+ * variant selects the expert:
+ *   0 = pi0.5 (Realtime-VLA blog, "pi0.5 inference flow"): AdaRMS norms
+ *       conditioned on the time MLP, gated residuals;
+ *   1 = pi0 ("Running VLAs at Real-time Speed" notes, section How; blog
+ *       section 3.2): RMS norms with a learnable scale gamma, plain residuals,
+ *       and as step input the action-time encoder
+ *       h = W_to SiLU(W_ti [action_in_proj(x) | emb(t)] + b_ti) + b_to;
+ *       final_norm = 1 adds an RMS norm with scale gamma before action_out_proj.
  */
 typedef struct pi_ae_config {
   int32_t num_layers;
@@ -75,6 +83,7 @@ typedef struct pi_ae_config {
   float rope_base;
   float rms_eps;
   int32_t final_norm;
+  int32_t variant;
 } pi_ae_config;
 
 /* One nn.Linear: weight [out][in] row-major, bias [out] (NULL where the layer
@@ -90,15 +99,26 @@ typedef struct pi_ae_linear {
  * gate and up [mlp_dim][width], down [width][mlp_dim]; these have no bias. */
 typedef struct pi_ae_layer_weights {
   pi_ae_linear attn_mod, q, k, v, o, ffn_mod, gate, up, down;
+  /* variant 1 only: the two RMS norms' scales gamma [width] (bf16); attn_mod
+   * and ffn_mod are then not read. */
+  const uint16_t* attn_norm;
+  const uint16_t* ffn_norm;
 } pi_ae_layer_weights;
 
 /* The unfolded expert.  action_in [width][action_dim] + b; time_in and
  * time_out [width][width] + b (the time MLP: cond = SiLU(time_out(SiLU(
  * time_in(emb(t)))))); final_mod [3*width][width] + b (read only when
- * final_norm = 1); action_out [action_dim][width] + b; layers[num_layers]. */
+ * final_norm = 1); action_out [action_dim][width] + b; layers[num_layers].
+ * Variant 1 reads action_in, action_out and the layers' q..down as above and,
+ * instead of time_in / time_out / final_mod / the modulation denses:
+ * action_time_in [width][2*width] + b (input: [action_in_proj(x) | emb(t)]),
+ * action_time_out [width][width] + b, final_norm (gamma [width], read when
+ * final_norm = 1) and the layers' attn_norm / ffn_norm. */
 typedef struct pi_ae_weights {
   pi_ae_linear action_in, time_in, time_out, final_mod, action_out;
   const pi_ae_layer_weights* layers;
+  pi_ae_linear action_time_in, action_time_out;
+  const uint16_t* final_norm;
 } pi_ae_weights;
 
 /* The VLM prefix cache for one call (device memory, read only).
@@ -176,7 +196,9 @@ const char* pi_ae_last_error(void);
  * 4 = final (1+scale) [S][width], 5 = c_out [S][action_dim] (shift @ W_out^T +
  * b_out), 6 = c_qkv [S][L][(heads+2)*head_dim] (natural q|k|v column order),
  * 7 = c_gu [S][L][2*mlp_dim] (natural gate|up order), 8 = timesteps [S],
- * 9 = cond [S][width].  n_floats must equal the table's size.  Synchronous. */
+ * 9 = cond [S][width] (variant 1: the action-time encoder's per-step bias
+ * before its SiLU, W_ti[:, :width] b_in + W_ti[:, width:] emb(t_k) + b_ti; its
+ * norm scales fill tables 0/2/4 as (1 + scale) = gamma, gates 1, shifts 0).  n_floats must equal the table's size.  Synchronous. */
 pi_ae_status pi_ae_debug_table(pi_ae_ctx* ctx, int32_t which, float* host_out, size_t n_floats);
 
 /* The same tables computed by the host half of pi_ae_prepare_weights alone
@@ -188,7 +210,8 @@ pi_ae_status pi_ae_debug_host_table(const pi_ae_config* cfg, const pi_ae_weights
 /* Run the loop only up to a point and copy an intermediate to host memory.
  * Runs steps 0..step-1 fully, then in step `step` the layers before `layer`
  * and, in layer `layer`, the phases up to and including `phase`
- * (0 = step input / action_in, 1 = QKV+RoPE, 2 = attention, 3 = O + gated
+ * (0 = step input: action_in, or for variant 1 the whole action-time encoder,
+ * 1 = QKV+RoPE, 2 = attention, 3 = O + gated
  * residual, 4 = gate/up, 5 = down + gated residual).  which: 0 = h fp32
  * [M][width], 1 = Q bf16 [M][heads][head_dim], 2 = K_s bf16 [M][head_dim],
  * 3 = V_s bf16 [M][head_dim], 4 = O bf16 [M][heads*head_dim], 5 = m bf16

@@ -131,3 +131,52 @@ def test_host_tables_match_oracle():
     cfg2 = cfg.replace(final_norm=False)
     close(pi_ae.host_table(cfg2, wb, 5, S * 32).astype(np.float64),
           np.tile(O.bf16_to_float(wb["action_out.b"]), S))
+
+
+@needs_lib
+def test_host_tables_match_oracle_pi0():
+    """pi0 variant: the library's fp64 preparation equals the oracle's folded
+    tables (norm scales as (1 + scale), unit gates, zero shift biases, the
+    action-time encoder's per-step bias before its SiLU)."""
+    cfg = inputs.WORKLOADS["c1pi0"].cfg.replace(num_steps=3, dt=-1.0 / 3)
+    wb = inputs.make_weights(cfg, seed=4, std=0.05, cache=False)
+    W = O.Weights(wb, cfg)
+    tabs = O.folded_tables(W)
+    S, L, D = cfg.num_steps, cfg.num_layers, cfg.width
+
+    def close(which, n, want, rtol=2e-6):
+        got = pi_ae.host_table(cfg, wb, which, n).astype(np.float64)
+        want = np.asarray(want, np.float64).ravel()
+        err = np.max(np.abs(got - want))
+        assert err <= rtol * max(1.0, np.max(np.abs(want))), (which, err)
+
+    close(8, S, tabs["t"])
+    close(9, S * D, np.concatenate(tabs["cond"]))
+    close(0, S * L * D, [tabs["attn"][k][l]["scale1"] for k in range(S) for l in range(L)])
+    close(1, S * L * D, [tabs["attn"][k][l]["gate"] for k in range(S) for l in range(L)])
+    close(2, S * L * D, [tabs["ffn"][k][l]["scale1"] for k in range(S) for l in range(L)])
+    close(3, S * L * D, [tabs["ffn"][k][l]["gate"] for k in range(S) for l in range(L)])
+    close(4, S * D, [tabs["final"][k]["scale1"] for k in range(S)])
+    close(5, S * 32, [tabs["final"][k]["c_out"] for k in range(S)])
+    close(6, S * L * 2560, np.zeros(S * L * 2560))
+    close(7, S * L * 8192, np.zeros(S * L * 8192))
+
+
+@needs_lib
+def test_pi0_weight_validation():
+    cfg = inputs.WORKLOADS["c1pi0"].cfg
+    w = _tiny_weights(cfg)
+    del w["layers.1.ffn_norm.w"]
+    with pytest.raises(pi_ae.PiAeError) as e:
+        pi_ae.host_table(cfg, w, 8, cfg.num_steps)
+    assert e.value.status == pi_ae.PI_AE_EINVAL and "layer 1" in str(e.value)
+    w = _tiny_weights(cfg)
+    del w["action_time_in.b"]
+    with pytest.raises(pi_ae.PiAeError):
+        pi_ae.host_table(cfg, w, 8, cfg.num_steps)
+    c = pi_ae.make_config(cfg, 1, 16)
+    c.variant = 2
+    mw = pi_ae._MarshalledWeights(cfg, _tiny_weights(cfg))
+    h = ctypes.c_void_p()
+    assert pi_ae.load_library().pi_ae_prepare_weights(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == \
+        pi_ae.PI_AE_EINVAL

@@ -182,7 +182,7 @@ def test_c1_end_to_end(c1_setup):
 
 
 # ------------------------------------------------------------------ full configs
-@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c2pi0"])
 def test_batch1_configs(name):
     w = inputs.WORKLOADS[name]
     wb, k, v, mask, noise = inputs.make_workload_inputs(w)
@@ -340,3 +340,40 @@ def test_in_place_zero_batch_and_errors(small_ctx):
     with pytest.raises(pi_ae.PiAeError) as e:
         ctx.sample(run.dk, run.dv, None, run.dnoise, mis, B, P)
     assert "aligned" in str(e.value)
+
+
+# ------------------------------------------------------------------ pi0 variant
+def test_pi0_step_input_and_end_to_end():
+    """pi0 (action-time encoder, RMS norm scales): the step input h of step 0
+    (the encoder's folded input layer, SiLU, output layer) against the
+    oracle's unfolded encoder, then the whole reduced loop."""
+    w = inputs.WORKLOADS["c1pi0"]
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    ctx = pi_ae.Context(w.cfg, wb, w.batch, w.prefix_len)
+    run = Run(k, v, mask, noise)
+    h0 = ctx.probe(run.dk, run.dv, run.dmask, run.dnoise, 1, run.P, 0, 0, 0, 0)
+    W = O.Weights(wb, w.cfg)
+    t = O.timesteps(w.cfg.num_steps, w.cfg.t0, w.cfg.dt)[0]
+    ref = O.encoder_pi0(W, noise[0].astype(np.float64), t)
+    e = rel_l2(h0, ref)
+    log(f"[c1pi0] step input h: rel_l2={e:.3e}")
+    assert e < 2e-2
+    check_actions(run.sample(ctx), O.sample(wb, w.cfg, k, v, mask, noise), noise, "c1pi0")
+    ctx.close()
+
+
+def test_pi0_many_rows_tiled_path():
+    """pi0 with enough rows (3 episodes x 63 = 189) for the tiled GEMMs and the
+    tiled encoder output layer; ragged masks; every episode against the oracle."""
+    cfg = inputs.WORKLOADS["c1pi0"].cfg
+    B, P = 3, 100
+    wb = inputs.make_weights(cfg)
+    k, v = inputs.make_prefix_kv(cfg, B, P, seed=7)
+    mask = inputs.make_pad_mask(B, P, [100, 57, 3])
+    noise = inputs.make_noise(cfg, B, seed=8)
+    ctx = pi_ae.Context(cfg, wb, B, P)
+    x = Run(k, v, mask, noise).sample(ctx)
+    ref = O.sample(wb, cfg, k, v, mask, noise)
+    for b in range(B):
+        check_actions(x[b], ref[b], noise[b], f"pi0-tiled[{b}]")
+    ctx.close()
