@@ -25,6 +25,12 @@ Draw recipe (stated here so that any reader can regenerate it):
     [batch][prefix_len][head_dim], N(0, 1) rounded to bf16.
   * noise: seed 2, [batch][chunk][action_dim] N(0, 1) in fp32 (not rounded).
   * pad mask: the first ``n_valid`` prefix positions are valid (1), the rest 0.
+  * the VLM prefix prefill (Realtime-VLA blog, "pi0.5 inference flow", Encoder
+    phase; section 4 encoder kernel list: width 2048, fused QKV 2560, MLP
+    16384, 18 layers): weights seed 3, per layer attn_norm, q, k, v, o,
+    ffn_norm, gate, up, down as above (norm scales 1 + N(0, 0.02)); the prefix
+    sequence (image and prompt embeddings after their sqrt(2048) scaling)
+    seed 4, [batch][prefix_len][2048] N(0, 1) rounded to bf16.
 """
 from __future__ import annotations
 
@@ -39,6 +45,8 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "make_weights", "make_prefix_kv", "make_pad_mask", "make_noise",
     "weight_shapes",
+    "PrefillConfig", "PrefillWorkload", "PREFILL_WORKLOADS", "prefill_weight_shapes",
+    "make_prefill_weights", "make_prefix_embeddings",
 ]
 
 
@@ -224,3 +232,76 @@ def make_workload_inputs(w: Workload, weight_seed: int = 0, kv_seed: int = 1, no
     mask = make_pad_mask(w.batch, w.prefix_len, w.n_valid)
     noise = make_noise(w.cfg, w.batch, noise_seed)
     return weights, k, v, mask, noise
+
+
+# ---------------------------------------------------------------- VLM prefix prefill
+@dataclass(frozen=True)
+class PrefillConfig:
+    """Shape of the Gemma-2B-shaped VLM whose layers fill the prefix KV cache."""
+    num_layers: int = 18
+    width: int = 2048
+    mlp_dim: int = 16384
+    num_heads: int = 8
+    num_kv_heads: int = 1
+    head_dim: int = 256
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+
+    def replace(self, **kw) -> "PrefillConfig":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    cfg: PrefillConfig
+    batch: int
+    prefix_len: int
+    n_valid: int
+    description: str = ""
+
+
+_VLM = PrefillConfig()
+
+PREFILL_WORKLOADS = {
+    "p1": PrefillWorkload("p1", _VLM, 1, 256, 256, "VLM prefill, 18 layers, 1 view (256 tokens), empty prompt"),
+    "p2": PrefillWorkload("p2", _VLM, 1, 512, 512, "VLM prefill, 18 layers, 2 views (512 tokens), empty prompt"),
+    "p3": PrefillWorkload("p3", _VLM, 1, 816, 800,
+                          "VLM prefill, 18 layers, 3 views + 48 prompt tokens, last 16 padded"),
+}
+
+
+def prefill_weight_shapes(cfg: PrefillConfig):
+    """(name, shape) in draw order; nn.Linear layout [out][in]."""
+    D, F, H, d = cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.head_dim
+    kv = cfg.num_kv_heads * d
+    out = []
+    for l in range(cfg.num_layers):
+        p = f"layers.{l}."
+        out += [
+            (p + "attn_norm.w", (D,)),
+            (p + "q.w", (H * d, D)), (p + "k.w", (kv, D)), (p + "v.w", (kv, D)),
+            (p + "o.w", (D, H * d)),
+            (p + "ffn_norm.w", (D,)),
+            (p + "gate.w", (F, D)), (p + "up.w", (F, D)), (p + "down.w", (D, F)),
+        ]
+    return out
+
+
+def make_prefill_weights(cfg: PrefillConfig, seed: int = 3, std: float = 0.02) -> dict:
+    """VLM weights as bf16 bit patterns keyed ``layers.{l}.<name>`` (a fresh dict)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in prefill_weight_shapes(cfg):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        x *= np.float32(std)
+        if name.endswith("norm.w"):
+            x += np.float32(1.0)
+        out[name] = f32_to_bf16_bits(x)
+    return out
+
+
+def make_prefix_embeddings(cfg: PrefillConfig, batch: int, prefix_len: int, seed: int = 4) -> np.ndarray:
+    """The prefix sequence, bf16 bits [batch][prefix_len][width] ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits(rng.standard_normal((batch, prefix_len, cfg.width), dtype=np.float32))

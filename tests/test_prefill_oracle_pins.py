@@ -1,0 +1,202 @@
+"""Pins of the VLM prefill oracle to facts that do not come from it.
+
+The prefill oracle (oracle/prefill_oracle.py) is checked against: the shapes
+the pages give for the encoder layers, brute force written with explicit loops
+on a tiny model, the already-pinned pi0 expert layer (which is the same layer
+when the expert has no prefix), and the invariants the method fixes (pad
+tokens cannot reach valid tokens, episodes are independent, the last layer's
+K/V do not depend on its attention and MLP).
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+from flow_matching_action_amd import inputs
+from oracle import pi_ae_oracle as O
+from oracle import prefill_oracle as PO
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")
+
+TINY = inputs.PrefillConfig(num_layers=3, width=32, mlp_dim=48, num_heads=2, head_dim=8)
+
+
+def tiny_inputs(batch=2, P=7, n_valid=(7, 5), seed=5):
+    w = inputs.make_prefill_weights(TINY, seed=seed, std=0.25)
+    e = inputs.make_prefix_embeddings(TINY, batch, P, seed=seed + 1)
+    m = inputs.make_pad_mask(batch, P, list(n_valid)[:batch])
+    return w, e, m
+
+
+def test_vlm_shapes_match_pages():
+    with open(GOLDEN) as f:
+        g = json.load(f)["vlm_shapes"]
+    cfg = inputs.PrefillConfig()
+    shapes = dict(inputs.prefill_weight_shapes(cfg))
+    q, k, v = shapes["layers.0.q.w"], shapes["layers.0.k.w"], shapes["layers.0.v.w"]
+    assert [q[1], q[0] + k[0] + v[0]] == g["qkv"]
+    assert list(shapes["layers.0.o.w"][::-1]) == g["o_proj"]
+    assert list(shapes["layers.0.gate.w"][::-1]) == g["gated_up"]
+    assert list(shapes["layers.0.up.w"][::-1]) == g["gated_up"]
+    assert list(shapes["layers.0.down.w"][::-1]) == g["down_proj"]
+    assert cfg.num_layers == g["layers"]
+    assert sum(1 for n in shapes if n.endswith(".q.w")) == g["layers"]
+    # the expert's heads read these keys: one KV head of the expert's head dim
+    assert cfg.num_kv_heads == 1 and cfg.head_dim == inputs.ExpertConfig().head_dim
+
+
+def _brute_prefill(wb, cfg, emb_bits, mask):
+    """The prefill with scalar loops only (no vectorised helper of the oracle)."""
+    f = lambda a: O.bf16_to_float(a).tolist()
+    D, H, d, F, eps = cfg.width, cfg.num_heads, cfg.head_dim, cfg.mlp_dim, cfg.rms_eps
+    L = cfg.num_layers
+    B, P = mask.shape
+    K = np.zeros((L, B, P, d))
+    V = np.zeros((L, B, P, d))
+    for b in range(B):
+        h = [list(r) for r in f(emb_bits[b])]
+        valid = [j for j in range(P) if mask[b][j]]
+        for l in range(L):
+            g = lambda n: f(wb[f"layers.{l}.{n}"])
+            ga, Wq, Wk, Wv, Wo = g("attn_norm.w"), g("q.w"), g("k.w"), g("v.w"), g("o.w")
+            u = []
+            for i in range(P):
+                r = math.sqrt(sum(x * x for x in h[i]) / D + eps)
+                u.append([h[i][c] / r * ga[c] for c in range(D)])
+            q = [[sum(u[i][c] * Wq[o][c] for c in range(D)) for o in range(H * d)] for i in range(P)]
+            k = [[sum(u[i][c] * Wk[o][c] for c in range(D)) for o in range(d)] for i in range(P)]
+            v = [[sum(u[i][c] * Wv[o][c] for c in range(D)) for o in range(d)] for i in range(P)]
+
+            def rot(x, pos):  # pairs (e, e + d/2), angle pos * base^(-2e/d)
+                y = list(x)
+                for e in range(d // 2):
+                    a = pos * cfg.rope_base ** (-2.0 * e / d)
+                    y[e] = x[e] * math.cos(a) - x[e + d // 2] * math.sin(a)
+                    y[e + d // 2] = x[e + d // 2] * math.cos(a) + x[e] * math.sin(a)
+                return y
+
+            k = [rot(k[i], i) for i in range(P)]
+            for hd in range(H):
+                for i in range(P):
+                    q[i][hd * d:(hd + 1) * d] = rot(q[i][hd * d:(hd + 1) * d], i)
+            K[l, b] = k
+            V[l, b] = v
+            if l == L - 1:
+                break
+            o = [[0.0] * (H * d) for _ in range(P)]
+            for i in range(P):
+                for hd in range(H):
+                    s = {j: sum(q[i][hd * d + e] * k[j][e] for e in range(d)) / math.sqrt(d) for j in valid}
+                    mx = max(s.values())
+                    z = sum(math.exp(s[j] - mx) for j in valid)
+                    for e in range(d):
+                        o[i][hd * d + e] = sum(math.exp(s[j] - mx) / z * v[j][e] for j in valid)
+            for i in range(P):
+                for c in range(D):
+                    h[i][c] += sum(o[i][x] * Wo[c][x] for x in range(H * d))
+            gf, Wg, Wu, Wd = g("ffn_norm.w"), g("gate.w"), g("up.w"), g("down.w")
+            for i in range(P):
+                r = math.sqrt(sum(x * x for x in h[i]) / D + eps)
+                u2 = [h[i][c] / r * gf[c] for c in range(D)]
+                m = []
+                for n in range(F):
+                    gt = sum(u2[c] * Wg[n][c] for c in range(D))
+                    up = sum(u2[c] * Wu[n][c] for c in range(D))
+                    m.append(0.5 * gt * (1 + math.tanh(math.sqrt(2 / math.pi) * (gt + 0.044715 * gt ** 3))) * up)
+                for c in range(D):
+                    h[i][c] += sum(m[n] * Wd[c][n] for n in range(F))
+    return K, V
+
+
+def test_prefill_matches_brute_force():
+    cfg = TINY.replace(width=8, mlp_dim=6, head_dim=4)
+    w = inputs.make_prefill_weights(cfg, seed=11, std=0.3)
+    e = inputs.make_prefix_embeddings(cfg, 2, 4, seed=12)
+    m = inputs.make_pad_mask(2, 4, [4, 3])
+    K, V = PO.prefill(w, cfg, e, m)
+    Kb, Vb = _brute_prefill(w, cfg, e, m)
+    np.testing.assert_allclose(K, Kb, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(V, Vb, rtol=1e-11, atol=1e-12)
+
+
+def test_prefill_layer_is_the_pinned_pi0_layer_without_prefix():
+    """With every token valid, a VLM layer is the pi0 expert layer (pinned to the
+    AdaRMS layer) whose suffix is the whole prefix and whose prefix is empty."""
+    w, e, _ = tiny_inputs(batch=1, P=6, n_valid=(6,))
+    W = O.Weights(w, TINY)
+    h = O.bf16_to_float(e[0])
+    d = TINY.head_dim
+    for l in range(TINY.num_layers - 1):
+        h_vlm, _, _ = PO.prefill_layer(lambda n: W.layer(l, n), l, h, np.ones(6, bool), np.arange(6), TINY)
+        h_exp = O.expert_layer_pi0(W, l, h, np.zeros((0, d)), np.zeros((0, d)), np.zeros(0, bool), np.arange(6))
+        np.testing.assert_allclose(h_vlm, h_exp, rtol=1e-12, atol=1e-12)
+        h = h_vlm
+
+
+def test_pad_tokens_do_not_reach_valid_tokens():
+    """Valid tokens' K/V equal those of the sequence with the pad tokens removed,
+    whatever the pad tokens hold."""
+    w, e, m = tiny_inputs()
+    K, V = PO.prefill(w, TINY, e, m)
+    e2 = e.copy()
+    e2[1, 5:] = inputs.f32_to_bf16_bits(np.full((2, TINY.width), 300.0, np.float32))
+    K2, V2 = PO.prefill(w, TINY, e2, m)
+    np.testing.assert_array_equal(K2[:, 1, :5], K[:, 1, :5])
+    np.testing.assert_array_equal(V2[:, 1, :5], V[:, 1, :5])
+    Kc, Vc = PO.prefill(w, TINY, e[1:2, :5], None)
+    np.testing.assert_allclose(K[:, 1, :5], Kc[:, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(V[:, 1, :5], Vc[:, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_episodes_are_independent():
+    w, e, m = tiny_inputs()
+    K, V = PO.prefill(w, TINY, e, m)
+    for b in range(2):
+        Kb, Vb = PO.prefill(w, TINY, e[b:b + 1], m[b:b + 1])
+        np.testing.assert_allclose(K[:, b], Kb[:, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(V[:, b], Vb[:, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_last_layer_kv_do_not_depend_on_its_attention_and_mlp():
+    w, e, m = tiny_inputs()
+    K, V = PO.prefill(w, TINY, e, m)
+    Kf, Vf = PO.prefill(w, TINY, e, m, full_last_layer=True)
+    np.testing.assert_array_equal(K, Kf)
+    np.testing.assert_array_equal(V, Vf)
+    # and the last layer's own attention / MLP weights are never read
+    w2 = dict(w)
+    last = TINY.num_layers - 1
+    for n in ("o.w", "ffn_norm.w", "gate.w", "up.w", "down.w", "q.w"):
+        w2[f"layers.{last}.{n}"] = np.full_like(w[f"layers.{last}.{n}"], 0x7FC0)  # NaN
+    K2, V2 = PO.prefill(w2, TINY, e, m)
+    np.testing.assert_array_equal(K2, K)
+    np.testing.assert_array_equal(V2, V)
+
+
+def test_first_layer_value_is_rms_normalised_projection_when_single_valid_token_rules():
+    """One valid token: every token's attention output is that token's value in
+    each head, so with W_o = 0 and W_down = 0 the second layer sees the input
+    unchanged (the residuals add exactly zero)."""
+    w, e, _ = tiny_inputs(batch=1, P=5, n_valid=(5,))
+    for n in ("o.w", "down.w"):
+        w[f"layers.0.{n}"] = np.zeros_like(w[f"layers.0.{n}"])
+    m = inputs.make_pad_mask(1, 5, [1])
+    K, V = PO.prefill(w, TINY, e, m)
+    # layer 1 on the unchanged input = layer 0 of a model whose first layer is layer 1
+    w1 = {k.replace("layers.1.", "layers.0."): v for k, v in w.items() if k.startswith("layers.1.")}
+    K1, V1 = PO.prefill(w1, TINY.replace(num_layers=1), e, m)
+    np.testing.assert_allclose(K[1], K1[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(V[1], V1[0], rtol=1e-12, atol=1e-12)
+
+
+def test_no_valid_token_gives_zero_attention():
+    w, e, _ = tiny_inputs(batch=1, P=4, n_valid=(4,))
+    m = np.zeros((1, 4), np.uint8)
+    K, V = PO.prefill(w, TINY, e, m)
+    assert np.all(np.isfinite(K)) and np.all(np.isfinite(V))
+    # with attention 0, layer 1 sees the input plus the MLP branch only
+    w0 = dict(w)
+    w0["layers.0.o.w"] = np.zeros_like(w["layers.0.o.w"])
+    K0, V0 = PO.prefill(w0, TINY, e, np.ones((1, 4), np.uint8))
+    np.testing.assert_allclose(K[1], K0[1], rtol=1e-12, atol=1e-12)
