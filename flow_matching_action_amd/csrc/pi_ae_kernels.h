@@ -17,6 +17,14 @@ constexpr int kNqkv = (kH + 2) * kHd; // fused QKV width, 2560
 constexpr int kNgu = 2 * kF;          // fused gate|up width, 8192
 constexpr int kRopeHalf = kHd / 2;    // 128 rotated pairs per head
 
+// The VLM whose layers fill the prefix KV cache (Realtime-VLA technical blog,
+// "pi0.5 inference flow", Encoder phase, and the section 4 encoder kernel
+// list: Gemma-2B-shaped, width 2048, fused QKV 2560, MLP 16384; the same 8
+// query heads x 256 and one KV head of 256 as the expert reads).
+constexpr int kVD = 2048;             // width
+constexpr int kVF = 16384;            // MLP dim
+constexpr int kVNgu = 2 * kVF;        // fused gate|up width, 32768
+
 // Per-call pointers, written by the args kernel into a device block that the
 // captured graph reads, so that one graph serves every call.
 struct DevArgs {
@@ -101,6 +109,10 @@ struct GemmParams {
   // query row's (max, sum) of both; the A operand is their weighted mean
   const uint16_t* a_frag2;
   const float* astat;
+  // QKV of the VLM prefill: this layer's K (rotated) and V in natural layout
+  // [M][256], the cache the expert reads (null: not written)
+  uint16_t* k_cache;
+  uint16_t* v_cache;
 };
 
 struct AttnParams {
@@ -135,6 +147,23 @@ struct PackParams {
   int B, P, T, nkb;
 };
 
+// Staging of one VLM prefill call (one workgroup per prefix row): the residual
+// stream h = the prefix sequence, the first layer's operand bf16(h * gamma)
+// with its h^2 partials, each row's RoPE (cos, sin) at position t (its index
+// in the episode) and the additive key bias of the episode's keys.
+struct VlmStageParams {
+  const uint16_t* emb;    // [B][P][2048] bf16, the scaled prefix sequence
+  const uint8_t* mask;    // [B][P] or null (all valid)
+  const float* s1;        // the first layer's attention-norm scale [2048]
+  const double* inv_freq; // RoPE inverse frequencies [128]
+  float* h;               // [Mpad][2048]
+  uint16_t* u;            // fragment-major [Mpad/16][64][64][8]
+  float* ssq;             // [Mpad][128]
+  float2* rope_cs;        // [B*P][128]
+  float* kbias;           // [B][nkb*32]
+  int B, P, nkb;
+};
+
 struct ArgsParams {
   DevArgs* da;
   DevArgs vals;
@@ -159,6 +188,15 @@ hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t
 // h += acc * gate with K = 1024 (the pi0 encoder's output layer), the same
 // residual epilogue as O and down
 hipError_t launch_enc(const GemmParams& p, hipStream_t s);
+
+// VLM prefill (width 2048, MLP 16384; always the tiled GEMMs)
+hipError_t launch_vlm_stage(const VlmStageParams& p, hipStream_t s);
+// kv_only: the K/V columns only (the last layer)
+hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_o(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_down(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

@@ -301,11 +301,14 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
 //     order) and applied in the epilogue (it commutes with the GEMM).
 // Epilogues:
 //   E_QKV:  * 1/rms, + shift-fold bias, RoPE on (i, i+128) pairs; Q to
-//           [M][8][256], suffix K/V into the packed per-layer buffers.
+//           [M][8][256], suffix K/V into the packed per-layer buffers (and,
+//           for the VLM prefill, K/V in natural layout into its cache).
+//   E_KV:   E_QKV restricted to the K/V columns (the last VLM layer, whose
+//           queries nothing reads).
 //   E_GELU: * 1/rms, + shift-fold bias, m = GELU(gate) * up, fragment-major.
 //   E_RES:  h += acc * gate; when the next consumer is a normalised GEMM also
 //           its operand bf16(h * (1 + scale_next)) and the h^2 partials.
-enum { E_QKV = 0, E_GELU = 1, E_RES = 2 };
+enum { E_QKV = 0, E_GELU = 1, E_RES = 2, E_KV = 3 };
 constexpr int kSsqTiles = kD / 16;  // partial sums of squares per row
 
 template <int MB, int NB, int NW, int KBW, int EPI, bool AM = false>
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 // in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
 // inputs): each of the NT threads takes 8 consecutive columns of one row per
 // pass, so that every global access is 16 or 32 contiguous bytes.
-template <int BM, int BN, int CS, int NT, int EPI>
+template <int BM, int BN, int CS, int NT, int EPI, int D, int F>
 __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* ct, const float* srstd, int mb0,
                                               int nb0) {
   constexpr int FB = BN / 16;
@@ -579,7 +582,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
         const int row = mb0 * 16 + (pb + q) * (NT / CPR) + threadIdx.x / CPR;
-        const size_t hoff = size_t(row < p.M ? row : 0) * kD + col;
+        const size_t hoff = size_t(row < p.M ? row : 0) * D + col;
         h0[q] = *reinterpret_cast<const float4*>(p.h_out + hoff);
         h1[q] = *reinterpret_cast<const float4*>(p.h_out + hoff + 4);
       }
@@ -593,7 +596,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
                                       h0[q].w + x0.w * g0.w);
         const float4 n1 = make_float4(h1[q].x + x1.x * g1.x, h1[q].y + x1.y * g1.y, h1[q].z + x1.z * g1.z,
                                       h1[q].w + x1.w * g1.w);
-        const size_t hoff = size_t(live ? row : 0) * kD + col;
+        const size_t hoff = size_t(live ? row : 0) * D + col;
         if (live) {
           *reinterpret_cast<float4*>(p.h_out + hoff) = n0;
           *reinterpret_cast<float4*>(p.h_out + hoff + 4) = n1;
@@ -603,10 +606,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
                      (n1.z * n1.z + n1.w * n1.w);
           sq += __shfl_xor(sq, 1);  // the other half of this 16-column tile
           if (live) {
-            *reinterpret_cast<uint4*>(p.u_out + afrag_index(row, col, kD / 32)) = __builtin_bit_cast(
+            *reinterpret_cast<uint4*>(p.u_out + afrag_index(row, col, D / 32)) = __builtin_bit_cast(
                 uint4, pack8(make_float4(n0.x * s0.x, n0.y * s0.y, n0.z * s0.z, n0.w * s0.w),
                              make_float4(n1.x * s1.x, n1.y * s1.y, n1.z * s1.z, n1.w * s1.w)));
-            if ((c8 & 1) == 0) p.ssq_out[size_t(row) * kSsqTiles + col / 16] = sq;
+            if ((c8 & 1) == 0) p.ssq_out[size_t(row) * (D / 16) + col / 16] = sq;
           }
         }
       }
@@ -623,7 +626,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
     const int ip = (jp & 7) * 16 + 8 * hf;  // RoPE pair of Q / K_s columns
     for (int pb = 0; pb < NP; pb += PB) {
       float4 cs[PB][4];
-      if constexpr (EPI == E_QKV) {
+      if constexpr (EPI == E_QKV || EPI == E_KV) {
         if (jp < 72) {
 #pragma unroll
           for (int q = 0; q < PB; ++q) {
@@ -651,9 +654,9 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
           float mv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(y0[e]) * y1[e];
-          *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, kF / 32)) = __builtin_bit_cast(
+          *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, F / 32)) = __builtin_bit_cast(
               uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
-        } else {  // E_QKV
+        } else {  // E_QKV, E_KV
           const int b = row / p.T, t = row - b * p.T;
           if (jp < 72) {  // Q heads and K_s: rotate pairs (ip, ip+128), ip = (jp%8)*16 + 8hf + e
             float o0[8], o1[8];
@@ -673,15 +676,29 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
               *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
             } else {
               const int key = p.P + t;
-              *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
-              *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
+              if (p.kp) {
+                *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
+                *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
+              }
+              if (p.k_cache) {
+                *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + ip) = w0;
+                *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + kRopeHalf + ip) = w1;
+              }
             }
           } else {  // V_s: head-dim (jp-72)*32 + 8hf + e and +16, no rotation
             const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
+            if (p.vp) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
-              p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
+              for (int e = 0; e < 8; ++e) {
+                p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
+                p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
+              }
+            }
+            if (p.v_cache) {
+              *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0) = __builtin_bit_cast(
+                  uint4, pack8(make_float4(y0[0], y0[1], y0[2], y0[3]), make_float4(y0[4], y0[5], y0[6], y0[7])));
+              *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0 + 16) = __builtin_bit_cast(
+                  uint4, pack8(make_float4(y1[0], y1[1], y1[2], y1[3]), make_float4(y1[4], y1[5], y1[6], y1[7])));
             }
           }
         }
@@ -724,7 +741,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
     }                                                                                  \
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);                                \
   }
-template <int WM, int TR, int TC, int EPI>
+template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF>
 __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
   constexpr int NW = WM, KS = 2;
   constexpr int NP = 4;                          // stages of loads in flight (register slots)
@@ -740,8 +757,9 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
   u32x4 (*st)[FBS][64] = reinterpret_cast<u32x4 (*)[FBS][64]>(lds_raw);
   __shared__ float srstd[BM];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int KB = K >> 5, NS = KB / KS;  // NS is a multiple of NP: K is a multiple of 256 for every GEMM of the expert
-  const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * FA;
+  const int KB = K >> 5, NS = KB / KS;  // NS is a multiple of NP: K is a multiple of 256 for every GEMM here
+  // E_KV covers the K/V columns only: n-blocks from 2 * 64 on (Q is 64 pairs)
+  const int nb0 = blockIdx.x * FB + (EPI == E_KV ? 128 : 0), mb0 = blockIdx.y * FA;
   const int sub = frag32_sub(lane);
   // this lane's A rows: fragments mb0 + 2(w*TR + r) + sub
   const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 2 * w * TR + sub) * KB * 64;
@@ -771,14 +789,14 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
   for (int sl = 0; sl < NP - 1; ++sl) PI_AE_B32_LOAD(sl, sl)
   if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
     for (int r = threadIdx.x; r < BM; r += NW * 64) {
-      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * kSsqTiles);
+      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * (D / 16));
       float sum = 0.f;
 #pragma unroll
-      for (int v = 0; v < kSsqTiles / 4; ++v) {
+      for (int v = 0; v < D / 64; ++v) {
         const float4 x = sp[v];
         sum += (x.x + x.y) + (x.z + x.w);
       }
-      srstd[r] = 1.f / sqrtf(sum * (1.f / kD) + p.eps);
+      srstd[r] = 1.f / sqrtf(sum * (1.f / D) + p.eps);
     }
   }
   PI_AE_B32_STORE_B(0, 0)
@@ -834,7 +852,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
       for (int i = 0; i < 16; ++i)
         ct[((w * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
   __syncthreads();
-  tile_epilogue<BM, BN, CS, NW * 64, EPI>(p, ct, srstd, mb0, nb0);
+  tile_epilogue<BM, BN, CS, NW * 64, EPI, D, F>(p, ct, srstd, mb0, nb0);
 }
 #undef PI_AE_B32_SCHED
 
@@ -1150,7 +1168,7 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int NWQ>
+template <int NWQ, bool SPREAD>
 __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   constexpr int NW = NWQ * 2;
   constexpr int FPW = 64 / NW;  // fragments of a block pair copied per wave
@@ -1171,8 +1189,11 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const int hh = lane >> 5, l32 = lane & 31, sub = (lane >> 4) & 1;
   const int nq = p.T * kH;
   const int per_ep = (nq + 32 * NWQ - 1) / (32 * NWQ);
+  // XCD-aware: episode e's workgroups on XCD residue e mod 8; SPREAD (few
+  // episodes, long sequences: the VLM prefill) deals them over all residues
   const int xr = int(blockIdx.x) & 7, j = int(blockIdx.x) >> 3;
-  const int b = xr + 8 * (j / per_ep), qw = j % per_ep;
+  const int b = SPREAD ? int(blockIdx.x) / per_ep : xr + 8 * (j / per_ep);
+  const int qw = SPREAD ? int(blockIdx.x) % per_ep : j % per_ep;
   if (b >= p.B) return;  // padding of the XCD-aware grid (uniform per workgroup)
   const int r = (qw * NWQ + rg) * 32 + l32;
   const int rc = r < nq ? r : nq - 1;
@@ -1316,9 +1337,12 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   __syncthreads();
   if (kh == 0) {
     const float m1 = mg[128 * 64 + lane], l1 = mg[129 * 64 + lane];
-    const float m = fmaxf(m_run, m1);  // finite: every row has its own suffix keys
+    // m is -inf only when no key of the row is valid (a VLM episode without
+    // valid tokens); its output is then 0
+    const float m = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.f : exp2f(m_run - m), a1 = m1 == -INFINITY ? 0.f : exp2f(m1 - m);
-    const float inv = 1.f / (a0 * xor32_sum(l_part) + a1 * l1);
+    const float den = a0 * xor32_sum(l_part) + a1 * l1;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     const float f0 = a0 * inv, f1 = a1 * inv;
     // two batches of four d-tiles: all reads of a batch are issued before its
     // writes (which the compiler may not reorder across, both being LDS)
@@ -1429,11 +1453,78 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t
   if (!p.o2 && p.B * nqb >= kAttnRowsMinBlocks && p.pf.nwg == 0) {  // many episodes: K/V shared through LDS
     const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
     const int groups = (p.B + 7) / 8;  // 8 episodes (one per XCD residue) per group
-    return go(k_attn_rows32<kAttn32Groups>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
+    return go(k_attn_rows32<kAttn32Groups, false>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
   }
   if (p.o2) return go(k_attn<2>, dim3(2 * nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
   return go(k_attn<1>, dim3(nqb + p.pf.nwg, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
+// ---------------------------------------------------------------------------
+// VLM prefill.  The encoder layer is the expert's with width 2048 and MLP
+// 16384 (blog section 4 encoder kernel list: RMSNorm + QKV + RoPE, O +
+// residual, RMSNorm + gated up, down + residual), so the same tiled GEMMs and
+// fused epilogues run it with those sizes: every GEMM is 256..816 rows per
+// view count, the MFMA-bound regime.  The norms have a plain learnable scale:
+// gates are ones and the QKV / gate-up biases zeros.
+__global__ __launch_bounds__(256) void k_vlm_stage(VlmStageParams p) {
+  const int row = blockIdx.x, b = row / p.P, t = row - b * p.P;
+  const int c0 = threadIdx.x * 8;
+  const uint4 e = *reinterpret_cast<const uint4*>(p.emb + size_t(row) * kVD + c0);
+  const float x[8] = {bf2f(e.x & 0xffffu), bf2f(e.x >> 16), bf2f(e.y & 0xffffu), bf2f(e.y >> 16),
+                      bf2f(e.z & 0xffffu), bf2f(e.z >> 16), bf2f(e.w & 0xffffu), bf2f(e.w >> 16)};
+  float* hr = p.h + size_t(row) * kVD + c0;
+  reinterpret_cast<float4*>(hr)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(hr)[1] = make_float4(x[4], x[5], x[6], x[7]);
+  const float4 g0 = *reinterpret_cast<const float4*>(p.s1 + c0), g1 = *reinterpret_cast<const float4*>(p.s1 + c0 + 4);
+  *reinterpret_cast<uint4*>(p.u + afrag_index(row, c0, kVD / 32)) = __builtin_bit_cast(
+      uint4, pack8(make_float4(x[0] * g0.x, x[1] * g0.y, x[2] * g0.z, x[3] * g0.w),
+                   make_float4(x[4] * g1.x, x[5] * g1.y, x[6] * g1.z, x[7] * g1.w)));
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sq += x[i] * x[i];
+  sq += __shfl_xor(sq, 1);  // the two threads of a 16-column tile
+  if ((threadIdx.x & 1) == 0) p.ssq[size_t(row) * (kVD / 16) + (threadIdx.x >> 1)] = sq;
+  if (threadIdx.x < kRopeHalf) {
+    const double a = double(t) * p.inv_freq[threadIdx.x];
+    p.rope_cs[size_t(row) * kRopeHalf + threadIdx.x] = make_float2(float(cos(a)), float(sin(a)));
+  }
+  if (threadIdx.x == 0) {
+    float* kb = p.kbias + size_t(b) * p.nkb * 32;
+    kb[t] = (!p.mask || p.mask[size_t(b) * p.P + t] != 0) ? 0.f : -INFINITY;
+    for (int k = p.P + t; k < p.nkb * 32; k += p.P) kb[k] = -INFINITY;  // block padding
+  }
+}
+
+hipError_t launch_vlm_stage(const VlmStageParams& p, hipStream_t s) {
+  if (p.B <= 0 || p.P <= 0) return hipSuccess;
+  k_vlm_stage<<<p.B * p.P, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, hipStream_t s, const KernelTiming* t) {
+  if (kv_only)
+    return go(k_gemm_big32<4, 1, 2, E_KV, kVD, kVF>, dim3(2 * kHd / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
+  return go(k_gemm_big32<4, 1, 2, E_QKV, kVD, kVF>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
+}
+hipError_t launch_vlm_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  return go(k_gemm_big32<4, 1, 2, E_RES, kVD, kVF>, dim3(kVD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+}
+hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  return go(k_gemm_big32<4, 1, 4, E_GELU, kVD, kVF>, dim3(kVNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
+}
+hipError_t launch_vlm_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  return go(k_gemm_big32<4, 1, 2, E_RES, kVD, kVF>, dim3(kVD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVF);
+}
+// Every prefix token is a query of its own episode's keys: the rows kernel
+// with T = P query tokens, no suffix keys, and (few episodes) the episode's
+// workgroups dealt over all XCDs.
+hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
+  const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
+  if (p.B >= 8) {
+    const int groups = (p.B + 7) / 8;
+    return go(k_attn_rows32<kAttn32Groups, false>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
+  }
+  return go(k_attn_rows32<kAttn32Groups, true>, dim3(p.B * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
+}
+
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {
   if (p.B <= 0 || p.nkb <= 0) return hipSuccess;
   k_pack<<<dim3(p.nkb, p.B, L), 256, 0, s>>>(p);

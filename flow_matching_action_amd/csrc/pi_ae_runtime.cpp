@@ -237,13 +237,13 @@ std::vector<int> qkv_perm() {
 }
 
 // Fused gate|up: workgroup j owns gate rows 16j.. (n-block 2j) and the same
-// up rows (n-block 2j+1).  Natural fused index: gate f -> f, up f -> 4096 + f.
-std::vector<int> gu_perm() {
-  std::vector<int> p(kNgu);
-  for (int j = 0; j < kF / 16; ++j)
+// up rows (n-block 2j+1).  Natural fused index: gate f -> f, up f -> F + f.
+std::vector<int> gu_perm(int F = kF) {
+  std::vector<int> p(2 * F);
+  for (int j = 0; j < F / 16; ++j)
     for (int c = 0; c < 16; ++c) {
       p[(2 * j) * 16 + c] = 16 * j + c;
-      p[(2 * j + 1) * 16 + c] = kF + 16 * j + c;
+      p[(2 * j + 1) * 16 + c] = F + 16 * j + c;
     }
   return p;
 }
@@ -1002,5 +1002,377 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
   }
   hipFree(actions);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("probe failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
+// ====================================================================== VLM prefill
+struct pi_ae_vlm {
+  pi_ae_vlm_config cfg{};
+  int device = 0;
+  bool broken = false;
+  std::vector<void*> allocs;
+  // prepared weights (device, swizzled; the last layer has only QKV)
+  uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr;
+  float *attn_s1 = nullptr, *ffn_s1 = nullptr;  // norm scales gamma [L][2048]
+  float *zero_qkv = nullptr, *zero_gu = nullptr, *ones = nullptr;
+  double* inv_freq = nullptr;
+  // workspaces
+  float *h = nullptr, *ssq = nullptr, *kbias = nullptr;
+  uint16_t *u = nullptr, *q = nullptr, *o = nullptr, *m = nullptr, *kp = nullptr, *vp = nullptr;
+  float2* rope_cs = nullptr;
+  uint16_t *k_cache = nullptr, *v_cache = nullptr;  // [L][B][P][256] of the last call
+  int Mpad = 0, nkb_max = 0;
+  hipStream_t cap = nullptr;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+
+  template <class T>
+  T* dalloc(size_t n) {
+    void* p = nullptr;
+    if (n == 0) n = 1;
+    hipError_t e = hipMalloc(&p, n * sizeof(T));
+    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
+    allocs.push_back(p);
+    return static_cast<T*>(p);
+  }
+  void release() {
+    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    graphs.clear();
+    for (void* p : allocs) hipFree(p);
+    allocs.clear();
+    if (cap) hipStreamDestroy(cap);
+    cap = nullptr;
+  }
+};
+
+namespace {
+
+pi_ae_status vlm_check_config(const pi_ae_vlm_config* c) {
+  if (c->width != kVD || c->mlp_dim != kVF || c->num_heads != kH || c->num_kv_heads != 1 || c->head_dim != kHd)
+    return fail(PI_AE_EUNSUPPORTED, "the VLM kernels implement width 2048, mlp_dim 16384, 8 heads x 256, one KV head");
+  if (c->num_layers < 1 || c->num_layers > 64) return fail(PI_AE_EINVAL, "num_layers must be in [1, 64]");
+  if (c->max_batch < 1 || c->max_prefix_len < 1 || c->max_prefix_len > 4096)
+    return fail(PI_AE_EINVAL, "max_batch >= 1 and max_prefix_len in [1, 4096]");
+  if (!(c->rope_base > 0.f) || !(c->rms_eps > 0.f)) return fail(PI_AE_EINVAL, "rope_base and rms_eps must be > 0");
+  return PI_AE_OK;
+}
+
+pi_ae_status vlm_check_weights(const pi_ae_vlm_config* c, const pi_ae_vlm_layer_weights* w) {
+  if (!w) return fail(PI_AE_EINVAL, "layers is NULL");
+  for (int l = 0; l < c->num_layers; ++l) {
+    const pi_ae_vlm_layer_weights& L = w[l];
+    const bool last = l == c->num_layers - 1;
+    if (!L.attn_norm || !L.q || !L.k || !L.v ||
+        (!last && (!L.o || !L.ffn_norm || !L.gate || !L.up || !L.down)))
+      return fail(PI_AE_EINVAL, "layer " + std::to_string(l) + ": a weight pointer is NULL");
+  }
+  return PI_AE_OK;
+}
+
+void vlm_prepare(pi_ae_vlm* ctx, const pi_ae_vlm_layer_weights* w) {
+  const pi_ae_vlm_config& cfg = ctx->cfg;
+  const int L = cfg.num_layers;
+  const std::vector<int> pq = qkv_perm(), pg = gu_perm(kVF);
+  std::vector<int> pid(kVD);
+  for (int i = 0; i < kVD; ++i) pid[i] = i;
+  const size_t n_qkv = size_t(kNqkv) * kVD, n_o = size_t(kVD) * kH * kHd, n_gu = size_t(kVNgu) * kVD,
+               n_d = size_t(kVD) * kVF;
+  ctx->w_qkv = ctx->dalloc<uint16_t>(n_qkv * L);
+  if (L > 1) {
+    ctx->w_o = ctx->dalloc<uint16_t>(n_o * (L - 1));
+    ctx->w_gu = ctx->dalloc<uint16_t>(n_gu * (L - 1));
+    ctx->w_d = ctx->dalloc<uint16_t>(n_d * (L - 1));
+  }
+  {
+    std::vector<uint16_t> fused(n_gu), sw(n_gu);
+    for (int l = 0; l < L; ++l) {
+      const pi_ae_vlm_layer_weights& Lw = w[l];
+      std::memcpy(fused.data(), Lw.q, sizeof(uint16_t) * kH * kHd * kVD);
+      std::memcpy(fused.data() + size_t(kH) * kHd * kVD, Lw.k, sizeof(uint16_t) * kHd * kVD);
+      std::memcpy(fused.data() + size_t(kH + 1) * kHd * kVD, Lw.v, sizeof(uint16_t) * kHd * kVD);
+      swizzle(fused.data(), kVD, pq, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_qkv + n_qkv * l, sw.data(), n_qkv * 2, hipMemcpyHostToDevice));
+      if (l == L - 1) break;
+      swizzle(Lw.o, kH * kHd, pid, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_o + n_o * l, sw.data(), n_o * 2, hipMemcpyHostToDevice));
+      std::memcpy(fused.data(), Lw.gate, sizeof(uint16_t) * kVF * kVD);
+      std::memcpy(fused.data() + size_t(kVF) * kVD, Lw.up, sizeof(uint16_t) * kVF * kVD);
+      swizzle(fused.data(), kVD, pg, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_gu + n_gu * l, sw.data(), n_gu * 2, hipMemcpyHostToDevice));
+      swizzle(Lw.down, kVF, pid, sw.data());
+      HIP_OR_THROW(hipMemcpy(ctx->w_d + n_d * l, sw.data(), n_d * 2, hipMemcpyHostToDevice));
+    }
+  }
+  auto upload = [&](const std::vector<float>& v) {
+    float* d = ctx->dalloc<float>(v.size());
+    HIP_OR_THROW(hipMemcpy(d, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+    return d;
+  };
+  {
+    std::vector<float> as1(size_t(L) * kVD, 1.f), fs1(size_t(L) * kVD, 1.f);
+    for (int l = 0; l < L; ++l)
+      for (int i = 0; i < kVD; ++i) {
+        as1[size_t(l) * kVD + i] = float(bf(w[l].attn_norm[i]));
+        if (l < L - 1) fs1[size_t(l) * kVD + i] = float(bf(w[l].ffn_norm[i]));
+      }
+    ctx->attn_s1 = upload(as1);
+    ctx->ffn_s1 = upload(fs1);
+    ctx->zero_qkv = upload(std::vector<float>(kNqkv, 0.f));
+    ctx->zero_gu = upload(std::vector<float>(kVNgu, 0.f));
+    ctx->ones = upload(std::vector<float>(kVD, 1.f));
+    std::vector<double> inv(kRopeHalf);
+    for (int i = 0; i < kRopeHalf; ++i) inv[i] = std::pow(double(cfg.rope_base), -2.0 * i / kHd);
+    ctx->inv_freq = ctx->dalloc<double>(kRopeHalf);
+    HIP_OR_THROW(hipMemcpy(ctx->inv_freq, inv.data(), kRopeHalf * 8, hipMemcpyHostToDevice));
+  }
+  // workspaces (zeroed once: rows past a call's M are read by whole GEMM
+  // tiles but never written by it, and must hold finite values)
+  const size_t Mmax = size_t(cfg.max_batch) * cfg.max_prefix_len;
+  ctx->Mpad = int((Mmax + 127) / 128 * 128);
+  const size_t Mp = size_t(ctx->Mpad);
+  ctx->nkb_max = (cfg.max_prefix_len + 31) / 32;
+  const size_t npack = size_t(cfg.max_batch) * ctx->nkb_max * 8192;
+  ctx->h = ctx->dalloc<float>(Mp * kVD);
+  ctx->u = ctx->dalloc<uint16_t>(Mp * kVD);
+  ctx->ssq = ctx->dalloc<float>(Mp * (kVD / 16));
+  ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->m = ctx->dalloc<uint16_t>(Mp * kVF);
+  ctx->kp = ctx->dalloc<uint16_t>(npack);
+  ctx->vp = ctx->dalloc<uint16_t>(npack);
+  ctx->kbias = ctx->dalloc<float>(size_t(cfg.max_batch) * ctx->nkb_max * 32);
+  ctx->rope_cs = ctx->dalloc<float2>(Mp * kRopeHalf);
+  const size_t ncache = size_t(L) * Mmax * kHd;
+  ctx->k_cache = ctx->dalloc<uint16_t>(ncache);
+  ctx->v_cache = ctx->dalloc<uint16_t>(ncache);
+  HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kVD * 4));
+  HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kVD * 2));
+  HIP_OR_THROW(hipMemset(ctx->ssq, 0, Mp * (kVD / 16) * 4));
+  HIP_OR_THROW(hipMemset(ctx->q, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kVF * 2));
+  HIP_OR_THROW(hipMemset(ctx->kp, 0, npack * 2));
+  HIP_OR_THROW(hipMemset(ctx->vp, 0, npack * 2));
+  HIP_OR_THROW(hipStreamCreateWithFlags(&ctx->cap, hipStreamNonBlocking));
+  HIP_OR_THROW(hipDeviceSynchronize());
+}
+
+// Phases of layer l: 1 = QKV (K/V only in the last layer), 2 = attention,
+// 3 = O + residual, 4 = gate/up, 5 = down + residual.
+hipError_t vlm_launch_phase(pi_ae_vlm* ctx, int B, int P, hipStream_t s, int l, int ph, const KernelTiming* t) {
+  const int L = ctx->cfg.num_layers, M = B * P, nkb = (P + 31) / 32;
+  const bool last = l == L - 1;
+  const size_t n_qkv = size_t(kNqkv) * kVD, n_o = size_t(kVD) * kH * kHd, n_gu = size_t(kVNgu) * kVD,
+               n_d = size_t(kVD) * kVF;
+  GemmParams g{};
+  g.M = M;
+  g.eps = ctx->cfg.rms_eps;
+  switch (ph) {
+    case 1:
+      g.w = ctx->w_qkv + n_qkv * l;
+      g.a_frag = ctx->u;
+      g.ssq = ctx->ssq;
+      g.bias = ctx->zero_qkv;
+      g.q_out = ctx->q;
+      g.rope_cs = ctx->rope_cs;
+      g.T = P;
+      g.P = 0;
+      g.nkb = nkb;
+      g.kp = last ? nullptr : ctx->kp;
+      g.vp = last ? nullptr : ctx->vp;
+      g.k_cache = ctx->k_cache + size_t(l) * M * kHd;
+      g.v_cache = ctx->v_cache + size_t(l) * M * kHd;
+      return launch_vlm_qkv(g, last, s, t);
+    case 2: {
+      AttnParams a{};
+      a.q = ctx->q;
+      a.kp = ctx->kp;
+      a.vp = ctx->vp;
+      a.kbias = ctx->kbias;
+      a.o = ctx->o;
+      a.B = B;
+      a.T = P;
+      a.P = 0;
+      a.nkb = nkb;
+      return launch_vlm_attn(a, s, t);
+    }
+    case 3:
+      g.w = ctx->w_o + n_o * l;
+      g.a_frag = ctx->o;
+      g.gate = ctx->ones;
+      g.h_out = ctx->h;
+      g.s1_next = ctx->ffn_s1 + size_t(l) * kVD;
+      g.u_out = ctx->u;
+      g.ssq_out = ctx->ssq;
+      return launch_vlm_o(g, s, t);
+    case 4:
+      g.w = ctx->w_gu + n_gu * l;
+      g.a_frag = ctx->u;
+      g.ssq = ctx->ssq;
+      g.bias = ctx->zero_gu;
+      g.m_out = ctx->m;
+      return launch_vlm_gu(g, s, t);
+    case 5:
+      g.w = ctx->w_d + n_d * l;
+      g.a_frag = ctx->m;
+      g.gate = ctx->ones;
+      g.h_out = ctx->h;
+      g.s1_next = ctx->attn_s1 + size_t(l + 1) * kVD;
+      g.u_out = ctx->u;
+      g.ssq_out = ctx->ssq;
+      return launch_vlm_down(g, s, t);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t vlm_enqueue(pi_ae_vlm* ctx, int B, int P, hipStream_t s, int timed_phase = -1,
+                       const KernelTiming* timing = nullptr) {
+  const int L = ctx->cfg.num_layers;
+  int n_timed = 0;
+  hipError_t e;
+  for (int l = 0; l < L; ++l)
+    for (int ph = 1; ph <= (l == L - 1 ? 1 : 5); ++ph) {
+      const KernelTiming* t = (timing && ph == timed_phase) ? &timing[n_timed++] : nullptr;
+      if ((e = vlm_launch_phase(ctx, B, P, s, l, ph, t)) != hipSuccess) return e;
+    }
+  return hipSuccess;
+}
+
+VlmStageParams vlm_stage_for(pi_ae_vlm* ctx, const uint16_t* emb, const uint8_t* mask, int B, int P) {
+  VlmStageParams v{};
+  v.emb = emb;
+  v.mask = mask;
+  v.s1 = ctx->attn_s1;
+  v.inv_freq = ctx->inv_freq;
+  v.h = ctx->h;
+  v.u = ctx->u;
+  v.ssq = ctx->ssq;
+  v.rope_cs = ctx->rope_cs;
+  v.kbias = ctx->kbias;
+  v.B = B;
+  v.P = P;
+  v.nkb = (P + 31) / 32;
+  return v;
+}
+
+pi_ae_status vlm_check_call(pi_ae_vlm* ctx, const uint16_t* emb, int32_t batch, int32_t P) {
+  if (!ctx) return fail(PI_AE_EINVAL, "ctx is NULL");
+  if (ctx->broken) return fail(PI_AE_ESTATE, "context is unusable after an earlier failure");
+  if (!emb) return fail(PI_AE_EINVAL, "prefix_emb is NULL");
+  if ((reinterpret_cast<uintptr_t>(emb) & 15u) != 0) return fail(PI_AE_EINVAL, "prefix_emb must be 16-byte aligned");
+  if (batch < 1 || batch > ctx->cfg.max_batch)
+    return fail(PI_AE_EINVAL, "batch " + std::to_string(batch) + " outside [1, max_batch]");
+  if (P < 1 || P > ctx->cfg.max_prefix_len)
+    return fail(PI_AE_EINVAL, "prefix_len " + std::to_string(P) + " outside [1, max_prefix_len]");
+  return PI_AE_OK;
+}
+
+}  // namespace
+
+PI_AE_API pi_ae_status pi_ae_vlm_prepare(const pi_ae_vlm_config* cfg, const pi_ae_vlm_layer_weights* layers,
+                                         pi_ae_vlm** out) {
+  if (!cfg || !layers || !out) return fail(PI_AE_EINVAL, "cfg, layers and out must be non-NULL");
+  pi_ae_status st = vlm_check_config(cfg);
+  if (st) return st;
+  if ((st = vlm_check_weights(cfg, layers))) return st;
+  pi_ae_vlm* ctx = new (std::nothrow) pi_ae_vlm();
+  if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
+  ctx->cfg = *cfg;
+  try {
+    HIP_OR_THROW(hipGetDevice(&ctx->device));
+    vlm_prepare(ctx, layers);
+  } catch (const HipError& e) {
+    ctx->release();
+    delete ctx;
+    return fail(e.e == hipErrorOutOfMemory ? PI_AE_ENOMEM : PI_AE_EHIP, e.what);
+  } catch (const std::bad_alloc&) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_ENOMEM, "host allocation failed during preparation");
+  } catch (...) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_EHIP, "unexpected failure during preparation");
+  }
+  *out = ctx;
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const uint8_t* pad_mask,
+                                         int32_t batch, int32_t prefix_len, pi_ae_prefix_kv* kv_out, void* stream) {
+  pi_ae_status st = vlm_check_call(ctx, prefix_emb, batch, prefix_len);
+  if (st) return st;
+  if (!kv_out) return fail(PI_AE_EINVAL, "kv_out is NULL");
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const std::pair<int, int> key(batch, prefix_len);
+  auto it = ctx->graphs.find(key);
+  if (it == ctx->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t e2 = vlm_enqueue(ctx, batch, prefix_len, ctx->cap);
+      e = hipStreamEndCapture(ctx->cap, &graph);
+      if (e2 != hipSuccess) e = e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(key, exec).first;
+  }
+  hipError_t e = launch_vlm_stage(vlm_stage_for(ctx, prefix_emb, pad_mask, batch, prefix_len), s);
+  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  kv_out->k = ctx->k_cache;
+  kv_out->v = ctx->v_cache;
+  kv_out->pad_mask = pad_mask;
+  kv_out->prefix_len = prefix_len;
+  return PI_AE_OK;
+}
+
+PI_AE_API void pi_ae_vlm_destroy(pi_ae_vlm* ctx) {
+  if (!ctx) return;
+  {
+    DeviceGuard dg(ctx->device);
+    hipDeviceSynchronize();
+    ctx->release();
+  }
+  delete ctx;
+}
+
+PI_AE_API pi_ae_status pi_ae_vlm_debug_time_phase(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const uint8_t* pad_mask,
+                                                  int32_t batch, int32_t prefix_len, int32_t phase, int32_t reps,
+                                                  void* stream, float* avg_us) {
+  pi_ae_status st = vlm_check_call(ctx, prefix_emb, batch, prefix_len);
+  if (st) return st;
+  const int L = ctx->cfg.num_layers;
+  if (phase < 1 || phase > 5 || reps < 1 || reps > 1000 || !avg_us || (phase > 1 && L < 2))
+    return fail(PI_AE_EINVAL, "time_phase: phase in [1, 5] (2..5 need 2 layers), reps in [1, 1000], avg_us non-NULL");
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int per = phase == 1 ? L : L - 1;
+  std::vector<KernelTiming> tv(size_t(per) * reps, KernelTiming{nullptr, nullptr});
+  hipError_t e = hipSuccess;
+  for (auto& t : tv) {
+    if (e == hipSuccess) e = hipEventCreate(&t.start);
+    if (e == hipSuccess) e = hipEventCreate(&t.stop);
+  }
+  for (int r = 0; r < reps && e == hipSuccess; ++r) {
+    e = launch_vlm_stage(vlm_stage_for(ctx, prefix_emb, pad_mask, batch, prefix_len), s);
+    if (e == hipSuccess) e = vlm_enqueue(ctx, batch, prefix_len, s, phase, &tv[size_t(r) * per]);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  double sum_ms = 0.0;
+  for (auto& t : tv) {
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    sum_ms += ms;
+  }
+  for (auto& t : tv) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("time_phase failed: ") + hipGetErrorString(e));
+  *avg_us = float(sum_ms * 1000.0 / double(tv.size()));
   return PI_AE_OK;
 }

@@ -20,7 +20,8 @@ PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTA
 # symbols declared in include/pi_ae.h
 EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_status_string",
            "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
-           "pi_ae_debug_time_phase")
+           "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
+           "pi_ae_vlm_debug_time_phase")
 
 
 class PiAeError(RuntimeError):
@@ -58,6 +59,20 @@ class PrefixKV(ctypes.Structure):
                 ("prefix_len", ctypes.c_int32)]
 
 
+class VlmConfig(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("width", ctypes.c_int32), ("mlp_dim", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_batch", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+
+VLM_LAYER_FIELDS = ("attn_norm", "q", "k", "v", "o", "ffn_norm", "gate", "up", "down")
+
+
+class VlmLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in VLM_LAYER_FIELDS]
+
+
 _lib = None
 
 
@@ -93,6 +108,18 @@ def load_library(path: str = LIB_PATH):
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_float)]
     lib.pi_ae_debug_time_phase.restype = ctypes.c_int
+    lib.pi_ae_vlm_prepare.argtypes = [ctypes.POINTER(VlmConfig), ctypes.POINTER(VlmLayerWeights),
+                                      ctypes.POINTER(ctypes.c_void_p)]
+    lib.pi_ae_vlm_prepare.restype = ctypes.c_int
+    lib.pi_ae_vlm_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.POINTER(PrefixKV), ctypes.c_void_p]
+    lib.pi_ae_vlm_prefill.restype = ctypes.c_int
+    lib.pi_ae_vlm_destroy.argtypes = [ctypes.c_void_p]
+    lib.pi_ae_vlm_destroy.restype = None
+    lib.pi_ae_vlm_debug_time_phase.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                               ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_vlm_debug_time_phase.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -224,3 +251,63 @@ class Context:
         _check(self._lib.pi_ae_debug_probe(self._h, ctypes.byref(kv), _ptr(noise), int(batch), int(step), int(layer),
                                            int(phase), int(which), out.ctypes.data, out.nbytes))
         return out
+
+
+def make_vlm_config(cfg, max_batch: int, max_prefix_len: int) -> VlmConfig:
+    """pi_ae_vlm_config from an :class:`inputs.PrefillConfig`-like object."""
+    return VlmConfig(cfg.num_layers, cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                     max_batch, max_prefix_len, cfg.rope_base, cfg.rms_eps)
+
+
+class _MarshalledVlmWeights:
+    """pi_ae_vlm_layer_weights[] pointing into host arrays kept alive by this object."""
+
+    def __init__(self, cfg, weights: dict):
+        self.keep = {n: np.ascontiguousarray(a, dtype=np.uint16) for n, a in weights.items()}
+        self.layers = (VlmLayerWeights * max(cfg.num_layers, 1))()
+        for l in range(cfg.num_layers):
+            self.layers[l] = VlmLayerWeights(*[_ptr(self.keep.get(f"layers.{l}.{n}.w")) for n in VLM_LAYER_FIELDS])
+
+
+class Prefill:
+    """A prepared VLM prefill (owns the library context and its prefix cache)."""
+
+    def __init__(self, cfg, weights: dict, max_batch: int, max_prefix_len: int):
+        lib = load_library()
+        self.cfg = cfg
+        self._c = make_vlm_config(cfg, max_batch, max_prefix_len)
+        mw = _MarshalledVlmWeights(cfg, weights)
+        handle = ctypes.c_void_p()
+        _check(lib.pi_ae_vlm_prepare(ctypes.byref(self._c), mw.layers, ctypes.byref(handle)))
+        self._h = handle
+        self._lib = lib
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.pi_ae_vlm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, emb, pad_mask, batch: int, prefix_len: int, stream=None) -> PrefixKV:
+        """Enqueue pi_ae_vlm_prefill; returns the pi_ae_prefix_kv of the cache it fills."""
+        kv = PrefixKV()
+        _check(self._lib.pi_ae_vlm_prefill(self._h, _ptr(emb), _ptr(pad_mask), int(batch), int(prefix_len),
+                                           ctypes.byref(kv), _stream_handle(stream)))
+        return kv
+
+    def time_phase(self, emb, pad_mask, batch, prefix_len, phase, reps, stream=None) -> float:
+        us = ctypes.c_float()
+        _check(self._lib.pi_ae_vlm_debug_time_phase(self._h, _ptr(emb), _ptr(pad_mask), int(batch), int(prefix_len),
+                                                    int(phase), int(reps), _stream_handle(stream), ctypes.byref(us)))
+        return float(us.value)
+
+
+def sample_from_cache(ctx: "Context", kv: PrefixKV, noise, actions, batch: int, stream=None):
+    """pi_ae_sample on the prefix cache a Prefill has just filled."""
+    _check(ctx._lib.pi_ae_sample(ctx._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
+                                 _stream_handle(stream)))

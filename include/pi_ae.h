@@ -188,6 +188,111 @@ const char* pi_ae_status_string(pi_ae_status status);
 const char* pi_ae_last_error(void);
 
 /* ------------------------------------------------------------------------
+ * The VLM prefix prefill: the step before the denoise loop, which fills the
+ * prefix cache that pi_ae_sample reads (Realtime-VLA technical blog, section
+ * "pi0.5 inference flow", Encoder (prefix) phase, run once per inference: the
+ * image tokens and the prompt tokens, each scaled by sqrt(2048), form the
+ * prefix sequence, which passes through the 18 layers of the Gemma-2B VLM;
+ * every layer's key and value are kept as the cache).  Layer l is
+ *   u = rms_norm(h) * gamma_attn;  q, k, v = u W_q^T, u W_k^T, u W_v^T;
+ *   RoPE on q and k at position j (token j of its episode);
+ *   cache[l] = (k, v);  h += attention(q, k, v) W_o^T  (every token attends to
+ *   every valid token of its episode: bidirectional, pad-masked keys excluded);
+ *   u = rms_norm(h) * gamma_ffn;  h += (GELU_tanh(u W_g^T) * (u W_u^T)) W_d^T
+ * (section 4 kernel list, Encoder layers).  The last layer stops after its
+ * keys and values, which are all the expert reads of it (section 4.1: 17
+ * layers run in full).  bf16 weights and activations, fp32 accumulation and
+ * residual stream.
+ * ------------------------------------------------------------------------ */
+
+/* VLM shape and call limits.  The kernels implement exactly width 2048,
+ * mlp_dim 16384, num_heads 8, num_kv_heads 1, head_dim 256 (the section 4
+ * kernel list's 2048 -> 2560 fused QKV and 2048 -> 16384 gated MLP, with the
+ * expert's 256-wide KV head) and return PI_AE_EUNSUPPORTED otherwise;
+ * 1 <= num_layers <= 64.  max_batch >= 1 and 1 <= max_prefix_len <= 4096 size
+ * the workspaces and the cache; rope_base is the RoPE base (10000), rms_eps
+ * the RMS-norm epsilon (1e-6). */
+typedef struct pi_ae_vlm_config {
+  int32_t num_layers;
+  int32_t width;
+  int32_t mlp_dim;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_batch;
+  int32_t max_prefix_len;
+  float rope_base;
+  float rms_eps;
+} pi_ae_vlm_config;
+
+/* One VLM layer, host pointers to bf16 bit patterns, nn.Linear layout
+ * [out][in], no biases: attn_norm and ffn_norm the norms' scales gamma
+ * [width]; q [heads*head_dim][width], k and v [head_dim][width],
+ * o [width][heads*head_dim], gate and up [mlp_dim][width], down
+ * [width][mlp_dim].  The last layer's o, ffn_norm, gate, up and down are not
+ * read (they may be NULL). */
+typedef struct pi_ae_vlm_layer_weights {
+  const uint16_t* attn_norm;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* ffn_norm;
+  const uint16_t* gate;
+  const uint16_t* up;
+  const uint16_t* down;
+} pi_ae_vlm_layer_weights;
+
+typedef struct pi_ae_vlm pi_ae_vlm;
+
+/* One-time preparation of the VLM (blog section 3.2: Q, K and V fused into
+ * one 2560-row matrix with RoPE in the GEMM epilogue, gate and up fused; the
+ * norms' scales kept as per-channel factors of the normalised operand).
+ * layers: num_layers entries.  Synchronous on the current HIP device; reads
+ * the host arrays only during the call; the library owns what it allocates,
+ * the prefix cache included.  *out is written only on success.  Errors:
+ * EINVAL (NULL pointers, sizes out of range), EUNSUPPORTED, ENOMEM, EHIP. */
+pi_ae_status pi_ae_vlm_prepare(const pi_ae_vlm_config* cfg, const pi_ae_vlm_layer_weights* layers,
+                               pi_ae_vlm** out);
+
+/* Run the prefill for `batch` episodes of `prefix_len` tokens.
+ *   prefix_emb: device bf16 [batch][prefix_len][width], 16-byte aligned: the
+ *               prefix sequence after the sqrt(2048) scaling.
+ *   pad_mask:   device u8 [batch][prefix_len], nonzero = valid token; NULL =
+ *               all valid.  Pad tokens are computed like the others but no
+ *               token attends to them; an episode without a valid token gets
+ *               a zero attention output.
+ *   batch:      1 <= batch <= max_batch; 1 <= prefix_len <= max_prefix_len.
+ *   kv_out:     host struct, filled on success: k and v point to the
+ *               context's cache, bf16 [num_layers][batch][prefix_len][256]
+ *               (k rotated), pad_mask = the argument, prefix_len: exactly
+ *               the pi_ae_prefix_kv that pi_ae_sample takes.  The cache stays
+ *               valid until the next prefill on this context or its
+ *               destruction.
+ *   stream:     hipStream_t (void*); asynchronous and stream-ordered; inputs
+ *               must stay alive until the stream has passed the call.
+ * One call in flight per context.  The layer sequence is captured as a
+ * hipGraph per (batch, prefix_len) on first use.  Errors: EINVAL (NULL
+ * ctx / prefix_emb / kv_out, sizes out of range, misaligned prefix_emb),
+ * ESTATE, EHIP. */
+pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const uint8_t* pad_mask, int32_t batch,
+                               int32_t prefix_len, pi_ae_prefix_kv* kv_out, void* stream);
+
+/* Synchronise the context's device, then free everything it owns (the cache
+ * included).  NULL is a no-op. */
+void pi_ae_vlm_destroy(pi_ae_vlm* ctx);
+
+/* Test-only: time one kernel of the prefill in its real sequence, as
+ * pi_ae_debug_time_phase does for the loop: the whole prefill is run `reps`
+ * times on `stream`, kernel by kernel, with a HIP event pair bound to each
+ * launch of `phase` (1 = QKV + RoPE, 2 = attention, 3 = O + residual,
+ * 4 = gate/up, 5 = down + residual); *avg_us = mean duration.  Same argument
+ * rules as pi_ae_vlm_prefill, plus 1 <= reps <= 1000.  Synchronises `stream`. */
+pi_ae_status pi_ae_vlm_debug_time_phase(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const uint8_t* pad_mask,
+                                        int32_t batch, int32_t prefix_len, int32_t phase, int32_t reps,
+                                        void* stream, float* avg_us);
+
+/* ------------------------------------------------------------------------
  * Test-only exports (unstable; used by the parity tests).
  * ------------------------------------------------------------------------ */
 
