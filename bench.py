@@ -7,6 +7,10 @@ chunk 63.
 
   python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--no-cpu]
 
+Workloads p1 / p2 / p3 time the VLM prefix prefill instead (one step = one
+pi_ae_vlm_prefill call: 17 full Gemma-2B-shaped layers and the last layer's
+K/V over 256 / 512 / 816 prefix tokens), reported as prefix tokens/s.
+
 Reported beside the throughput: the roofline of the dominant kernel (the
 gate/up GEMM: at batch 1 its algorithmic bytes = its bf16 weights per launch;
 at batch 32 its flops), its duration timed live inside the loop with a HIP
@@ -58,6 +62,12 @@ def algorithmic_flops_per_step(w) -> float:
     return gemm + attn
 
 
+# VLM prefill: per-launch algorithmic bytes (bf16 weights) and flops per row
+VLM_PHASE_NAMES = {1: "k_gemm<vlm qkv>", 2: "k_attn<vlm>", 3: "k_gemm<vlm o>", 4: "k_gemm<vlm gate_up>",
+                   5: "k_gemm<vlm down>"}
+VLM_PHASE_NK = {1: (2560, 2048), 3: (2048, 2048), 4: (32768, 2048), 5: (2048, 16384)}  # (N, K) per layer
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -105,12 +115,127 @@ def calibrate_copy(torch):
           flush=True)
 
 
+def prefill_cpu_baseline(w, wb, emb, mask, target_layers: int = 2):
+    """The prefill oracle (fp32) on a bounded sample: the first two layers of
+    episode 0, scaled to the whole prefill (17 full layers + the last K/V)."""
+    import numpy as np
+    from oracle import prefill_oracle as PO
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cfg = w.cfg
+    t0 = time.time()
+    PO.prefill(wb, cfg, emb[:1], mask[:1], dtype=np.float32, layers=target_layers)
+    per_layer = (time.time() - t0) / target_layers
+    full = per_layer * (cfg.num_layers - 1) + per_layer * 0.05  # the last layer's K/V: ~5% of a layer's MACs
+    return {"value": round(w.prefix_len / full, 1), "unit": "prefix tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"layers 0-{target_layers - 1} of episode 0 (NumPy fp32), {per_layer * 1e3:.0f} ms per layer, "
+                      f"scaled to {cfg.num_layers - 1} full layers + the last layer's K/V"}
+
+
+def bench_prefill(args, np, torch):
+    from flow_matching_action_amd import inputs, pi_ae
+    w = inputs.PREFILL_WORKLOADS[args.workload]
+    cfg, B, P = w.cfg, w.batch, w.prefix_len
+    print(f"bench: workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    wb = inputs.make_prefill_weights(cfg)
+    emb = inputs.make_prefix_embeddings(cfg, B, P)
+    mask = inputs.make_pad_mask(B, P, w.n_valid)
+    pf = pi_ae.Prefill(cfg, wb, B, P)
+    dev = torch.device("cuda:0")
+    de = torch.from_numpy(emb.view(np.int16)).to(dev)
+    dm = torch.from_numpy(mask).to(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pf.run(de, dm, B, P, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        pf.run(de, dm, B, P, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    median_us = statistics.median(per_call_ms) * 1e3
+    p99_us = float(np.percentile(per_call_ms, 99)) * 1e3
+    print(f"bench: {ms_per_step * 1e3:.1f} us/prefill (median {median_us:.1f}, p99 {p99_us:.1f})",
+          file=sys.stderr, flush=True)
+    phase_us = {ph: pf.time_phase(de, dm, B, P, ph, args.kernel_chunks, stream) for ph in range(1, 6)}
+    print("bench: per-launch us " + ", ".join(f"{VLM_PHASE_NAMES[p]}={t:.2f}" for p, t in phase_us.items()),
+          file=sys.stderr, flush=True)
+    L, M = cfg.num_layers, B * P
+    nv = w.n_valid
+    alg_bytes = {ph: n * k * 2 for ph, (n, k) in VLM_PHASE_NK.items()}
+    alg_flops = {ph: 2 * M * n * k for ph, (n, k) in VLM_PHASE_NK.items()}
+    alg_bytes[2] = B * nv * 256 * 2 * 2
+    alg_flops[2] = 4 * 8 * P * nv * 256 * B
+    launches = {1: L, 2: L - 1, 3: L - 1, 4: L - 1, 5: L - 1}
+    # whole prefill: 17 full layers + the last layer's K/V columns (512 of 2560)
+    bytes_call = sum(alg_bytes[ph] * (L - 1) for ph in (1, 2, 3, 4, 5)) + 512 * 2048 * 2
+    flops_call = sum(alg_flops[ph] * (L - 1) for ph in (1, 2, 3, 4, 5)) + 2 * M * 512 * 2048
+    call_s = ms_per_step * 1e-3
+    t_hbm, t_mfma = bytes_call / (HBM_PEAK_GBS * 1e9), flops_call / (MFMA_BF16_PEAK_TFS * 1e12)
+    dom = 4
+    sec = phase_us[dom] * 1e-6
+    if alg_flops[dom] / (MFMA_BF16_PEAK_TFS * 1e12) >= alg_bytes[dom] / (HBM_PEAK_GBS * 1e9):
+        a = alg_flops[dom] / sec / 1e12
+        roof = {"kernel": VLM_PHASE_NAMES[dom], "bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+    else:
+        a = alg_bytes[dom] / sec / 1e9
+        roof = {"kernel": VLM_PHASE_NAMES[dom], "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}
+    by_kernel = {}
+    for ph in range(1, 6):
+        sec = phase_us[ph] * 1e-6
+        gbs, tfs = alg_bytes[ph] / sec / 1e9, alg_flops[ph] / sec / 1e12
+        by_kernel[VLM_PHASE_NAMES[ph]] = {
+            "us": round(phase_us[ph], 3), "alg_bytes": alg_bytes[ph], "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "alg_flops": alg_flops[ph], "TFLOP/s": round(tfs, 2),
+            "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "time_share": round(phase_us[ph] * launches[ph] / (ms_per_step * 1e3), 4)}
+    cpu = None if args.no_cpu else prefill_cpu_baseline(w, wb, emb, mask)
+    pf.close()
+    line = {
+        "metric": "VLM prefix prefill: prefix tokens/s (18-layer Gemma-2B-shaped VLM filling the expert's KV cache)",
+        "value": round(B * P / call_s, 1),
+        "unit": "prefix tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": B, "prefix_len": P, "valid_prefix": nv,
+                   "layers": L},
+        "us_per_prefill": {"mean": round(ms_per_step * 1e3, 1), "median": round(median_us, 1),
+                           "p99": round(p99_us, 1)},
+        "whole_prefill_roofline": {"hbm_us": round(t_hbm * 1e6, 1), "mfma_us": round(t_mfma * 1e6, 1),
+                                   "frac": round(max(t_hbm, t_mfma) / call_s, 4)},
+        "per_launch_us": {VLM_PHASE_NAMES[p]: round(t, 3) for p, t in phase_us.items()},
+        "roofline": roof,
+        "roofline_by_kernel": by_kernel,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0", "p1", "p2", "p3"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-chunks", type=int, default=2,
                     help="whole loop passes over which each kernel's in-loop duration is averaged")
@@ -126,6 +251,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.workload.startswith("p"):
+        bench_prefill(args, np, torch)
         return
 
     from flow_matching_action_amd import inputs, pi_ae

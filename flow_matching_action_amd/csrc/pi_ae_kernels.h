@@ -191,12 +191,16 @@ hipError_t launch_enc(const GemmParams& p, hipStream_t s);
 
 // VLM prefill (width 2048, MLP 16384; always the tiled GEMMs)
 hipError_t launch_vlm_stage(const VlmStageParams& p, hipStream_t s);
-// kv_only: the K/V columns only (the last layer)
-hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, hipStream_t s, const KernelTiming* t = nullptr);
+// kv_only: the K/V columns only (the last layer).  S > 1 splits K over S
+// workgroups per tile (K / S a multiple of 256) with fp32 partials in `part`
+// (S x row_tiles(M, 128) * 128 x N floats), summed by a second kernel that
+// runs the epilogue.
+hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, int S, float* part, hipStream_t s,
+                          const KernelTiming* t = nullptr);
 hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
-hipError_t launch_vlm_o(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_o(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
-hipError_t launch_vlm_down(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vlm_down(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t = nullptr);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

@@ -554,6 +554,21 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmParams p) {
 // fragment-major global layouts); global loads run PD blocks ahead in
 // registers.  The fused epilogues are those of k_gemm, applied by each wave to
 // its own accumulators.
+// 1/rms of BM rows from row mb0*16 on, out of the producer's h^2 partials
+// (D/16 per row, summed in a fixed order).
+template <int BM, int NT, int D>
+__device__ __forceinline__ void tile_rstd(const GemmParams& p, float* srstd, int mb0) {
+  for (int r = threadIdx.x; r < BM; r += NT) {
+    const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * (D / 16));
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < D / 64; ++v) {
+      const float4 x = sp[v];
+      sum += (x.x + x.y) + (x.z + x.w);
+    }
+    srstd[r] = 1.f / sqrtf(sum * (1.f / D) + p.eps);
+  }
+}
 // Epilogue of the large-M GEMMs, after the BM x BN fp32 tile has been placed
 // in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
 // inputs): each of the NT threads takes 8 consecutive columns of one row per
@@ -741,8 +756,12 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
     }                                                                                  \
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);                                \
   }
-template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF>
-__global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
+// SPLIT: K is divided over gridDim.z workgroups per tile; each writes its raw
+// fp32 tile to part[z][row][col] ([z][gridDim.y * BM][gridDim.x * BN]) and
+// k_splitk_reduce sums them and runs the epilogue (for GEMMs whose tiles alone
+// would not fill the chip).
+template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF, bool SPLIT = false>
+__global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, float* part) {
   constexpr int NW = WM, KS = 2;
   constexpr int NP = 4;                          // stages of loads in flight (register slots)
   constexpr int FA = 2 * TR * WM, FB = 2 * TC;  // 16-row / 16-column fragments of the tile
@@ -757,13 +776,18 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
   u32x4 (*st)[FBS][64] = reinterpret_cast<u32x4 (*)[FBS][64]>(lds_raw);
   __shared__ float srstd[BM];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int KB = K >> 5, NS = KB / KS;  // NS is a multiple of NP: K is a multiple of 256 for every GEMM here
+  // KB: k-blocks of the whole K (the operands' row stride); this workgroup
+  // takes KBs of them from kb0 on.  NS is a multiple of NP: each K range is a
+  // multiple of 256 for every GEMM here.
+  const int KB = K >> 5;
+  const int KBs = SPLIT ? KB / int(gridDim.z) : KB, kb0 = SPLIT ? int(blockIdx.z) * KBs : 0;
+  const int NS = KBs / KS;
   // E_KV covers the K/V columns only: n-blocks from 2 * 64 on (Q is 64 pairs)
   const int nb0 = blockIdx.x * FB + (EPI == E_KV ? 128 : 0), mb0 = blockIdx.y * FA;
   const int sub = frag32_sub(lane);
   // this lane's A rows: fragments mb0 + 2(w*TR + r) + sub
-  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 2 * w * TR + sub) * KB * 64;
-  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w) + size_t(nb0) * KB * 64 + lane;
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + (size_t(mb0 + 2 * w * TR + sub) * KB + kb0) * 64;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w) + (size_t(nb0) * KB + kb0) * 64 + lane;
   const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
 
   // register slot SL holds stage s = SL (mod NP): its A operands and its B
@@ -787,18 +811,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
 
 #pragma unroll
   for (int sl = 0; sl < NP - 1; ++sl) PI_AE_B32_LOAD(sl, sl)
-  if constexpr (NORM) {  // 1/rms of the tile's rows from the producer's h^2 partials
-    for (int r = threadIdx.x; r < BM; r += NW * 64) {
-      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + r) * (D / 16));
-      float sum = 0.f;
-#pragma unroll
-      for (int v = 0; v < D / 64; ++v) {
-        const float4 x = sp[v];
-        sum += (x.x + x.y) + (x.z + x.w);
-      }
-      srstd[r] = 1.f / sqrtf(sum * (1.f / D) + p.eps);
-    }
-  }
+  if constexpr (NORM && !SPLIT) tile_rstd<BM, NW * 64, D>(p, srstd, mb0);
   PI_AE_B32_STORE_B(0, 0)
   lds_barrier();
 
@@ -841,6 +854,19 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
 #undef PI_AE_B32_STORE_B
 #undef PI_AE_B32_LOAD
 
+  if constexpr (SPLIT) {  // raw partial tile, D layout: 32 consecutive columns per half-wave
+    const size_t Np = size_t(gridDim.x) * BN;
+    float* dst = part + (size_t(blockIdx.z) * gridDim.y * BM + size_t(blockIdx.y) * BM) * Np + size_t(blockIdx.x) * BN;
+#pragma unroll
+    for (int r = 0; r < TR; ++r)
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          dst[size_t((w * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * Np + c * 32 + (lane & 31)] =
+              acc[r][c][i];
+    return;
+  }
   // epilogue: D layout to LDS (row 8(i/4) + 4(l/32) + i%4, column l%32 of each 32x32 tile)
   __syncthreads();
   float* ct = lds_raw;
@@ -855,6 +881,43 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K) {
   tile_epilogue<BM, BN, CS, NW * 64, EPI, D, F>(p, ct, srstd, mb0, nb0);
 }
 #undef PI_AE_B32_SCHED
+
+// The second half of a split-K GEMM: sum the S partial tiles of a BM x BN
+// output tile (fixed order z = 0 .. S-1) into LDS and run the GEMM's fused
+// epilogue on it.  Partials: [S][Mp][Np] fp32, columns local to the GEMM's
+// grid (E_KV adds its column offset here as the GEMM does).
+template <int BM, int BN, int EPI, int D, int F>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmParams p, const float* part, int S, int Mp, int Np) {
+  constexpr int NT = 256, CS = BN + 4, PT = BM * BN / 4 / NT;  // float4 per thread
+  static_assert(PT * NT * 4 == BM * BN, "whole float4 per thread");
+  __shared__ __attribute__((aligned(16))) float ct[BM * CS];
+  __shared__ float srstd[BM];
+  kernarg_touch(p);
+  const int mb0 = blockIdx.y * (BM / 16), nbl = blockIdx.x * (BN / 16);
+  const size_t zs = size_t(Mp) * Np;
+  float4 v[PT];
+  size_t off[PT];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int idx = threadIdx.x + q * NT, r = idx / (BN / 4), c4 = idx % (BN / 4);
+    off[q] = size_t(mb0 * 16 + r) * Np + nbl * 16 + c4 * 4;
+    v[q] = *reinterpret_cast<const float4*>(part + off[q]);
+  }
+  for (int z = 1; z < S; ++z)
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(part + z * zs + off[q]);
+      v[q].x += x.x; v[q].y += x.y; v[q].z += x.z; v[q].w += x.w;
+    }
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int idx = threadIdx.x + q * NT, r = idx / (BN / 4), c4 = idx % (BN / 4);
+    *reinterpret_cast<float4*>(&ct[r * CS + c4 * 4]) = v[q];
+  }
+  if constexpr (EPI != E_RES) tile_rstd<BM, NT, D>(p, srstd, mb0);
+  __syncthreads();
+  tile_epilogue<BM, BN, CS, NT, EPI, D, F>(p, ct, srstd, mb0, nbl + (EPI == E_KV ? 128 : 0));
+}
 
 
 // ---------------------------------------------------------------------------
@@ -1408,14 +1471,14 @@ hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 2, E_QKV>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+    return go(k_gemm_big32<4, 1, 2, E_QKV>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kD, (float*)nullptr);
   if (p.M <= 64)  // 32-row tiles: half the activation bytes per workgroup, twice the CUs
     return go(k_gemm<2, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M, 32)), dim3(256), s, t, p);
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 4, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD);
+    return go(k_gemm_big32<4, 1, 4, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD, (float*)nullptr);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 // O and down: at small M, 16-row tiles quarter each workgroup's activation
@@ -1423,7 +1486,7 @@ hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) 
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows) {
     if (p.a_frag2) return hipErrorInvalidValue;  // the key split is only taken at small M
-    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd, (float*)nullptr);
   }
   if (p.a_frag2) {
     if (p.M <= 64)
@@ -1436,14 +1499,14 @@ hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kF);
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kF, (float*)nullptr);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
 }
 hipError_t launch_enc(const GemmParams& p, hipStream_t s) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, nullptr, p, kD);
+    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, nullptr, p, kD, (float*)nullptr);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 4, E_RES>, dim3(kD / 16, row_tiles(p.M, 16)), dim3(512), s, nullptr, p);
   return go(k_gemm<4, 1, 8, 4, E_RES>, dim3(kD / 16, row_tiles(p.M)), dim3(512), s, nullptr, p);
@@ -1499,30 +1562,49 @@ hipError_t launch_vlm_stage(const VlmStageParams& p, hipStream_t s) {
   k_vlm_stage<<<p.B * p.P, 256, 0, s>>>(p);
   return hipGetLastError();
 }
-hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, hipStream_t s, const KernelTiming* t) {
-  if (kv_only)
-    return go(k_gemm_big32<4, 1, 2, E_KV, kVD, kVF>, dim3(2 * kHd / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
-  return go(k_gemm_big32<4, 1, 2, E_QKV, kVD, kVF>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
+// A tiled GEMM with N = ncols over K, split over S K-ranges when S > 1 (then
+// `part` holds S x Mp x ncols floats).  With a KernelTiming the events span
+// both kernels.
+template <int EPI>
+static hipError_t vlm_gemm(const GemmParams& p, int ncols, int K, int S, float* part, hipStream_t s,
+                           const KernelTiming* t) {
+  constexpr int TC = EPI == E_GELU ? 4 : 2, BN = 32 * TC;
+  const dim3 grid(ncols / BN, row_tiles(p.M, 128), S);
+  if (S <= 1) return go(k_gemm_big32<4, 1, TC, EPI, kVD, kVF>, grid, dim3(256), s, t, p, K, (float*)nullptr);
+  const KernelTiming t0{t ? t->start : nullptr, nullptr}, t1{nullptr, t ? t->stop : nullptr};
+  hipError_t e = go(k_gemm_big32<4, 1, TC, EPI, kVD, kVF, true>, grid, dim3(256), s, t ? &t0 : nullptr, p, K, part);
+  if (e != hipSuccess) return e;
+  const int Mp = int(grid.y) * 128;
+  return go(k_splitk_reduce<64, 64, EPI, kVD, kVF>, dim3(ncols / 64, Mp / 64), dim3(256), s, t ? &t1 : nullptr, p,
+            (const float*)part, S, Mp, ncols);
 }
-hipError_t launch_vlm_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  return go(k_gemm_big32<4, 1, 2, E_RES, kVD, kVF>, dim3(kVD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd);
+hipError_t launch_vlm_qkv(const GemmParams& p, bool kv_only, int S, float* part, hipStream_t s,
+                          const KernelTiming* t) {
+  if (kv_only) return vlm_gemm<E_KV>(p, 2 * kHd, kVD, S, part, s, t);
+  return vlm_gemm<E_QKV>(p, kNqkv, kVD, S, part, s, t);
+}
+hipError_t launch_vlm_o(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t) {
+  return vlm_gemm<E_RES>(p, kVD, kH * kHd, S, part, s, t);
 }
 hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  return go(k_gemm_big32<4, 1, 4, E_GELU, kVD, kVF>, dim3(kVNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kVD);
+  return vlm_gemm<E_GELU>(p, kVNgu, kVD, 1, nullptr, s, t);
 }
-hipError_t launch_vlm_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  return go(k_gemm_big32<4, 1, 2, E_RES, kVD, kVF>, dim3(kVD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kVF);
+hipError_t launch_vlm_down(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t) {
+  return vlm_gemm<E_RES>(p, kVD, kVF, S, part, s, t);
 }
-// Every prefix token is a query of its own episode's keys: the rows kernel
-// with T = P query tokens, no suffix keys, and (few episodes) the episode's
-// workgroups dealt over all XCDs.
+// Every prefix token is a query of its own episode's keys (T = P query
+// tokens, no suffix keys).  Few episodes: the batch-1 kernel (16 query rows
+// per workgroup, its 8 waves over the keys), which spreads one episode over
+// four times the workgroups of the rows kernel (measured at 256 / 816 tokens:
+// 8.7 / 26.5 us against 15.7 / 32.6 us); from 8 episodes on, the rows kernel
+// with each episode's K/V in one XCD's L2.
 hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTiming* t) {
-  const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
   if (p.B >= 8) {
+    const int per_ep = (p.T * kH + 32 * kAttn32Groups - 1) / (32 * kAttn32Groups);
     const int groups = (p.B + 7) / 8;
     return go(k_attn_rows32<kAttn32Groups, false>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
   }
-  return go(k_attn_rows32<kAttn32Groups, true>, dim3(p.B * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
+  return go(k_attn<1>, dim3((p.T * kH + 15) / 16, p.B), dim3(kAttnWaves * 64), s, t, p);
 }
 
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {

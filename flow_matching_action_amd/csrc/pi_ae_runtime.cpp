@@ -1021,6 +1021,7 @@ struct pi_ae_vlm {
   uint16_t *u = nullptr, *q = nullptr, *o = nullptr, *m = nullptr, *kp = nullptr, *vp = nullptr;
   float2* rope_cs = nullptr;
   uint16_t *k_cache = nullptr, *v_cache = nullptr;  // [L][B][P][256] of the last call
+  float* part = nullptr;  // split-K partial tiles, up to kVlmMaxSplit x Mpad x 2560
   int Mpad = 0, nkb_max = 0;
   hipStream_t cap = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
@@ -1045,6 +1046,23 @@ struct pi_ae_vlm {
 };
 
 namespace {
+
+// K splits of a tiled VLM GEMM (powers of two, at most kVlmMaxSplit, each K
+// range a multiple of 256): split while the tiles fill less than half of the
+// 256 CUs, or less than all of them while each K range stays >= 4096.  At one
+// view (256 rows) the O and down projections have only 64 tiles of 128 x 64,
+// QKV 80.  Measured: splitting a K = 2048 GEMM that already has 224 tiles,
+// or targeting 512 workgroups, is slower (the partial tiles' extra traffic
+// and the second kernel outweigh the parallelism).
+constexpr int kVlmMaxSplit = 8;
+int vlm_ksplit(int M, int ncols, int bn, int K) {
+  const int wgs = (ncols / bn) * ((M + 127) / 128);
+  int S = 1;
+  while (S < kVlmMaxSplit && K % (256 * S * 2) == 0 &&
+         (wgs * S < 128 || (wgs * S < 256 && K / (2 * S) >= 4096)))
+    S *= 2;
+  return S;
+}
 
 pi_ae_status vlm_check_config(const pi_ae_vlm_config* c) {
   if (c->width != kVD || c->mlp_dim != kVF || c->num_heads != kH || c->num_kv_heads != 1 || c->head_dim != kHd)
@@ -1144,6 +1162,7 @@ void vlm_prepare(pi_ae_vlm* ctx, const pi_ae_vlm_layer_weights* w) {
   const size_t ncache = size_t(L) * Mmax * kHd;
   ctx->k_cache = ctx->dalloc<uint16_t>(ncache);
   ctx->v_cache = ctx->dalloc<uint16_t>(ncache);
+  ctx->part = ctx->dalloc<float>(size_t(kVlmMaxSplit) * Mp * kNqkv);
   HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kVD * 4));
   HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kVD * 2));
   HIP_OR_THROW(hipMemset(ctx->ssq, 0, Mp * (kVD / 16) * 4));
@@ -1181,7 +1200,7 @@ hipError_t vlm_launch_phase(pi_ae_vlm* ctx, int B, int P, hipStream_t s, int l, 
       g.vp = last ? nullptr : ctx->vp;
       g.k_cache = ctx->k_cache + size_t(l) * M * kHd;
       g.v_cache = ctx->v_cache + size_t(l) * M * kHd;
-      return launch_vlm_qkv(g, last, s, t);
+      return launch_vlm_qkv(g, last, vlm_ksplit(M, last ? 2 * kHd : kNqkv, 64, kVD), ctx->part, s, t);
     case 2: {
       AttnParams a{};
       a.q = ctx->q;
@@ -1203,7 +1222,7 @@ hipError_t vlm_launch_phase(pi_ae_vlm* ctx, int B, int P, hipStream_t s, int l, 
       g.s1_next = ctx->ffn_s1 + size_t(l) * kVD;
       g.u_out = ctx->u;
       g.ssq_out = ctx->ssq;
-      return launch_vlm_o(g, s, t);
+      return launch_vlm_o(g, vlm_ksplit(M, kVD, 64, kH * kHd), ctx->part, s, t);
     case 4:
       g.w = ctx->w_gu + n_gu * l;
       g.a_frag = ctx->u;
@@ -1219,7 +1238,7 @@ hipError_t vlm_launch_phase(pi_ae_vlm* ctx, int B, int P, hipStream_t s, int l, 
       g.s1_next = ctx->attn_s1 + size_t(l + 1) * kVD;
       g.u_out = ctx->u;
       g.ssq_out = ctx->ssq;
-      return launch_vlm_down(g, s, t);
+      return launch_vlm_down(g, vlm_ksplit(M, kVD, 64, kVF), ctx->part, s, t);
   }
   return hipErrorInvalidValue;
 }
