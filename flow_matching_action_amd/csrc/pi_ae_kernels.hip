@@ -147,6 +147,8 @@ __device__ __forceinline__ size_t afrag_index(int row, int k, int KB) {
 // scalar registers and only the lane offset takes a vector register; reads
 // past `bytes` return zeros.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// LDS address as the buffer-to-LDS loads take it
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
@@ -882,6 +884,125 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
 }
 #undef PI_AE_B32_SCHED
 
+// Wide-tile GEMM for the gate/up projection at many rows (the batched loop
+// and the VLM prefill): 256 x 128 tiles, 4 waves each computing 64 rows x 128
+// columns on 32x32x16 MFMAs (8 accumulator tiles).  Per 32-wide k-block a
+// 128 x 128 tile needs as many load-path and LDS bytes per clock as MFMA
+// clocks; 256 x 128 leaves both about a quarter idle.  Each wave loads its
+// own A rows straight into registers, 3 k-blocks ahead; the weight
+// fragments, which all 4 waves read, go from memory to LDS directly
+// (buffer-to-LDS loads, no registers), into a 4-slot ring (4 separate LDS
+// objects, so that the compiler's wait counts stay per slot).  One barrier
+// per k-block: each wave first waits for its own loads of that block
+// (vmcnt: the loads of the two later blocks may stay in flight), the barrier
+// then makes every wave's weight fragments visible and retires all reads of
+// the slot that the next copy overwrites.  The fused epilogue runs in
+// quarters of 64 rows through a 64 x 132 LDS tile, so two workgroups fit on
+// a CU (about 67 KB of LDS each) and one's epilogue overlaps the other's
+// MFMAs.
+template <int EPI, int D, int F>
+__global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
+  constexpr int TR = 2, TC = 4, BM = 256, BN = 128, FB = BN / 16, CS = BN + 4, QR = 64;
+  constexpr bool NORM = EPI != E_RES;
+  __shared__ __attribute__((aligned(16))) u32x4 ring0[FB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring1[FB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring2[FB][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring3[FB][64];
+  __shared__ __attribute__((aligned(16))) float ct[QR * CS];
+  __shared__ float srstd[BM];
+  kernarg_touch(p);
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KB = K >> 5, NS = KB;  // one 32-wide k-block per stage; NS is a multiple of 4
+  const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * (BM / 16);
+  const int sub = frag32_sub(lane);
+  const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
+  // wave w: rows 64w.., fragments mb0 + 4w + 2r + sub (row tile r)
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 4 * w + sub) * KB * 64;
+  // the tile's 8 weight fragment columns: fragment (nb0 + f, kb) at (f KB + kb) KiB
+  const rsrc_t wr = make_rsrc(p.w + size_t(nb0) * KB * 512, uint32_t(FB) * uint32_t(KB) * 1024u);
+
+  u32x4 av[4][TR][2];
+#define PI_AE_W_LOADA(SL, KBK)                                                        \
+  {                                                                                   \
+    const int kb_ = (KBK) < NS ? (KBK) : 0;                                           \
+    _Pragma("unroll") for (int r = 0; r < TR; ++r)                                    \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h)                                   \
+        av[SL][r][h] = ap[(size_t(2 * r) * KB + kb_) * 64 + al[h]];                   \
+  }
+  // fragments w and w + 4 of k-block KBK into slot RING (a missing block
+  // re-reads block 0: in bounds, never used)
+#define PI_AE_W_DMA(RING, KBK)                                                        \
+  {                                                                                   \
+    const uint32_t kb_ = uint32_t((KBK) < NS ? (KBK) : 0);                            \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                   \
+      const int f = q * 4 + w;                                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&RING[f][0], 16, uint32_t(lane) * 16u, \
+                                               (uint32_t(f) * uint32_t(KB) + kb_) * 1024u, 0, 0);    \
+    }                                                                                 \
+  }
+  PI_AE_W_LOADA(0, 0)
+  PI_AE_W_DMA(ring0, 0)
+  PI_AE_W_LOADA(1, 1)
+  PI_AE_W_DMA(ring1, 1)
+  PI_AE_W_LOADA(2, 2)
+  PI_AE_W_DMA(ring2, 2)
+  if constexpr (NORM) tile_rstd<BM, 256, D>(p, srstd, mb0);
+
+  f32x16 acc[TR][TC];
+#pragma unroll
+  for (int r = 0; r < TR; ++r)
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
+
+  // stage SG (register slot SL = SG mod 4, weights in RING): its loads have
+  // landed (6 per wave per stage; the two later stages' 12 may be pending),
+  // barrier, then k-block SG+3 is issued into slot SL+3 / RING3 (= the slot
+  // of stage SG-1, read by every wave before the barrier), and the 16 MFMAs.
+#define PI_AE_W_STEP(RING, SL, SG, RING3)                                             \
+  {                                                                                   \
+    __builtin_amdgcn_s_waitcnt(0x0f7c); /* vmcnt(12) */                               \
+    lds_barrier();                                                                    \
+    PI_AE_W_LOADA(((SL) + 3) & 3, (SG) + 3)                                           \
+    PI_AE_W_DMA(RING3, (SG) + 3)                                                      \
+    u32x4 b[TC][2];                                                                   \
+    _Pragma("unroll") for (int c = 0; c < TC; ++c)                                    \
+      _Pragma("unroll") for (int h = 0; h < 2; ++h) b[c][h] = RING[2 * c + sub][al[h]]; \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
+      _Pragma("unroll") for (int r = 0; r < TR; ++r)                                  \
+        _Pragma("unroll") for (int c = 0; c < TC; ++c)                                \
+          acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, av[SL][r][h]), __builtin_bit_cast(bf16x8, b[c][h]), acc[r][c]); \
+  }
+  for (int sg = 0; sg < NS; sg += 4) {
+    PI_AE_W_STEP(ring0, 0, sg, ring3)
+    PI_AE_W_STEP(ring1, 1, sg + 1, ring0)
+    PI_AE_W_STEP(ring2, 2, sg + 2, ring1)
+    PI_AE_W_STEP(ring3, 3, sg + 3, ring2)
+  }
+#undef PI_AE_W_STEP
+#undef PI_AE_W_DMA
+#undef PI_AE_W_LOADA
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the re-reads past the last block have landed
+  __syncthreads();
+  // epilogue by quarters: wave q's 64 rows through the LDS tile
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    if (w == qt) {
+#pragma unroll
+      for (int r = 0; r < TR; ++r)
+#pragma unroll
+        for (int c = 0; c < TC; ++c)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            ct[(r * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
+    }
+    __syncthreads();
+    tile_epilogue<QR, BN, CS, 256, EPI, D, F>(p, ct, srstd + qt * QR, mb0 + qt * (QR / 16), nb0);
+    __syncthreads();
+  }
+}
+
 // The second half of a split-K GEMM: sum the S partial tiles of a BM x BN
 // output tile (fixed order z = 0 .. S-1) into LDS and run the GEMM's fused
 // epilogue on it.  Partials: [S][Mp][Np] fp32, columns local to the GEMM's
@@ -1229,7 +1350,6 @@ __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <int NWQ, bool SPREAD>
 __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
@@ -1478,7 +1598,7 @@ hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t)
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 4, E_GELU>, dim3(kNgu / 128, row_tiles(p.M, 128)), dim3(256), s, t, p, kD, (float*)nullptr);
+    return go(k_gemm_wide<E_GELU, kD, kF>, dim3(kNgu / 128, row_tiles(p.M, 256)), dim3(256), s, t, p, kD);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 // O and down: at small M, 16-row tiles quarter each workgroup's activation
@@ -1587,7 +1707,7 @@ hipError_t launch_vlm_o(const GemmParams& p, int S, float* part, hipStream_t s, 
   return vlm_gemm<E_RES>(p, kVD, kH * kHd, S, part, s, t);
 }
 hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  return vlm_gemm<E_GELU>(p, kVNgu, kVD, 1, nullptr, s, t);
+  return go(k_gemm_wide<E_GELU, kVD, kVF>, dim3(kVNgu / 128, row_tiles(p.M, 256)), dim3(256), s, t, p, kVD);
 }
 hipError_t launch_vlm_down(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t) {
   return vlm_gemm<E_RES>(p, kVD, kVF, S, part, s, t);

@@ -479,7 +479,7 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   }
   // ---- workspaces (zeroed once; padded rows are never written)
   ctx->Mmax = cfg.max_batch * T;
-  ctx->Mpad = (ctx->Mmax + 127) / 128 * 128;  // whole 128-row tiles of the large-M GEMM
+  ctx->Mpad = (ctx->Mmax + 255) / 256 * 256;  // whole 256-row tiles of the wide gate/up GEMM
   const size_t Mp = size_t(ctx->Mpad);
   ctx->h = ctx->dalloc<float>(Mp * kD);
   ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
@@ -1145,7 +1145,7 @@ void vlm_prepare(pi_ae_vlm* ctx, const pi_ae_vlm_layer_weights* w) {
   // workspaces (zeroed once: rows past a call's M are read by whole GEMM
   // tiles but never written by it, and must hold finite values)
   const size_t Mmax = size_t(cfg.max_batch) * cfg.max_prefix_len;
-  ctx->Mpad = int((Mmax + 127) / 128 * 128);
+  ctx->Mpad = int((Mmax + 255) / 256 * 256);  // whole 256-row tiles of the wide gate/up GEMM
   const size_t Mp = size_t(ctx->Mpad);
   ctx->nkb_max = (cfg.max_prefix_len + 31) / 32;
   const size_t npack = size_t(cfg.max_batch) * ctx->nkb_max * 8192;
