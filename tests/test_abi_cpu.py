@@ -180,3 +180,59 @@ def test_pi0_weight_validation():
     h = ctypes.c_void_p()
     assert pi_ae.load_library().pi_ae_prepare_weights(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == \
         pi_ae.PI_AE_EINVAL
+
+
+# ------------------------------------------------------------------ VLM prefill
+def _vlm_null_layers(L):
+    return (pi_ae.VlmLayerWeights * L)()
+
+
+@needs_lib
+@pytest.mark.parametrize("field,value,status", [
+    ("width", 1024, pi_ae.PI_AE_EUNSUPPORTED),
+    ("mlp_dim", 8192, pi_ae.PI_AE_EUNSUPPORTED),
+    ("num_kv_heads", 8, pi_ae.PI_AE_EUNSUPPORTED),
+    ("head_dim", 128, pi_ae.PI_AE_EUNSUPPORTED),
+    ("num_layers", 0, pi_ae.PI_AE_EINVAL),
+    ("num_layers", 65, pi_ae.PI_AE_EINVAL),
+    ("max_batch", 0, pi_ae.PI_AE_EINVAL),
+    ("max_prefix_len", 0, pi_ae.PI_AE_EINVAL),
+    ("max_prefix_len", 4097, pi_ae.PI_AE_EINVAL),
+    ("rms_eps", 0.0, pi_ae.PI_AE_EINVAL),
+])
+def test_vlm_config_validation(field, value, status):
+    """pi_ae_vlm_prepare rejects unsupported shapes and bad limits before any
+    device work (no GPU needed)."""
+    cfg = inputs.PrefillConfig(num_layers=2)
+    c = pi_ae.make_vlm_config(cfg, 1, 256)
+    setattr(c, field, value)
+    lib = pi_ae.load_library()
+    h = ctypes.c_void_p()
+    layers = _vlm_null_layers(max(c.num_layers, 1))
+    assert lib.pi_ae_vlm_prepare(ctypes.byref(c), layers, ctypes.byref(h)) == status
+    assert h.value is None
+    assert lib.pi_ae_last_error() != b""
+
+
+@needs_lib
+def test_vlm_weight_pointers_and_null_arguments():
+    lib = pi_ae.load_library()
+    cfg = inputs.PrefillConfig(num_layers=2)
+    c = pi_ae.make_vlm_config(cfg, 1, 256)
+    h = ctypes.c_void_p()
+    assert lib.pi_ae_vlm_prepare(None, None, None) == pi_ae.PI_AE_EINVAL
+    # every pointer NULL: layer 0 is named
+    assert lib.pi_ae_vlm_prepare(ctypes.byref(c), _vlm_null_layers(2), ctypes.byref(h)) == pi_ae.PI_AE_EINVAL
+    assert b"layer 0" in lib.pi_ae_last_error()
+    # the last layer needs only its norm and Q/K/V; the others everything
+    keep = {n: np.zeros(s, np.uint16) for n, s in inputs.prefill_weight_shapes(cfg)}
+    for n in ("o", "ffn_norm", "gate", "up", "down"):
+        del keep[f"layers.0.{n}.w"]
+    mw = pi_ae._MarshalledVlmWeights(cfg, keep)
+    assert lib.pi_ae_vlm_prepare(ctypes.byref(c), mw.layers, ctypes.byref(h)) == pi_ae.PI_AE_EINVAL
+    assert b"layer 0" in lib.pi_ae_last_error()
+    kv = pi_ae.PrefixKV()
+    assert lib.pi_ae_vlm_prefill(None, None, None, 1, 1, ctypes.byref(kv), None) == pi_ae.PI_AE_EINVAL
+    us = ctypes.c_float()
+    assert lib.pi_ae_vlm_debug_time_phase(None, None, None, 1, 1, 1, 1, None, ctypes.byref(us)) == pi_ae.PI_AE_EINVAL
+    assert lib.pi_ae_vlm_destroy(None) is None
