@@ -10,6 +10,10 @@ chunk 63.
 Workloads p1 / p2 / p3 time the VLM prefix prefill instead (one step = one
 pi_ae_vlm_prefill call: 17 full Gemma-2B-shaped layers and the last layer's
 K/V over 256 / 512 / 816 prefix tokens), reported as prefix tokens/s.
+Workloads e1 / e2 / e3 time one whole inference without the vision encoder
+(pi_ae_pipeline_run: the prefill of 1 / 2 / 3 views, then the 10-step loop of
+a 63-action chunk on the cache it leaves, one graph), reported as
+inferences/s and ms per inference.
 
 Reported beside the throughput: the roofline of the dominant kernel (the
 gate/up GEMM: at batch 1 its algorithmic bytes = its bf16 weights per launch;
@@ -229,13 +233,64 @@ def bench_prefill(args, np, torch):
     print(json.dumps(line), flush=True)
 
 
+PIPELINES = {"e1": ("p1", "c2"), "e2": ("p2", "c3"), "e3": ("p3", "c4")}
+
+
+def bench_pipeline(args, np, torch):
+    from flow_matching_action_amd import inputs, pi_ae
+    pw = inputs.PREFILL_WORKLOADS[PIPELINES[args.workload][0]]
+    ew = inputs.WORKLOADS[PIPELINES[args.workload][1]]
+    B, P = pw.batch, pw.prefix_len
+    print(f"bench: pipeline {args.workload}: {pw.description}, then {ew.description}", file=sys.stderr, flush=True)
+    pf = pi_ae.Prefill(pw.cfg, inputs.make_prefill_weights(pw.cfg), B, P)
+    ctx = pi_ae.Context(ew.cfg, inputs.make_weights(ew.cfg), B, P)
+    pipe = pi_ae.Pipeline(pf, ctx)
+    dev = torch.device("cuda:0")
+    de = torch.from_numpy(inputs.make_prefix_embeddings(pw.cfg, B, P).view(np.int16)).to(dev)
+    dm = torch.from_numpy(inputs.make_pad_mask(B, P, pw.n_valid)).to(dev)
+    dn = torch.from_numpy(inputs.make_noise(ew.cfg, B)).to(dev)
+    out = torch.empty_like(dn)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pipe.run(de, dm, dn, out, B, P, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        pipe.run(de, dm, dn, out, B, P, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = wall * 1e3 / args.steps
+    med, p99 = statistics.median(per_call_ms), float(np.percentile(per_call_ms, 99))
+    print(f"bench: {ms * 1e3:.1f} us/inference (median {med * 1e3:.1f}, p99 {p99 * 1e3:.1f})", file=sys.stderr, flush=True)
+    pipe.close()
+    ctx.close()
+    pf.close()
+    line = {
+        "metric": "inferences/s (VLM prefix prefill + 10-step denoise loop, one graph; no vision encoder)",
+        "value": round(B / (ms * 1e-3), 2), "unit": "inferences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {pw.description}; then {ew.description}", "batch": B,
+                   "prefix_len": P, "valid_prefix": pw.n_valid, "chunk_len": ew.cfg.chunk_len,
+                   "vlm_layers": pw.cfg.num_layers, "expert_layers": ew.cfg.num_layers,
+                   "euler_steps": ew.cfg.num_steps},
+        "ms_per_inference": {"mean": round(ms, 3), "median": round(med, 3), "p99": round(p99, 3)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0", "p1", "p2", "p3"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0", "p1", "p2", "p3", "e1", "e2", "e3"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-chunks", type=int, default=2,
                     help="whole loop passes over which each kernel's in-loop duration is averaged")
@@ -254,6 +309,9 @@ def main():
         return
     if args.workload.startswith("p"):
         bench_prefill(args, np, torch)
+        return
+    if args.workload.startswith("e"):
+        bench_pipeline(args, np, torch)
         return
 
     from flow_matching_action_amd import inputs, pi_ae

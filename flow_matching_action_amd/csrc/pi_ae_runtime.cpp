@@ -1395,3 +1395,74 @@ PI_AE_API pi_ae_status pi_ae_vlm_debug_time_phase(pi_ae_vlm* ctx, const uint16_t
   *avg_us = float(sum_ms * 1000.0 / double(tv.size()));
   return PI_AE_OK;
 }
+
+// ====================================================================== pipeline
+struct pi_ae_pipeline {
+  pi_ae_vlm* vlm = nullptr;
+  pi_ae_ctx* ctx = nullptr;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  void release() {
+    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    graphs.clear();
+  }
+};
+
+PI_AE_API pi_ae_status pi_ae_pipeline_create(pi_ae_vlm* vlm, pi_ae_ctx* expert, pi_ae_pipeline** out) {
+  if (!vlm || !expert || !out) return fail(PI_AE_EINVAL, "vlm, expert and out must be non-NULL");
+  if (vlm->cfg.num_layers != expert->cfg.num_layers)
+    return fail(PI_AE_EINVAL, "the VLM has " + std::to_string(vlm->cfg.num_layers) + " layers, the expert " +
+                                  std::to_string(expert->cfg.num_layers));
+  if (vlm->device != expert->device) return fail(PI_AE_EINVAL, "the two contexts live on different devices");
+  pi_ae_pipeline* p = new (std::nothrow) pi_ae_pipeline();
+  if (!p) return fail(PI_AE_ENOMEM, "host allocation failed");
+  p->vlm = vlm;
+  p->ctx = expert;
+  *out = p;
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_pipeline_run(pi_ae_pipeline* pipe, const uint16_t* prefix_emb, const uint8_t* pad_mask,
+                                          const float* noise, float* actions, int32_t batch, int32_t prefix_len,
+                                          void* stream) {
+  if (!pipe) return fail(PI_AE_EINVAL, "pipe is NULL");
+  pi_ae_vlm* vlm = pipe->vlm;
+  pi_ae_ctx* ctx = pipe->ctx;
+  pi_ae_status st = vlm_check_call(vlm, prefix_emb, batch, prefix_len);
+  if (st) return st;
+  pi_ae_prefix_kv kv{vlm->k_cache, vlm->v_cache, pad_mask, prefix_len};
+  if ((st = check_call(ctx, &kv, noise, actions, batch))) return st;
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const std::pair<int, int> key(batch, prefix_len);
+  auto it = pipe->graphs.find(key);
+  if (it == pipe->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      hipError_t e2 = vlm_enqueue(vlm, batch, prefix_len, ctx->cap);
+      if (e2 == hipSuccess) e2 = enqueue(ctx, batch, prefix_len, ctx->cap, StopAt{});
+      e = hipStreamEndCapture(ctx->cap, &graph);
+      if (e2 != hipSuccess) e = e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    it = pipe->graphs.emplace(key, exec).first;
+  }
+  hipError_t e = launch_vlm_stage(vlm_stage_for(vlm, prefix_emb, pad_mask, batch, prefix_len), s);
+  if (e == hipSuccess) e = launch_args(args_for(ctx, &kv, noise, actions, batch), s);
+  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
+PI_AE_API void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe) {
+  if (!pipe) return;
+  {
+    DeviceGuard dg(pipe->ctx->device);
+    hipDeviceSynchronize();
+    pipe->release();
+  }
+  delete pipe;
+}

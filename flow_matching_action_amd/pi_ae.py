@@ -21,7 +21,7 @@ PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTA
 EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_status_string",
            "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
            "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
-           "pi_ae_vlm_debug_time_phase")
+           "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy")
 
 
 class PiAeError(RuntimeError):
@@ -120,6 +120,13 @@ def load_library(path: str = LIB_PATH):
                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                ctypes.POINTER(ctypes.c_float)]
     lib.pi_ae_vlm_debug_time_phase.restype = ctypes.c_int
+    lib.pi_ae_pipeline_create.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pi_ae_pipeline_create.restype = ctypes.c_int
+    lib.pi_ae_pipeline_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.pi_ae_pipeline_run.restype = ctypes.c_int
+    lib.pi_ae_pipeline_destroy.argtypes = [ctypes.c_void_p]
+    lib.pi_ae_pipeline_destroy.restype = None
     _lib = lib
     return lib
 
@@ -311,3 +318,29 @@ def sample_from_cache(ctx: "Context", kv: PrefixKV, noise, actions, batch: int, 
     """pi_ae_sample on the prefix cache a Prefill has just filled."""
     _check(ctx._lib.pi_ae_sample(ctx._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
                                  _stream_handle(stream)))
+
+
+class Pipeline:
+    """pi_ae_pipeline: a Prefill and an expert Context run as one graph per call."""
+
+    def __init__(self, prefill: Prefill, ctx: "Context"):
+        self._lib = load_library()
+        self.prefill, self.ctx = prefill, ctx  # keeps both alive
+        handle = ctypes.c_void_p()
+        _check(self._lib.pi_ae_pipeline_create(prefill._h, ctx._h, ctypes.byref(handle)))
+        self._h = handle
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.pi_ae_pipeline_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, emb, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
+        _check(self._lib.pi_ae_pipeline_run(self._h, _ptr(emb), _ptr(pad_mask), _ptr(noise), _ptr(actions),
+                                            int(batch), int(prefix_len), _stream_handle(stream)))

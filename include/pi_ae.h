@@ -282,6 +282,29 @@ pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const
  * included).  NULL is a no-op. */
 void pi_ae_vlm_destroy(pi_ae_vlm* ctx);
 
+/* The VLM prefill and the denoise loop as one pipeline (RV-blog sections
+ * "CUDA Graph" and "static buffers": the whole inference is one captured
+ * graph over static buffers).  A pipeline pairs a prepared VLM with a
+ * prepared expert of the same depth (the expert's layer l reads the VLM
+ * layer l's keys and values); both must outlive it.  Errors: EINVAL (NULL
+ * pointers, different layer counts). */
+typedef struct pi_ae_pipeline pi_ae_pipeline;
+pi_ae_status pi_ae_pipeline_create(pi_ae_vlm* vlm, pi_ae_ctx* expert, pi_ae_pipeline** out);
+
+/* One inference: the prefill of prefix_emb (as pi_ae_vlm_prefill) and then
+ * the denoise loop of noise into actions (as pi_ae_sample) on the cache it
+ * leaves.  Per call, a staging kernel for each model; the layer sequences of
+ * both are captured once per (batch, prefix_len) as a single hipGraph.  Same
+ * argument rules as the two calls (batch and prefix_len within both
+ * contexts' limits); asynchronous and stream-ordered; one call in flight per
+ * pipeline and its two contexts.  The cache stays in the VLM context as
+ * after pi_ae_vlm_prefill. */
+pi_ae_status pi_ae_pipeline_run(pi_ae_pipeline* pipe, const uint16_t* prefix_emb, const uint8_t* pad_mask,
+                                const float* noise, float* actions, int32_t batch, int32_t prefix_len, void* stream);
+
+/* Free the pipeline's graphs (not the two contexts).  NULL is a no-op. */
+void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe);
+
 /* Test-only: time one kernel of the prefill in its real sequence, as
  * pi_ae_debug_time_phase does for the loop: the whole prefill is run `reps`
  * times on `stream`, kernel by kernel, with a HIP event pair bound to each

@@ -210,3 +210,43 @@ def test_prefill_then_denoise_loop(full_p1):
     log(f"[prefill+loop] rel_l2={e:.3e} max_abs={mx:.3e} delta_rel_l2={d:.3e}")
     assert np.all(np.isfinite(x))
     assert e <= TOL_REL_L2 and mx <= TOL_MAX_ABS and d <= 2e-2, (e, mx, d)
+
+
+def test_pipeline_graph_equals_separate_calls():
+    """pi_ae_pipeline_run (prefill and loop in one graph) gives bitwise the
+    actions of pi_ae_vlm_prefill followed by pi_ae_sample, and both match the
+    oracle pipeline; two sizes on one pipeline."""
+    L = 2
+    cfg = inputs.PrefillConfig(num_layers=L)
+    ecfg = inputs.ExpertConfig(num_layers=L)
+    w = inputs.make_prefill_weights(cfg)
+    ew = inputs.make_weights(ecfg)
+    pf = pi_ae.Prefill(cfg, w, 2, 300)
+    ctx = pi_ae.Context(ecfg, ew, 2, 300)
+    pipe = pi_ae.Pipeline(pf, ctx)
+    try:
+        for B, P, nv in ((1, 256, [256]), (2, 300, [300, 290])):
+            log(f"step: pipeline B={B} P={P}")
+            emb = inputs.make_prefix_embeddings(cfg, B, P)
+            mask = inputs.make_pad_mask(B, P, nv)
+            noise = inputs.make_noise(ecfg, B)
+            demb, dmask, dnoise = to_dev(emb), to_dev(mask), to_dev(noise)
+            a_pipe = torch.empty_like(dnoise)
+            pipe.run(demb, dmask, dnoise, a_pipe, B, P)
+            torch.cuda.synchronize()
+            a_sep = torch.empty_like(dnoise)
+            kv = pf.run(demb, dmask, B, P)
+            pi_ae.sample_from_cache(ctx, kv, dnoise, a_sep, B)
+            torch.cuda.synchronize()
+            x = a_pipe.cpu().numpy()
+            assert np.array_equal(x, a_sep.cpu().numpy())
+            K, V = PO.prefill(w, cfg, emb, mask)
+            ref = O.sample(ew, ecfg, inputs.f32_to_bf16_bits(K.astype(np.float32)),
+                           inputs.f32_to_bf16_bits(V.astype(np.float32)), mask, noise)
+            e, mx = rel_l2(x, ref), float(np.max(np.abs(x - ref)))
+            log(f"[pipeline B={B} P={P}] rel_l2={e:.3e} max_abs={mx:.3e}")
+            assert e <= TOL_REL_L2 and mx <= TOL_MAX_ABS
+    finally:
+        pipe.close()
+        ctx.close()
+        pf.close()
