@@ -103,11 +103,11 @@ struct pi_ae_ctx {
     return static_cast<T*>(p);
   }
   void release() {
-    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
-    for (void* p : allocs) hipFree(p);
+    for (void* p : allocs) (void)hipFree(p);
     allocs.clear();
-    if (cap) hipStreamDestroy(cap);
+    if (cap) (void)hipStreamDestroy(cap);
     cap = nullptr;
   }
 };
@@ -746,11 +746,11 @@ struct DeviceGuard {
   int prev = -1;
   explicit DeviceGuard(int dev) {
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-    if (prev != dev) hipSetDevice(dev);
+    if (prev != dev) (void)hipSetDevice(dev);
   }
   ~DeviceGuard() {
     int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
 
@@ -817,7 +817,7 @@ PI_AE_API pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, c
       if (e2 != hipSuccess) e = e2;
     }
     if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) hipGraphDestroy(graph);
+    if (graph) (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
     it = ctx->graphs.emplace(key, exec).first;
   }
@@ -831,7 +831,7 @@ PI_AE_API void pi_ae_destroy(pi_ae_ctx* ctx) {
   if (!ctx) return;
   {
     DeviceGuard dg(ctx->device);
-    hipDeviceSynchronize();
+    (void)hipDeviceSynchronize();
     ctx->release();
   }
   delete ctx;
@@ -943,7 +943,7 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
   DeviceGuard dg(ctx->device);
   if (hipMalloc(&actions, size_t(M) * kA * 4) != hipSuccess) return fail(PI_AE_ENOMEM, "probe scratch");
   if ((st = check_call(ctx, kv, noise, actions, batch))) {
-    hipFree(actions);
+    (void)hipFree(actions);
     return st;
   }
   StopAt stop;
@@ -1000,7 +1000,7 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
         }
     }
   }
-  hipFree(actions);
+  (void)hipFree(actions);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("probe failed: ") + hipGetErrorString(e));
   return PI_AE_OK;
 }
@@ -1036,11 +1036,11 @@ struct pi_ae_vlm {
     return static_cast<T*>(p);
   }
   void release() {
-    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
-    for (void* p : allocs) hipFree(p);
+    for (void* p : allocs) (void)hipFree(p);
     allocs.clear();
-    if (cap) hipStreamDestroy(cap);
+    if (cap) (void)hipStreamDestroy(cap);
     cap = nullptr;
   }
 };
@@ -1335,7 +1335,7 @@ PI_AE_API pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_
       if (e2 != hipSuccess) e = e2;
     }
     if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) hipGraphDestroy(graph);
+    if (graph) (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
     it = ctx->graphs.emplace(key, exec).first;
   }
@@ -1353,7 +1353,7 @@ PI_AE_API void pi_ae_vlm_destroy(pi_ae_vlm* ctx) {
   if (!ctx) return;
   {
     DeviceGuard dg(ctx->device);
-    hipDeviceSynchronize();
+    (void)hipDeviceSynchronize();
     ctx->release();
   }
   delete ctx;
@@ -1402,7 +1402,7 @@ struct pi_ae_pipeline {
   pi_ae_ctx* ctx = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   void release() {
-    for (auto& kv : graphs) hipGraphExecDestroy(kv.second);
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
   }
 };
@@ -1446,7 +1446,7 @@ PI_AE_API pi_ae_status pi_ae_pipeline_run(pi_ae_pipeline* pipe, const uint16_t* 
       if (e2 != hipSuccess) e = e2;
     }
     if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) hipGraphDestroy(graph);
+    if (graph) (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
     it = pipe->graphs.emplace(key, exec).first;
   }
@@ -1461,7 +1461,7 @@ PI_AE_API void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe) {
   if (!pipe) return;
   {
     DeviceGuard dg(pipe->ctx->device);
-    hipDeviceSynchronize();
+    (void)hipDeviceSynchronize();
     pipe->release();
   }
   delete pipe;
