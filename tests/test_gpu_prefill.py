@@ -147,6 +147,22 @@ def test_prefill_edge_sizes():
         pf.close()
 
 
+def test_prefill_many_episodes_rows_attention():
+    """From 8 episodes on the prefill's attention runs the rows kernel (each
+    episode's K/V on one XCD): 9 episodes of 40 tokens, ragged masks, one
+    episode without a valid token, 2 layers."""
+    cfg = inputs.PrefillConfig(num_layers=2)
+    w = inputs.make_prefill_weights(cfg)
+    nv = [40, 33, 1, 0, 17, 40, 39, 2, 25]
+    B, P = len(nv), 40
+    emb = inputs.make_prefix_embeddings(cfg, B, P, seed=21)
+    mask = inputs.make_pad_mask(B, P, nv)
+    log(f"step: prefill 2 layers, B={B} P={P} n_valid={nv}")
+    k, v = run_prefill(cfg, w, emb, mask)
+    K, V = PO.prefill(w, cfg, emb, mask)
+    check_cache(k, v, K, V, "p-9ep")
+
+
 def test_prefill_three_views_with_padded_prompt():
     """The 3-view shape (816 tokens, last 16 padded), 2 layers."""
     cfg = inputs.PrefillConfig(num_layers=2)
