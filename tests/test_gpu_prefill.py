@@ -163,6 +163,20 @@ def test_prefill_many_episodes_rows_attention():
     check_cache(k, v, K, V, "p-9ep")
 
 
+def test_prefill_maximum_prefix_length():
+    """The context's largest prefix (4096 tokens: 128 key blocks per query,
+    2048 query blocks), 2 layers, a ragged tail of pad tokens."""
+    cfg = inputs.PrefillConfig(num_layers=2)
+    w = inputs.make_prefill_weights(cfg)
+    P = 4096
+    emb = inputs.make_prefix_embeddings(cfg, 1, P, seed=31)
+    mask = inputs.make_pad_mask(1, P, P - 37)
+    log(f"step: prefill 2 layers, P={P} (max), {P - 37} valid")
+    k, v = run_prefill(cfg, w, emb, mask, max_prefix=4096)
+    K, V = PO.prefill(w, cfg, emb, mask)
+    check_cache(k, v, K, V, "p-max")
+
+
 def test_prefill_three_views_with_padded_prompt():
     """The 3-view shape (816 tokens, last 16 padded), 2 layers."""
     cfg = inputs.PrefillConfig(num_layers=2)
