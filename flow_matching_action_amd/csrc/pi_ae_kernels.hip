@@ -575,9 +575,12 @@ __device__ __forceinline__ void tile_rstd(const GemmParams& p, float* srstd, int
 // in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
 // inputs): each of the NT threads takes 8 consecutive columns of one row per
 // pass, so that every global access is 16 or 32 contiguous bytes.
+// bias_pre (QKV / gate-up): this thread's four bias float4 (gate / Q-K-V
+// columns c0, c0 + 4, then c1, c1 + 4 of its chunk) already in registers,
+// when the caller loaded them ahead (they are the same in every pass).
 template <int BM, int BN, int CS, int NT, int EPI, int D, int F>
 __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* ct, const float* srstd, int mb0,
-                                              int nb0) {
+                                              int nb0, const float4* bias_pre = nullptr) {
   constexpr int FB = BN / 16;
   // A thread's column chunk is the same in every pass (NT is a multiple of the
   // chunks per row), so per-column operands are loaded once; per-row operands
@@ -638,8 +641,10 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
     const int c = threadIdx.x % CPR, pp = c >> 1, hf = c & 1;
     const int jp = nb0 / 2 + pp;  // global pair index
     const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;  // bias columns
-    const float4 b00 = *reinterpret_cast<const float4*>(p.bias + c0), b01 = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
-    const float4 b10 = *reinterpret_cast<const float4*>(p.bias + c1), b11 = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
+    const float4 b00 = bias_pre ? bias_pre[0] : *reinterpret_cast<const float4*>(p.bias + c0);
+    const float4 b01 = bias_pre ? bias_pre[1] : *reinterpret_cast<const float4*>(p.bias + c0 + 4);
+    const float4 b10 = bias_pre ? bias_pre[2] : *reinterpret_cast<const float4*>(p.bias + c1);
+    const float4 b11 = bias_pre ? bias_pre[3] : *reinterpret_cast<const float4*>(p.bias + c1 + 4);
     const int ip = (jp & 7) * 16 + 8 * hf;  // RoPE pair of Q / K_s columns
     for (int pb = 0; pb < NP; pb += PB) {
       float4 cs[PB][4];
@@ -947,6 +952,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   PI_AE_W_LOADA(2, 2)
   PI_AE_W_DMA(ring2, 2)
   if constexpr (NORM) tile_rstd<BM, 256, D>(p, srstd, mb0);
+  // the epilogue's bias chunk of this thread (the same in every quarter),
+  // loaded now so that its latency hides behind the main loop
+  float4 bpre[4];
+  if constexpr (NORM) {
+    const int c = threadIdx.x % FB, jp = nb0 / 2 + (c >> 1), hf = c & 1;
+    const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;
+    bpre[0] = *reinterpret_cast<const float4*>(p.bias + c0);
+    bpre[1] = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
+    bpre[2] = *reinterpret_cast<const float4*>(p.bias + c1);
+    bpre[3] = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
+  }
 
   f32x16 acc[TR][TC];
 #pragma unroll
@@ -998,7 +1014,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
             ct[(r * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
     }
     __syncthreads();
-    tile_epilogue<QR, BN, CS, 256, EPI, D, F>(p, ct, srstd + qt * QR, mb0 + qt * (QR / 16), nb0);
+    tile_epilogue<QR, BN, CS, 256, EPI, D, F>(p, ct, srstd + qt * QR, mb0 + qt * (QR / 16), nb0,
+                                              NORM ? bpre : nullptr);
     __syncthreads();
   }
 }
