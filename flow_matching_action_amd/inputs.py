@@ -31,6 +31,12 @@ Draw recipe (stated here so that any reader can regenerate it):
     ffn_norm, gate, up, down as above (norm scales 1 + N(0, 0.02)); the prefix
     sequence (image and prompt embeddings after their sqrt(2048) scaling)
     seed 4, [batch][prefix_len][2048] N(0, 1) rounded to bf16.
+  * the vision encoder (Realtime-VLA blog, "pi0.5 inference flow" and
+    "LeRobot implementation": SigLIP, 27 layers, 224x224 -> 256 tokens, width
+    1152, projector 1152 -> 2048): weights seed 5 in the order of
+    vision_weight_shapes, N(0, 0.02) (LayerNorm scales 1 + N(0, 0.02), their
+    biases N(0, 0.02)); images seed 6, [views][224][224][3] uniform in
+    [-1, 1) rounded to bf16.
 """
 from __future__ import annotations
 
@@ -47,6 +53,7 @@ __all__ = [
     "weight_shapes",
     "PrefillConfig", "PrefillWorkload", "PREFILL_WORKLOADS", "prefill_weight_shapes",
     "make_prefill_weights", "make_prefix_embeddings",
+    "VisionConfig", "vision_weight_shapes", "make_vision_weights", "make_images",
 ]
 
 
@@ -305,3 +312,58 @@ def make_prefix_embeddings(cfg: PrefillConfig, batch: int, prefix_len: int, seed
     """The prefix sequence, bf16 bits [batch][prefix_len][width] ~ N(0, 1)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return f32_to_bf16_bits(rng.standard_normal((batch, prefix_len, cfg.width), dtype=np.float32))
+
+
+# ---------------------------------------------------------------- vision encoder
+@dataclass(frozen=True)
+class VisionConfig:
+    """Shape of the SigLIP-shaped vision encoder (one view: 256 patch tokens)."""
+    num_layers: int = 27
+    width: int = 1152
+    mlp_dim: int = 4304
+    num_heads: int = 16
+    head_dim: int = 72
+    patch: int = 14
+    image: int = 224
+    channels: int = 3
+    out_width: int = 2048
+    ln_eps: float = 1e-6
+
+    def replace(self, **kw) -> "VisionConfig":
+        return dataclasses.replace(self, **kw)
+
+
+def vision_weight_shapes(cfg: VisionConfig):
+    """(name, shape) in draw order; nn.Linear layout [out][in], convolution [out][c][y][x]."""
+    D, F, P, C = cfg.width, cfg.mlp_dim, cfg.patch, cfg.channels
+    n = (cfg.image // P) ** 2
+    out = [("patch.w", (D, C, P, P)), ("patch.b", (D,)), ("pos", (n, D))]
+    for l in range(cfg.num_layers):
+        p = f"layers.{l}."
+        out += [(p + "ln1.w", (D,)), (p + "ln1.b", (D,)),
+                (p + "q.w", (D, D)), (p + "q.b", (D,)), (p + "k.w", (D, D)), (p + "k.b", (D,)),
+                (p + "v.w", (D, D)), (p + "v.b", (D,)), (p + "o.w", (D, D)), (p + "o.b", (D,)),
+                (p + "ln2.w", (D,)), (p + "ln2.b", (D,)),
+                (p + "fc1.w", (F, D)), (p + "fc1.b", (F,)), (p + "fc2.w", (D, F)), (p + "fc2.b", (D,))]
+    out += [("post_ln.w", (D,)), ("post_ln.b", (D,)), ("proj.w", (cfg.out_width, D)), ("proj.b", (cfg.out_width,))]
+    return out
+
+
+def make_vision_weights(cfg: VisionConfig, seed: int = 5, std: float = 0.02) -> dict:
+    """Vision-encoder weights as bf16 bit patterns (a fresh dict)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, shape in vision_weight_shapes(cfg):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        x *= np.float32(std)
+        if name.endswith("ln1.w") or name.endswith("ln2.w") or name == "post_ln.w":
+            x += np.float32(1.0)
+        out[name] = f32_to_bf16_bits(x)
+    return out
+
+
+def make_images(cfg: VisionConfig, views: int, seed: int = 6) -> np.ndarray:
+    """bf16 bits [views][image][image][channels], uniform in [-1, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.random((views, cfg.image, cfg.image, cfg.channels), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    return f32_to_bf16_bits(x)
