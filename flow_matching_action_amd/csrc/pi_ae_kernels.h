@@ -25,6 +25,23 @@ constexpr int kVD = 2048;             // width
 constexpr int kVF = 16384;            // MLP dim
 constexpr int kVNgu = 2 * kVF;        // fused gate|up width, 32768
 
+// The SigLIP-shaped vision encoder (Realtime-VLA technical blog, "pi0.5
+// inference flow" and "LeRobot implementation": 27 layers, 224x224 -> 256
+// tokens, width 1152, projector 1152 -> 2048).  GEMM operands are padded to
+// whole 256-wide k-blocks with zeros: width inputs 1152 -> 1280, the MLP
+// hidden 4304 -> 4352 columns (fc1 output) / 4608 (fc2 input), the patch
+// vectors 3 x 14 x 14 = 588 -> 768.
+constexpr int kSD = 1152;             // width
+constexpr int kSF = 4304;             // MLP dim
+constexpr int kSFn = 4352;            // fc1 output columns (padded N)
+constexpr int kSFk = 4608;            // fc2 input columns (padded K) = MLP operand stride
+constexpr int kSKp = 1280;            // padded K of the width-input GEMMs
+constexpr int kSH = 16, kSHd = 72;    // heads x head dim
+constexpr int kSPatch = 14, kSImg = 224, kSC = 3;
+constexpr int kSTok = (kSImg / kSPatch) * (kSImg / kSPatch);  // 256 tokens per view
+constexpr int kSKpatch = 768;         // padded patch vector (588)
+constexpr int kSOut = 2048;           // projector output (the VLM width)
+
 // Per-call pointers, written by the args kernel into a device block that the
 // captured graph reads, so that one graph serves every call.
 struct DevArgs {
@@ -113,6 +130,10 @@ struct GemmParams {
   // [M][256], the cache the expert reads (null: not written)
   uint16_t* k_cache;
   uint16_t* v_cache;
+  // vision epilogues: the position embedding [256][1152] fp32 (patch
+  // embedding); their natural bf16 outputs go to q_out (Q|K|V [M][3456],
+  // projector [M][2048]), the MLP operand to m_out, the residual to h_out
+  const float* aux;
 };
 
 struct AttnParams {
@@ -164,6 +185,32 @@ struct VlmStageParams {
   int B, P, nkb;
 };
 
+// Vision encoder, per call: the patch vectors of every view (im2col of the
+// 14x14x3 patches, (channel, y, x) order, zero-padded to 768) as the patch
+// GEMM's fragment-major operand.
+struct VisPatchParams {
+  const uint16_t* images;  // [V][224][224][3] bf16
+  uint16_t* a;             // fragment-major [Mpad/16][768/32][64][8]
+  int V;
+};
+// LayerNorm of the residual stream into a GEMM operand: u = (h - mean) /
+// sqrt(var + eps) * w + b, bf16, fragment-major [Mpad/16][1280/32][64][8]
+// (columns 1152.. stay zero).
+struct VisLnParams {
+  const float* h;          // [Mpad][1152]
+  const float* w;          // [1152]
+  const float* b;          // [1152]
+  uint16_t* u;
+  float eps;
+  int M;
+};
+// Attention of one view's 256 tokens, 16 heads x 72, all keys valid.
+struct VisAttnParams {
+  const uint16_t* qkv;     // [M][3456] natural: q | k | v, head h at columns 72h..
+  uint16_t* o;             // fragment-major [Mpad/16][1280/32][64][8]
+  int V;
+};
+
 struct ArgsParams {
   DevArgs* da;
   DevArgs vals;
@@ -201,6 +248,15 @@ hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTimin
 hipError_t launch_vlm_o(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_vlm_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_vlm_down(const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t = nullptr);
+
+// vision encoder (tiled GEMMs with the vision epilogues; which: 0 patch
+// embedding, 1 QKV, 2 O + residual, 3 fc1 + GELU, 4 fc2 + residual, 5
+// projector).  S > 1 splits K (fc2 only).
+hipError_t launch_vis_patch(const VisPatchParams& p, hipStream_t s);
+hipError_t launch_vis_ln(const VisLnParams& p, hipStream_t s);
+hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s,
+                           const KernelTiming* t = nullptr);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

@@ -310,7 +310,14 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
 //   E_GELU: * 1/rms, + shift-fold bias, m = GELU(gate) * up, fragment-major.
 //   E_RES:  h += acc * gate; when the next consumer is a normalised GEMM also
 //           its operand bf16(h * (1 + scale_next)) and the h^2 partials.
-enum { E_QKV = 0, E_GELU = 1, E_RES = 2, E_KV = 3 };
+//   vision encoder (bias on every linear, norms by a separate LayerNorm
+//   kernel): E_VPATCH h = acc + b + pos; E_VQKV natural bf16 acc + b;
+//   E_VGELU the MLP operand bf16(GELU(acc + b)); E_VRES h += acc + b;
+//   E_VPROJ natural bf16 (acc + b) * sqrt(2048).
+enum { E_QKV = 0, E_GELU = 1, E_RES = 2, E_KV = 3, E_VPATCH = 4, E_VQKV = 5, E_VGELU = 6, E_VRES = 7, E_VPROJ = 8 };
+// epilogues whose input is an RMS-normalised operand (1/rms from the h^2 partials)
+constexpr bool epi_norm(int e) { return e == E_QKV || e == E_GELU || e == E_KV; }
+constexpr bool epi_vision(int e) { return e >= E_VPATCH; }
 constexpr int kSsqTiles = kD / 16;  // partial sums of squares per row
 
 template <int MB, int NB, int NW, int KBW, int EPI, bool AM = false>
@@ -634,6 +641,53 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
         }
       }
     }
+  } else if constexpr (epi_vision(EPI)) {
+    // chunk = (row, 8 consecutive columns); D = the residual width, F = the
+    // MLP operand's K stride
+    constexpr int CPR = BN / 8, NP = BM * CPR / NT, PB = NP < 8 ? NP : 8;
+    static_assert(NT % CPR == 0 && NP % PB == 0, "pass-invariant columns, whole batches");
+    const int c8 = threadIdx.x % CPR, col = nb0 * 16 + c8 * 8;
+    const float4 b0 = *reinterpret_cast<const float4*>(p.bias + col);
+    const float4 b1 = *reinterpret_cast<const float4*>(p.bias + col + 4);
+    for (int pb = 0; pb < NP; pb += PB) {
+      float4 x0[PB], x1[PB];  // residual (E_VRES) or position embedding (E_VPATCH) of the batch's rows
+      if constexpr (EPI == E_VRES || EPI == E_VPATCH) {
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+          const int row = mb0 * 16 + (pb + q) * (NT / CPR) + threadIdx.x / CPR, rr = row < p.M ? row : 0;
+          const float* src = EPI == E_VRES ? p.h_out + size_t(rr) * D + col : p.aux + size_t(rr % kSTok) * D + col;
+          x0[q] = *reinterpret_cast<const float4*>(src);
+          x1[q] = *reinterpret_cast<const float4*>(src + 4);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int rl = (pb + q) * (NT / CPR) + threadIdx.x / CPR, row = mb0 * 16 + rl;
+        const float4 a0 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&ct[rl * CS + c8 * 8 + 4]);
+        float y[8] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w, a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
+        if (row >= p.M) continue;
+        if constexpr (EPI == E_VRES || EPI == E_VPATCH) {
+          float* dst = p.h_out + size_t(row) * D + col;
+          *reinterpret_cast<float4*>(dst) = make_float4(x0[q].x + y[0], x0[q].y + y[1], x0[q].z + y[2], x0[q].w + y[3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(x1[q].x + y[4], x1[q].y + y[5], x1[q].z + y[6], x1[q].w + y[7]);
+        } else {
+          if constexpr (EPI == E_VGELU) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = gelu_tanh(y[e]);
+          }
+          if constexpr (EPI == E_VPROJ) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= 45.254833995939045f;  // sqrt(2048)
+          }
+          const uint4 v = __builtin_bit_cast(uint4, pack8(make_float4(y[0], y[1], y[2], y[3]), make_float4(y[4], y[5], y[6], y[7])));
+          if constexpr (EPI == E_VGELU)
+            *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, col, F / 32)) = v;
+          else
+            *reinterpret_cast<uint4*>(p.q_out + size_t(row) * (EPI == E_VQKV ? 3 * D : kSOut) + col) = v;
+        }
+      }
+    }
   } else {
     // chunk = (row, pair pp of n-blocks 2pp / 2pp+1, half hf: columns 8hf..8hf+7 of each)
     constexpr int CPR = FB, NP = BM * CPR / NT, PB = NP < 4 ? NP : 4;  // pairs per tile row (FB / 2) x 2 halves
@@ -775,7 +829,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
   constexpr int BM = 16 * FA, BN = 16 * FB;
   constexpr int FBS = FB * KS;                  // B fragments per stage
   constexpr int BPW = FBS / NW;                 // B fragments copied per wave and stage
-  constexpr bool NORM = EPI != E_RES;
+  constexpr bool NORM = epi_norm(EPI);
   static_assert(FBS % NW == 0, "stage B fragments split evenly over the waves");
   constexpr int CS = BN + 4;
   constexpr int kStFloats = 2 * FBS * 64 * 4, kCtFloats = BM * CS;
@@ -908,7 +962,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
 template <int EPI, int D, int F>
 __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   constexpr int TR = 2, TC = 4, BM = 256, BN = 128, FB = BN / 16, CS = BN + 4, QR = 64;
-  constexpr bool NORM = EPI != E_RES;
+  constexpr bool NORM = epi_norm(EPI);
   __shared__ __attribute__((aligned(16))) u32x4 ring0[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring1[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring2[FB][64];
@@ -1052,7 +1106,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmParams p, const float
     const int idx = threadIdx.x + q * NT, r = idx / (BN / 4), c4 = idx % (BN / 4);
     *reinterpret_cast<float4*>(&ct[r * CS + c4 * 4]) = v[q];
   }
-  if constexpr (EPI != E_RES) tile_rstd<BM, NT, D>(p, srstd, mb0);
+  if constexpr (epi_norm(EPI)) tile_rstd<BM, NT, D>(p, srstd, mb0);
   __syncthreads();
   tile_epilogue<BM, BN, CS, NT, EPI, D, F>(p, ct, srstd, mb0, nbl + (EPI == E_KV ? 128 : 0));
 }
@@ -1742,6 +1796,223 @@ hipError_t launch_vlm_attn(const AttnParams& p, hipStream_t s, const KernelTimin
     return go(k_attn_rows32<kAttn32Groups, false>, dim3(8 * groups * per_ep), dim3(kAttn32Groups * 2 * 64), s, t, p);
   }
   return go(k_attn<1>, dim3((p.T * kH + 15) / 16, p.B), dim3(kAttnWaves * 64), s, t, p);
+}
+
+// ---------------------------------------------------------------------------
+// Vision encoder (SigLIP-shaped: 14x14 patches of a 224x224 view, 27 pre-norm
+// LayerNorm layers, 16 heads x 72, MLP 4304, projector 1152 -> 2048; the
+// blog's "pi0.5 inference flow" and "LeRobot implementation").
+
+// Patch vectors: one workgroup per token row (view v, patch py, px); element
+// k = c*196 + y*14 + x of its vector is pixel (14 py + y, 14 px + x), channel c
+// (the order of a convolution weight [out][c][y][x]); 588..767 are zero.
+__global__ __launch_bounds__(128) void k_vis_patch(VisPatchParams p) {
+  const int row = blockIdx.x, v = row / kSTok, t = row % kSTok, py = t / 16, px = t % 16;
+  const int c8 = threadIdx.x;  // 8 consecutive k per thread, 96 chunks
+  if (c8 >= kSKpatch / 8) return;
+  const uint16_t* img = p.images + size_t(v) * kSImg * kSImg * kSC;
+  uint32_t w[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = c8 * 8 + 2 * e2 + h;
+      uint32_t val = 0;
+      if (k < kSC * kSPatch * kSPatch) {
+        const int c = k / (kSPatch * kSPatch), y = (k / kSPatch) % kSPatch, x = k % kSPatch;
+        val = img[(size_t(py * kSPatch + y) * kSImg + px * kSPatch + x) * kSC + c];
+      }
+      pair |= val << (16 * h);
+    }
+    w[e2] = pair;
+  }
+  *reinterpret_cast<uint4*>(p.a + afrag_index(row, c8 * 8, kSKpatch / 32)) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+hipError_t launch_vis_patch(const VisPatchParams& p, hipStream_t s) {
+  if (p.V <= 0) return hipSuccess;
+  k_vis_patch<<<p.V * kSTok, 128, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// LayerNorm, one workgroup (4 waves) per token row: 144 threads hold 8
+// values each; mean, then the variance about it (two passes over registers,
+// fp32); the bf16 operand in the GEMM's fragment-major layout.
+__global__ __launch_bounds__(256) void k_vis_ln(VisLnParams p) {
+  __shared__ float red[2][4];
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bool act = t < kSD / 8;
+  float x[8];
+  if (act) {
+    const float4 a = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t);
+    const float4 b = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  float s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s1 += x[e];
+  s1 = wave_sum(s1);
+  if (lane == 0) red[0][w] = s1;
+  __syncthreads();
+  const float mean = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) * (1.f / kSD);
+  float s2 = 0.f;
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s2 += (x[e] - mean) * (x[e] - mean);
+  }
+  s2 = wave_sum(s2);
+  if (lane == 0) red[1][w] = s2;
+  __syncthreads();
+  const float rstd = 1.f / sqrtf((red[1][0] + red[1][1] + red[1][2] + red[1][3]) * (1.f / kSD) + p.eps);
+  if (!act) return;
+  const float4 g0 = *reinterpret_cast<const float4*>(p.w + 8 * t), g1 = *reinterpret_cast<const float4*>(p.w + 8 * t + 4);
+  const float4 c0 = *reinterpret_cast<const float4*>(p.b + 8 * t), c1 = *reinterpret_cast<const float4*>(p.b + 8 * t + 4);
+  const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w}, cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (x[e] - mean) * rstd * gg[e] + cc[e];
+  *reinterpret_cast<uint4*>(p.u + afrag_index(row, 8 * t, kSKp / 32)) = __builtin_bit_cast(
+      uint4, pack8(make_float4(y[0], y[1], y[2], y[3]), make_float4(y[4], y[5], y[6], y[7])));
+}
+
+hipError_t launch_vis_ln(const VisLnParams& p, hipStream_t s) {
+  if (p.M <= 0) return hipSuccess;
+  k_vis_ln<<<p.M, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// Attention of one view's 256 tokens for one head and 64 queries (grid: 4
+// query blocks x 16 heads x views; 4 waves of 16 queries).  The head's K
+// ([key][dim], dims 72..95 zero) and V^T ([dim][key]) are staged in LDS once
+// per workgroup; each wave computes its 16 x 256 scores on 16x16x32 MFMAs
+// (head dim padded to 96 with zeros in Q), takes the exact softmax over all
+// 256 keys in fp32 (no mask: every patch is valid), passes the probabilities
+// through LDS into the A-operand order and contracts them with V (head dim
+// padded to 80; the pad columns are not stored).
+constexpr int kSKs = 104, kSVs = 264, kSPs = 264;  // LDS row strides (bf16), staggered banks
+__global__ __launch_bounds__(256) void k_vis_attn(VisAttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kSTok * kSKs];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[80 * kSVs];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[4 * 16 * kSPs];
+  const int qb = blockIdx.x, hh = blockIdx.y, v = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const size_t rs = 3 * kSD;  // q|k|v row stride
+  const uint16_t* base = p.qkv + size_t(v) * kSTok * rs;
+  // stage K (9 chunks of 8 dims per key, then 3 zero chunks) and V^T
+  for (int i = t; i < kSTok * 9; i += 256) {
+    const int key = i / 9, c = i % 9;
+    const uint4 kv = *reinterpret_cast<const uint4*>(base + size_t(key) * rs + kSD + hh * kSHd + 8 * c);
+    *reinterpret_cast<uint4*>(&ks[key * kSKs + 8 * c]) = kv;
+    const uint4 vv = *reinterpret_cast<const uint4*>(base + size_t(key) * rs + 2 * kSD + hh * kSHd + 8 * c);
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[(8 * c + e) * kSVs + key] = uint16_t(vw[e >> 1] >> (16 * (e & 1)));
+  }
+  for (int i = t; i < kSTok * 3; i += 256)
+    *reinterpret_cast<uint4*>(&ks[(i / 3) * kSKs + kSHd + 8 * (i % 3)]) = make_uint4(0, 0, 0, 0);
+  // this wave's Q as A operands: lane l, row l%16, dims 32kc + 8(l/16) .. +7 (zero past 72)
+  const int q0 = qb * 64 + w * 16;
+  bf16x8 qf[3];
+#pragma unroll
+  for (int kc = 0; kc < 3; ++kc) {
+    const int d0 = 32 * kc + 8 * (lane >> 4);
+    qf[kc] = as_bf(d0 < kSHd ? *reinterpret_cast<const uint4*>(base + size_t(q0 + (lane & 15)) * rs + hh * kSHd + d0)
+                             : make_uint4(0, 0, 0, 0));
+  }
+  __syncthreads();
+  // scores: tile nt holds S[4(l/16) + i][16 nt + l%16]
+  f32x4 sc[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) {
+    sc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 3; ++kc)
+      sc[nt] = mfma(qf[kc], as_bf(*reinterpret_cast<const uint4*>(&ks[(16 * nt + (lane & 15)) * kSKs + 32 * kc + 8 * (lane >> 4)])), sc[nt]);
+  }
+  const float scl = 1.4426950408889634f / 8.48528137423857f;  // log2(e) / sqrt(72)
+  float mx[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) m = fmaxf(m, sc[nt][i]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    mx[i] = m;
+    sm[i] = 0.f;
+  }
+  uint16_t* pw = ps + w * 16 * kSPs;
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = exp2f((sc[nt][i] - mx[i]) * scl);
+      sm[i] += pv;
+      pw[(4 * (lane >> 4) + i) * kSPs + 16 * nt + (lane & 15)] = f2bf(pv);
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sm[i] += __shfl_xor(sm[i], o);
+  __syncthreads();
+  // O = P V over 8 chunks of 32 keys, 5 tiles of 16 dims
+  f32x4 oc[5];
+#pragma unroll
+  for (int dt = 0; dt < 5; ++dt) oc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const bf16x8 a = as_bf(*reinterpret_cast<const uint4*>(&pw[(lane & 15) * kSPs + 32 * kc + 8 * (lane >> 4)]));
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt)
+      oc[dt] = mfma(a, as_bf(*reinterpret_cast<const uint4*>(&vt[(16 * dt + (lane & 15)) * kSVs + 32 * kc + 8 * (lane >> 4)])), oc[dt]);
+  }
+  // normalise and store O[row][72 hh + dim] into the O projection's operand
+#pragma unroll
+  for (int dt = 0; dt < 5; ++dt) {
+    const int dim = 16 * dt + (lane & 15);
+    if (dim >= kSHd) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = v * kSTok + q0 + 4 * (lane >> 4) + i;
+      p.o[afrag_index(row, hh * kSHd + dim, kSKp / 32)] = f2bf(oc[dt][i] / sm[i]);
+    }
+  }
+}
+
+hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.V <= 0) return hipSuccess;
+  return go(k_vis_attn, dim3(kSTok / 64, kSH, p.V), dim3(256), s, t, p);
+}
+
+// which: 0 patch embedding (K 768), 1 QKV (N 3456), 2 O + residual, 3 fc1 +
+// GELU (N 4352), 4 fc2 + residual (K 4608), 5 projector (N 2048); tiles
+// 128 x 64; with S > 1 the K ranges' partial tiles and the reduce kernel.
+template <int EPI>
+static hipError_t vis_gemm(const GemmParams& p, int ncols, int K, int S, float* part, hipStream_t s,
+                           const KernelTiming* t) {
+  const dim3 grid(ncols / 64, row_tiles(p.M, 128), S);
+  if (S <= 1) return go(k_gemm_big32<4, 1, 2, EPI, kSD, kSFk>, grid, dim3(256), s, t, p, K, (float*)nullptr);
+  const KernelTiming t0{t ? t->start : nullptr, nullptr}, t1{nullptr, t ? t->stop : nullptr};
+  hipError_t e = go(k_gemm_big32<4, 1, 2, EPI, kSD, kSFk, true>, grid, dim3(256), s, t ? &t0 : nullptr, p, K, part);
+  if (e != hipSuccess) return e;
+  const int Mp = int(grid.y) * 128;
+  return go(k_splitk_reduce<64, 64, EPI, kSD, kSFk>, dim3(ncols / 64, Mp / 64), dim3(256), s, t ? &t1 : nullptr, p,
+            (const float*)part, S, Mp, ncols);
+}
+hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t) {
+  switch (which) {
+    case 0: return vis_gemm<E_VPATCH>(p, kSD, kSKpatch, S, part, s, t);
+    case 1: return vis_gemm<E_VQKV>(p, 3 * kSD, kSKp, S, part, s, t);
+    case 2: return vis_gemm<E_VRES>(p, kSD, kSKp, S, part, s, t);
+    case 3: return vis_gemm<E_VGELU>(p, kSFn, kSKp, S, part, s, t);
+    case 4: return vis_gemm<E_VRES>(p, kSD, kSFk, S, part, s, t);
+    case 5: return vis_gemm<E_VPROJ>(p, kSOut, kSKp, S, part, s, t);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pack(const PackParams& p, int L, hipStream_t s) {

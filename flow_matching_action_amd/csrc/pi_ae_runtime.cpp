@@ -1466,3 +1466,387 @@ PI_AE_API void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe) {
   }
   delete pipe;
 }
+
+// ====================================================================== vision encoder
+struct pi_ae_vision {
+  pi_ae_vision_config cfg{};
+  int device = 0;
+  bool broken = false;
+  std::vector<void*> allocs;
+  // prepared weights (device, swizzled, K padded with zero columns)
+  uint16_t *w_patch = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_fc1 = nullptr, *w_fc2 = nullptr,
+           *w_proj = nullptr;
+  float *b_patch = nullptr, *pos = nullptr, *b_qkv = nullptr, *b_o = nullptr, *b_fc1 = nullptr, *b_fc2 = nullptr,
+        *b_proj = nullptr, *ln1_w = nullptr, *ln1_b = nullptr, *ln2_w = nullptr, *ln2_b = nullptr,
+        *post_w = nullptr, *post_b = nullptr;
+  // workspaces
+  uint16_t *apatch = nullptr, *u = nullptr, *qkv = nullptr, *o = nullptr, *m = nullptr;
+  float *h = nullptr, *part = nullptr;
+  int Mpad = 0;
+  hipStream_t cap = nullptr;
+  std::map<int, hipGraphExec_t> graphs;
+
+  template <class T>
+  T* dalloc(size_t n) {
+    void* p = nullptr;
+    if (n == 0) n = 1;
+    hipError_t e = hipMalloc(&p, n * sizeof(T));
+    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
+    allocs.push_back(p);
+    return static_cast<T*>(p);
+  }
+  void release() {
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
+    graphs.clear();
+    for (void* p : allocs) (void)hipFree(p);
+    allocs.clear();
+    if (cap) (void)hipStreamDestroy(cap);
+    cap = nullptr;
+  }
+};
+
+namespace {
+
+// fc2 splits K (4608 = 2 x 2304) in two: its 18 column tiles alone would
+// leave most CUs idle at a few views; the other K (1280, 768) are odd
+// multiples of 256 and stay whole.
+constexpr int kVisFc2Split = 2;
+
+pi_ae_status vis_check_config(const pi_ae_vision_config* c) {
+  if (c->width != kSD || c->mlp_dim != kSF || c->num_heads != kSH || c->head_dim != kSHd || c->patch != kSPatch ||
+      c->image != kSImg || c->out_width != kSOut)
+    return fail(PI_AE_EUNSUPPORTED,
+                "the vision kernels implement width 1152, mlp_dim 4304, 16 heads x 72, patch 14, image 224, out 2048");
+  if (c->num_layers < 1 || c->num_layers > 64) return fail(PI_AE_EINVAL, "num_layers must be in [1, 64]");
+  if (c->max_views < 1 || c->max_views > 64) return fail(PI_AE_EINVAL, "max_views must be in [1, 64]");
+  if (!(c->ln_eps > 0.f)) return fail(PI_AE_EINVAL, "ln_eps must be > 0");
+  return PI_AE_OK;
+}
+
+pi_ae_status vis_check_weights(const pi_ae_vision_config* c, const pi_ae_vision_weights* w) {
+  if (!w->patch_w || !w->patch_b || !w->pos || !w->layers || !w->post_ln_w || !w->post_ln_b || !w->proj_w || !w->proj_b)
+    return fail(PI_AE_EINVAL, "a vision weight pointer is NULL");
+  for (int l = 0; l < c->num_layers; ++l) {
+    const pi_ae_vision_layer_weights& L = w->layers[l];
+    const uint16_t* ps[] = {L.ln1_w, L.ln1_b, L.q_w, L.q_b, L.k_w, L.k_b, L.v_w, L.v_b, L.o_w, L.o_b,
+                            L.ln2_w, L.ln2_b, L.fc1_w, L.fc1_b, L.fc2_w, L.fc2_b};
+    for (const uint16_t* q : ps)
+      if (!q) return fail(PI_AE_EINVAL, "vision layer " + std::to_string(l) + ": a weight pointer is NULL");
+  }
+  return PI_AE_OK;
+}
+
+// W [N][K] -> [Np][Kp] with zero rows / columns past N / K
+std::vector<uint16_t> pad2(const uint16_t* W, int N, int K, int Np, int Kp) {
+  std::vector<uint16_t> out(size_t(Np) * Kp, 0);
+  for (int n = 0; n < N; ++n) std::memcpy(out.data() + size_t(n) * Kp, W + size_t(n) * K, size_t(K) * 2);
+  return out;
+}
+
+std::vector<float> to_f32(const uint16_t* b, int n, int npad) {
+  std::vector<float> out(npad, 0.f);
+  for (int i = 0; i < n; ++i) out[i] = float(bf(b[i]));
+  return out;
+}
+
+void vis_prepare(pi_ae_vision* ctx, const pi_ae_vision_weights* w) {
+  const int L = ctx->cfg.num_layers;
+  auto ident = [](int n) {
+    std::vector<int> p(n);
+    for (int i = 0; i < n; ++i) p[i] = i;
+    return p;
+  };
+  auto upload16 = [&](const std::vector<uint16_t>& v, uint16_t* dst) {
+    HIP_OR_THROW(hipMemcpy(dst, v.data(), v.size() * 2, hipMemcpyHostToDevice));
+  };
+  auto swz = [&](const uint16_t* W, int N, int K, int Np, int Kp, uint16_t* dst) {
+    const std::vector<uint16_t> padded = pad2(W, N, K, Np, Kp);
+    std::vector<uint16_t> sw(padded.size());
+    swizzle(padded.data(), Kp, ident(Np), sw.data());
+    upload16(sw, dst);
+  };
+  const int kpv = kSC * kSPatch * kSPatch;  // 588
+  const size_t n_qkv = size_t(3 * kSD) * kSKp, n_o = size_t(kSD) * kSKp, n_fc1 = size_t(kSFn) * kSKp,
+               n_fc2 = size_t(kSD) * kSFk;
+  ctx->w_patch = ctx->dalloc<uint16_t>(size_t(kSD) * kSKpatch);
+  swz(w->patch_w, kSD, kpv, kSD, kSKpatch, ctx->w_patch);
+  ctx->w_qkv = ctx->dalloc<uint16_t>(n_qkv * L);
+  ctx->w_o = ctx->dalloc<uint16_t>(n_o * L);
+  ctx->w_fc1 = ctx->dalloc<uint16_t>(n_fc1 * L);
+  ctx->w_fc2 = ctx->dalloc<uint16_t>(n_fc2 * L);
+  std::vector<float> bqkv(size_t(L) * 3 * kSD), bo(size_t(L) * kSD), bfc1(size_t(L) * kSFn, 0.f), bfc2(size_t(L) * kSD),
+      l1w(size_t(L) * kSD), l1b(size_t(L) * kSD), l2w(size_t(L) * kSD), l2b(size_t(L) * kSD);
+  for (int l = 0; l < L; ++l) {
+    const pi_ae_vision_layer_weights& Lw = w->layers[l];
+    std::vector<uint16_t> fused(size_t(3 * kSD) * kSD);
+    std::memcpy(fused.data(), Lw.q_w, size_t(kSD) * kSD * 2);
+    std::memcpy(fused.data() + size_t(kSD) * kSD, Lw.k_w, size_t(kSD) * kSD * 2);
+    std::memcpy(fused.data() + size_t(2 * kSD) * kSD, Lw.v_w, size_t(kSD) * kSD * 2);
+    swz(fused.data(), 3 * kSD, kSD, 3 * kSD, kSKp, ctx->w_qkv + n_qkv * l);
+    swz(Lw.o_w, kSD, kSD, kSD, kSKp, ctx->w_o + n_o * l);
+    swz(Lw.fc1_w, kSF, kSD, kSFn, kSKp, ctx->w_fc1 + n_fc1 * l);
+    swz(Lw.fc2_w, kSD, kSF, kSD, kSFk, ctx->w_fc2 + n_fc2 * l);
+    for (int i = 0; i < kSD; ++i) {
+      bqkv[size_t(l) * 3 * kSD + i] = float(bf(Lw.q_b[i]));
+      bqkv[size_t(l) * 3 * kSD + kSD + i] = float(bf(Lw.k_b[i]));
+      bqkv[size_t(l) * 3 * kSD + 2 * kSD + i] = float(bf(Lw.v_b[i]));
+      bo[size_t(l) * kSD + i] = float(bf(Lw.o_b[i]));
+      bfc2[size_t(l) * kSD + i] = float(bf(Lw.fc2_b[i]));
+      l1w[size_t(l) * kSD + i] = float(bf(Lw.ln1_w[i]));
+      l1b[size_t(l) * kSD + i] = float(bf(Lw.ln1_b[i]));
+      l2w[size_t(l) * kSD + i] = float(bf(Lw.ln2_w[i]));
+      l2b[size_t(l) * kSD + i] = float(bf(Lw.ln2_b[i]));
+    }
+    for (int i = 0; i < kSF; ++i) bfc1[size_t(l) * kSFn + i] = float(bf(Lw.fc1_b[i]));
+  }
+  ctx->w_proj = ctx->dalloc<uint16_t>(size_t(kSOut) * kSKp);
+  swz(w->proj_w, kSOut, kSD, kSOut, kSKp, ctx->w_proj);
+  auto upload = [&](const std::vector<float>& v) {
+    float* d = ctx->dalloc<float>(v.size());
+    HIP_OR_THROW(hipMemcpy(d, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+    return d;
+  };
+  ctx->b_patch = upload(to_f32(w->patch_b, kSD, kSD));
+  ctx->pos = upload(to_f32(w->pos, kSTok * kSD, kSTok * kSD));
+  ctx->b_qkv = upload(bqkv);
+  ctx->b_o = upload(bo);
+  ctx->b_fc1 = upload(bfc1);
+  ctx->b_fc2 = upload(bfc2);
+  ctx->ln1_w = upload(l1w);
+  ctx->ln1_b = upload(l1b);
+  ctx->ln2_w = upload(l2w);
+  ctx->ln2_b = upload(l2b);
+  ctx->post_w = upload(to_f32(w->post_ln_w, kSD, kSD));
+  ctx->post_b = upload(to_f32(w->post_ln_b, kSD, kSD));
+  ctx->b_proj = upload(to_f32(w->proj_b, kSOut, kSOut));
+  // workspaces; zeroed once: padded operand columns are never written
+  const size_t Mmax = size_t(ctx->cfg.max_views) * kSTok;
+  ctx->Mpad = int((Mmax + 255) / 256 * 256);
+  const size_t Mp = size_t(ctx->Mpad);
+  ctx->apatch = ctx->dalloc<uint16_t>(Mp * kSKpatch);
+  ctx->h = ctx->dalloc<float>(Mp * kSD);
+  ctx->u = ctx->dalloc<uint16_t>(Mp * kSKp);
+  ctx->qkv = ctx->dalloc<uint16_t>(Mp * 3 * kSD);
+  ctx->o = ctx->dalloc<uint16_t>(Mp * kSKp);
+  ctx->m = ctx->dalloc<uint16_t>(Mp * kSFk);
+  ctx->part = ctx->dalloc<float>(size_t(kVisFc2Split) * Mp * kSD);
+  HIP_OR_THROW(hipMemset(ctx->apatch, 0, Mp * kSKpatch * 2));
+  HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kSD * 4));
+  HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kSKp * 2));
+  HIP_OR_THROW(hipMemset(ctx->qkv, 0, Mp * 3 * kSD * 2));
+  HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kSKp * 2));
+  HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kSFk * 2));
+  HIP_OR_THROW(hipStreamCreateWithFlags(&ctx->cap, hipStreamNonBlocking));
+  HIP_OR_THROW(hipDeviceSynchronize());
+}
+
+// Phases (numbering of pi_ae_vision_debug_time_phase): 0 patch embedding,
+// per layer 1 LayerNorm (twice), 2 QKV, 3 attention, 4 O, 5 fc1, 6 fc2; 7
+// projector.  The graph holds the patch GEMM through the final LayerNorm;
+// the patch vectors (before it) and the projector (after it) take the call's
+// pointers.
+hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed, const KernelTiming* tv,
+                              int* n_timed) {
+  const int L = ctx->cfg.num_layers, M = V * kSTok;
+  auto tm = [&](int ph) { return (tv && ph == timed) ? &tv[(*n_timed)++] : nullptr; };
+  hipError_t e;
+  GemmParams g{};
+  g.M = M;
+  g.w = ctx->w_patch;
+  g.a_frag = ctx->apatch;
+  g.bias = ctx->b_patch;
+  g.aux = ctx->pos;
+  g.h_out = ctx->h;
+  if ((e = launch_vis_gemm(0, g, 1, nullptr, s, tm(0))) != hipSuccess) return e;
+  VisLnParams ln{};
+  ln.h = ctx->h;
+  ln.u = ctx->u;
+  ln.eps = ctx->cfg.ln_eps;
+  ln.M = M;
+  const size_t n_qkv = size_t(3 * kSD) * kSKp, n_o = size_t(kSD) * kSKp, n_fc1 = size_t(kSFn) * kSKp,
+               n_fc2 = size_t(kSD) * kSFk;
+  for (int l = 0; l < L; ++l) {
+    ln.w = ctx->ln1_w + size_t(l) * kSD;
+    ln.b = ctx->ln1_b + size_t(l) * kSD;
+    {
+      const KernelTiming* t = tm(1);
+      if ((e = (t ? hipSuccess : launch_vis_ln(ln, s))) != hipSuccess) return e;
+      if (t) {  // phase 1 times the layer's first LayerNorm (the second is the same kernel)
+        if ((e = hipEventRecord(t->start, s)) != hipSuccess) return e;
+        if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
+        if ((e = hipEventRecord(t->stop, s)) != hipSuccess) return e;
+      }
+    }
+    GemmParams q{};
+    q.M = M;
+    q.w = ctx->w_qkv + n_qkv * l;
+    q.a_frag = ctx->u;
+    q.bias = ctx->b_qkv + size_t(l) * 3 * kSD;
+    q.q_out = ctx->qkv;
+    if ((e = launch_vis_gemm(1, q, 1, nullptr, s, tm(2))) != hipSuccess) return e;
+    VisAttnParams a{};
+    a.qkv = ctx->qkv;
+    a.o = ctx->o;
+    a.V = V;
+    if ((e = launch_vis_attn(a, s, tm(3))) != hipSuccess) return e;
+    GemmParams og{};
+    og.M = M;
+    og.w = ctx->w_o + n_o * l;
+    og.a_frag = ctx->o;
+    og.bias = ctx->b_o + size_t(l) * kSD;
+    og.h_out = ctx->h;
+    if ((e = launch_vis_gemm(2, og, 1, nullptr, s, tm(4))) != hipSuccess) return e;
+    ln.w = ctx->ln2_w + size_t(l) * kSD;
+    ln.b = ctx->ln2_b + size_t(l) * kSD;
+    if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
+    GemmParams f1{};
+    f1.M = M;
+    f1.w = ctx->w_fc1 + n_fc1 * l;
+    f1.a_frag = ctx->u;
+    f1.bias = ctx->b_fc1 + size_t(l) * kSFn;
+    f1.m_out = ctx->m;
+    if ((e = launch_vis_gemm(3, f1, 1, nullptr, s, tm(5))) != hipSuccess) return e;
+    GemmParams f2{};
+    f2.M = M;
+    f2.w = ctx->w_fc2 + n_fc2 * l;
+    f2.a_frag = ctx->m;
+    f2.bias = ctx->b_fc2 + size_t(l) * kSD;
+    f2.h_out = ctx->h;
+    if ((e = launch_vis_gemm(4, f2, kVisFc2Split, ctx->part, s, tm(6))) != hipSuccess) return e;
+  }
+  ln.w = ctx->post_w;
+  ln.b = ctx->post_b;
+  return launch_vis_ln(ln, s);
+}
+
+hipError_t vis_projector(pi_ae_vision* ctx, int V, uint16_t* tokens, hipStream_t s, const KernelTiming* t) {
+  GemmParams g{};
+  g.M = V * kSTok;
+  g.w = ctx->w_proj;
+  g.a_frag = ctx->u;
+  g.bias = ctx->b_proj;
+  g.q_out = tokens;
+  return launch_vis_gemm(5, g, 1, nullptr, s, t);
+}
+
+pi_ae_status vis_check_call(pi_ae_vision* ctx, const uint16_t* images, int32_t views, const uint16_t* tokens) {
+  if (!ctx) return fail(PI_AE_EINVAL, "ctx is NULL");
+  if (ctx->broken) return fail(PI_AE_ESTATE, "context is unusable after an earlier failure");
+  if (!images || !tokens) return fail(PI_AE_EINVAL, "images and tokens must be non-NULL");
+  if (((reinterpret_cast<uintptr_t>(images) | reinterpret_cast<uintptr_t>(tokens)) & 15u) != 0)
+    return fail(PI_AE_EINVAL, "images and tokens must be 16-byte aligned");
+  if (views < 1 || views > ctx->cfg.max_views)
+    return fail(PI_AE_EINVAL, "views " + std::to_string(views) + " outside [1, max_views]");
+  return PI_AE_OK;
+}
+
+}  // namespace
+
+PI_AE_API pi_ae_status pi_ae_vision_prepare(const pi_ae_vision_config* cfg, const pi_ae_vision_weights* w,
+                                            pi_ae_vision** out) {
+  if (!cfg || !w || !out) return fail(PI_AE_EINVAL, "cfg, w and out must be non-NULL");
+  pi_ae_status st = vis_check_config(cfg);
+  if (st) return st;
+  if ((st = vis_check_weights(cfg, w))) return st;
+  pi_ae_vision* ctx = new (std::nothrow) pi_ae_vision();
+  if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
+  ctx->cfg = *cfg;
+  try {
+    HIP_OR_THROW(hipGetDevice(&ctx->device));
+    vis_prepare(ctx, w);
+  } catch (const HipError& e) {
+    ctx->release();
+    delete ctx;
+    return fail(e.e == hipErrorOutOfMemory ? PI_AE_ENOMEM : PI_AE_EHIP, e.what);
+  } catch (const std::bad_alloc&) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_ENOMEM, "host allocation failed during preparation");
+  } catch (...) {
+    ctx->release();
+    delete ctx;
+    return fail(PI_AE_EHIP, "unexpected failure during preparation");
+  }
+  *out = ctx;
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_vision_encode(pi_ae_vision* ctx, const uint16_t* images, int32_t views, uint16_t* tokens,
+                                           void* stream) {
+  pi_ae_status st = vis_check_call(ctx, images, views, tokens);
+  if (st) return st;
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto it = ctx->graphs.find(views);
+  if (it == ctx->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      int n = 0;
+      hipError_t e2 = vis_enqueue_layers(ctx, views, ctx->cap, -1, nullptr, &n);
+      e = hipStreamEndCapture(ctx->cap, &graph);
+      if (e2 != hipSuccess) e = e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(views, exec).first;
+  }
+  VisPatchParams pp{images, ctx->apatch, views};
+  hipError_t e = launch_vis_patch(pp, s);
+  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e == hipSuccess) e = vis_projector(ctx, views, tokens, s, nullptr);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
+PI_AE_API void pi_ae_vision_destroy(pi_ae_vision* ctx) {
+  if (!ctx) return;
+  {
+    DeviceGuard dg(ctx->device);
+    (void)hipDeviceSynchronize();
+    ctx->release();
+  }
+  delete ctx;
+}
+
+PI_AE_API pi_ae_status pi_ae_vision_debug_time_phase(pi_ae_vision* ctx, const uint16_t* images, int32_t views,
+                                                     uint16_t* tokens, int32_t phase, int32_t reps, void* stream,
+                                                     float* avg_us) {
+  pi_ae_status st = vis_check_call(ctx, images, views, tokens);
+  if (st) return st;
+  if (phase < 0 || phase > 7 || reps < 1 || reps > 1000 || !avg_us)
+    return fail(PI_AE_EINVAL, "time_phase: phase in [0, 7], reps in [1, 1000], avg_us non-NULL");
+  DeviceGuard dg(ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = ctx->cfg.num_layers;
+  const int per = (phase == 0 || phase == 7) ? 1 : L;
+  std::vector<KernelTiming> tv(size_t(per) * reps, KernelTiming{nullptr, nullptr});
+  hipError_t e = hipSuccess;
+  for (auto& t : tv) {
+    if (e == hipSuccess) e = hipEventCreate(&t.start);
+    if (e == hipSuccess) e = hipEventCreate(&t.stop);
+  }
+  for (int r = 0; r < reps && e == hipSuccess; ++r) {
+    VisPatchParams pp{images, ctx->apatch, views};
+    e = launch_vis_patch(pp, s);
+    int n = 0;
+    if (e == hipSuccess) e = vis_enqueue_layers(ctx, views, s, phase, &tv[size_t(r) * per], &n);
+    if (e == hipSuccess) e = vis_projector(ctx, views, tokens, s, phase == 7 ? &tv[size_t(r) * per] : nullptr);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  double sum_ms = 0.0;
+  for (auto& t : tv) {
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    sum_ms += ms;
+  }
+  for (auto& t : tv) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("time_phase failed: ") + hipGetErrorString(e));
+  *avg_us = float(sum_ms * 1000.0 / double(tv.size()));
+  return PI_AE_OK;
+}

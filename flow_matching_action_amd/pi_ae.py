@@ -21,7 +21,8 @@ PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTA
 EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_status_string",
            "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
            "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
-           "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy")
+           "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy",
+           "pi_ae_vision_prepare", "pi_ae_vision_encode", "pi_ae_vision_destroy", "pi_ae_vision_debug_time_phase")
 
 
 class PiAeError(RuntimeError):
@@ -71,6 +72,25 @@ VLM_LAYER_FIELDS = ("attn_norm", "q", "k", "v", "o", "ffn_norm", "gate", "up", "
 
 class VlmLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in VLM_LAYER_FIELDS]
+
+
+class VisionConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("num_layers", "width", "mlp_dim", "num_heads", "head_dim", "patch",
+                                              "image", "out_width", "max_views")] + [("ln_eps", ctypes.c_float)]
+
+
+VISION_LAYER_FIELDS = ("ln1_w", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b", "o_w", "o_b",
+                       "ln2_w", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+
+
+class VisionLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in VISION_LAYER_FIELDS]
+
+
+class VisionWeights(ctypes.Structure):
+    _fields_ = [("patch_w", ctypes.c_void_p), ("patch_b", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(VisionLayerWeights)), ("post_ln_w", ctypes.c_void_p),
+                ("post_ln_b", ctypes.c_void_p), ("proj_w", ctypes.c_void_p), ("proj_b", ctypes.c_void_p)]
 
 
 _lib = None
@@ -127,6 +147,18 @@ def load_library(path: str = LIB_PATH):
     lib.pi_ae_pipeline_run.restype = ctypes.c_int
     lib.pi_ae_pipeline_destroy.argtypes = [ctypes.c_void_p]
     lib.pi_ae_pipeline_destroy.restype = None
+    lib.pi_ae_vision_prepare.argtypes = [ctypes.POINTER(VisionConfig), ctypes.POINTER(VisionWeights),
+                                         ctypes.POINTER(ctypes.c_void_p)]
+    lib.pi_ae_vision_prepare.restype = ctypes.c_int
+    lib.pi_ae_vision_encode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.pi_ae_vision_encode.restype = ctypes.c_int
+    lib.pi_ae_vision_destroy.argtypes = [ctypes.c_void_p]
+    lib.pi_ae_vision_destroy.restype = None
+    lib.pi_ae_vision_debug_time_phase.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                  ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_vision_debug_time_phase.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -344,3 +376,58 @@ class Pipeline:
     def run(self, emb, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
         _check(self._lib.pi_ae_pipeline_run(self._h, _ptr(emb), _ptr(pad_mask), _ptr(noise), _ptr(actions),
                                             int(batch), int(prefix_len), _stream_handle(stream)))
+
+
+def make_vision_config(cfg, max_views: int) -> VisionConfig:
+    """pi_ae_vision_config from an :class:`inputs.VisionConfig`-like object."""
+    return VisionConfig(cfg.num_layers, cfg.width, cfg.mlp_dim, cfg.num_heads, cfg.head_dim, cfg.patch, cfg.image,
+                        cfg.out_width, max_views, cfg.ln_eps)
+
+
+class _MarshalledVisionWeights:
+    """pi_ae_vision_weights pointing into host arrays kept alive by this object."""
+
+    def __init__(self, cfg, weights: dict):
+        self.keep = {n: np.ascontiguousarray(a, dtype=np.uint16) for n, a in weights.items()}
+        g = lambda n: _ptr(self.keep.get(n))
+        self.layers = (VisionLayerWeights * max(cfg.num_layers, 1))()
+        for l in range(cfg.num_layers):
+            self.layers[l] = VisionLayerWeights(
+                *[g(f"layers.{l}.{f.rsplit('_', 1)[0]}.{f.rsplit('_', 1)[1]}") for f in VISION_LAYER_FIELDS])
+        self.w = VisionWeights(g("patch.w"), g("patch.b"), g("pos"), ctypes.cast(self.layers, ctypes.POINTER(VisionLayerWeights)),
+                               g("post_ln.w"), g("post_ln.b"), g("proj.w"), g("proj.b"))
+
+
+class Vision:
+    """A prepared vision encoder (owns the library context)."""
+
+    def __init__(self, cfg, weights: dict, max_views: int):
+        lib = load_library()
+        self.cfg = cfg
+        self._c = make_vision_config(cfg, max_views)
+        mw = _MarshalledVisionWeights(cfg, weights)
+        handle = ctypes.c_void_p()
+        _check(lib.pi_ae_vision_prepare(ctypes.byref(self._c), ctypes.byref(mw.w), ctypes.byref(handle)))
+        self._h = handle
+        self._lib = lib
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.pi_ae_vision_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def encode(self, images, views: int, tokens, stream=None):
+        """Enqueue pi_ae_vision_encode: images [views][224][224][3] bf16 -> tokens [views*256][2048] bf16."""
+        _check(self._lib.pi_ae_vision_encode(self._h, _ptr(images), int(views), _ptr(tokens), _stream_handle(stream)))
+
+    def time_phase(self, images, views, tokens, phase, reps, stream=None) -> float:
+        us = ctypes.c_float()
+        _check(self._lib.pi_ae_vision_debug_time_phase(self._h, _ptr(images), int(views), _ptr(tokens), int(phase),
+                                                       int(reps), _stream_handle(stream), ctypes.byref(us)))
+        return float(us.value)

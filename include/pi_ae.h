@@ -316,6 +316,88 @@ pi_ae_status pi_ae_vlm_debug_time_phase(pi_ae_vlm* ctx, const uint16_t* prefix_e
                                         void* stream, float* avg_us);
 
 /* ------------------------------------------------------------------------
+ * The vision encoder: each camera view becomes the 256 image tokens of the
+ * VLM prefix (Realtime-VLA technical blog, "pi0.5 inference flow": SigLIP
+ * turns a 224x224 view into 256 tokens, scaled by sqrt(2048); "LeRobot
+ * implementation": a 27-layer vision tower and the multi-modal projector,
+ * Linear 1152 -> 2048).  Per view: the 14x14 patches (row by row, each in
+ * (channel, y, x) order) embedded by a strided convolution with bias, plus a
+ * learned position embedding; 27 pre-norm layers h += attn(LN1(h)) (16
+ * heads x 72, bidirectional over the 256 patches, biases on q, k, v, o),
+ * h += fc2(GELU_tanh(fc1(LN2(h)))) (MLP 4304, biases); a final LayerNorm and
+ * the projector, whose output is multiplied by sqrt(2048).  LayerNorms have a
+ * scale and a bias, eps as configured.  bf16 weights and activations, fp32
+ * accumulation and residual stream.
+ * ------------------------------------------------------------------------ */
+
+/* The kernels implement exactly width 1152, mlp_dim 4304, 16 heads x 72,
+ * patch 14, image 224, out_width 2048 (EUNSUPPORTED otherwise);
+ * 1 <= num_layers <= 64; 1 <= max_views <= 64 sizes the workspaces. */
+typedef struct pi_ae_vision_config {
+  int32_t num_layers;
+  int32_t width;
+  int32_t mlp_dim;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t patch;
+  int32_t image;
+  int32_t out_width;
+  int32_t max_views;
+  float ln_eps;
+} pi_ae_vision_config;
+
+/* One vision layer, host bf16 bit patterns, nn.Linear layout [out][in]:
+ * LayerNorm scales / biases [width]; q, k, v, o [width][width] with biases
+ * [width]; fc1 [mlp_dim][width] + [mlp_dim]; fc2 [width][mlp_dim] + [width]. */
+typedef struct pi_ae_vision_layer_weights {
+  const uint16_t *ln1_w, *ln1_b, *q_w, *q_b, *k_w, *k_b, *v_w, *v_b, *o_w, *o_b;
+  const uint16_t *ln2_w, *ln2_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+} pi_ae_vision_layer_weights;
+
+/* patch_w [width][3][patch][patch] (convolution layout) + patch_b [width];
+ * pos [256][width]; layers[num_layers]; post_ln_w / post_ln_b [width];
+ * proj_w [out_width][width] + proj_b [out_width]. */
+typedef struct pi_ae_vision_weights {
+  const uint16_t *patch_w, *patch_b, *pos;
+  const pi_ae_vision_layer_weights* layers;
+  const uint16_t *post_ln_w, *post_ln_b, *proj_w, *proj_b;
+} pi_ae_vision_weights;
+
+typedef struct pi_ae_vision pi_ae_vision;
+
+/* One-time preparation (fused q|k|v, operands padded with zero columns to
+ * whole k-blocks, weights swizzled into MFMA fragments).  Synchronous on the
+ * current device; reads the host arrays only during the call.  Errors:
+ * EINVAL, EUNSUPPORTED, ENOMEM, EHIP. */
+pi_ae_status pi_ae_vision_prepare(const pi_ae_vision_config* cfg, const pi_ae_vision_weights* w,
+                                  pi_ae_vision** out);
+
+/* Encode `views` images into their tokens.
+ *   images: device bf16 [views][224][224][3] (rows, columns, RGB), resized
+ *           and normalised, 16-byte aligned.
+ *   tokens: device bf16 [views * 256][2048], 16-byte aligned: view v's token
+ *           t at row 256 v + t, scaled by sqrt(2048) -- the image part of the
+ *           prefix sequence that pi_ae_vlm_prefill takes (an episode's prompt
+ *           tokens follow its views).
+ *   1 <= views <= max_views.  Asynchronous and stream-ordered; the layer
+ *   sequence is captured as a hipGraph per view count on first use; one call
+ *   in flight per context.  Errors: EINVAL, ESTATE, EHIP. */
+pi_ae_status pi_ae_vision_encode(pi_ae_vision* ctx, const uint16_t* images, int32_t views, uint16_t* tokens,
+                                 void* stream);
+
+/* Synchronise the context's device, then free everything it owns.  NULL is a no-op. */
+void pi_ae_vision_destroy(pi_ae_vision* ctx);
+
+/* Test-only: time one kernel of the encoder in its real sequence (as
+ * pi_ae_vlm_debug_time_phase): phase 0 = patch embedding, 1 = a layer's
+ * first LayerNorm (the second is the same kernel), 2 = QKV, 3 = attention, 4 = O + residual, 5 = fc1 +
+ * GELU, 6 = fc2 + residual, 7 = projector; `reps` whole encodes on `stream`;
+ * *avg_us = mean duration of one launch of that phase. */
+pi_ae_status pi_ae_vision_debug_time_phase(pi_ae_vision* ctx, const uint16_t* images, int32_t views,
+                                           uint16_t* tokens, int32_t phase, int32_t reps, void* stream,
+                                           float* avg_us);
+
+/* ------------------------------------------------------------------------
  * Test-only exports (unstable; used by the parity tests).
  * ------------------------------------------------------------------------ */
 

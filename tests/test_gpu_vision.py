@@ -1,0 +1,141 @@
+"""Parity of the vision encoder (HIP path, through the C-ABI) with the CPU
+oracle (oracle/vision_oracle.py), and of the whole chain vision -> VLM
+prefill -> denoise loop.
+
+Bars.  The tokens are compared with the fp64 oracle on the same seeded
+inputs.  The HIP path rounds every GEMM operand (the LayerNorm outputs, Q, K,
+V, the attention output, the MLP hidden) and the tokens to bf16; like the
+prefill's cache, the rounding of each layer is carried forward by the
+residual stream and adds up as the square root of the depth, so the bar is
+rel-L2 <= 3.5e-3 * sqrt(layers + 2) (the patch embedding and the projector
+count as one layer each) and max-abs <= 4x that times the tokens' largest
+magnitude (measured: 3.6e-3 at 2 layers, 4.5e-3 at 27 -- the pre-norm
+LayerNorms keep the growth below the bound).  The chain's final actions keep the loop's own bar (rel-L2 <= 1e-2,
+max-abs <= 5e-2).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from flow_matching_action_amd import inputs
+from flow_matching_action_amd import pi_ae
+from oracle import pi_ae_oracle as O
+from oracle import prefill_oracle as PO
+from oracle import vision_oracle as VO
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    pi_ae.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def encode(cfg, w, imgs, max_views=None):
+    V = imgs.shape[0]
+    vis = pi_ae.Vision(cfg, w, max_views or V)
+    tok = torch.empty(V * 256 * 2048, dtype=torch.int16, device="cuda")
+    vis.encode(to_dev(imgs), V, tok)
+    torch.cuda.synchronize()
+    vis.close()
+    return O.bf16_to_float(tok.cpu().numpy().view(np.uint16)).reshape(V, 256, 2048)
+
+
+def check_tokens(got, ref, layers, tag):
+    bar = 3.5e-3 * (layers + 2) ** 0.5
+    e = rel_l2(got, ref)
+    mx = float(np.max(np.abs(got - ref)))
+    amax = float(np.max(np.abs(ref)))
+    log(f"[{tag}] tokens rel_l2={e:.3e} max_abs={mx:.3e} (|ref| max {amax:.2f}; bar {bar:.2e} / {4 * bar * amax:.2e})")
+    assert np.all(np.isfinite(got))
+    assert e <= bar and mx <= 4 * bar * amax, (e, mx)
+
+
+def test_vision_reduced_three_views():
+    """2 layers at full width, 3 views (each view its own attention), and a
+    second call with 1 view on the same context."""
+    cfg = inputs.VisionConfig(num_layers=2)
+    w = inputs.make_vision_weights(cfg)
+    imgs = inputs.make_images(cfg, 3)
+    log("step: vision 2 layers, 3 views")
+    vis = pi_ae.Vision(cfg, w, 3)
+    try:
+        for V in (3, 1):
+            tok = torch.empty(V * 256 * 2048, dtype=torch.int16, device="cuda")
+            vis.encode(to_dev(imgs[:V]), V, tok)
+            torch.cuda.synchronize()
+            got = O.bf16_to_float(tok.cpu().numpy().view(np.uint16)).reshape(V, 256, 2048)
+            check_tokens(got, VO.vision_encode(w, cfg, imgs[:V]), cfg.num_layers, f"vision-2L V={V}")
+    finally:
+        vis.close()
+
+
+def test_vision_full_depth_one_view():
+    cfg = inputs.VisionConfig()
+    w = inputs.make_vision_weights(cfg)
+    imgs = inputs.make_images(cfg, 1)
+    log("step: vision 27 layers, 1 view")
+    got = encode(cfg, w, imgs)
+    check_tokens(got, VO.vision_encode(w, cfg, imgs), cfg.num_layers, "vision-27L")
+
+
+def test_vision_prefill_and_loop_chain():
+    """Images -> tokens -> VLM prefill -> 10-step loop (2 layers each), with a
+    16-token prompt after the view's 256 image tokens, against the oracle chain
+    (each model's output rounded to the bf16 format the next one takes)."""
+    vcfg = inputs.VisionConfig(num_layers=2)
+    pcfg = inputs.PrefillConfig(num_layers=2)
+    ecfg = inputs.ExpertConfig(num_layers=2)
+    vw, pw, ew = inputs.make_vision_weights(vcfg), inputs.make_prefill_weights(pcfg), inputs.make_weights(ecfg)
+    imgs = inputs.make_images(vcfg, 1)
+    P = 256 + 16
+    prompt = inputs.make_prefix_embeddings(pcfg, 1, 16, seed=13)
+    mask = inputs.make_pad_mask(1, P, P - 5)
+    noise = inputs.make_noise(ecfg, 1)
+    log("step: vision -> prefill -> loop, 2 layers each, 1 view + 16 prompt tokens")
+    vis = pi_ae.Vision(vcfg, vw, 1)
+    pf = pi_ae.Prefill(pcfg, pw, 1, P)
+    ctx = pi_ae.Context(ecfg, ew, 1, P)
+    try:
+        emb = torch.empty(P * 2048, dtype=torch.int16, device="cuda")
+        emb[256 * 2048:] = to_dev(prompt.reshape(-1))
+        vis.encode(to_dev(imgs), 1, emb)      # writes rows 0..255 of the prefix sequence
+        dmask, dnoise = to_dev(mask), to_dev(noise)
+        actions = torch.empty_like(dnoise)
+        kv = pf.run(emb, dmask, 1, P)
+        pi_ae.sample_from_cache(ctx, kv, dnoise, actions, 1)
+        torch.cuda.synchronize()
+        x = actions.cpu().numpy()
+    finally:
+        ctx.close()
+        pf.close()
+        vis.close()
+    tok = VO.vision_encode(vw, vcfg, imgs)
+    emb_ref = np.concatenate([inputs.f32_to_bf16_bits(tok.astype(np.float32)), prompt], axis=1)
+    K, V = PO.prefill(pw, pcfg, emb_ref, mask)
+    ref = O.sample(ew, ecfg, inputs.f32_to_bf16_bits(K.astype(np.float32)),
+                   inputs.f32_to_bf16_bits(V.astype(np.float32)), mask, noise)
+    e, mx = rel_l2(x, ref), float(np.max(np.abs(x - ref)))
+    d = rel_l2(x - noise, ref - noise)
+    log(f"[vision->prefill->loop] rel_l2={e:.3e} max_abs={mx:.3e} delta_rel_l2={d:.3e}")
+    assert np.all(np.isfinite(x))
+    assert e <= 1e-2 and mx <= 5e-2 and d <= 2e-2, (e, mx, d)
