@@ -10,6 +10,11 @@ chunk 63.
 Workloads p1 / p2 / p3 time the VLM prefix prefill instead (one step = one
 pi_ae_vlm_prefill call: 17 full Gemma-2B-shaped layers and the last layer's
 K/V over 256 / 512 / 816 prefix tokens), reported as prefix tokens/s.
+Workloads s1 / s3 time the vision encoder alone (1 / 3 views -> 256 tokens
+each), reported as views/s.  Workloads f1 / f2 / f3 time one whole inference
+at the shapes of the pages' Table 1 (1 / 2 / 3 views, empty prompt, a
+63-action chunk, 10 steps): the vision encoder, then the prefill and the
+loop as one graph.
 Workloads e1 / e2 / e3 time one whole inference without the vision encoder
 (pi_ae_pipeline_run: the prefill of 1 / 2 / 3 views, then the 10-step loop of
 a 63-action chunk on the cache it leaves, one graph), reported as
@@ -235,6 +240,111 @@ def bench_prefill(args, np, torch):
 
 PIPELINES = {"e1": ("p1", "c2"), "e2": ("p2", "c3"), "e3": ("p3", "c4")}
 
+# vision encoder: per-launch algorithmic flops (unpadded shapes) and bf16 weight bytes per view of 256 tokens
+VIS_PHASE_NAMES = {0: "k_gemm<vis patch>", 1: "k_vis_ln", 2: "k_gemm<vis qkv>", 3: "k_vis_attn", 4: "k_gemm<vis o>",
+                   5: "k_gemm<vis fc1>", 6: "k_gemm<vis fc2>", 7: "k_gemm<vis proj>"}
+VIS_NK = {0: (1152, 588), 2: (3456, 1152), 4: (1152, 1152), 5: (4304, 1152), 6: (1152, 4304), 7: (2048, 1152)}
+
+
+def _timed_calls(run, torch, stream, steps, warmup):
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return wall * 1e3 / steps, statistics.median(per), max(per)
+
+
+def bench_vision(args, np, torch):
+    from flow_matching_action_amd import inputs, pi_ae
+    V = {"s1": 1, "s3": 3}[args.workload]
+    cfg = inputs.VisionConfig()
+    print(f"bench: vision encoder, {V} view(s) of 224x224 -> {256 * V} tokens", file=sys.stderr, flush=True)
+    vis = pi_ae.Vision(cfg, inputs.make_vision_weights(cfg), V)
+    dev = torch.device("cuda:0")
+    imgs = torch.from_numpy(inputs.make_images(cfg, V).view(np.int16)).to(dev)
+    tok = torch.empty(V * 256 * 2048, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    ms, med, mx = _timed_calls(lambda: vis.encode(imgs, V, tok, stream), torch, stream, args.steps, args.warmup)
+    print(f"bench: {ms * 1e3:.1f} us/encode (median {med * 1e3:.1f})", file=sys.stderr, flush=True)
+    phase_us = {ph: vis.time_phase(imgs, V, tok, ph, args.kernel_chunks, stream) for ph in range(8)}
+    print("bench: per-launch us " + ", ".join(f"{VIS_PHASE_NAMES[p]}={t:.2f}" for p, t in phase_us.items()),
+          file=sys.stderr, flush=True)
+    vis.close()
+    M, L = 256 * V, cfg.num_layers
+    flops = {ph: 2 * M * n * k for ph, (n, k) in VIS_NK.items()}
+    flops[3] = 4 * cfg.num_heads * 256 * 256 * cfg.head_dim * V
+    wbytes = {ph: n * k * 2 for ph, (n, k) in VIS_NK.items()}
+    per_call = flops[0] + flops[7] + L * (flops[2] + flops[3] + flops[4] + flops[5] + flops[6])
+    bytes_call = wbytes[0] + wbytes[7] + L * (wbytes[2] + wbytes[4] + wbytes[5] + wbytes[6])
+    dom = 5
+    a = flops[dom] / (phase_us[dom] * 1e-6) / 1e12
+    roof = {"kernel": VIS_PHASE_NAMES[dom], "bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(a / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+    t_mfma, t_hbm = per_call / (MFMA_BF16_PEAK_TFS * 1e12), bytes_call / (HBM_PEAK_GBS * 1e9)
+    line = {
+        "metric": "vision encoder: views/s (27-layer SigLIP-shaped, 224x224 -> 256 tokens per view)",
+        "value": round(V / (ms * 1e-3), 1), "unit": "views/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {V} view(s), 27 layers, width 1152, 16 heads x 72, MLP 4304",
+                   "views": V},
+        "us_per_encode": {"mean": round(ms * 1e3, 1), "median": round(med * 1e3, 1)},
+        "whole_encode_roofline": {"hbm_us": round(t_hbm * 1e6, 1), "mfma_us": round(t_mfma * 1e6, 1),
+                                  "frac": round(max(t_hbm, t_mfma) / (ms * 1e-3), 4)},
+        "per_launch_us": {VIS_PHASE_NAMES[p]: round(t, 3) for p, t in phase_us.items()},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_full(args, np, torch):
+    """Table 1 shapes: V views (256 tokens each), empty prompt, chunk 63, 10 steps."""
+    from flow_matching_action_amd import inputs, pi_ae
+    V = {"f1": 1, "f2": 2, "f3": 3}[args.workload]
+    P = 256 * V
+    vcfg, pcfg, ecfg = inputs.VisionConfig(), inputs.PrefillConfig(), inputs.ExpertConfig()
+    print(f"bench: full inference, {V} view(s), empty prompt, chunk 63, 10 steps", file=sys.stderr, flush=True)
+    vis = pi_ae.Vision(vcfg, inputs.make_vision_weights(vcfg), V)
+    pf = pi_ae.Prefill(pcfg, inputs.make_prefill_weights(pcfg), 1, P)
+    ctx = pi_ae.Context(ecfg, inputs.make_weights(ecfg), 1, P)
+    pipe = pi_ae.Pipeline(pf, ctx)
+    dev = torch.device("cuda:0")
+    imgs = torch.from_numpy(inputs.make_images(vcfg, V).view(np.int16)).to(dev)
+    emb = torch.empty(P * 2048, dtype=torch.int16, device=dev)
+    dn = torch.from_numpy(inputs.make_noise(ecfg, 1)).to(dev)
+    out = torch.empty_like(dn)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        vis.encode(imgs, V, emb, stream)
+        pipe.run(emb, None, dn, out, 1, P, stream)
+
+    ms, med, mx = _timed_calls(run, torch, stream, args.steps, args.warmup)
+    print(f"bench: {ms * 1e3:.1f} us/inference (median {med * 1e3:.1f})", file=sys.stderr, flush=True)
+    pipe.close()
+    ctx.close()
+    pf.close()
+    vis.close()
+    line = {
+        "metric": "inferences/s (vision encoder + VLM prefix prefill + 10-step denoise loop)",
+        "value": round(1 / (ms * 1e-3), 2), "unit": "inferences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {V} view(s) x 256 tokens, empty prompt, chunk 63 x 32, 10 steps",
+                   "views": V, "prefix_len": P, "chunk_len": ecfg.chunk_len, "euler_steps": ecfg.num_steps},
+        "ms_per_inference": {"mean": round(ms, 3), "median": round(med, 3)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
 
 def bench_pipeline(args, np, torch):
     from flow_matching_action_amd import inputs, pi_ae
@@ -290,7 +400,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0", "p1", "p2", "p3", "e1", "e2", "e3"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "c1pi0", "c2pi0", "p1", "p2", "p3", "e1", "e2", "e3",
+                             "s1", "s3", "f1", "f2", "f3"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-chunks", type=int, default=2,
                     help="whole loop passes over which each kernel's in-loop duration is averaged")
@@ -312,6 +423,12 @@ def main():
         return
     if args.workload.startswith("e"):
         bench_pipeline(args, np, torch)
+        return
+    if args.workload.startswith("s"):
+        bench_vision(args, np, torch)
+        return
+    if args.workload.startswith("f"):
+        bench_full(args, np, torch)
         return
 
     from flow_matching_action_amd import inputs, pi_ae

@@ -10,11 +10,9 @@ residual stream and adds up as the square root of the depth, so the bar is
 rel-L2 <= 3.5e-3 * sqrt(layers + 2) (the patch embedding and the projector
 count as one layer each) and max-abs <= 4x that times the tokens' largest
 magnitude (measured: 3.6e-3 at 2 layers, 4.5e-3 at 27 -- the pre-norm
-LayerNorms keep the growth below the bound).  The chain's final actions keep the loop's own bar (rel-L2 <= 1e-2,
-max-abs <= 5e-2).
+LayerNorms keep the growth below the bound).  The chain's final actions keep
+the loop's own bar (rel-L2 <= 1e-2, max-abs <= 5e-2).
 """
-import ctypes
-
 import numpy as np
 import pytest
 import torch
