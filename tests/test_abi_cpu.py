@@ -236,3 +236,47 @@ def test_vlm_weight_pointers_and_null_arguments():
     us = ctypes.c_float()
     assert lib.pi_ae_vlm_debug_time_phase(None, None, None, 1, 1, 1, 1, None, ctypes.byref(us)) == pi_ae.PI_AE_EINVAL
     assert lib.pi_ae_vlm_destroy(None) is None
+
+
+
+# ------------------------------------------------------------------ vision encoder
+@needs_lib
+@pytest.mark.parametrize("field,value,status", [
+    ("width", 1024, pi_ae.PI_AE_EUNSUPPORTED),
+    ("head_dim", 64, pi_ae.PI_AE_EUNSUPPORTED),
+    ("patch", 16, pi_ae.PI_AE_EUNSUPPORTED),
+    ("num_layers", 0, pi_ae.PI_AE_EINVAL),
+    ("max_views", 0, pi_ae.PI_AE_EINVAL),
+    ("max_views", 65, pi_ae.PI_AE_EINVAL),
+    ("ln_eps", 0.0, pi_ae.PI_AE_EINVAL),
+])
+def test_vision_config_validation(field, value, status):
+    """pi_ae_vision_prepare rejects unsupported shapes and bad limits before
+    any device work (no GPU needed)."""
+    cfg = inputs.VisionConfig(num_layers=2)
+    c = pi_ae.make_vision_config(cfg, 1)
+    setattr(c, field, value)
+    lib = pi_ae.load_library()
+    w = pi_ae.VisionWeights()
+    h = ctypes.c_void_p()
+    assert lib.pi_ae_vision_prepare(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == status
+    assert h.value is None
+    assert lib.pi_ae_last_error() != b""
+
+
+@needs_lib
+def test_vision_weight_pointers_and_null_arguments():
+    lib = pi_ae.load_library()
+    cfg = inputs.VisionConfig(num_layers=2)
+    c = pi_ae.make_vision_config(cfg, 1)
+    h = ctypes.c_void_p()
+    assert lib.pi_ae_vision_prepare(None, None, None) == pi_ae.PI_AE_EINVAL
+    w = {n: np.zeros(s, np.uint16) for n, s in inputs.vision_weight_shapes(cfg)}
+    del w["layers.1.fc2.b"]
+    mw = pi_ae._MarshalledVisionWeights(cfg, w)
+    assert lib.pi_ae_vision_prepare(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == pi_ae.PI_AE_EINVAL
+    assert b"layer 1" in lib.pi_ae_last_error()
+    assert lib.pi_ae_vision_encode(None, None, 1, None, None) == pi_ae.PI_AE_EINVAL
+    us = ctypes.c_float()
+    assert lib.pi_ae_vision_debug_time_phase(None, None, 1, None, 0, 1, None, ctypes.byref(us)) == pi_ae.PI_AE_EINVAL
+    assert lib.pi_ae_vision_destroy(None) is None
