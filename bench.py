@@ -13,8 +13,8 @@ K/V over 256 / 512 / 816 prefix tokens), reported as prefix tokens/s.
 Workloads s1 / s3 time the vision encoder alone (1 / 3 views -> 256 tokens
 each), reported as views/s.  Workloads f1 / f2 / f3 time one whole inference
 at the shapes of the pages' Table 1 (1 / 2 / 3 views, empty prompt, a
-63-action chunk, 10 steps): the vision encoder, then the prefill and the
-loop as one graph.
+63-action chunk, 10 steps): pi_ae_inference_run, the vision encoder, the
+prefill and the loop as one graph.
 Workloads e1 / e2 / e3 time one whole inference without the vision encoder
 (pi_ae_pipeline_run: the prefill of 1 / 2 / 3 views, then the 10-step loop of
 a 63-action chunk on the cache it leaves, one graph), reported as
@@ -315,26 +315,24 @@ def bench_full(args, np, torch):
     vis = pi_ae.Vision(vcfg, inputs.make_vision_weights(vcfg), V)
     pf = pi_ae.Prefill(pcfg, inputs.make_prefill_weights(pcfg), 1, P)
     ctx = pi_ae.Context(ecfg, inputs.make_weights(ecfg), 1, P)
-    pipe = pi_ae.Pipeline(pf, ctx)
+    inf = pi_ae.Inference(vis, pf, ctx)
     dev = torch.device("cuda:0")
     imgs = torch.from_numpy(inputs.make_images(vcfg, V).view(np.int16)).to(dev)
-    emb = torch.empty(P * 2048, dtype=torch.int16, device=dev)
     dn = torch.from_numpy(inputs.make_noise(ecfg, 1)).to(dev)
     out = torch.empty_like(dn)
     stream = torch.cuda.current_stream()
 
     def run():
-        vis.encode(imgs, V, emb, stream)
-        pipe.run(emb, None, dn, out, 1, P, stream)
+        inf.run(imgs, V, None, 0, None, dn, out, stream)
 
     ms, med, mx = _timed_calls(run, torch, stream, args.steps, args.warmup)
     print(f"bench: {ms * 1e3:.1f} us/inference (median {med * 1e3:.1f})", file=sys.stderr, flush=True)
-    pipe.close()
+    inf.close()
     ctx.close()
     pf.close()
     vis.close()
     line = {
-        "metric": "inferences/s (vision encoder + VLM prefix prefill + 10-step denoise loop)",
+        "metric": "inferences/s (vision encoder + VLM prefix prefill + 10-step denoise loop, one graph)",
         "value": round(1 / (ms * 1e-3), 2), "unit": "inferences/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

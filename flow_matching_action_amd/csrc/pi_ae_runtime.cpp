@@ -1850,3 +1850,109 @@ PI_AE_API pi_ae_status pi_ae_vision_debug_time_phase(pi_ae_vision* ctx, const ui
   *avg_us = float(sum_ms * 1000.0 / double(tv.size()));
   return PI_AE_OK;
 }
+
+// ====================================================================== whole inference
+struct pi_ae_inference {
+  pi_ae_vision* vis = nullptr;
+  pi_ae_vlm* vlm = nullptr;
+  pi_ae_ctx* ctx = nullptr;
+  uint16_t* prefix = nullptr;  // [max_prefix_len][2048] bf16: the views' tokens, then the prompt's
+  uint8_t* mask = nullptr;     // [max_prefix_len]
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  void release() {
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
+    graphs.clear();
+    if (prefix) (void)hipFree(prefix);
+    if (mask) (void)hipFree(mask);
+    prefix = nullptr;
+    mask = nullptr;
+  }
+};
+
+PI_AE_API pi_ae_status pi_ae_inference_create(pi_ae_vision* vision, pi_ae_vlm* vlm, pi_ae_ctx* expert,
+                                              pi_ae_inference** out) {
+  if (!vision || !vlm || !expert || !out) return fail(PI_AE_EINVAL, "vision, vlm, expert and out must be non-NULL");
+  if (vlm->cfg.num_layers != expert->cfg.num_layers)
+    return fail(PI_AE_EINVAL, "the VLM and the expert must have the same number of layers");
+  if (vision->device != vlm->device || vlm->device != expert->device)
+    return fail(PI_AE_EINVAL, "the three contexts live on different devices");
+  pi_ae_inference* inf = new (std::nothrow) pi_ae_inference();
+  if (!inf) return fail(PI_AE_ENOMEM, "host allocation failed");
+  inf->vis = vision;
+  inf->vlm = vlm;
+  inf->ctx = expert;
+  DeviceGuard dg(vlm->device);
+  const size_t P = size_t(vlm->cfg.max_prefix_len);
+  hipError_t e = hipMalloc(&inf->prefix, P * kSOut * 2);
+  if (e == hipSuccess) e = hipMalloc(&inf->mask, P);
+  if (e == hipSuccess) e = hipMemset(inf->prefix, 0, P * kSOut * 2);
+  if (e != hipSuccess) {
+    inf->release();
+    delete inf;
+    return fail(e == hipErrorOutOfMemory ? PI_AE_ENOMEM : PI_AE_EHIP, std::string("inference buffers: ") + hipGetErrorString(e));
+  }
+  *out = inf;
+  return PI_AE_OK;
+}
+
+PI_AE_API pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t* images, int32_t views,
+                                           const uint16_t* prompt_emb, int32_t prompt_len, const uint8_t* pad_mask,
+                                           const float* noise, float* actions, void* stream) {
+  if (!inf) return fail(PI_AE_EINVAL, "inf is NULL");
+  pi_ae_status st = vis_check_call(inf->vis, images, views, inf->prefix);
+  if (st) return st;
+  if (prompt_len < 0 || (prompt_len > 0 && !prompt_emb)) return fail(PI_AE_EINVAL, "prompt_emb / prompt_len");
+  const int P = views * kSTok + prompt_len;
+  if ((st = vlm_check_call(inf->vlm, inf->prefix, 1, P))) return st;
+  pi_ae_prefix_kv kv{inf->vlm->k_cache, inf->vlm->v_cache, inf->mask, P};
+  if ((st = check_call(inf->ctx, &kv, noise, actions, 1))) return st;
+  DeviceGuard dg(inf->ctx->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const std::pair<int, int> key(views, prompt_len);
+  auto it = inf->graphs.find(key);
+  if (it == inf->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipStream_t c = inf->ctx->cap;
+    hipError_t e = hipStreamBeginCapture(c, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+      int n = 0;
+      hipError_t e2 = vis_enqueue_layers(inf->vis, views, c, -1, nullptr, &n);
+      if (e2 == hipSuccess) e2 = vis_projector(inf->vis, views, inf->prefix, c, nullptr);
+      if (e2 == hipSuccess) e2 = launch_vlm_stage(vlm_stage_for(inf->vlm, inf->prefix, inf->mask, 1, P), c);
+      if (e2 == hipSuccess) e2 = vlm_enqueue(inf->vlm, 1, P, c);
+      if (e2 == hipSuccess) e2 = enqueue(inf->ctx, 1, P, c, StopAt{});
+      e = hipStreamEndCapture(c, &graph);
+      if (e2 != hipSuccess) e = e2;
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
+    it = inf->graphs.emplace(key, exec).first;
+  }
+  hipError_t e = hipSuccess;
+  if (prompt_len > 0)
+    e = hipMemcpyAsync(inf->prefix + size_t(views) * kSTok * kSOut, prompt_emb, size_t(prompt_len) * kSOut * 2,
+                       hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = pad_mask ? hipMemcpyAsync(inf->mask, pad_mask, size_t(P), hipMemcpyDeviceToDevice, s)
+                 : hipMemsetAsync(inf->mask, 1, size_t(P), s);
+  if (e == hipSuccess) {
+    VisPatchParams pp{images, inf->vis->apatch, views};
+    e = launch_vis_patch(pp, s);
+  }
+  if (e == hipSuccess) e = launch_args(args_for(inf->ctx, &kv, noise, actions, 1), s);
+  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
+PI_AE_API void pi_ae_inference_destroy(pi_ae_inference* inf) {
+  if (!inf) return;
+  {
+    DeviceGuard dg(inf->ctx->device);
+    (void)hipDeviceSynchronize();
+    inf->release();
+  }
+  delete inf;
+}

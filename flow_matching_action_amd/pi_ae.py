@@ -22,7 +22,8 @@ EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_stat
            "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
            "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
            "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy",
-           "pi_ae_vision_prepare", "pi_ae_vision_encode", "pi_ae_vision_destroy", "pi_ae_vision_debug_time_phase")
+           "pi_ae_vision_prepare", "pi_ae_vision_encode", "pi_ae_vision_destroy", "pi_ae_vision_debug_time_phase",
+           "pi_ae_inference_create", "pi_ae_inference_run", "pi_ae_inference_destroy")
 
 
 class PiAeError(RuntimeError):
@@ -159,6 +160,15 @@ def load_library(path: str = LIB_PATH):
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                   ctypes.POINTER(ctypes.c_float)]
     lib.pi_ae_vision_debug_time_phase.restype = ctypes.c_int
+    lib.pi_ae_inference_create.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_void_p)]
+    lib.pi_ae_inference_create.restype = ctypes.c_int
+    lib.pi_ae_inference_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.pi_ae_inference_run.restype = ctypes.c_int
+    lib.pi_ae_inference_destroy.argtypes = [ctypes.c_void_p]
+    lib.pi_ae_inference_destroy.restype = None
     _lib = lib
     return lib
 
@@ -431,3 +441,29 @@ class Vision:
         _check(self._lib.pi_ae_vision_debug_time_phase(self._h, _ptr(images), int(views), _ptr(tokens), int(phase),
                                                        int(reps), _stream_handle(stream), ctypes.byref(us)))
         return float(us.value)
+
+
+class Inference:
+    """pi_ae_inference: vision encoder, VLM prefill and denoise loop of one episode as one graph."""
+
+    def __init__(self, vision: Vision, prefill: Prefill, ctx: "Context"):
+        self._lib = load_library()
+        self.vision, self.prefill, self.ctx = vision, prefill, ctx  # keeps the three alive
+        handle = ctypes.c_void_p()
+        _check(self._lib.pi_ae_inference_create(vision._h, prefill._h, ctx._h, ctypes.byref(handle)))
+        self._h = handle
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.pi_ae_inference_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, images, views: int, prompt_emb, prompt_len: int, pad_mask, noise, actions, stream=None):
+        _check(self._lib.pi_ae_inference_run(self._h, _ptr(images), int(views), _ptr(prompt_emb), int(prompt_len),
+                                             _ptr(pad_mask), _ptr(noise), _ptr(actions), _stream_handle(stream)))

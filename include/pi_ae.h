@@ -388,6 +388,32 @@ pi_ae_status pi_ae_vision_encode(pi_ae_vision* ctx, const uint16_t* images, int3
 /* Synchronise the context's device, then free everything it owns.  NULL is a no-op. */
 void pi_ae_vision_destroy(pi_ae_vision* ctx);
 
+/* The whole inference as one graph (RV-blog sections "CUDA Graph" and
+ * "static buffers"): the vision encoder, the VLM prefill and the denoise loop
+ * of one episode.  The three contexts must outlive the object; the VLM and
+ * the expert must have the same depth.  The prefix sequence (the views' tokens
+ * then the prompt's) and the pad mask live in static buffers of the object,
+ * sized by the VLM's max_prefix_len.  Errors: EINVAL, ENOMEM, EHIP. */
+typedef struct pi_ae_inference pi_ae_inference;
+pi_ae_status pi_ae_inference_create(pi_ae_vision* vision, pi_ae_vlm* vlm, pi_ae_ctx* expert, pi_ae_inference** out);
+
+/* Images to actions for one episode:
+ *   images:     device bf16 [views][224][224][3], 16-byte aligned;
+ *   prompt_emb: device bf16 [prompt_len][2048] (the prompt's embedded tokens,
+ *               after their sqrt(2048) scaling), or NULL with prompt_len 0;
+ *   pad_mask:   device u8 [views * 256 + prompt_len], or NULL (all valid);
+ *   noise, actions: device fp32 [chunk_len][action_dim] (may alias).
+ * Per call: the prompt and the mask are copied into the static buffers, the
+ * images staged and the loop's arguments published; then one hipGraph per
+ * (views, prompt_len) runs every layer of the three models.  Asynchronous and
+ * stream-ordered; one call in flight per object and its contexts. */
+pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t* images, int32_t views,
+                                 const uint16_t* prompt_emb, int32_t prompt_len, const uint8_t* pad_mask,
+                                 const float* noise, float* actions, void* stream);
+
+/* Free the object's graphs and static buffers (not the contexts).  NULL is a no-op. */
+void pi_ae_inference_destroy(pi_ae_inference* inf);
+
 /* Test-only: time one kernel of the encoder in its real sequence (as
  * pi_ae_vlm_debug_time_phase): phase 0 = patch embedding, 1 = a layer's
  * first LayerNorm (the second is the same kernel), 2 = QKV, 3 = attention, 4 = O + residual, 5 = fc1 +

@@ -137,3 +137,44 @@ def test_vision_prefill_and_loop_chain():
     log(f"[vision->prefill->loop] rel_l2={e:.3e} max_abs={mx:.3e} delta_rel_l2={d:.3e}")
     assert np.all(np.isfinite(x))
     assert e <= 1e-2 and mx <= 5e-2 and d <= 2e-2, (e, mx, d)
+
+
+def test_whole_inference_graph_equals_separate_calls():
+    """pi_ae_inference_run (images -> actions in one graph) gives bitwise the
+    actions of the vision encode followed by the prefill + loop pipeline, with
+    and without a prompt, on one object."""
+    vcfg = inputs.VisionConfig(num_layers=2)
+    pcfg = inputs.PrefillConfig(num_layers=2)
+    ecfg = inputs.ExpertConfig(num_layers=2)
+    vis = pi_ae.Vision(vcfg, inputs.make_vision_weights(vcfg), 2)
+    pf = pi_ae.Prefill(pcfg, inputs.make_prefill_weights(pcfg), 1, 600)
+    ctx = pi_ae.Context(ecfg, inputs.make_weights(ecfg), 1, 600)
+    inf = pi_ae.Inference(vis, pf, ctx)
+    pipe = pi_ae.Pipeline(pf, ctx)
+    try:
+        for V, n_prompt in ((1, 0), (2, 20)):
+            log(f"step: whole inference V={V} prompt={n_prompt}")
+            P = 256 * V + n_prompt
+            imgs = to_dev(inputs.make_images(vcfg, V, seed=40 + V))
+            prompt = to_dev(inputs.make_prefix_embeddings(pcfg, 1, max(n_prompt, 1), seed=50)[:, :n_prompt].reshape(-1))
+            mask = to_dev(inputs.make_pad_mask(1, P, P - 3))
+            noise = to_dev(inputs.make_noise(ecfg, 1))
+            a_one = torch.empty_like(noise)
+            inf.run(imgs, V, prompt if n_prompt else None, n_prompt, mask, noise, a_one)
+            torch.cuda.synchronize()
+            emb = torch.empty(P * 2048, dtype=torch.int16, device="cuda")
+            if n_prompt:
+                emb[256 * V * 2048:] = prompt
+            vis.encode(imgs, V, emb)
+            a_sep = torch.empty_like(noise)
+            pipe.run(emb, mask, noise, a_sep, 1, P)
+            torch.cuda.synchronize()
+            x, y = a_one.cpu().numpy(), a_sep.cpu().numpy()
+            log(f"[inference V={V} prompt={n_prompt}] max |one graph - separate| = {float(np.max(np.abs(x - y))):.3e}")
+            assert np.all(np.isfinite(x)) and np.array_equal(x, y)
+    finally:
+        pipe.close()
+        inf.close()
+        ctx.close()
+        pf.close()
+        vis.close()
