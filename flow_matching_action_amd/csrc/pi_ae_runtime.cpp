@@ -1507,10 +1507,22 @@ struct pi_ae_vision {
 
 namespace {
 
-// fc2 splits K (4608 = 2 x 2304) in two: its 18 column tiles alone would
-// leave most CUs idle at a few views; the other K (1280, 768) are odd
-// multiples of 256 and stay whole.
-constexpr int kVisFc2Split = 2;
+// K split of a vision GEMM (128 x 64 tiles): the largest of 2, 3, 6 whose K
+// ranges are whole 256-wide blocks of at least 768 and whose launch stays
+// within one workgroup per CU.  Only fc2 (K 4608) qualifies: 6 ranges at one
+// view, 3 at two, 2 at three.  Measured at one view: fc2 22.0 -> 16.5 us with
+// 6 ranges; splitting the K = 1280 GEMMs into five 256-wide ranges, or fc2
+// at three views beyond 2, was slower (the partial tiles and the reduce cost
+// more than the shorter K loop saves).
+constexpr int kVisMaxSplit = 6;
+int vis_ksplit(int M, int ncols, int K) {
+  if (ncols > kSD) return 1;  // the partial-tile buffer holds kVisMaxSplit x Mpad x 1152
+  const int wgs = (ncols / 64) * ((M + 127) / 128);
+  int S = 1;
+  for (int c : {2, 3, 6})
+    if (K % (256 * c) == 0 && K / c >= 768 && wgs * c <= 256) S = c;
+  return S;
+}
 
 pi_ae_status vis_check_config(const pi_ae_vision_config* c) {
   if (c->width != kSD || c->mlp_dim != kSF || c->num_heads != kSH || c->head_dim != kSHd || c->patch != kSPatch ||
@@ -1629,7 +1641,7 @@ void vis_prepare(pi_ae_vision* ctx, const pi_ae_vision_weights* w) {
   ctx->qkv = ctx->dalloc<uint16_t>(Mp * 3 * kSD);
   ctx->o = ctx->dalloc<uint16_t>(Mp * kSKp);
   ctx->m = ctx->dalloc<uint16_t>(Mp * kSFk);
-  ctx->part = ctx->dalloc<float>(size_t(kVisFc2Split) * Mp * kSD);
+  ctx->part = ctx->dalloc<float>(size_t(kVisMaxSplit) * Mp * kSD);
   HIP_OR_THROW(hipMemset(ctx->apatch, 0, Mp * kSKpatch * 2));
   HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kSD * 4));
   HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kSKp * 2));
@@ -1657,7 +1669,7 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
   g.bias = ctx->b_patch;
   g.aux = ctx->pos;
   g.h_out = ctx->h;
-  if ((e = launch_vis_gemm(0, g, 1, nullptr, s, tm(0))) != hipSuccess) return e;
+  if ((e = launch_vis_gemm(0, g, vis_ksplit(M, kSD, kSKpatch), ctx->part, s, tm(0))) != hipSuccess) return e;
   VisLnParams ln{};
   ln.h = ctx->h;
   ln.u = ctx->u;
@@ -1683,7 +1695,7 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
     q.a_frag = ctx->u;
     q.bias = ctx->b_qkv + size_t(l) * 3 * kSD;
     q.q_out = ctx->qkv;
-    if ((e = launch_vis_gemm(1, q, 1, nullptr, s, tm(2))) != hipSuccess) return e;
+    if ((e = launch_vis_gemm(1, q, vis_ksplit(M, 3 * kSD, kSKp), ctx->part, s, tm(2))) != hipSuccess) return e;
     VisAttnParams a{};
     a.qkv = ctx->qkv;
     a.o = ctx->o;
@@ -1695,7 +1707,7 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
     og.a_frag = ctx->o;
     og.bias = ctx->b_o + size_t(l) * kSD;
     og.h_out = ctx->h;
-    if ((e = launch_vis_gemm(2, og, 1, nullptr, s, tm(4))) != hipSuccess) return e;
+    if ((e = launch_vis_gemm(2, og, vis_ksplit(M, kSD, kSKp), ctx->part, s, tm(4))) != hipSuccess) return e;
     ln.w = ctx->ln2_w + size_t(l) * kSD;
     ln.b = ctx->ln2_b + size_t(l) * kSD;
     if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
@@ -1705,14 +1717,14 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
     f1.a_frag = ctx->u;
     f1.bias = ctx->b_fc1 + size_t(l) * kSFn;
     f1.m_out = ctx->m;
-    if ((e = launch_vis_gemm(3, f1, 1, nullptr, s, tm(5))) != hipSuccess) return e;
+    if ((e = launch_vis_gemm(3, f1, vis_ksplit(M, kSFn, kSKp), ctx->part, s, tm(5))) != hipSuccess) return e;
     GemmParams f2{};
     f2.M = M;
     f2.w = ctx->w_fc2 + n_fc2 * l;
     f2.a_frag = ctx->m;
     f2.bias = ctx->b_fc2 + size_t(l) * kSD;
     f2.h_out = ctx->h;
-    if ((e = launch_vis_gemm(4, f2, kVisFc2Split, ctx->part, s, tm(6))) != hipSuccess) return e;
+    if ((e = launch_vis_gemm(4, f2, vis_ksplit(M, kSD, kSFk), ctx->part, s, tm(6))) != hipSuccess) return e;
   }
   ln.w = ctx->post_w;
   ln.b = ctx->post_b;
@@ -1726,7 +1738,7 @@ hipError_t vis_projector(pi_ae_vision* ctx, int V, uint16_t* tokens, hipStream_t
   g.a_frag = ctx->u;
   g.bias = ctx->b_proj;
   g.q_out = tokens;
-  return launch_vis_gemm(5, g, 1, nullptr, s, t);
+  return launch_vis_gemm(5, g, vis_ksplit(g.M, kSOut, kSKp), ctx->part, s, t);
 }
 
 pi_ae_status vis_check_call(pi_ae_vision* ctx, const uint16_t* images, int32_t views, const uint16_t* tokens) {
