@@ -128,13 +128,15 @@ __device__ __forceinline__ void kernarg_touch(const P& p) {
   }
 
 // GELU, tanh approximation (the MLP activation of the Gemma-shaped expert).
-// tanh through one exp2 and one reciprocal: tanh(z) = 1 - 2 / (e^(2z) + 1),
-// exact at both tails (e^(2z) -> inf gives 1, -> 0 gives -1); relative error
-// a few ulp, far below the bf16 rounding of its result.
+// tanh through one exp2 and one hardware reciprocal (v_rcp_f32, 1 ulp):
+// tanh(z) = 1 - 2 / (e^(2z) + 1), exact at both tails (e^(2z) -> inf gives 1,
+// -> 0 gives -1); relative error a few ulp, far below the bf16 rounding of its
+// result.  The reciprocal instead of an IEEE division trims the fused GELU
+// epilogues (the batched gate/up GEMM: 40.0 -> 38.3 us per launch).
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float z = 0.7978845608028654f * (x + 0.044715f * x * x * x);
   const float e = exp2f(z * 2.8853900817779268f);  // e^(2z)
-  return 0.5f * x * (2.f - 2.f / (e + 1.f));
+  return 0.5f * x * (2.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
 }
 // Offset (in bf16 elements) of activation (row, k) in the fragment-major
 // layout [rows/16][K/32][64 lanes][8] that the GEMM A operand loads directly.
