@@ -407,7 +407,7 @@ def main():
                     help="only run a plain elementwise copy of known size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the denoise loop on exactly one GPU; --gpus must be 1", file=sys.stderr)
+        print("bench.py: every path here runs on exactly one GPU (there is no multi-GPU path); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
