@@ -241,8 +241,9 @@ def bench_prefill(args, np, torch):
 PIPELINES = {"e1": ("p1", "c2"), "e2": ("p2", "c3"), "e3": ("p3", "c4")}
 
 # vision encoder: per-launch algorithmic flops (unpadded shapes) and bf16 weight bytes per view of 256 tokens
-VIS_PHASE_NAMES = {0: "k_gemm<vis patch>", 1: "k_vis_ln", 2: "k_gemm<vis qkv>", 3: "k_vis_attn", 4: "k_gemm<vis o>",
-                   5: "k_gemm<vis fc1>", 6: "k_gemm<vis fc2>", 7: "k_gemm<vis proj>"}
+VIS_PHASE_NAMES = {0: "k_gemm<vis patch>", 1: "k_vis_ln", 2: "k_gemm<vis qkv>", 3: "k_vis_attn",
+                   4: "k_gemm<vis o>+k_vis_res_ln", 5: "k_gemm<vis fc1>", 6: "k_gemm<vis fc2>+k_vis_res_ln",
+                   7: "k_gemm<vis proj>"}
 VIS_NK = {0: (1152, 588), 2: (3456, 1152), 4: (1152, 1152), 5: (4304, 1152), 6: (1152, 4304), 7: (2048, 1152)}
 
 

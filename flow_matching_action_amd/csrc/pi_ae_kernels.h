@@ -197,12 +197,18 @@ struct VisPatchParams {
 // sqrt(var + eps) * w + b, bf16, fragment-major [Mpad/16][1280/32][64][8]
 // (columns 1152.. stay zero).
 struct VisLnParams {
-  const float* h;          // [Mpad][1152]
+  float* h;                // [Mpad][1152]
   const float* w;          // [1152]
   const float* b;          // [1152]
   uint16_t* u;
   float eps;
   int M;
+  // residual form (launch_vis_res_ln): first h += sum of the S partial tiles
+  // part[z][Mp][1152] of a 1152-column GEMM (fixed order z = 0 .. S-1) +
+  // bias, then the LayerNorm of the new h
+  const float* part;
+  const float* bias;       // [1152]
+  int S, Mp;
 };
 // Attention of one view's 256 tokens, 16 heads x 72, all keys valid.
 struct VisAttnParams {
@@ -254,6 +260,11 @@ hipError_t launch_vlm_down(const GemmParams& p, int S, float* part, hipStream_t 
 // projector).  S > 1 splits K (fc2 only).
 hipError_t launch_vis_patch(const VisPatchParams& p, hipStream_t s);
 hipError_t launch_vis_ln(const VisLnParams& p, hipStream_t s);
+hipError_t launch_vis_res_ln(const VisLnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
+// which as in launch_vis_gemm (2 = O, 4 = fc2): only the raw K-split GEMM
+// (S ranges into part[z][Mp][1152]); launch_vis_res_ln finishes it
+hipError_t launch_vis_gemm_raw(int which, const GemmParams& p, int S, float* part, hipStream_t s,
+                               const KernelTiming* t = nullptr);
 hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s,
                            const KernelTiming* t = nullptr);

@@ -1840,20 +1840,12 @@ hipError_t launch_vis_patch(const VisPatchParams& p, hipStream_t s) {
 
 // LayerNorm, one workgroup (4 waves) per token row: 144 threads hold 8
 // values each; mean, then the variance about it (two passes over registers,
-// fp32); the bf16 operand in the GEMM's fragment-major layout.
-__global__ __launch_bounds__(256) void k_vis_ln(VisLnParams p) {
+// fp32); the bf16 operand in the GEMM's fragment-major layout.  x: this
+// thread's 8 values (zeros for the threads past the row's 144).
+__device__ __forceinline__ void vis_ln_row(const VisLnParams& p, int row, float (&x)[8]) {
   __shared__ float red[2][4];
-  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const bool act = t < kSD / 8;
-  float x[8];
-  if (act) {
-    const float4 a = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t);
-    const float4 b = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-  }
   float s1 = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) s1 += x[e];
@@ -1881,10 +1873,63 @@ __global__ __launch_bounds__(256) void k_vis_ln(VisLnParams p) {
       uint4, pack8(make_float4(y[0], y[1], y[2], y[3]), make_float4(y[4], y[5], y[6], y[7])));
 }
 
+__global__ __launch_bounds__(256) void k_vis_ln(VisLnParams p) {
+  const int row = blockIdx.x, t = threadIdx.x;
+  float x[8];
+  if (t < kSD / 8) {
+    const float4 a = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t);
+    const float4 b = *reinterpret_cast<const float4*>(p.h + size_t(row) * kSD + 8 * t + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  vis_ln_row(p, row, x);
+}
+
+// The end of a residual GEMM (O or fc2: 1152 columns, K split into S ranges)
+// and the LayerNorm that follows it, one workgroup per row: the partial
+// tiles summed in a fixed order, + bias, added to the residual stream (the
+// same operations, in the same order, as the split-K reduce with the
+// residual epilogue), then the LayerNorm of the updated row.  A row is whole
+// in one workgroup here, so the norm needs no second kernel.
+__global__ __launch_bounds__(256) void k_vis_res_ln(VisLnParams p) {
+  const int row = blockIdx.x, t = threadIdx.x;
+  float x[8];
+  if (t < kSD / 8) {
+    const size_t zs = size_t(p.Mp) * kSD, off = size_t(row) * kSD + 8 * t;
+    float4 a0 = *reinterpret_cast<const float4*>(p.part + off);
+    float4 a1 = *reinterpret_cast<const float4*>(p.part + off + 4);
+    for (int z = 1; z < p.S; ++z) {
+      const float4 c0 = *reinterpret_cast<const float4*>(p.part + z * zs + off);
+      const float4 c1 = *reinterpret_cast<const float4*>(p.part + z * zs + off + 4);
+      a0.x += c0.x; a0.y += c0.y; a0.z += c0.z; a0.w += c0.w;
+      a1.x += c1.x; a1.y += c1.y; a1.z += c1.z; a1.w += c1.w;
+    }
+    const float4 b0 = *reinterpret_cast<const float4*>(p.bias + 8 * t);
+    const float4 b1 = *reinterpret_cast<const float4*>(p.bias + 8 * t + 4);
+    float* hp = p.h + off;
+    const float4 h0 = *reinterpret_cast<const float4*>(hp), h1 = *reinterpret_cast<const float4*>(hp + 4);
+    x[0] = h0.x + (a0.x + b0.x); x[1] = h0.y + (a0.y + b0.y); x[2] = h0.z + (a0.z + b0.z); x[3] = h0.w + (a0.w + b0.w);
+    x[4] = h1.x + (a1.x + b1.x); x[5] = h1.y + (a1.y + b1.y); x[6] = h1.z + (a1.z + b1.z); x[7] = h1.w + (a1.w + b1.w);
+    *reinterpret_cast<float4*>(hp) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(hp + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+  vis_ln_row(p, row, x);
+}
+
 hipError_t launch_vis_ln(const VisLnParams& p, hipStream_t s) {
   if (p.M <= 0) return hipSuccess;
   k_vis_ln<<<p.M, 256, 0, s>>>(p);
   return hipGetLastError();
+}
+hipError_t launch_vis_res_ln(const VisLnParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M <= 0) return hipSuccess;
+  if (p.S < 1 || !p.part || !p.bias || p.Mp < p.M) return hipErrorInvalidValue;
+  return go(k_vis_res_ln, dim3(p.M), dim3(256), s, t, p);
 }
 
 // Attention of one view's 256 tokens for one head and 64 queries (grid: 4
@@ -2004,6 +2049,14 @@ static hipError_t vis_gemm(const GemmParams& p, int ncols, int K, int S, float* 
   const int Mp = int(grid.y) * 128;
   return go(k_splitk_reduce<64, 64, EPI, kSD, kSFk>, dim3(ncols / 64, Mp / 64), dim3(256), s, t ? &t1 : nullptr, p,
             (const float*)part, S, Mp, ncols);
+}
+hipError_t launch_vis_gemm_raw(int which, const GemmParams& p, int S, float* part, hipStream_t s,
+                               const KernelTiming* t) {
+  if (which != 2 && which != 4) return hipErrorInvalidValue;
+  const int K = which == 2 ? kSKp : kSFk;
+  if (S < 1 || K % (256 * S) != 0) return hipErrorInvalidValue;  // whole 4-stage groups of 64-wide k per range
+  return go(k_gemm_big32<4, 1, 2, E_VRES, kSD, kSFk, true>, dim3(kSD / 64, row_tiles(p.M, 128), S), dim3(256), s, t,
+            p, K, part);
 }
 hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s, const KernelTiming* t) {
   switch (which) {

@@ -1515,6 +1515,10 @@ namespace {
 // at three views beyond 2, was slower (the partial tiles and the reduce cost
 // more than the shorter K loop saves).
 constexpr int kVisMaxSplit = 6;
+// K ranges of the O projection (K 1280 = 5 x 256): five when they still fit
+// in one round of workgroups, else one
+int vis_osplit(int M) { return (kSD / 64) * ((M + 127) / 128) * 5 <= 256 ? 5 : 1; }
+unsigned row_tiles128(int M) { return unsigned((M + 127) / 128); }
 int vis_ksplit(int M, int ncols, int K) {
   if (ncols > kSD) return 1;  // the partial-tile buffer holds kVisMaxSplit x Mpad x 1152
   const int wgs = (ncols / 64) * ((M + 127) / 128);
@@ -1670,25 +1674,41 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
   g.aux = ctx->pos;
   g.h_out = ctx->h;
   if ((e = launch_vis_gemm(0, g, vis_ksplit(M, kSD, kSKpatch), ctx->part, s, tm(0))) != hipSuccess) return e;
+  // every LayerNorm but layer 0's first one ends the residual GEMM before it
+  // (O, fc2): the raw K-split GEMM, then one kernel that sums its ranges,
+  // adds bias and residual and normalises the whole row
   VisLnParams ln{};
   ln.h = ctx->h;
   ln.u = ctx->u;
   ln.eps = ctx->cfg.ln_eps;
   ln.M = M;
+  ln.part = ctx->part;
+  ln.Mp = int(row_tiles128(M)) * 128;
+  ln.w = ctx->ln1_w;
+  ln.b = ctx->ln1_b;
+  {
+    const KernelTiming* t = tm(1);
+    if (t && (e = hipEventRecord(t->start, s)) != hipSuccess) return e;
+    if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
+    if (t && (e = hipEventRecord(t->stop, s)) != hipSuccess) return e;
+  }
+  const int So = vis_osplit(M), Sf = vis_ksplit(M, kSD, kSFk);
+  // the raw GEMM and the residual + LayerNorm kernel, timed as one phase
+  auto res_ln = [&](int which, const GemmParams& g, int S, const float* bias, const float* w, const float* b,
+                    const KernelTiming* t) {
+    const KernelTiming t0{t ? t->start : nullptr, nullptr}, t1{nullptr, t ? t->stop : nullptr};
+    hipError_t r = launch_vis_gemm_raw(which, g, S, ctx->part, s, t ? &t0 : nullptr);
+    if (r != hipSuccess) return r;
+    VisLnParams q = ln;
+    q.S = S;
+    q.bias = bias;
+    q.w = w;
+    q.b = b;
+    return launch_vis_res_ln(q, s, t ? &t1 : nullptr);
+  };
   const size_t n_qkv = size_t(3 * kSD) * kSKp, n_o = size_t(kSD) * kSKp, n_fc1 = size_t(kSFn) * kSKp,
                n_fc2 = size_t(kSD) * kSFk;
   for (int l = 0; l < L; ++l) {
-    ln.w = ctx->ln1_w + size_t(l) * kSD;
-    ln.b = ctx->ln1_b + size_t(l) * kSD;
-    {
-      const KernelTiming* t = tm(1);
-      if ((e = (t ? hipSuccess : launch_vis_ln(ln, s))) != hipSuccess) return e;
-      if (t) {  // phase 1 times the layer's first LayerNorm (the second is the same kernel)
-        if ((e = hipEventRecord(t->start, s)) != hipSuccess) return e;
-        if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
-        if ((e = hipEventRecord(t->stop, s)) != hipSuccess) return e;
-      }
-    }
     GemmParams q{};
     q.M = M;
     q.w = ctx->w_qkv + n_qkv * l;
@@ -1705,12 +1725,9 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
     og.M = M;
     og.w = ctx->w_o + n_o * l;
     og.a_frag = ctx->o;
-    og.bias = ctx->b_o + size_t(l) * kSD;
-    og.h_out = ctx->h;
-    if ((e = launch_vis_gemm(2, og, vis_ksplit(M, kSD, kSKp), ctx->part, s, tm(4))) != hipSuccess) return e;
-    ln.w = ctx->ln2_w + size_t(l) * kSD;
-    ln.b = ctx->ln2_b + size_t(l) * kSD;
-    if ((e = launch_vis_ln(ln, s)) != hipSuccess) return e;
+    if ((e = res_ln(2, og, So, ctx->b_o + size_t(l) * kSD, ctx->ln2_w + size_t(l) * kSD, ctx->ln2_b + size_t(l) * kSD,
+                    tm(4))) != hipSuccess)
+      return e;
     GemmParams f1{};
     f1.M = M;
     f1.w = ctx->w_fc1 + n_fc1 * l;
@@ -1722,13 +1739,13 @@ hipError_t vis_enqueue_layers(pi_ae_vision* ctx, int V, hipStream_t s, int timed
     f2.M = M;
     f2.w = ctx->w_fc2 + n_fc2 * l;
     f2.a_frag = ctx->m;
-    f2.bias = ctx->b_fc2 + size_t(l) * kSD;
-    f2.h_out = ctx->h;
-    if ((e = launch_vis_gemm(4, f2, vis_ksplit(M, kSD, kSFk), ctx->part, s, tm(6))) != hipSuccess) return e;
+    // the next layer's first LayerNorm, or the final one before the projector
+    const bool last = l + 1 == L;
+    const float* nw = last ? ctx->post_w : ctx->ln1_w + size_t(l + 1) * kSD;
+    const float* nb = last ? ctx->post_b : ctx->ln1_b + size_t(l + 1) * kSD;
+    if ((e = res_ln(4, f2, Sf, ctx->b_fc2 + size_t(l) * kSD, nw, nb, tm(6))) != hipSuccess) return e;
   }
-  ln.w = ctx->post_w;
-  ln.b = ctx->post_b;
-  return launch_vis_ln(ln, s);
+  return hipSuccess;
 }
 
 hipError_t vis_projector(pi_ae_vision* ctx, int V, uint16_t* tokens, hipStream_t s, const KernelTiming* t) {
@@ -1833,7 +1850,7 @@ PI_AE_API pi_ae_status pi_ae_vision_debug_time_phase(pi_ae_vision* ctx, const ui
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int L = ctx->cfg.num_layers;
-  const int per = (phase == 0 || phase == 7) ? 1 : L;
+  const int per = (phase == 0 || phase == 1 || phase == 7) ? 1 : L;  // phase 1: layer 0's first LayerNorm
   std::vector<KernelTiming> tv(size_t(per) * reps, KernelTiming{nullptr, nullptr});
   hipError_t e = hipSuccess;
   for (auto& t : tv) {

@@ -415,10 +415,13 @@ pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t* images, i
 void pi_ae_inference_destroy(pi_ae_inference* inf);
 
 /* Test-only: time one kernel of the encoder in its real sequence (as
- * pi_ae_vlm_debug_time_phase): phase 0 = patch embedding, 1 = a layer's
- * first LayerNorm (the second is the same kernel), 2 = QKV, 3 = attention, 4 = O + residual, 5 = fc1 +
- * GELU, 6 = fc2 + residual, 7 = projector; `reps` whole encodes on `stream`;
- * *avg_us = mean duration of one launch of that phase. */
+ * pi_ae_vlm_debug_time_phase): phase 0 = patch embedding, 1 = layer 0's
+ * first LayerNorm (every later LayerNorm is part of phase 4 or 6), 2 = QKV,
+ * 3 = attention, 4 = O + residual + the layer's second LayerNorm, 5 = fc1 +
+ * GELU, 6 = fc2 + residual + the next layer's first (or the final)
+ * LayerNorm, 7 = projector; phases 4 and 6 are two kernels each, timed from
+ * the start of the first to the end of the second; `reps` whole encodes on
+ * `stream`; *avg_us = mean duration of one instance of that phase. */
 pi_ae_status pi_ae_vision_debug_time_phase(pi_ae_vision* ctx, const uint16_t* images, int32_t views,
                                            uint16_t* tokens, int32_t phase, int32_t reps, void* stream,
                                            float* avg_us);
