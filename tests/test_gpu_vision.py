@@ -87,6 +87,26 @@ def test_vision_reduced_three_views():
         vis.close()
 
 
+def test_vision_five_views_unsplit_residual_gemms():
+    """5 and 4 views (1280 / 1024 rows): the O and fc2 GEMMs no longer split K
+    (one range of raw tiles, then the residual + LayerNorm kernel), unlike at
+    1-3 views."""
+    cfg = inputs.VisionConfig(num_layers=2)
+    w = inputs.make_vision_weights(cfg, seed=21)
+    imgs = inputs.make_images(cfg, 5, seed=22)
+    log("step: vision 2 layers, 5 then 4 views")
+    vis = pi_ae.Vision(cfg, w, 5)
+    try:
+        for V in (5, 4):
+            tok = torch.empty(V * 256 * 2048, dtype=torch.int16, device="cuda")
+            vis.encode(to_dev(imgs[:V]), V, tok)
+            torch.cuda.synchronize()
+            got = O.bf16_to_float(tok.cpu().numpy().view(np.uint16)).reshape(V, 256, 2048)
+            check_tokens(got, VO.vision_encode(w, cfg, imgs[:V]), cfg.num_layers, f"vision-2L V={V}")
+    finally:
+        vis.close()
+
+
 def test_vision_full_depth_one_view():
     cfg = inputs.VisionConfig()
     w = inputs.make_vision_weights(cfg)
