@@ -312,10 +312,12 @@ __global__ __launch_bounds__(256) void k_io(IoParams p) {
 //   E_GELU: * 1/rms, + shift-fold bias, m = GELU(gate) * up, fragment-major.
 //   E_RES:  h += acc * gate; when the next consumer is a normalised GEMM also
 //           its operand bf16(h * (1 + scale_next)) and the h^2 partials.
-//   vision encoder (bias on every linear, norms by a separate LayerNorm
-//   kernel): E_VPATCH h = acc + b + pos; E_VQKV natural bf16 acc + b;
-//   E_VGELU the MLP operand bf16(GELU(acc + b)); E_VRES h += acc + b;
-//   E_VPROJ natural bf16 (acc + b) * sqrt(2048).
+//   vision encoder (bias on every linear; LayerNorm operands written by the
+//   LayerNorm kernels): E_VPATCH h = acc + b + pos; E_VQKV natural bf16
+//   acc + b; E_VGELU the MLP operand bf16(GELU(acc + b)); E_VPROJ natural
+//   bf16 (acc + b) * sqrt(2048); E_VRES (h += acc + b) tags the O and fc2
+//   GEMMs, which run as raw K-split tiles that k_vis_res_ln finishes
+//   together with the LayerNorm after them.
 enum { E_QKV = 0, E_GELU = 1, E_RES = 2, E_KV = 3, E_VPATCH = 4, E_VQKV = 5, E_VGELU = 6, E_VRES = 7, E_VPROJ = 8 };
 // epilogues whose input is an RMS-normalised operand (1/rms from the h^2 partials)
 constexpr bool epi_norm(int e) { return e == E_QKV || e == E_GELU || e == E_KV; }
@@ -2035,9 +2037,10 @@ hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTi
   return go(k_vis_attn, dim3(kSTok / 64, kSH, p.V), dim3(256), s, t, p);
 }
 
-// which: 0 patch embedding (K 768), 1 QKV (N 3456), 2 O + residual, 3 fc1 +
-// GELU (N 4352), 4 fc2 + residual (K 4608), 5 projector (N 2048); tiles
-// 128 x 64; with S > 1 the K ranges' partial tiles and the reduce kernel.
+// which: 0 patch embedding (K 768), 1 QKV (N 3456), 3 fc1 + GELU (N 4352),
+// 5 projector (N 2048); tiles 128 x 64; with S > 1 the K ranges' partial
+// tiles and the reduce kernel.  The residual GEMMs (2 = O, 4 = fc2) go through
+// launch_vis_gemm_raw and launch_vis_res_ln.
 template <int EPI>
 static hipError_t vis_gemm(const GemmParams& p, int ncols, int K, int S, float* part, hipStream_t s,
                            const KernelTiming* t) {
@@ -2062,9 +2065,7 @@ hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, h
   switch (which) {
     case 0: return vis_gemm<E_VPATCH>(p, kSD, kSKpatch, S, part, s, t);
     case 1: return vis_gemm<E_VQKV>(p, 3 * kSD, kSKp, S, part, s, t);
-    case 2: return vis_gemm<E_VRES>(p, kSD, kSKp, S, part, s, t);
     case 3: return vis_gemm<E_VGELU>(p, kSFn, kSKp, S, part, s, t);
-    case 4: return vis_gemm<E_VRES>(p, kSD, kSFk, S, part, s, t);
     case 5: return vis_gemm<E_VPROJ>(p, kSOut, kSKp, S, part, s, t);
   }
   return hipErrorInvalidValue;
