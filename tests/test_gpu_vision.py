@@ -107,6 +107,21 @@ def test_vision_five_views_unsplit_residual_gemms():
         vis.close()
 
 
+def test_vision_maximum_views_sampled():
+    """The largest view count a context takes (64 views, 16384 rows), 2 layers:
+    views 0, 31 and 63 against the oracle run on those views alone (views
+    are independent, which the oracle pins check)."""
+    cfg = inputs.VisionConfig(num_layers=2)
+    w = inputs.make_vision_weights(cfg, seed=23)
+    V = 64
+    imgs = inputs.make_images(cfg, V, seed=24)
+    log(f"step: vision 2 layers, {V} views (maximum), sampled views")
+    got = encode(cfg, w, imgs)
+    assert np.all(np.isfinite(got))
+    pick = [0, 31, 63]
+    check_tokens(got[pick], VO.vision_encode(w, cfg, imgs[pick]), cfg.num_layers, f"vision-2L V={V} sampled")
+
+
 def test_vision_full_depth_one_view():
     cfg = inputs.VisionConfig()
     w = inputs.make_vision_weights(cfg)
@@ -166,18 +181,19 @@ def test_whole_inference_graph_equals_separate_calls():
     vcfg = inputs.VisionConfig(num_layers=2)
     pcfg = inputs.PrefillConfig(num_layers=2)
     ecfg = inputs.ExpertConfig(num_layers=2)
-    vis = pi_ae.Vision(vcfg, inputs.make_vision_weights(vcfg), 2)
-    pf = pi_ae.Prefill(pcfg, inputs.make_prefill_weights(pcfg), 1, 600)
-    ctx = pi_ae.Context(ecfg, inputs.make_weights(ecfg), 1, 600)
+    vis = pi_ae.Vision(vcfg, inputs.make_vision_weights(vcfg), 3)
+    pf = pi_ae.Prefill(pcfg, inputs.make_prefill_weights(pcfg), 1, 816)
+    ctx = pi_ae.Context(ecfg, inputs.make_weights(ecfg), 1, 816)
     inf = pi_ae.Inference(vis, pf, ctx)
     pipe = pi_ae.Pipeline(pf, ctx)
     try:
-        for V, n_prompt in ((1, 0), (2, 20)):
+        # the last: the 3-view shape with 48 prompt tokens, the last 16 padded
+        for V, n_prompt, n_pad in ((1, 0, 3), (2, 20, 3), (3, 48, 16)):
             log(f"step: whole inference V={V} prompt={n_prompt}")
             P = 256 * V + n_prompt
             imgs = to_dev(inputs.make_images(vcfg, V, seed=40 + V))
             prompt = to_dev(inputs.make_prefix_embeddings(pcfg, 1, max(n_prompt, 1), seed=50)[:, :n_prompt].reshape(-1))
-            mask = to_dev(inputs.make_pad_mask(1, P, P - 3))
+            mask = to_dev(inputs.make_pad_mask(1, P, P - n_pad))
             noise = to_dev(inputs.make_noise(ecfg, 1))
             a_one = torch.empty_like(noise)
             inf.run(imgs, V, prompt if n_prompt else None, n_prompt, mask, noise, a_one)
