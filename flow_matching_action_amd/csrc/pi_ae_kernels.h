@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <string>
 
 namespace pi_ae {
 
@@ -170,8 +171,9 @@ struct PackParams {
 
 // Staging of one VLM prefill call (one workgroup per prefix row): the residual
 // stream h = the prefix sequence, the first layer's operand bf16(h * gamma)
-// with its h^2 partials, each row's RoPE (cos, sin) at position t (its index
-// in the episode) and the additive key bias of the episode's keys.
+// with its h^2 partials, each row's RoPE (cos, sin) at its position (the number
+// of valid tokens before it in its episode) and the additive key bias of the
+// episode's keys.
 struct VlmStageParams {
   const uint16_t* emb;    // [B][P][2048] bf16, the scaled prefix sequence
   const uint8_t* mask;    // [B][P] or null (all valid)
@@ -268,6 +270,10 @@ hipError_t launch_vis_gemm_raw(int which, const GemmParams& p, int S, float* par
 hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTiming* t = nullptr);
 hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s,
                            const KernelTiming* t = nullptr);
+
+// The thread-local message that pi_ae_last_error returns (set by every
+// translation unit of the library on failure).
+void set_last_error(const std::string& msg);
 
 // Swizzled weight geometry (shared by prep and kernels): a weight W[N][K]
 // (nn.Linear layout) is stored as 1 KiB fragments, fragment (nb, kb) =

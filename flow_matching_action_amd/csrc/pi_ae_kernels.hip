@@ -1741,8 +1741,22 @@ __global__ __launch_bounds__(256) void k_vlm_stage(VlmStageParams p) {
   for (int i = 0; i < 8; ++i) sq += x[i] * x[i];
   sq += __shfl_xor(sq, 1);  // the two threads of a 16-column tile
   if ((threadIdx.x & 1) == 0) p.ssq[size_t(row) * (kVD / 16) + (threadIdx.x >> 1)] = sq;
+  // RoPE position: the number of valid tokens before this one in its episode,
+  // so that the valid tokens sit at 0 .. n_valid - 1 whatever pads lie between
+  // them and the expert's suffix (at n_valid + j) continues them
+  __shared__ int spos[4];
+  int pos = t;
+  if (p.mask) {
+    const uint8_t* mrow = p.mask + size_t(b) * p.P;
+    int c = 0;
+    for (int i = threadIdx.x; i < t; i += 256) c += mrow[i] != 0;
+    c = int(wave_sum(float(c)));  // exact: at most 4096
+    if ((threadIdx.x & 63) == 0) spos[threadIdx.x >> 6] = c;
+    __syncthreads();
+    pos = spos[0] + spos[1] + spos[2] + spos[3];
+  }
   if (threadIdx.x < kRopeHalf) {
-    const double a = double(t) * p.inv_freq[threadIdx.x];
+    const double a = double(pos) * p.inv_freq[threadIdx.x];
     p.rope_cs[size_t(row) * kRopeHalf + threadIdx.x] = make_float2(float(cos(a)), float(sin(a)));
   }
   if (threadIdx.x == 0) {

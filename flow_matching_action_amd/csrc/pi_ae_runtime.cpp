@@ -6,8 +6,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <new>
@@ -30,6 +32,12 @@ pi_ae_status fail(pi_ae_status st, const std::string& msg) {
   g_last_error = msg;
   return st;
 }
+
+}  // namespace
+
+void pi_ae::set_last_error(const std::string& msg) { g_last_error = msg; }
+
+namespace {
 
 struct HipError {
   hipError_t e;
@@ -58,13 +66,176 @@ inline uint16_t bf16_of(double x) {
   return uint16_t(u >> 16);
 }
 
+// Device allocations of one library object.  Each allocation carries a
+// 256-byte guard on both sides filled with a fixed byte pattern, which
+// check() reads back: a kernel that wrote past either end of a buffer leaves
+// a changed guard.  PI_AE_FAIL_ALLOC=N (environment, read when the object is
+// prepared) makes its N-th allocation fail as out of memory, so that tests
+// can check that every failure path frees what was allocated before it.
+constexpr size_t kGuardBytes = 256;
+constexpr unsigned char kGuardByte = 0xA5;
+// device bytes held by every live arena of the process (guards included)
+std::atomic<int64_t> g_live_device_bytes{0};
+
+struct DeviceArena {
+  struct Block {
+    char* base;      // the hipMalloc'ed range: guard, buffer, guard
+    size_t bytes;    // buffer bytes (between the guards)
+  };
+  std::vector<Block> blocks;
+  int count = 0, fail_at = 0;
+
+  void arm_fault_injection() {
+    count = 0;
+    const char* e = std::getenv("PI_AE_FAIL_ALLOC");
+    fail_at = e ? std::atoi(e) : 0;
+  }
+  template <class T>
+  T* alloc(size_t n) {
+    if (n == 0) n = 1;
+    const size_t bytes = n * sizeof(T);
+    if (++count == fail_at)
+      throw HipError{hipErrorOutOfMemory, "injected failure of device allocation " + std::to_string(count) +
+                                              " (PI_AE_FAIL_ALLOC)"};
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes + 2 * kGuardBytes);
+    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(bytes) + " bytes"};
+    char* base = static_cast<char*>(p);
+    blocks.push_back(Block{base, bytes});
+    g_live_device_bytes += int64_t(bytes + 2 * kGuardBytes);
+    e = hipMemset(base, kGuardByte, kGuardBytes);
+    if (e == hipSuccess) e = hipMemset(base + kGuardBytes + bytes, kGuardByte, kGuardBytes);
+    if (e != hipSuccess) throw HipError{e, "guard fill"};
+    return reinterpret_cast<T*>(base + kGuardBytes);
+  }
+  // index of the first block whose guards changed, -1 if none; corrupt >= 0
+  // first overwrites one byte right after that block's buffer (a host-side
+  // write of the guard, to show that the check sees it)
+  int check(int corrupt, hipError_t* err) {
+    *err = hipSuccess;
+    if (corrupt >= 0 && corrupt < int(blocks.size())) {
+      *err = hipMemset(blocks[corrupt].base + kGuardBytes + blocks[corrupt].bytes, 0, 1);
+      if (*err != hipSuccess) return -1;
+    }
+    std::vector<unsigned char> g(kGuardBytes);
+    for (size_t i = 0; i < blocks.size(); ++i) {
+      for (int side = 0; side < 2; ++side) {
+        const char* src = side ? blocks[i].base + kGuardBytes + blocks[i].bytes : blocks[i].base;
+        *err = hipMemcpy(g.data(), src, kGuardBytes, hipMemcpyDeviceToHost);
+        if (*err != hipSuccess) return -1;
+        for (unsigned char c : g)
+          if (c != kGuardByte) return int(i);
+      }
+    }
+    return -1;
+  }
+  void release() {
+    for (const Block& b : blocks) {
+      (void)hipFree(b.base);
+      g_live_device_bytes -= int64_t(b.bytes + 2 * kGuardBytes);
+    }
+    blocks.clear();
+  }
+};
+
+// Executable graphs of one library object, keyed by call shape.  At most
+// kGraphCacheMax are kept (the least recently used is dropped), and each holds
+// an event recorded after its latest launch, so that dropping it, and
+// destroying the object, wait for that object's own work only.
+constexpr size_t kGraphCacheMax = 8;
+
+template <class Key>
+struct GraphCache {
+  struct Entry {
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;
+    uint64_t used = 0;
+  };
+  std::map<Key, Entry> m;
+  uint64_t tick = 0;
+
+  Entry* find(const Key& k) {
+    auto it = m.find(k);
+    if (it == m.end()) return nullptr;
+    it->second.used = ++tick;
+    return &it->second;
+  }
+  // takes ownership of exec (destroyed here on failure)
+  hipError_t insert(const Key& k, hipGraphExec_t exec, Entry** out) {
+    if (m.size() >= kGraphCacheMax) {
+      auto lru = m.begin();
+      for (auto it = m.begin(); it != m.end(); ++it)
+        if (it->second.used < lru->second.used) lru = it;
+      drop(lru->second);
+      m.erase(lru);
+    }
+    hipEvent_t ev = nullptr;
+    const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipGraphExecDestroy(exec);
+      return e;
+    }
+    Entry& en = m[k];
+    en.exec = exec;
+    en.done = ev;
+    en.used = ++tick;
+    *out = &en;
+    return hipSuccess;
+  }
+  static hipError_t launch(Entry* en, hipStream_t s) { return hipGraphLaunch(en->exec, s); }
+  // after the call's last work on s (the graph and anything enqueued after it)
+  static hipError_t mark(Entry* en, hipStream_t s) { return hipEventRecord(en->done, s); }
+  static void drop(Entry& en) {
+    (void)hipEventSynchronize(en.done);  // a launch of it may still be in flight
+    (void)hipGraphExecDestroy(en.exec);
+    (void)hipEventDestroy(en.done);
+  }
+  void clear() {
+    for (auto& kv : m) drop(kv.second);
+    m.clear();
+  }
+};
+
+// Captures what `enq` enqueues on `cap` into a new executable graph.
+template <class F>
+hipError_t capture_graph(hipStream_t cap, F&& enq, hipGraphExec_t* out) {
+  hipGraph_t graph = nullptr;
+  *out = nullptr;
+  hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    const hipError_t e2 = enq();
+    e = hipStreamEndCapture(cap, &graph);
+    if (e2 != hipSuccess) e = e2;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(out, graph, nullptr, nullptr, 0);
+  if (graph) (void)hipGraphDestroy(graph);
+  return e;
+}
+
 }  // namespace
+
+// The device memory one call of the loop works in: the residual stream and
+// the GEMM operands, the call's packed K/V and key bias, its RoPE rows, valid
+// prefix counts and argument block.  A context owns one (allocated when it is
+// prepared); the allocation-free entry point carves one out of a fixed device
+// array instead.
+struct Workspace {
+  float* h = nullptr;                       // [Mpad][1024] fp32 residual stream
+  uint16_t *q = nullptr, *o = nullptr, *m = nullptr, *u = nullptr;
+  uint16_t* o2 = nullptr;                   // second key range's partial attention output, then row statistics
+  float* ssq = nullptr;                     // [Mpad][64] partial sums of h^2
+  uint16_t *kp = nullptr, *vp = nullptr;    // packed K/V of every layer, one call
+  float* kbias = nullptr;
+  float2* rope_cs = nullptr;
+  int* n_valid = nullptr;
+  DevArgs* da = nullptr;
+};
 
 struct pi_ae_ctx {
   pi_ae_config cfg{};
   int device = 0;
   bool broken = false;
-  std::vector<void*> allocs;
+  DeviceArena arena;
   // prepared weights (device)
   uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr, *w_in = nullptr, *w_out = nullptr;
   float* b_in = nullptr;
@@ -76,37 +247,21 @@ struct pi_ae_ctx {
   float *attn_s1 = nullptr, *attn_g = nullptr, *c_qkv = nullptr, *ffn_s1 = nullptr, *ffn_g = nullptr,
         *c_gu = nullptr, *fin_s1 = nullptr, *c_out = nullptr;
   double* inv_freq = nullptr;
-  float2* rope_cs = nullptr;
-  // workspaces
-  float* h = nullptr;
-  uint16_t *q = nullptr, *o = nullptr, *m = nullptr, *u = nullptr;
-  uint16_t* o2 = nullptr;  // second key range's partial attention output (small M), then the row statistics
-  float* ssq = nullptr;
-  uint16_t *kp = nullptr, *vp = nullptr;  // packed K/V of every layer, one call
-  float* kbias = nullptr;
+  Workspace ws;
   int nkb_max = 0;
-  int* n_valid = nullptr;
-  DevArgs* da = nullptr;
   int Mmax = 0, Mpad = 0;
   // host copies of the tables in natural column order (debug export)
   std::vector<float> tab[10];
   hipStream_t cap = nullptr;
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  GraphCache<std::pair<int, int>> graphs;
 
   template <class T>
   T* dalloc(size_t n) {
-    void* p = nullptr;
-    if (n == 0) n = 1;
-    hipError_t e = hipMalloc(&p, n * sizeof(T));
-    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
-    allocs.push_back(p);
-    return static_cast<T*>(p);
+    return arena.alloc<T>(n);
   }
   void release() {
-    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
-    for (void* p : allocs) (void)hipFree(p);
-    allocs.clear();
+    arena.release();
     if (cap) (void)hipStreamDestroy(cap);
     cap = nullptr;
   }
@@ -123,9 +278,11 @@ pi_ae_status check_config(const pi_ae_config* c) {
   if (c->num_layers < 1 || c->num_layers > 64) return fail(PI_AE_EINVAL, "num_layers must be in [1, 64]");
   if (c->num_steps < 1 || c->num_steps > 64) return fail(PI_AE_EINVAL, "num_steps must be in [1, 64]");
   if (c->chunk_len < 1 || c->chunk_len > 256) return fail(PI_AE_EINVAL, "chunk_len must be in [1, 256]");
-  if (c->max_batch < 1 || c->max_batch > 4096) return fail(PI_AE_EINVAL, "max_batch must be in [1, 4096]");
-  if (c->max_prefix_len < 0 || c->max_prefix_len > 32768)
-    return fail(PI_AE_EINVAL, "max_prefix_len must be in [0, 32768]");
+  if (c->max_batch < 1 || c->max_batch > 1024) return fail(PI_AE_EINVAL, "max_batch must be in [1, 1024]");
+  if (c->max_batch * c->chunk_len > 65536)
+    return fail(PI_AE_EINVAL, "max_batch * chunk_len (rows per GEMM) must be at most 65536");
+  if (c->max_prefix_len < 0 || c->max_prefix_len > 8192)
+    return fail(PI_AE_EINVAL, "max_prefix_len must be in [0, 8192]");
   if (!std::isfinite(c->t0) || !std::isfinite(c->dt)) return fail(PI_AE_EINVAL, "t0 and dt must be finite");
   if (!(c->rope_base > 0.f) || !std::isfinite(c->rope_base)) return fail(PI_AE_EINVAL, "rope_base must be > 0");
   if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps)) return fail(PI_AE_EINVAL, "rms_eps must be >= 0");
@@ -481,32 +638,32 @@ void prepare(pi_ae_ctx* ctx, const pi_ae_weights* w) {
   ctx->Mmax = cfg.max_batch * T;
   ctx->Mpad = (ctx->Mmax + 255) / 256 * 256;  // whole 256-row tiles of the wide gate/up GEMM
   const size_t Mp = size_t(ctx->Mpad);
-  ctx->h = ctx->dalloc<float>(Mp * kD);
-  ctx->q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->ws.h = ctx->dalloc<float>(Mp * kD);
+  ctx->ws.q = ctx->dalloc<uint16_t>(Mp * kH * kHd);
   ctx->nkb_max = (cfg.max_prefix_len + T + 31) / 32;
   const size_t npack = size_t(L) * cfg.max_batch * ctx->nkb_max * 8192;
-  ctx->kp = ctx->dalloc<uint16_t>(npack);
-  ctx->vp = ctx->dalloc<uint16_t>(npack);
-  ctx->kbias = ctx->dalloc<float>(size_t(cfg.max_batch) * ctx->nkb_max * 32);
-  ctx->o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
-  ctx->rope_cs = ctx->dalloc<float2>(Mp * kRopeHalf);
-  ctx->u = ctx->dalloc<uint16_t>(Mp * kD);
-  ctx->ssq = ctx->dalloc<float>(Mp * (kD / 16));
-  ctx->m = ctx->dalloc<uint16_t>(Mp * kF);
-  ctx->n_valid = ctx->dalloc<int>(cfg.max_batch);
-  ctx->da = ctx->dalloc<DevArgs>(1);
-  ctx->o2 = ctx->dalloc<uint16_t>(Mp * kH * kHd + Mp * kH * 4 * 2);  // + row statistics (fp32)
-  HIP_OR_THROW(hipMemset(ctx->h, 0, Mp * kD * 4));
-  HIP_OR_THROW(hipMemset(ctx->q, 0, Mp * kH * kHd * 2));
-  HIP_OR_THROW(hipMemset(ctx->kp, 0, npack * 2));
-  HIP_OR_THROW(hipMemset(ctx->vp, 0, npack * 2));
-  HIP_OR_THROW(hipMemset(ctx->o, 0, Mp * kH * kHd * 2));
-  HIP_OR_THROW(hipMemset(ctx->o2, 0, (Mp * kH * kHd + Mp * kH * 4 * 2) * 2));
-  HIP_OR_THROW(hipMemset(ctx->u, 0, Mp * kD * 2));
-  HIP_OR_THROW(hipMemset(ctx->ssq, 0, Mp * (kD / 16) * 4));
-  HIP_OR_THROW(hipMemset(ctx->m, 0, Mp * kF * 2));
-  HIP_OR_THROW(hipMemset(ctx->n_valid, 0, cfg.max_batch * 4));
-  HIP_OR_THROW(hipMemset(ctx->da, 0, sizeof(DevArgs)));
+  ctx->ws.kp = ctx->dalloc<uint16_t>(npack);
+  ctx->ws.vp = ctx->dalloc<uint16_t>(npack);
+  ctx->ws.kbias = ctx->dalloc<float>(size_t(cfg.max_batch) * ctx->nkb_max * 32);
+  ctx->ws.o = ctx->dalloc<uint16_t>(Mp * kH * kHd);
+  ctx->ws.rope_cs = ctx->dalloc<float2>(Mp * kRopeHalf);
+  ctx->ws.u = ctx->dalloc<uint16_t>(Mp * kD);
+  ctx->ws.ssq = ctx->dalloc<float>(Mp * (kD / 16));
+  ctx->ws.m = ctx->dalloc<uint16_t>(Mp * kF);
+  ctx->ws.n_valid = ctx->dalloc<int>(cfg.max_batch);
+  ctx->ws.da = ctx->dalloc<DevArgs>(1);
+  ctx->ws.o2 = ctx->dalloc<uint16_t>(Mp * kH * kHd + Mp * kH * 4 * 2);  // + row statistics (fp32)
+  HIP_OR_THROW(hipMemset(ctx->ws.h, 0, Mp * kD * 4));
+  HIP_OR_THROW(hipMemset(ctx->ws.q, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.kp, 0, npack * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.vp, 0, npack * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.o, 0, Mp * kH * kHd * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.o2, 0, (Mp * kH * kHd + Mp * kH * 4 * 2) * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.u, 0, Mp * kD * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.ssq, 0, Mp * (kD / 16) * 4));
+  HIP_OR_THROW(hipMemset(ctx->ws.m, 0, Mp * kF * 2));
+  HIP_OR_THROW(hipMemset(ctx->ws.n_valid, 0, cfg.max_batch * 4));
+  HIP_OR_THROW(hipMemset(ctx->ws.da, 0, sizeof(DevArgs)));
   HIP_OR_THROW(hipStreamCreateWithFlags(&ctx->cap, hipStreamNonBlocking));
   HIP_OR_THROW(hipDeviceSynchronize());
 }
@@ -540,7 +697,7 @@ Prefetch broadcast(const void* base, size_t bytes) { return Prefetch{base, uint3
 //   step input     -> layer 0 QKV weights
 //   QKV(l)         -> layer l prefix K and V (batch 1)
 //   attention(l)   -> layer l O and gate/up weights
-PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phase) {
+PrefetchSet warm_plan(const pi_ae_ctx* ctx, const Workspace& ws, int B, int P, int k, int l, int phase) {
   const pi_ae_config& cfg = ctx->cfg;
   const int T = cfg.chunk_len;
   PrefetchSet pf{};
@@ -557,8 +714,8 @@ PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phas
       const int nkb = (P + T + 31) / 32, full = P / 32;
       if (B == 1 && full > 0) {
         const size_t off = size_t(l) * nkb * 8192;
-        pf.r[0] = broadcast(ctx->kp + off, size_t(full) * 8192 * 2);
-        pf.r[1] = broadcast(ctx->vp + off, size_t(full) * 8192 * 2);
+        pf.r[0] = broadcast(ws.kp + off, size_t(full) * 8192 * 2);
+        pf.r[1] = broadcast(ws.vp + off, size_t(full) * 8192 * 2);
         pf.nwg = 32;
       }
       break;
@@ -574,18 +731,19 @@ PrefetchSet warm_plan(const pi_ae_ctx* ctx, int B, int P, int k, int l, int phas
 
 // Launch one phase of one (step, layer); phase 0 is the step-boundary kernel
 // of step k (k == num_steps: the final output projection and Euler update).
-hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int l, int phase,
+hipError_t launch_phase(pi_ae_ctx* ctx, const Workspace& ws, int B, int P, hipStream_t s, int k, int l,
+                        int phase,
                         const KernelTiming* t = nullptr) {
   const pi_ae_config& cfg = ctx->cfg;
   const int L = cfg.num_layers, S = cfg.num_steps, T = cfg.chunk_len, M = B * T;
   const size_t kl = size_t(k) * L + l;
-  const PrefetchSet pf = warm_plan(ctx, B, P, k, l, phase);
+  const PrefetchSet pf = warm_plan(ctx, ws, B, P, k, l, phase);
   switch (phase) {
     case 0: {
       IoParams io{};
       io.pf = pf;
-      io.da = ctx->da;
-      io.h = ctx->h;
+      io.da = ws.da;
+      io.h = ws.h;
       io.w_in = ctx->w_in;
       io.b_in = ctx->b_in;
       io.w_out = ctx->w_out;
@@ -598,24 +756,24 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       io.fin_s1 = (k > 0 && cfg.final_norm) ? ctx->fin_s1 + size_t(k - 1) * kD : nullptr;
       io.c_out = k > 0 ? ctx->c_out + size_t(k - 1) * kA : nullptr;
       io.s1_next = k < S ? ctx->attn_s1 + size_t(k) * L * kD : nullptr;
-      io.u_out = ctx->u;
-      io.ssq_out = ctx->ssq;
+      io.u_out = ws.u;
+      io.ssq_out = ws.ssq;
       if (cfg.variant == 1) {  // pi0: the action-time encoder, then its output layer
         io.enc = 1;
         io.h_init = ctx->b_to;
-        io.u_out = ctx->o;
+        io.u_out = ws.o;
         io.b_in = k < S ? ctx->enc_bias + size_t(k) * kD : ctx->b_to;
         hipError_t e = launch_io(io, s, t);
         if (e != hipSuccess || k >= S) return e;
         GemmParams g{};
         g.M = M;
         g.w = ctx->w_to;
-        g.a_frag = ctx->o;
+        g.a_frag = ws.o;
         g.gate = ctx->ones;
-        g.h_out = ctx->h;
+        g.h_out = ws.h;
         g.s1_next = ctx->attn_s1 + size_t(k) * L * kD;
-        g.u_out = ctx->u;
-        g.ssq_out = ctx->ssq;
+        g.u_out = ws.u;
+        g.ssq_out = ws.ssq;
         return launch_enc(g, s);
       }
       return launch_io(io, s, t);
@@ -627,35 +785,35 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       g.M = M;
       g.eps = cfg.rms_eps;
       g.T = T;
-      g.rope_cs = ctx->rope_cs;
-      g.a_frag = ctx->u;
-      g.ssq = ctx->ssq;
+      g.rope_cs = ws.rope_cs;
+      g.a_frag = ws.u;
+      g.ssq = ws.ssq;
       if (phase == 1) {
         const int nkb = (P + T + 31) / 32;
         g.w = ctx->w_qkv + size_t(kNqkv) * kD * l;
         g.bias = ctx->c_qkv + kl * kNqkv;
-        g.q_out = ctx->q;
+        g.q_out = ws.q;
         g.P = P;
         g.nkb = nkb;
-        g.kp = ctx->kp + size_t(l) * B * nkb * 8192;
-        g.vp = ctx->vp + size_t(l) * B * nkb * 8192;
+        g.kp = ws.kp + size_t(l) * B * nkb * 8192;
+        g.vp = ws.vp + size_t(l) * B * nkb * 8192;
         return launch_qkv(g, s, t);
       }
       g.w = ctx->w_gu + size_t(kNgu) * kD * l;
       g.bias = ctx->c_gu + kl * kNgu;
-      g.m_out = ctx->m;
+      g.m_out = ws.m;
       return launch_gu(g, s, t);
     }
     case 2: {
       AttnParams a{};
       a.pf = pf;
       const int nkb = (P + T + 31) / 32;
-      a.q = ctx->q;
-      a.kp = ctx->kp + size_t(l) * B * nkb * 8192;
-      a.vp = ctx->vp + size_t(l) * B * nkb * 8192;
-      a.kbias = ctx->kbias;
-      a.o = ctx->o;
-      a.o2 = attn_ksplit(M, nkb) == 2 ? ctx->o2 : nullptr;
+      a.q = ws.q;
+      a.kp = ws.kp + size_t(l) * B * nkb * 8192;
+      a.vp = ws.vp + size_t(l) * B * nkb * 8192;
+      a.kbias = ws.kbias;
+      a.o = ws.o;
+      a.o2 = attn_ksplit(M, nkb) == 2 ? ws.o2 : nullptr;
       a.B = B;
       a.T = T;
       a.P = P;
@@ -667,15 +825,15 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       GemmParams g{};
       g.pf = pf;
       g.M = M;
-      g.h_out = ctx->h;
-      g.u_out = ctx->u;
-      g.ssq_out = ctx->ssq;
+      g.h_out = ws.h;
+      g.u_out = ws.u;
+      g.ssq_out = ws.ssq;
       if (phase == 3) {  // next: this layer's gate/up
         g.w = ctx->w_o + size_t(kD) * kH * kHd * l;
-        g.a_frag = ctx->o;
+        g.a_frag = ws.o;
         if (attn_ksplit(M, (P + T + 31) / 32) == 2) {
-          g.a_frag2 = ctx->o2;
-          g.astat = attn_row_stats(ctx->o2, M);
+          g.a_frag2 = ws.o2;
+          g.astat = attn_row_stats(ws.o2, M);
         }
         g.gate = ctx->attn_g + kl * kD;
         g.s1_next = ctx->ffn_s1 + kl * kD;
@@ -683,7 +841,7 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
       }
       // next: the following layer's QKV, or (last layer) the step boundary
       g.w = ctx->w_d + size_t(kD) * kF * l;
-      g.a_frag = ctx->m;
+      g.a_frag = ws.m;
       g.gate = ctx->ffn_g + kl * kD;
       g.s1_next = (l + 1 < L) ? ctx->attn_s1 + (kl + 1) * kD : nullptr;
       return launch_down(g, s, t);
@@ -693,18 +851,18 @@ hipError_t launch_phase(pi_ae_ctx* ctx, int B, int P, hipStream_t s, int k, int 
 }
 
 // timed_phase / timing: launch i of that phase (in loop order) gets timing[i].
-hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& stop, int timed_phase = -1,
-                   const KernelTiming* timing = nullptr) {
+hipError_t enqueue(pi_ae_ctx* ctx, const Workspace& ws, int B, int P, hipStream_t s, const StopAt& stop,
+                   int timed_phase = -1, const KernelTiming* timing = nullptr) {
   const int L = ctx->cfg.num_layers, S = ctx->cfg.num_steps;
   hipError_t e;
   PackParams pp{};
-  pp.da = ctx->da;
-  pp.n_valid = ctx->n_valid;
+  pp.da = ws.da;
+  pp.n_valid = ws.n_valid;
   pp.inv_freq = ctx->inv_freq;
-  pp.rope_cs = ctx->rope_cs;
-  pp.kp = ctx->kp;
-  pp.vp = ctx->vp;
-  pp.kbias = ctx->kbias;
+  pp.rope_cs = ws.rope_cs;
+  pp.kp = ws.kp;
+  pp.vp = ws.vp;
+  pp.kbias = ws.kbias;
   pp.B = B;
   pp.P = P;
   pp.T = ctx->cfg.chunk_len;
@@ -713,11 +871,11 @@ hipError_t enqueue(pi_ae_ctx* ctx, int B, int P, hipStream_t s, const StopAt& st
   int n_timed = 0;
   auto tm = [&](int ph) { return (timing && ph == timed_phase) ? &timing[n_timed++] : nullptr; };
   for (int k = 0; k <= S; ++k) {
-    if ((e = launch_phase(ctx, B, P, s, k, 0, 0, tm(0))) != hipSuccess) return e;
+    if ((e = launch_phase(ctx, ws, B, P, s, k, 0, 0, tm(0))) != hipSuccess) return e;
     if (stop.hit(k, 0, 0) || k == S) return hipSuccess;
     for (int l = 0; l < L; ++l)
       for (int ph = 1; ph <= 5; ++ph) {
-        if ((e = launch_phase(ctx, B, P, s, k, l, ph, tm(ph))) != hipSuccess) return e;
+        if ((e = launch_phase(ctx, ws, B, P, s, k, l, ph, tm(ph))) != hipSuccess) return e;
         if (stop.hit(k, l, ph)) return hipSuccess;
       }
   }
@@ -754,15 +912,15 @@ struct DeviceGuard {
   }
 };
 
-ArgsParams args_for(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions, int batch) {
+ArgsParams args_for(const Workspace& ws, const pi_ae_prefix_kv* kv, const float* noise, float* actions, int batch) {
   ArgsParams a{};
-  a.da = ctx->da;
+  a.da = ws.da;
   a.vals.pk = static_cast<const uint16_t*>(kv->k);
   a.vals.pv = static_cast<const uint16_t*>(kv->v);
   a.vals.mask = kv->pad_mask;
   a.vals.noise = noise;
   a.vals.actions = actions;
-  a.n_valid = ctx->n_valid;
+  a.n_valid = ws.n_valid;
   a.B = batch;
   a.P = kv->prefix_len;
   return a;
@@ -779,6 +937,7 @@ PI_AE_API pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_a
   pi_ae_ctx* ctx = new (std::nothrow) pi_ae_ctx();
   if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
   ctx->cfg = *cfg;
+  ctx->arena.arm_fault_injection();
   try {
     HIP_OR_THROW(hipGetDevice(&ctx->device));
     prepare(ctx, w);
@@ -806,23 +965,17 @@ PI_AE_API pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, c
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const std::pair<int, int> key(batch, kv->prefix_len);
-  auto it = ctx->graphs.find(key);
-  if (it == ctx->graphs.end()) {
-    hipGraph_t graph = nullptr;
+  auto* g = ctx->graphs.find(key);
+  if (!g) {
     hipGraphExec_t exec = nullptr;
-    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
-    if (e == hipSuccess) {
-      hipError_t e2 = enqueue(ctx, batch, kv->prefix_len, ctx->cap, StopAt{});
-      e = hipStreamEndCapture(ctx->cap, &graph);
-      if (e2 != hipSuccess) e = e2;
-    }
-    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) (void)hipGraphDestroy(graph);
+    hipError_t e = capture_graph(ctx->cap, [&] { return enqueue(ctx, ctx->ws, batch, kv->prefix_len, ctx->cap, StopAt{}); },
+                                 &exec);
+    if (e == hipSuccess) e = ctx->graphs.insert(key, exec, &g);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    it = ctx->graphs.emplace(key, exec).first;
   }
-  hipError_t e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
-  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  hipError_t e = launch_args(args_for(ctx->ws, kv, noise, actions, batch), s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::launch(g, s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::mark(g, s);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return PI_AE_OK;
 }
@@ -831,13 +984,12 @@ PI_AE_API void pi_ae_destroy(pi_ae_ctx* ctx) {
   if (!ctx) return;
   {
     DeviceGuard dg(ctx->device);
-    (void)hipDeviceSynchronize();
-    ctx->release();
+    ctx->release();  // waits for this context's launched graphs, then frees
   }
   delete ctx;
 }
 
-PI_AE_API const char* pi_ae_status_string(pi_ae_status s) {
+PI_AE_API const char* pi_ae_status_string(int32_t s) {
   switch (s) {
     case PI_AE_OK: return "ok";
     case PI_AE_EINVAL: return "invalid argument";
@@ -898,8 +1050,8 @@ PI_AE_API pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix
     if (e == hipSuccess) e = hipEventCreate(&t.stop);
   }
   for (int c = 0; c < chunks && e == hipSuccess; ++c) {
-    e = launch_args(args_for(ctx, kv, noise, actions, batch), s);
-    if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, s, StopAt{}, phase, &tv[size_t(c) * per_chunk]);
+    e = launch_args(args_for(ctx->ws, kv, noise, actions, batch), s);
+    if (e == hipSuccess) e = enqueue(ctx, ctx->ws, batch, kv->prefix_len, s, StopAt{}, phase, &tv[size_t(c) * per_chunk]);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   double sum_ms = 0.0;
@@ -923,7 +1075,7 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
   if (!ctx) return fail(PI_AE_EINVAL, "ctx is NULL");
   float* actions = nullptr;
   pi_ae_status st = PI_AE_OK;
-  if (batch < 1) return fail(PI_AE_EINVAL, "probe needs batch >= 1");
+  if (batch < 1 || batch > ctx->cfg.max_batch) return fail(PI_AE_EINVAL, "probe needs batch in [1, max_batch]");
   if (step < 0 || step > ctx->cfg.num_steps || layer < 0 || layer >= ctx->cfg.num_layers || phase < 0 || phase > 5)
     return fail(PI_AE_EINVAL, "probe position out of range");
   const int T = ctx->cfg.chunk_len, M = batch * T;
@@ -950,25 +1102,25 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
   stop.step = step;
   stop.layer = layer;
   stop.phase = phase;
-  hipError_t e = launch_args(args_for(ctx, kv, noise, actions, batch), nullptr);
-  if (e == hipSuccess) e = enqueue(ctx, batch, kv->prefix_len, nullptr, stop);
+  hipError_t e = launch_args(args_for(ctx->ws, kv, noise, actions, batch), nullptr);
+  if (e == hipSuccess) e = enqueue(ctx, ctx->ws, batch, kv->prefix_len, nullptr, stop);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   std::vector<uint16_t> buf;
   if (e == hipSuccess) {
     if (which == 0) {
-      e = hipMemcpy(host_out, ctx->h, need, hipMemcpyDeviceToHost);
+      e = hipMemcpy(host_out, ctx->ws.h, need, hipMemcpyDeviceToHost);
     } else if (which == 6) {
       e = hipMemcpy(host_out, actions, need, hipMemcpyDeviceToHost);
     } else if (which == 1) {
-      e = hipMemcpy(host_out, ctx->q, need, hipMemcpyDeviceToHost);
+      e = hipMemcpy(host_out, ctx->ws.q, need, hipMemcpyDeviceToHost);
     } else if (which == 8) {
-      e = hipMemcpy(host_out, attn_row_stats(ctx->o2, M), need, hipMemcpyDeviceToHost);
+      e = hipMemcpy(host_out, attn_row_stats(ctx->ws.o2, M), need, hipMemcpyDeviceToHost);
     } else if (which == 2 || which == 3) {
       // suffix keys of layer `layer` from the packed K / V (see kpack_index / vpack_index)
       const int P = kv->prefix_len, nkb = (P + T + 31) / 32;
       const size_t n = size_t(batch) * nkb * 8192;
       buf.resize(n);
-      const uint16_t* src = (which == 2 ? ctx->kp : ctx->vp) + size_t(layer) * batch * nkb * 8192;
+      const uint16_t* src = (which == 2 ? ctx->ws.kp : ctx->ws.vp) + size_t(layer) * batch * nkb * 8192;
       e = hipMemcpy(buf.data(), src, n * 2, hipMemcpyDeviceToHost);
       uint16_t* dst = static_cast<uint16_t*>(host_out);
       for (int b = 0; b < batch; ++b)
@@ -990,7 +1142,7 @@ PI_AE_API pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* 
       const int K = which == 5 ? kF : kH * kHd;
       const size_t rows = size_t((M + 15) / 16) * 16;
       buf.resize(rows * K);
-      e = hipMemcpy(buf.data(), which == 4 ? ctx->o : which == 7 ? ctx->o2 : ctx->m, buf.size() * 2,
+      e = hipMemcpy(buf.data(), which == 4 ? ctx->ws.o : which == 7 ? ctx->ws.o2 : ctx->ws.m, buf.size() * 2,
                     hipMemcpyDeviceToHost);
       uint16_t* dst = static_cast<uint16_t*>(host_out);
       for (int r = 0; r < M; ++r)
@@ -1010,7 +1162,7 @@ struct pi_ae_vlm {
   pi_ae_vlm_config cfg{};
   int device = 0;
   bool broken = false;
-  std::vector<void*> allocs;
+  DeviceArena arena;
   // prepared weights (device, swizzled; the last layer has only QKV)
   uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr;
   float *attn_s1 = nullptr, *ffn_s1 = nullptr;  // norm scales gamma [L][2048]
@@ -1024,22 +1176,15 @@ struct pi_ae_vlm {
   float* part = nullptr;  // split-K partial tiles, up to kVlmMaxSplit x Mpad x 2560
   int Mpad = 0, nkb_max = 0;
   hipStream_t cap = nullptr;
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  GraphCache<std::pair<int, int>> graphs;
 
   template <class T>
   T* dalloc(size_t n) {
-    void* p = nullptr;
-    if (n == 0) n = 1;
-    hipError_t e = hipMalloc(&p, n * sizeof(T));
-    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
-    allocs.push_back(p);
-    return static_cast<T*>(p);
+    return arena.alloc<T>(n);
   }
   void release() {
-    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
-    for (void* p : allocs) (void)hipFree(p);
-    allocs.clear();
+    arena.release();
     if (cap) (void)hipStreamDestroy(cap);
     cap = nullptr;
   }
@@ -1296,6 +1441,7 @@ PI_AE_API pi_ae_status pi_ae_vlm_prepare(const pi_ae_vlm_config* cfg, const pi_a
   pi_ae_vlm* ctx = new (std::nothrow) pi_ae_vlm();
   if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
   ctx->cfg = *cfg;
+  ctx->arena.arm_fault_injection();
   try {
     HIP_OR_THROW(hipGetDevice(&ctx->device));
     vlm_prepare(ctx, layers);
@@ -1324,23 +1470,16 @@ PI_AE_API pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const std::pair<int, int> key(batch, prefix_len);
-  auto it = ctx->graphs.find(key);
-  if (it == ctx->graphs.end()) {
-    hipGraph_t graph = nullptr;
+  auto* g = ctx->graphs.find(key);
+  if (!g) {
     hipGraphExec_t exec = nullptr;
-    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
-    if (e == hipSuccess) {
-      hipError_t e2 = vlm_enqueue(ctx, batch, prefix_len, ctx->cap);
-      e = hipStreamEndCapture(ctx->cap, &graph);
-      if (e2 != hipSuccess) e = e2;
-    }
-    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) (void)hipGraphDestroy(graph);
+    hipError_t e = capture_graph(ctx->cap, [&] { return vlm_enqueue(ctx, batch, prefix_len, ctx->cap); }, &exec);
+    if (e == hipSuccess) e = ctx->graphs.insert(key, exec, &g);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    it = ctx->graphs.emplace(key, exec).first;
   }
   hipError_t e = launch_vlm_stage(vlm_stage_for(ctx, prefix_emb, pad_mask, batch, prefix_len), s);
-  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::launch(g, s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::mark(g, s);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   kv_out->k = ctx->k_cache;
   kv_out->v = ctx->v_cache;
@@ -1353,8 +1492,7 @@ PI_AE_API void pi_ae_vlm_destroy(pi_ae_vlm* ctx) {
   if (!ctx) return;
   {
     DeviceGuard dg(ctx->device);
-    (void)hipDeviceSynchronize();
-    ctx->release();
+    ctx->release();  // waits for its own launched graphs, then frees
   }
   delete ctx;
 }
@@ -1400,11 +1538,8 @@ PI_AE_API pi_ae_status pi_ae_vlm_debug_time_phase(pi_ae_vlm* ctx, const uint16_t
 struct pi_ae_pipeline {
   pi_ae_vlm* vlm = nullptr;
   pi_ae_ctx* ctx = nullptr;
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
-  void release() {
-    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
-    graphs.clear();
-  }
+  GraphCache<std::pair<int, int>> graphs;
+  void release() { graphs.clear(); }
 };
 
 PI_AE_API pi_ae_status pi_ae_pipeline_create(pi_ae_vlm* vlm, pi_ae_ctx* expert, pi_ae_pipeline** out) {
@@ -1434,25 +1569,21 @@ PI_AE_API pi_ae_status pi_ae_pipeline_run(pi_ae_pipeline* pipe, const uint16_t* 
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const std::pair<int, int> key(batch, prefix_len);
-  auto it = pipe->graphs.find(key);
-  if (it == pipe->graphs.end()) {
-    hipGraph_t graph = nullptr;
+  auto* g = pipe->graphs.find(key);
+  if (!g) {
     hipGraphExec_t exec = nullptr;
-    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
-    if (e == hipSuccess) {
+    hipError_t e = capture_graph(ctx->cap, [&] {
       hipError_t e2 = vlm_enqueue(vlm, batch, prefix_len, ctx->cap);
-      if (e2 == hipSuccess) e2 = enqueue(ctx, batch, prefix_len, ctx->cap, StopAt{});
-      e = hipStreamEndCapture(ctx->cap, &graph);
-      if (e2 != hipSuccess) e = e2;
-    }
-    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) (void)hipGraphDestroy(graph);
+      if (e2 == hipSuccess) e2 = enqueue(ctx, ctx->ws, batch, prefix_len, ctx->cap, StopAt{});
+      return e2;
+    }, &exec);
+    if (e == hipSuccess) e = pipe->graphs.insert(key, exec, &g);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    it = pipe->graphs.emplace(key, exec).first;
   }
   hipError_t e = launch_vlm_stage(vlm_stage_for(vlm, prefix_emb, pad_mask, batch, prefix_len), s);
-  if (e == hipSuccess) e = launch_args(args_for(ctx, &kv, noise, actions, batch), s);
-  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e == hipSuccess) e = launch_args(args_for(ctx->ws, &kv, noise, actions, batch), s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::launch(g, s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::mark(g, s);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return PI_AE_OK;
 }
@@ -1461,8 +1592,7 @@ PI_AE_API void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe) {
   if (!pipe) return;
   {
     DeviceGuard dg(pipe->ctx->device);
-    (void)hipDeviceSynchronize();
-    pipe->release();
+    pipe->release();  // waits for its own launched graphs, then frees
   }
   delete pipe;
 }
@@ -1472,7 +1602,7 @@ struct pi_ae_vision {
   pi_ae_vision_config cfg{};
   int device = 0;
   bool broken = false;
-  std::vector<void*> allocs;
+  DeviceArena arena;
   // prepared weights (device, swizzled, K padded with zero columns)
   uint16_t *w_patch = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_fc1 = nullptr, *w_fc2 = nullptr,
            *w_proj = nullptr;
@@ -1484,22 +1614,15 @@ struct pi_ae_vision {
   float *h = nullptr, *part = nullptr;
   int Mpad = 0;
   hipStream_t cap = nullptr;
-  std::map<int, hipGraphExec_t> graphs;
+  GraphCache<int> graphs;
 
   template <class T>
   T* dalloc(size_t n) {
-    void* p = nullptr;
-    if (n == 0) n = 1;
-    hipError_t e = hipMalloc(&p, n * sizeof(T));
-    if (e != hipSuccess) throw HipError{e, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes"};
-    allocs.push_back(p);
-    return static_cast<T*>(p);
+    return arena.alloc<T>(n);
   }
   void release() {
-    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
-    for (void* p : allocs) (void)hipFree(p);
-    allocs.clear();
+    arena.release();
     if (cap) (void)hipStreamDestroy(cap);
     cap = nullptr;
   }
@@ -1780,6 +1903,7 @@ PI_AE_API pi_ae_status pi_ae_vision_prepare(const pi_ae_vision_config* cfg, cons
   pi_ae_vision* ctx = new (std::nothrow) pi_ae_vision();
   if (!ctx) return fail(PI_AE_ENOMEM, "host allocation failed");
   ctx->cfg = *cfg;
+  ctx->arena.arm_fault_injection();
   try {
     HIP_OR_THROW(hipGetDevice(&ctx->device));
     vis_prepare(ctx, w);
@@ -1806,26 +1930,21 @@ PI_AE_API pi_ae_status pi_ae_vision_encode(pi_ae_vision* ctx, const uint16_t* im
   if (st) return st;
   DeviceGuard dg(ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto it = ctx->graphs.find(views);
-  if (it == ctx->graphs.end()) {
-    hipGraph_t graph = nullptr;
+  auto* g = ctx->graphs.find(views);
+  if (!g) {
     hipGraphExec_t exec = nullptr;
-    hipError_t e = hipStreamBeginCapture(ctx->cap, hipStreamCaptureModeThreadLocal);
-    if (e == hipSuccess) {
+    hipError_t e = capture_graph(ctx->cap, [&] {
       int n = 0;
-      hipError_t e2 = vis_enqueue_layers(ctx, views, ctx->cap, -1, nullptr, &n);
-      e = hipStreamEndCapture(ctx->cap, &graph);
-      if (e2 != hipSuccess) e = e2;
-    }
-    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) (void)hipGraphDestroy(graph);
+      return vis_enqueue_layers(ctx, views, ctx->cap, -1, nullptr, &n);
+    }, &exec);
+    if (e == hipSuccess) e = ctx->graphs.insert(views, exec, &g);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    it = ctx->graphs.emplace(views, exec).first;
   }
   VisPatchParams pp{images, ctx->apatch, views};
   hipError_t e = launch_vis_patch(pp, s);
-  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e == hipSuccess) e = GraphCache<int>::launch(g, s);
   if (e == hipSuccess) e = vis_projector(ctx, views, tokens, s, nullptr);
+  if (e == hipSuccess) e = GraphCache<int>::mark(g, s);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return PI_AE_OK;
 }
@@ -1834,8 +1953,7 @@ PI_AE_API void pi_ae_vision_destroy(pi_ae_vision* ctx) {
   if (!ctx) return;
   {
     DeviceGuard dg(ctx->device);
-    (void)hipDeviceSynchronize();
-    ctx->release();
+    ctx->release();  // waits for its own launched graphs, then frees
   }
   delete ctx;
 }
@@ -1887,9 +2005,8 @@ struct pi_ae_inference {
   pi_ae_ctx* ctx = nullptr;
   uint16_t* prefix = nullptr;  // [max_prefix_len][2048] bf16: the views' tokens, then the prompt's
   uint8_t* mask = nullptr;     // [max_prefix_len]
-  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  GraphCache<std::pair<int, int>> graphs;
   void release() {
-    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
     if (prefix) (void)hipFree(prefix);
     if (mask) (void)hipFree(mask);
@@ -1938,26 +2055,21 @@ PI_AE_API pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t*
   DeviceGuard dg(inf->ctx->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const std::pair<int, int> key(views, prompt_len);
-  auto it = inf->graphs.find(key);
-  if (it == inf->graphs.end()) {
-    hipGraph_t graph = nullptr;
+  auto* g = inf->graphs.find(key);
+  if (!g) {
     hipGraphExec_t exec = nullptr;
     hipStream_t c = inf->ctx->cap;
-    hipError_t e = hipStreamBeginCapture(c, hipStreamCaptureModeThreadLocal);
-    if (e == hipSuccess) {
+    hipError_t e = capture_graph(c, [&] {
       int n = 0;
       hipError_t e2 = vis_enqueue_layers(inf->vis, views, c, -1, nullptr, &n);
       if (e2 == hipSuccess) e2 = vis_projector(inf->vis, views, inf->prefix, c, nullptr);
       if (e2 == hipSuccess) e2 = launch_vlm_stage(vlm_stage_for(inf->vlm, inf->prefix, inf->mask, 1, P), c);
       if (e2 == hipSuccess) e2 = vlm_enqueue(inf->vlm, 1, P, c);
-      if (e2 == hipSuccess) e2 = enqueue(inf->ctx, 1, P, c, StopAt{});
-      e = hipStreamEndCapture(c, &graph);
-      if (e2 != hipSuccess) e = e2;
-    }
-    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (graph) (void)hipGraphDestroy(graph);
+      if (e2 == hipSuccess) e2 = enqueue(inf->ctx, inf->ctx->ws, 1, P, c, StopAt{});
+      return e2;
+    }, &exec);
+    if (e == hipSuccess) e = inf->graphs.insert(key, exec, &g);
     if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("graph capture failed: ") + hipGetErrorString(e));
-    it = inf->graphs.emplace(key, exec).first;
   }
   hipError_t e = hipSuccess;
   if (prompt_len > 0)
@@ -1970,8 +2082,9 @@ PI_AE_API pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t*
     VisPatchParams pp{images, inf->vis->apatch, views};
     e = launch_vis_patch(pp, s);
   }
-  if (e == hipSuccess) e = launch_args(args_for(inf->ctx, &kv, noise, actions, 1), s);
-  if (e == hipSuccess) e = hipGraphLaunch(it->second, s);
+  if (e == hipSuccess) e = launch_args(args_for(inf->ctx->ws, &kv, noise, actions, 1), s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::launch(g, s);
+  if (e == hipSuccess) e = GraphCache<std::pair<int, int>>::mark(g, s);
   if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
   return PI_AE_OK;
 }
@@ -1980,8 +2093,38 @@ PI_AE_API void pi_ae_inference_destroy(pi_ae_inference* inf) {
   if (!inf) return;
   {
     DeviceGuard dg(inf->ctx->device);
-    (void)hipDeviceSynchronize();
-    inf->release();
+    inf->release();  // waits for its own launched graphs, then frees
   }
   delete inf;
 }
+
+// ====================================================================== guards
+PI_AE_API pi_ae_status pi_ae_debug_check_guards(const void* object, int32_t kind, int32_t corrupt,
+                                                int32_t* first_bad) {
+  if (!object || !first_bad || kind < 0 || kind > 2)
+    return fail(PI_AE_EINVAL, "check_guards: object and first_bad non-NULL, kind 0 (expert), 1 (VLM) or 2 (vision)");
+  DeviceArena* arena = nullptr;
+  int device = 0;
+  if (kind == 0) {
+    auto* c = static_cast<pi_ae_ctx*>(const_cast<void*>(object));
+    arena = &c->arena;
+    device = c->device;
+  } else if (kind == 1) {
+    auto* c = static_cast<pi_ae_vlm*>(const_cast<void*>(object));
+    arena = &c->arena;
+    device = c->device;
+  } else {
+    auto* c = static_cast<pi_ae_vision*>(const_cast<void*>(object));
+    arena = &c->arena;
+    device = c->device;
+  }
+  DeviceGuard dg(device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) *first_bad = arena->check(corrupt, &e);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("check_guards: ") + hipGetErrorString(e));
+  if (*first_bad >= 0)
+    return fail(PI_AE_ESTATE, "check_guards: the guard of allocation " + std::to_string(*first_bad) + " changed");
+  return PI_AE_OK;
+}
+
+PI_AE_API int64_t pi_ae_debug_live_device_bytes(void) { return g_live_device_bytes.load(); }

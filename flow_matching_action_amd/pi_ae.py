@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpi_ae.so")
+# the in-tree build; PI_AE_LIB names another build of the same library (the
+# host-sanitized one the CPU tests load)
+LIB_PATH = os.environ.get("PI_AE_LIB") or os.path.join(HERE, "libpi_ae.so")
 
 PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTATE = range(6)
 
@@ -23,7 +25,9 @@ EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_stat
            "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
            "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy",
            "pi_ae_vision_prepare", "pi_ae_vision_encode", "pi_ae_vision_destroy", "pi_ae_vision_debug_time_phase",
-           "pi_ae_inference_create", "pi_ae_inference_run", "pi_ae_inference_destroy")
+           "pi_ae_inference_create", "pi_ae_inference_run", "pi_ae_inference_destroy",
+           "pi_ae_debug_stream_read", "pi_ae_debug_graph_floor", "pi_ae_debug_grid_sync",
+           "pi_ae_debug_check_guards", "pi_ae_debug_live_device_bytes")
 
 
 class PiAeError(RuntimeError):
@@ -169,6 +173,20 @@ def load_library(path: str = LIB_PATH):
     lib.pi_ae_inference_run.restype = ctypes.c_int
     lib.pi_ae_inference_destroy.argtypes = [ctypes.c_void_p]
     lib.pi_ae_inference_destroy.restype = None
+    lib.pi_ae_debug_stream_read.argtypes = [ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_debug_stream_read.restype = ctypes.c_int
+    lib.pi_ae_debug_graph_floor.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_debug_graph_floor.restype = ctypes.c_int
+    lib.pi_ae_debug_grid_sync.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_float)]
+    lib.pi_ae_debug_grid_sync.restype = ctypes.c_int
+    lib.pi_ae_debug_check_guards.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int32)]
+    lib.pi_ae_debug_check_guards.restype = ctypes.c_int
+    lib.pi_ae_debug_live_device_bytes.argtypes = []
+    lib.pi_ae_debug_live_device_bytes.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -199,6 +217,31 @@ def _ptr(a):
             raise ValueError("device tensors must be contiguous")
         return a.data_ptr()
     return int(a)
+
+
+_DTYPES = {"bf16": ("torch.int16", "torch.uint16", "torch.bfloat16"), "f32": ("torch.float32",),
+           "u8": ("torch.uint8", "torch.int8", "torch.bool")}
+
+
+def _dev(t, name: str, kind: str, numel: int):
+    """Device pointer of a call buffer, after the checks the C ABI cannot make:
+    a contiguous torch tensor on the GPU, of the element type the call reads
+    (bf16 bits as int16 / bfloat16, fp32, or a byte mask), holding at least
+    ``numel`` elements.  None passes as NULL (the ABI rejects it where a buffer
+    is required)."""
+    if t is None:
+        return None
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_cuda"):
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if str(t.dtype) not in _DTYPES[kind]:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {_DTYPES[kind]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call reads {numel}")
+    return t.data_ptr()
 
 
 def _stream_handle(stream):
@@ -264,23 +307,29 @@ class Context:
         except Exception:
             pass
 
-    @staticmethod
-    def _kv(k, v, pad_mask, prefix_len):
-        return PrefixKV(_ptr(k), _ptr(v), _ptr(pad_mask), int(prefix_len))
+    def _kv(self, k, v, pad_mask, batch, prefix_len):
+        b, p = max(int(batch), 0), max(int(prefix_len), 0)
+        n = self.cfg.num_layers * b * p * self.cfg.head_dim
+        return PrefixKV(_dev(k, "k", "bf16", n), _dev(v, "v", "bf16", n), _dev(pad_mask, "pad_mask", "u8", b * p),
+                        int(prefix_len))
+
+    def _xbuf(self, t, name, batch):
+        return _dev(t, name, "f32", max(int(batch), 0) * self.cfg.chunk_len * self.cfg.action_dim)
 
     def sample(self, k, v, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
         """Enqueue pi_ae_sample on `stream` (torch tensors on the device)."""
-        kv = self._kv(k, v, pad_mask, prefix_len)
-        _check(self._lib.pi_ae_sample(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
-                                      _stream_handle(stream)))
+        kv = self._kv(k, v, pad_mask, batch, prefix_len)
+        _check(self._lib.pi_ae_sample(self._h, ctypes.byref(kv), self._xbuf(noise, "noise", batch),
+                                      self._xbuf(actions, "actions", batch), int(batch), _stream_handle(stream)))
 
     def time_phase(self, k, v, pad_mask, noise, actions, batch, prefix_len, phase, chunks, stream=None) -> float:
         """Mean duration (us) of one phase's kernel inside the loop: `chunks` whole
         passes on `stream`, a HIP event pair bound to each launch of that kernel."""
-        kv = self._kv(k, v, pad_mask, prefix_len)
+        kv = self._kv(k, v, pad_mask, batch, prefix_len)
         us = ctypes.c_float()
-        _check(self._lib.pi_ae_debug_time_phase(self._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
-                                                int(phase), int(chunks), _stream_handle(stream), ctypes.byref(us)))
+        _check(self._lib.pi_ae_debug_time_phase(self._h, ctypes.byref(kv), self._xbuf(noise, "noise", batch),
+                                                self._xbuf(actions, "actions", batch), int(batch), int(phase),
+                                                int(chunks), _stream_handle(stream), ctypes.byref(us)))
         return float(us.value)
 
     def table(self, which: int, n: int) -> np.ndarray:
@@ -296,8 +345,9 @@ class Context:
                   6: ((M, 32), np.float32), 7: ((M, 2048), np.uint16), 8: ((M, 8, 4), np.float32)}
         shape, dt = shapes[which]
         out = np.empty(shape, dt)
-        kv = self._kv(k, v, pad_mask, prefix_len)
-        _check(self._lib.pi_ae_debug_probe(self._h, ctypes.byref(kv), _ptr(noise), int(batch), int(step), int(layer),
+        kv = self._kv(k, v, pad_mask, batch, prefix_len)
+        _check(self._lib.pi_ae_debug_probe(self._h, ctypes.byref(kv), self._xbuf(noise, "noise", batch), int(batch),
+                                           int(step), int(layer),
                                            int(phase), int(which), out.ctypes.data, out.nbytes))
         return out
 
@@ -345,21 +395,26 @@ class Prefill:
     def run(self, emb, pad_mask, batch: int, prefix_len: int, stream=None) -> PrefixKV:
         """Enqueue pi_ae_vlm_prefill; returns the pi_ae_prefix_kv of the cache it fills."""
         kv = PrefixKV()
-        _check(self._lib.pi_ae_vlm_prefill(self._h, _ptr(emb), _ptr(pad_mask), int(batch), int(prefix_len),
-                                           ctypes.byref(kv), _stream_handle(stream)))
+        _check(self._lib.pi_ae_vlm_prefill(self._h, *self._in(emb, pad_mask, batch, prefix_len), int(batch),
+                                           int(prefix_len), ctypes.byref(kv), _stream_handle(stream)))
         return kv
+
+    def _in(self, emb, pad_mask, batch, prefix_len):
+        n = max(int(batch), 0) * max(int(prefix_len), 0)
+        return _dev(emb, "prefix_emb", "bf16", n * self.cfg.width), _dev(pad_mask, "pad_mask", "u8", n)
 
     def time_phase(self, emb, pad_mask, batch, prefix_len, phase, reps, stream=None) -> float:
         us = ctypes.c_float()
-        _check(self._lib.pi_ae_vlm_debug_time_phase(self._h, _ptr(emb), _ptr(pad_mask), int(batch), int(prefix_len),
-                                                    int(phase), int(reps), _stream_handle(stream), ctypes.byref(us)))
+        _check(self._lib.pi_ae_vlm_debug_time_phase(self._h, *self._in(emb, pad_mask, batch, prefix_len), int(batch),
+                                                    int(prefix_len), int(phase), int(reps), _stream_handle(stream),
+                                                    ctypes.byref(us)))
         return float(us.value)
 
 
 def sample_from_cache(ctx: "Context", kv: PrefixKV, noise, actions, batch: int, stream=None):
     """pi_ae_sample on the prefix cache a Prefill has just filled."""
-    _check(ctx._lib.pi_ae_sample(ctx._h, ctypes.byref(kv), _ptr(noise), _ptr(actions), int(batch),
-                                 _stream_handle(stream)))
+    _check(ctx._lib.pi_ae_sample(ctx._h, ctypes.byref(kv), ctx._xbuf(noise, "noise", batch),
+                                 ctx._xbuf(actions, "actions", batch), int(batch), _stream_handle(stream)))
 
 
 class Pipeline:
@@ -384,8 +439,10 @@ class Pipeline:
             pass
 
     def run(self, emb, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
-        _check(self._lib.pi_ae_pipeline_run(self._h, _ptr(emb), _ptr(pad_mask), _ptr(noise), _ptr(actions),
-                                            int(batch), int(prefix_len), _stream_handle(stream)))
+        e, m = self.prefill._in(emb, pad_mask, batch, prefix_len)
+        _check(self._lib.pi_ae_pipeline_run(self._h, e, m, self.ctx._xbuf(noise, "noise", batch),
+                                            self.ctx._xbuf(actions, "actions", batch), int(batch), int(prefix_len),
+                                            _stream_handle(stream)))
 
 
 def make_vision_config(cfg, max_views: int) -> VisionConfig:
@@ -434,13 +491,60 @@ class Vision:
 
     def encode(self, images, views: int, tokens, stream=None):
         """Enqueue pi_ae_vision_encode: images [views][224][224][3] bf16 -> tokens [views*256][2048] bf16."""
-        _check(self._lib.pi_ae_vision_encode(self._h, _ptr(images), int(views), _ptr(tokens), _stream_handle(stream)))
+        im, tk = self._io(images, views, tokens)
+        _check(self._lib.pi_ae_vision_encode(self._h, im, int(views), tk, _stream_handle(stream)))
+
+    def _io(self, images, views, tokens):
+        v = max(int(views), 0)
+        c = self.cfg
+        return (_dev(images, "images", "bf16", v * c.image * c.image * 3),
+                _dev(tokens, "tokens", "bf16", v * (c.image // c.patch) ** 2 * c.out_width))
 
     def time_phase(self, images, views, tokens, phase, reps, stream=None) -> float:
         us = ctypes.c_float()
-        _check(self._lib.pi_ae_vision_debug_time_phase(self._h, _ptr(images), int(views), _ptr(tokens), int(phase),
+        im, tk = self._io(images, views, tokens)
+        _check(self._lib.pi_ae_vision_debug_time_phase(self._h, im, int(views), tk, int(phase),
                                                        int(reps), _stream_handle(stream), ctypes.byref(us)))
         return float(us.value)
+
+
+def check_guards(obj, corrupt: int = -1) -> int:
+    """pi_ae_debug_check_guards on a Context / Prefill / Vision: -1 if every
+    guard is intact, else raises PiAeError (ESTATE) naming the first changed one."""
+    lib = load_library()
+    kind = {"Context": 0, "Prefill": 1, "Vision": 2}[type(obj).__name__]
+    bad = ctypes.c_int32(-1)
+    _check(lib.pi_ae_debug_check_guards(obj._h, kind, int(corrupt), ctypes.byref(bad)))
+    return bad.value
+
+
+def live_device_bytes() -> int:
+    """pi_ae_debug_live_device_bytes: device bytes held by the process's prepared objects."""
+    return int(load_library().pi_ae_debug_live_device_bytes())
+
+
+def stream_read_gbps(nbytes: int = 2 << 30, reps: int = 5, stream=None) -> float:
+    """pi_ae_debug_stream_read: the best plain streaming-read rate in GB/s."""
+    lib = load_library()
+    out = ctypes.c_float()
+    _check(lib.pi_ae_debug_stream_read(int(nbytes), int(reps), _stream_handle(stream), ctypes.byref(out)))
+    return float(out.value)
+
+
+def graph_floor_us(kernels: int = 200, grid: int = 256, stream=None) -> float:
+    """pi_ae_debug_graph_floor: time per kernel of a replayed graph of empty dependent kernels."""
+    lib = load_library()
+    out = ctypes.c_float()
+    _check(lib.pi_ae_debug_graph_floor(int(kernels), int(grid), _stream_handle(stream), ctypes.byref(out)))
+    return float(out.value)
+
+
+def grid_sync_us(rounds: int = 2000, mode: int = 0, stream=None) -> float:
+    """pi_ae_debug_grid_sync: time per grid-wide barrier round inside one persistent kernel."""
+    lib = load_library()
+    out = ctypes.c_float()
+    _check(lib.pi_ae_debug_grid_sync(int(rounds), int(mode), _stream_handle(stream), ctypes.byref(out)))
+    return float(out.value)
 
 
 class Inference:
@@ -465,5 +569,10 @@ class Inference:
             pass
 
     def run(self, images, views: int, prompt_emb, prompt_len: int, pad_mask, noise, actions, stream=None):
-        _check(self._lib.pi_ae_inference_run(self._h, _ptr(images), int(views), _ptr(prompt_emb), int(prompt_len),
-                                             _ptr(pad_mask), _ptr(noise), _ptr(actions), _stream_handle(stream)))
+        im, _ = self.vision._io(images, views, None)
+        c = self.vision.cfg
+        n = max(int(views), 0) * (c.image // c.patch) ** 2 + max(int(prompt_len), 0)
+        pe = _dev(prompt_emb, "prompt_emb", "bf16", max(int(prompt_len), 0) * self.prefill.cfg.width)
+        _check(self._lib.pi_ae_inference_run(self._h, im, int(views), pe, int(prompt_len),
+                                             _dev(pad_mask, "pad_mask", "u8", n), self.ctx._xbuf(noise, "noise", 1),
+                                             self.ctx._xbuf(actions, "actions", 1), _stream_handle(stream)))

@@ -170,7 +170,10 @@ pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_ae_weights*
  * call.  One call in flight per context: concurrent calls on one context (on
  * any streams) race on its workspaces; use one context per concurrent stream.
  * The step sequence is captured as a hipGraph per (batch, prefix_len) on first
- * use and replayed afterwards.  Errors: EINVAL (NULL ctx/kv/noise/actions,
+ * use and replayed afterwards; a context keeps at most 8 such graphs (the
+ * least recently used is dropped, after its last launch has finished), so
+ * callers with many prefix lengths should pad them to a few fixed ones.
+ * Errors: EINVAL (NULL ctx/kv/noise/actions,
  * batch or prefix_len out of range, misaligned pointers), ESTATE (ctx
  * unusable), EHIP (a launch failed).  Device faults surface at the caller's
  * next synchronisation.
@@ -178,11 +181,14 @@ pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_ae_weights*
 pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
                           int32_t batch, void* stream);
 
-/* Synchronise the context's device, then free everything it owns.  NULL is a no-op. */
+/* Wait for the work this context has enqueued (the graphs it launched, on
+ * whatever streams), then free everything it owns.  Other work on the device
+ * is not waited for.  NULL is a no-op. */
 void pi_ae_destroy(pi_ae_ctx* ctx);
 
-/* Static string for a status code. */
-const char* pi_ae_status_string(pi_ae_status status);
+/* Static string for a status code: any integer (a pi_ae_status value, or
+ * anything else, which gives "unknown status"). */
+const char* pi_ae_status_string(int32_t status);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pi_ae_last_error(void);
@@ -278,8 +284,9 @@ pi_ae_status pi_ae_vlm_prepare(const pi_ae_vlm_config* cfg, const pi_ae_vlm_laye
 pi_ae_status pi_ae_vlm_prefill(pi_ae_vlm* ctx, const uint16_t* prefix_emb, const uint8_t* pad_mask, int32_t batch,
                                int32_t prefix_len, pi_ae_prefix_kv* kv_out, void* stream);
 
-/* Synchronise the context's device, then free everything it owns (the cache
- * included).  NULL is a no-op. */
+/* Wait for the work this context has enqueued, then free everything it owns
+ * (the cache included).  A pipeline or inference object that joins this
+ * context must be destroyed first.  NULL is a no-op. */
 void pi_ae_vlm_destroy(pi_ae_vlm* ctx);
 
 /* The VLM prefill and the denoise loop as one pipeline (RV-blog sections
@@ -302,7 +309,8 @@ pi_ae_status pi_ae_pipeline_create(pi_ae_vlm* vlm, pi_ae_ctx* expert, pi_ae_pipe
 pi_ae_status pi_ae_pipeline_run(pi_ae_pipeline* pipe, const uint16_t* prefix_emb, const uint8_t* pad_mask,
                                 const float* noise, float* actions, int32_t batch, int32_t prefix_len, void* stream);
 
-/* Free the pipeline's graphs (not the two contexts).  NULL is a no-op. */
+/* Wait for the pipeline's own launched graphs, then free them (not the two
+ * contexts, which must outlive it).  NULL is a no-op. */
 void pi_ae_pipeline_destroy(pi_ae_pipeline* pipe);
 
 /* Test-only: time one kernel of the prefill in its real sequence, as
@@ -385,7 +393,8 @@ pi_ae_status pi_ae_vision_prepare(const pi_ae_vision_config* cfg, const pi_ae_vi
 pi_ae_status pi_ae_vision_encode(pi_ae_vision* ctx, const uint16_t* images, int32_t views, uint16_t* tokens,
                                  void* stream);
 
-/* Synchronise the context's device, then free everything it owns.  NULL is a no-op. */
+/* Wait for the work this context has enqueued, then free everything it owns.
+ * An inference object that joins it must be destroyed first.  NULL is a no-op. */
 void pi_ae_vision_destroy(pi_ae_vision* ctx);
 
 /* The whole inference as one graph (RV-blog sections "CUDA Graph" and
@@ -411,7 +420,8 @@ pi_ae_status pi_ae_inference_run(pi_ae_inference* inf, const uint16_t* images, i
                                  const uint16_t* prompt_emb, int32_t prompt_len, const uint8_t* pad_mask,
                                  const float* noise, float* actions, void* stream);
 
-/* Free the object's graphs and static buffers (not the contexts).  NULL is a no-op. */
+/* Wait for the object's own launched graphs, then free them and its static
+ * buffers (not the contexts, which must outlive it).  NULL is a no-op. */
 void pi_ae_inference_destroy(pi_ae_inference* inf);
 
 /* Test-only: time one kernel of the encoder in its real sequence (as
@@ -481,6 +491,52 @@ pi_ae_status pi_ae_debug_probe(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const 
  * plus batch >= 1 and 1 <= chunks <= 1000. */
 pi_ae_status pi_ae_debug_time_phase(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
                                     int32_t batch, int32_t phase, int32_t chunks, void* stream, float* avg_us);
+
+/* Check the guard bytes around every device allocation of a prepared object
+ * (kind 0: pi_ae_ctx, 1: pi_ae_vlm, 2: pi_ae_vision): each allocation is
+ * flanked by 256 bytes of a fixed pattern, and a kernel that wrote past either
+ * end of a buffer leaves a changed guard.  Synchronises the device first.
+ * corrupt >= 0 first overwrites one guard byte of allocation `corrupt` from
+ * the host (a test of the check itself; the object stays usable).  Returns
+ * PI_AE_OK with *first_bad = -1, or PI_AE_ESTATE with *first_bad = the first
+ * allocation whose guard changed.  (Test-only.  A prepared object's device
+ * allocations also honour PI_AE_FAIL_ALLOC=N in the environment, read when it
+ * is prepared: its N-th allocation then fails as out of memory.) */
+pi_ae_status pi_ae_debug_check_guards(const void* object, int32_t kind, int32_t corrupt, int32_t* first_bad);
+
+/* Device bytes held by every prepared object of the process (expert, VLM and
+ * vision contexts; guards included): what a failed preparation must leave
+ * unchanged.  (Test-only.) */
+int64_t pi_ae_debug_live_device_bytes(void);
+
+/* ---------------------------------------------------------------------------
+ * Measurement diagnostics (test-only; no context needed).  They measure the
+ * floors under the loop's design on the current device (Realtime-VLA
+ * technical blog, section 5: the roofline lower bound is the weights streamed
+ * once per step; sections "CUDA Graph" and 4: the loop is a replayed graph of
+ * about 900 decoder kernels).  Each allocates and frees its own device
+ * buffers, runs on `stream` (NULL: the null stream) and synchronises it.
+ * ------------------------------------------------------------------------- */
+
+/* Plain streaming read of a `bytes` buffer (1 MiB .. 16 GiB), `reps` timed
+ * passes (1 .. 1000) after one warm-up; *gbps = the best pass's rate in GB/s
+ * (1e9 bytes per second). */
+pi_ae_status pi_ae_debug_stream_read(size_t bytes, int32_t reps, void* stream, float* gbps);
+
+/* A graph of `kernels` (1 .. 4096) dependent empty kernels of `grid`
+ * (1 .. 65536) workgroups of 256 threads, replayed 10 times after 2 warm-up
+ * replays; *us_per_kernel = elapsed time / (10 * kernels): what each kernel
+ * boundary of a replayed graph costs with no work in it. */
+pi_ae_status pi_ae_debug_graph_floor(int32_t kernels, int32_t grid, void* stream, float* us_per_kernel);
+
+/* `rounds` (1 .. 100000) grid-wide barriers inside one kernel of one
+ * workgroup per CU.  mode 0: per-workgroup flags, each on its own 128-byte
+ * line, stored with agent scope and polled by every workgroup; mode 1:
+ * counters per XCD residue (workgroup index mod 8) whose last arriver bumps
+ * one global counter.  *us_per_round = elapsed time / rounds.  Every wait is
+ * bounded: PI_AE_ESTATE if one passed its spin limit (the kernel still ends),
+ * PI_AE_EUNSUPPORTED if one workgroup per CU cannot be resident. */
+pi_ae_status pi_ae_debug_grid_sync(int32_t rounds, int32_t mode, void* stream, float* us_per_round);
 
 #ifdef __cplusplus
 }

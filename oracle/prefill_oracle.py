@@ -30,9 +30,12 @@ design notes):
     expert attends to these keys with its own 256-wide heads);
   * attention is bidirectional over the prefix: every token attends to every
     valid (pad mask 1) token of its episode, masked keys excluded exactly;
-  * token j of an episode sits at RoPE position j (rotate-half pairs, base
-    10000, as for the expert's keys); the cache holds the rotated keys, which
-    is what the expert expects of its prefix cache;
+  * a token sits at the RoPE position given by the number of valid tokens
+    before it in its episode (rotate-half pairs, base 10000, as for the
+    expert's keys): the valid tokens take positions 0 .. n_valid - 1 in order
+    whatever pads lie between them, which is where the expert's suffix, at
+    n_valid + j, continues them; the cache holds the rotated keys, which is
+    what the expert expects of its prefix cache;
   * the MLP is GELU(tanh)(x W_g^T) * (x W_u^T), then W_d;
   * an episode without any valid token has no softmax support: its attention
     output is taken as 0.
@@ -77,6 +80,18 @@ def prefill_layer(get, l: int, h, key_valid, positions, cfg, kv_only: bool = Fal
     return h + m @ get("down.w").T, k, v
 
 
+def token_positions(key_valid):
+    """RoPE position of every prefix token: the number of valid tokens before it.
+
+    (The expert's suffix token j sits at n_valid + j, right after the valid
+    prefix tokens; this places those at 0 .. n_valid - 1 in order, so that pads
+    anywhere in the prefix leave no gap in the positions.  With trailing pads it
+    is simply the token's index.)
+    """
+    v = np.asarray(key_valid, bool)
+    return np.concatenate([[0], np.cumsum(v)[:-1]]) if v.size else np.zeros(0, np.int64)
+
+
 def prefill(weight_bits: dict, cfg, emb_bits, pad_mask, dtype=np.float64, full_last_layer: bool = False,
             layers=None):
     """The prefix KV cache of every layer.
@@ -96,7 +111,6 @@ def prefill(weight_bits: dict, cfg, emb_bits, pad_mask, dtype=np.float64, full_l
     d = cfg.num_kv_heads * cfg.head_dim
     K = np.empty((L, B, P, d), dtype)
     V = np.empty((L, B, P, d), dtype)
-    positions = np.arange(P)
     cache = {}
 
     def getter(l):
@@ -114,5 +128,6 @@ def prefill(weight_bits: dict, cfg, emb_bits, pad_mask, dtype=np.float64, full_l
         get = getter(l)
         last = (l == cfg.num_layers - 1) and not full_last_layer
         for b in range(B):
-            hs[b], K[l, b], V[l, b] = prefill_layer(get, l, hs[b], valid[b], positions, cfg, kv_only=last)
+            hs[b], K[l, b], V[l, b] = prefill_layer(get, l, hs[b], valid[b], token_positions(valid[b]), cfg,
+                                                    kv_only=last)
     return K, V

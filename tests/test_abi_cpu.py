@@ -16,7 +16,16 @@ from oracle import pi_ae_oracle as O
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pi_ae.h")
 
-needs_lib = pytest.mark.skipif(not os.path.exists(pi_ae.LIB_PATH), reason="libpi_ae.so not built")
+def _has_hipcc():
+    import shutil
+    return bool(shutil.which("hipcc")) or os.path.exists("/opt/rocm/bin/hipcc")
+
+
+# Where the toolchain is present the library must have been built (a missing
+# build is a failure, not a skip); only a machine without hipcc skips.
+needs_lib = pytest.mark.skipif(not os.path.exists(pi_ae.LIB_PATH) and not _has_hipcc(),
+                               reason="no ROCm toolchain to build libpi_ae.so")
+
 
 
 def header_functions():
@@ -66,7 +75,9 @@ def _tiny_weights(cfg):
     ("chunk_len", 0, pi_ae.PI_AE_EINVAL),
     ("chunk_len", 257, pi_ae.PI_AE_EINVAL),
     ("max_batch", 0, pi_ae.PI_AE_EINVAL),
+    ("max_batch", 1025, pi_ae.PI_AE_EINVAL),
     ("max_prefix_len", -1, pi_ae.PI_AE_EINVAL),
+    ("max_prefix_len", 8193, pi_ae.PI_AE_EINVAL),
     ("rope_base", 0.0, pi_ae.PI_AE_EINVAL),
     ("final_norm", 2, pi_ae.PI_AE_EINVAL),
 ])
@@ -81,6 +92,19 @@ def test_config_validation(field, value, status):
     assert lib.pi_ae_prepare_weights(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == status
     assert h.value is None
     assert lib.pi_ae_last_error() != b""
+
+
+@needs_lib
+def test_rows_per_gemm_limit():
+    """max_batch x chunk_len (the rows of every GEMM) is limited to 65536."""
+    cfg = inputs.WORKLOADS["c1"].cfg
+    mw = pi_ae._MarshalledWeights(cfg, _tiny_weights(cfg))
+    lib = pi_ae.load_library()
+    for batch, T, status in [(1024, 65, pi_ae.PI_AE_EINVAL), (257, 256, pi_ae.PI_AE_EINVAL)]:
+        c = pi_ae.make_config(cfg.replace(chunk_len=T), batch, 16)
+        h = ctypes.c_void_p()
+        assert lib.pi_ae_prepare_weights(ctypes.byref(c), ctypes.byref(mw.w), ctypes.byref(h)) == status
+        assert h.value is None and b"65536" in lib.pi_ae_last_error()
 
 
 @needs_lib

@@ -5,8 +5,14 @@ Bar (per the target of this path): on the final actions, relative L2 error
 seeded inputs; the relative L2 error of the integrated displacement
 (x_final - x_0) is checked too (<= 2e-2), because x_final is dominated by
 the noise that both sides share.  Intermediates of one step are compared
-phase by phase (bf16 storage of activations gives ~0.4% per element, so
-those use relative L2 <= 2e-2).  Invariances that hold exactly for this
+phase by phase: each is stored in bf16 (a relative rounding of at most 2^-9
+per element) from bf16 operands, so the relative L2 error is about 1.6e-3
+(two such roundings in quadrature) and the largest element error a few times
+that in units of the tensor's RMS; the bars are relative L2 <= 5e-3 and,
+element by element, |error| <= 2.5e-2 x RMS(reference) + 2^-6 x |reference|
+(an absolute part for elements near zero, whose error is the propagated
+rounding of their inputs, and four bf16 units relative for the large ones),
+which an error confined to one head, row tile or column tile would exceed.  Invariances that hold exactly for this
 implementation (no atomics, row-independent GEMM tiles) are checked bitwise.
 """
 import time
@@ -65,6 +71,27 @@ class Run:
         ctx.sample(self.dk, self.dv, self.dmask, self.dnoise, out, self.B, self.P, stream)
         torch.cuda.synchronize()
         return out.cpu().numpy()
+
+
+TOL_PROBE_REL_L2 = 5e-3
+TOL_PROBE_ABS_RMS = 2.5e-2
+TOL_PROBE_REL = 2.0 ** -6
+
+
+def check_probe(name, got, ref):
+    """One phase's intermediate against the oracle's: relative L2, and every
+    element within 2.5e-2 RMS + 2^-6 of its own magnitude (the worst ratio of
+    error to that bound is logged)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    e = rel_l2(got, ref)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    worst = float(np.max(err / (TOL_PROBE_ABS_RMS * rms + TOL_PROBE_REL * np.abs(ref))))
+    log(f"  {name}: rel_l2={e:.3e} max_abs/rms={float(np.max(err)) / max(rms, 1e-30):.3e} "
+        f"worst element / bound={worst:.3f}")
+    assert np.all(np.isfinite(got)), name
+    assert e <= TOL_PROBE_REL_L2 and worst <= 1.0, (name, e, worst)
 
 
 def check_actions(x_gpu, x_ref, noise, tag):
@@ -139,9 +166,10 @@ def test_c1_phase_by_phase(c1_setup):
     ks = bf(probe(1, 2))
     vs = bf(probe(1, 3))
     for name, got in [("q", q), ("ks", ks), ("vs", vs)]:
-        e = rel_l2(got, ref[name])
-        log(f"  {name}: rel_l2={e:.3e}")
-        assert e < 2e-2, name
+        check_probe(name, got, ref[name])
+    # per head as well: an error confined to one head must not hide in the whole
+    for hd in range(8):
+        check_probe(f"q head {hd}", q[:, hd], ref["q"][:, hd])
     M, nkb = w.cfg.chunk_len, (run.P + w.cfg.chunk_len + 31) // 32
     if M < 129 and nkb >= 16:
         # the keys of every query are split into two ranges: merge the two
@@ -158,21 +186,15 @@ def test_c1_phase_by_phase(c1_setup):
         tag = "o (two key ranges merged)"
     else:
         o, tag = bf(probe(2, 4)), "o"
-    e = rel_l2(o, ref["o"])
-    log(f"  {tag}: rel_l2={e:.3e}")
-    assert e < 2e-2
+    check_probe(tag, o, ref["o"])
+    for hd in range(8):
+        check_probe(f"o head {hd}", o[:, hd * 256:(hd + 1) * 256], ref["o"][:, hd * 256:(hd + 1) * 256])
     h1 = probe(3, 0)
-    e = rel_l2(h1 - h0, ref["h1"] - ref["h0"])
-    log(f"  h1-h0: rel_l2={e:.3e}")
-    assert e < 2e-2
+    check_probe("h1-h0", h1 - h0, ref["h1"] - ref["h0"])
     m = bf(probe(4, 5))
-    e = rel_l2(m, ref["m"])
-    log(f"  m: rel_l2={e:.3e}")
-    assert e < 2e-2
+    check_probe("m", m, ref["m"])
     h2 = probe(5, 0)
-    e = rel_l2(h2 - h1, ref["h2"] - ref["h1"])
-    log(f"  h2-h1: rel_l2={e:.3e}")
-    assert e < 2e-2
+    check_probe("h2-h1", h2 - h1, ref["h2"] - ref["h1"])
 
 
 def test_c1_end_to_end(c1_setup):
@@ -197,22 +219,30 @@ def test_batch1_configs(name):
     ctx.close()
 
 
-def test_c5_batched_sampled_episodes():
-    """32 episodes at once; the oracle checks three of them one by one (the
-    episodes are independent, so each alone is the exact reference)."""
+@pytest.fixture(scope="module")
+def c5_run():
+    """The 32 episodes of c5 in one call (run once; the tests below check them
+    against the oracle eight at a time)."""
     w = inputs.WORKLOADS["c5"]
     wb, k, v, mask, noise = inputs.make_workload_inputs(w)
     log("[c5] preparing")
     ctx = pi_ae.Context(w.cfg, wb, w.batch, w.prefix_len)
     x = Run(k, v, mask, noise).sample(ctx)
+    ctx.close()
     assert np.all(np.isfinite(x))
-    W = O.Weights(wb, w.cfg)
-    for b in [0, 13, 31]:
+    return w, wb, k, v, mask, noise, x, O.Weights(wb, w.cfg)
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_c5_every_episode(c5_run, group):
+    """All 32 episodes of the batched call, each against the oracle run on that
+    episode alone (episodes are independent, so that is the exact reference)."""
+    w, wb, k, v, mask, noise, x, W = c5_run
+    for b in range(8 * group, 8 * group + 8):
         t0 = time.time()
         x_ref = O.sample(wb, w.cfg, k[:, b:b + 1], v[:, b:b + 1], mask[b:b + 1], noise[b:b + 1], weights=W)
         log(f"[c5] episode {b} oracle {time.time() - t0:.1f}s")
         check_actions(x[b:b + 1], x_ref, noise[b:b + 1], f"c5[{b}]")
-    ctx.close()
 
 
 # ------------------------------------------------------------------ edge cases
@@ -329,13 +359,24 @@ def test_in_place_zero_batch_and_errors(small_ctx):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(buf.cpu().numpy(), ref)
     ctx.sample(run.dk, run.dv, None, run.dnoise, run.dnoise, 0, P)  # batch 0: nothing happens
+    # limits the library checks (buffers large enough for the binding's own checks)
+    L, T = SMALL.num_layers, SMALL.chunk_len
+    big_kv = torch.zeros(L * 5 * 97 * 256, dtype=torch.int16, device="cuda")
+    big_x = torch.zeros(5 * T * 32, dtype=torch.float32, device="cuda")
     with pytest.raises(pi_ae.PiAeError) as e:
-        ctx.sample(run.dk, run.dv, None, run.dnoise, buf, 5, P)
+        ctx.sample(big_kv, big_kv, None, big_x, big_x, 5, P)
     assert e.value.status == pi_ae.PI_AE_EINVAL
     with pytest.raises(pi_ae.PiAeError):
-        ctx.sample(run.dk, run.dv, None, run.dnoise, buf, B, 97)
+        ctx.sample(big_kv, big_kv, None, big_x, big_x, B, 97)
+    # what the binding refuses before the call: not contiguous, too small, wrong dtype, host memory
     with pytest.raises(ValueError):
-        ctx.sample(run.dk, run.dv, None, run.dnoise[:, :, 1:], buf, B, P)  # not contiguous -> binding refuses
+        ctx.sample(run.dk, run.dv, None, run.dnoise[:, :, 1:], buf, B, P)
+    with pytest.raises(ValueError):
+        ctx.sample(run.dk, run.dv, None, run.dnoise[:1], buf, B, P)
+    with pytest.raises(TypeError):
+        ctx.sample(run.dk.float(), run.dv, None, run.dnoise, buf, B, P)
+    with pytest.raises(ValueError):
+        ctx.sample(run.dk, run.dv, None, run.dnoise.cpu(), buf, B, P)
     mis = torch.empty(run.dnoise.numel() + 1, device="cuda")[1:]
     with pytest.raises(pi_ae.PiAeError) as e:
         ctx.sample(run.dk, run.dv, None, run.dnoise, mis, B, P)
@@ -377,3 +418,77 @@ def test_pi0_many_rows_tiled_path():
     for b in range(B):
         check_actions(x[b], ref[b], noise[b], f"pi0-tiled[{b}]")
     ctx.close()
+
+
+# ------------------------------------------------------------------ every shape the ABI accepts
+def _ragged_case(cfg, B, P, seed):
+    k, v = inputs.make_prefix_kv(cfg, B, P, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    mask = (rng.random((B, P)) < 0.8).astype(np.uint8) if P else None
+    noise = inputs.make_noise(cfg, B, seed=seed + 2)
+    return k, v, mask, noise
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (1, 64), (1, 65), (1, 128), (1, 129), (1, 256), (2, 64), (3, 1)])
+def test_chunk_lengths(B, T):
+    """Chunk lengths across the ABI's range [1, 256], on both sides of the
+    switch from the weight-streaming GEMMs (up to 128 rows) to the tiled ones
+    (129 rows on), at batch 1 and above; 2 layers, 2 steps, holed masks."""
+    cfg = SMALL.replace(chunk_len=T)
+    wb = inputs.make_weights(cfg, seed=31, cache=False)
+    P = 100
+    ctx = pi_ae.Context(cfg, wb, max_batch=B, max_prefix_len=P)
+    k, v, mask, noise = _ragged_case(cfg, B, P, seed=40 + T)
+    x = Run(k, v, mask, noise).sample(ctx)
+    x_ref = O.sample(wb, cfg, k, v, mask, noise)
+    for b in range(B):
+        check_actions(x[b:b + 1], x_ref[b:b + 1], noise[b:b + 1], f"T={T} B={B} [{b}]")
+    ctx.close()
+
+
+def test_without_final_norm():
+    """final_norm = 0: action_out_proj reads the residual stream directly."""
+    w = inputs.WORKLOADS["c1"]
+    cfg = w.cfg.replace(final_norm=False)
+    wb, k, v, mask, noise = inputs.make_workload_inputs(w)
+    ctx = pi_ae.Context(cfg, wb, w.batch, w.prefix_len)
+    x = Run(k, v, mask, noise).sample(ctx)
+    check_actions(x, O.sample(wb, cfg, k, v, mask, noise), noise, "c1 final_norm=0")
+    ctx.close()
+
+
+def test_longest_prefixes():
+    """Prefixes of 4096 and of the ABI's maximum 8192 keys (batch 1, 2 layers,
+    1 step), with pads in the middle of the prefix."""
+    cfg = inputs.WORKLOADS["c1"].cfg
+    wb = inputs.make_weights(cfg)
+    ctx = pi_ae.Context(cfg, wb, 1, 8192)
+    for P in (4096, 8192):
+        k, v = inputs.make_prefix_kv(cfg, 1, P, seed=P)
+        mask = np.ones((1, P), np.uint8)
+        mask[0, P // 3:P // 3 + 100] = 0
+        noise = inputs.make_noise(cfg, 1, seed=P + 1)
+        x = Run(k, v, mask, noise).sample(ctx)
+        check_actions(x, O.sample(wb, cfg, k, v, mask, noise), noise, f"P={P}")
+    ctx.close()
+
+
+def test_largest_batch():
+    """The ABI's largest call: 1024 episodes x 64 actions (65536 rows per GEMM),
+    2 layers, 1 step.  Eight distinct episodes are repeated over the batch:
+    each of the eight against the oracle, and every repeat bitwise equal to
+    its first occurrence (episodes are independent and every row takes the
+    same arithmetic)."""
+    cfg = SMALL.replace(chunk_len=64, num_steps=1, dt=-1.0)
+    wb = inputs.make_weights(cfg, seed=51, cache=False)
+    B, P, U = 1024, 40, 8
+    ctx = pi_ae.Context(cfg, wb, max_batch=B, max_prefix_len=P)
+    k8, v8, mask8, noise8 = _ragged_case(cfg, U, P, seed=60)
+    rep = np.arange(B) % U
+    k, v = np.ascontiguousarray(k8[:, rep]), np.ascontiguousarray(v8[:, rep])
+    x = Run(k, v, np.ascontiguousarray(mask8[rep]), np.ascontiguousarray(noise8[rep])).sample(ctx)
+    ctx.close()
+    x_ref = O.sample(wb, cfg, k8, v8, mask8, noise8)
+    for b in range(U):
+        check_actions(x[b:b + 1], x_ref[b:b + 1], noise8[b:b + 1], f"B=1024 [{b}]")
+    np.testing.assert_array_equal(x, x[rep])

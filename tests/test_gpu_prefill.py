@@ -280,3 +280,52 @@ def test_pipeline_graph_equals_separate_calls():
         pipe.close()
         ctx.close()
         pf.close()
+
+
+def test_holed_and_left_padded_prompts_then_loop():
+    """Pads inside the prefix (a hole) and in front of it (left padding): every
+    token sits at the count of valid tokens before it, the expert's suffix
+    right after the valid ones.  The cache against the oracle prefill, then the
+    loop on it against the oracle chain, then the same through the pipeline
+    graph (bitwise equal to the separate calls)."""
+    L = 2
+    cfg = inputs.PrefillConfig(num_layers=L)
+    ecfg = inputs.ExpertConfig(num_layers=L, num_steps=2, dt=-0.5)
+    w = inputs.make_prefill_weights(cfg)
+    ew = inputs.make_weights(ecfg)
+    B, P = 2, 120
+    mask = np.ones((B, P), np.uint8)
+    mask[0, 40:60] = 0      # a hole in the middle
+    mask[0, 110:] = 0       # and trailing pads
+    mask[1, :30] = 0        # left padding
+    emb = inputs.make_prefix_embeddings(cfg, B, P, seed=77)
+    noise = inputs.make_noise(ecfg, B, seed=78)
+    pf = pi_ae.Prefill(cfg, w, B, P)
+    ctx = pi_ae.Context(ecfg, ew, B, P)
+    pipe = pi_ae.Pipeline(pf, ctx)
+    try:
+        log("step: prefill with holed / left-padded masks")
+        demb, dmask, dnoise = to_dev(emb), to_dev(mask), to_dev(noise)
+        kv = pf.run(demb, dmask, B, P)
+        torch.cuda.synchronize()
+        k, v = cache_to_host(kv, L, B, P)
+        K, V = PO.prefill(w, cfg, emb, mask)
+        check_cache(k, v, K, V, "p-holed")
+        a_sep = torch.empty_like(dnoise)
+        pi_ae.sample_from_cache(ctx, kv, dnoise, a_sep, B)
+        torch.cuda.synchronize()
+        a_pipe = torch.empty_like(dnoise)
+        pipe.run(demb, dmask, dnoise, a_pipe, B, P)
+        torch.cuda.synchronize()
+        x = a_sep.cpu().numpy()
+        assert np.array_equal(x, a_pipe.cpu().numpy())
+    finally:
+        pipe.close()
+        ctx.close()
+        pf.close()
+    ref = O.sample(ew, ecfg, inputs.f32_to_bf16_bits(K.astype(np.float32)),
+                   inputs.f32_to_bf16_bits(V.astype(np.float32)), mask, noise)
+    for b in range(B):
+        e, mx = rel_l2(x[b], ref[b]), float(np.max(np.abs(x[b] - ref[b])))
+        log(f"[prefill+loop holed b={b}] rel_l2={e:.3e} max_abs={mx:.3e}")
+        assert e <= TOL_REL_L2 and mx <= TOL_MAX_ABS

@@ -423,6 +423,49 @@ def test_degenerate_sizes():
     np.testing.assert_allclose(x2, x, rtol=1e-14, atol=1e-15)
 
 
+def test_suffix_positions_follow_valid_prefix_count():
+    """Suffix token j sits at RoPE position n_valid + j (reading of the blog's
+    prefix/suffix softmax kernel, which reads the prefix's valid length).
+
+    Closed form, independent of the oracle's position code: prefix key i is
+    the fixed vector c rotated at its own index i (complex form, written here),
+    every suffix query is alpha * c before its rotation, suffix keys and values
+    are zero, and value i carries i in channel 0.  <R_p c, R_i c> =
+    sum_e |c_e|^2 cos((p - i) theta_e) is largest exactly at i = p, so with a
+    large alpha the attention output of suffix token j is the index of the
+    valid prefix key at its position.  A holed mask makes n_valid + j, P + j,
+    j and n_valid + j + 1 land on different keys.
+    """
+    D, d, H, T, P = 64, 16, 2, 2, 64
+    cfg = inputs.ExpertConfig(num_layers=1, width=D, mlp_dim=32, num_heads=H, head_dim=d,
+                              action_dim=4, chunk_len=T, num_steps=1, final_norm=False)
+    w = {n: np.zeros(sh, np.float64) for n, sh in inputs.weight_shapes(cfg)}
+    w["action_in.b"][0] = 1.0                       # h = e_0 for every token; u = sqrt(D) e_0
+    w["layers.0.attn_mod.b"][2 * D:] = 1.0          # attention gate 1 (scale 0, shift 0)
+    c = np.zeros(d)
+    c[:d // 2] = 1.0                                # every rotated pair, unit weight
+    alpha = 512.0
+    w["layers.0.q.w"][:d, 0] = alpha * c / math.sqrt(D)   # head 0 query = alpha c
+    w["layers.0.o.w"][0, 0] = 1.0                   # h[:, 0] += head 0's output channel 0
+    w["action_out.w"][0, 0] = 1.0                   # v[:, 0] = h[:, 0]
+    wb = {n: bits(a) for n, a in w.items()}
+    theta = cfg.rope_base ** (-2.0 * np.arange(d // 2) / d)
+    ang = np.arange(P)[:, None] * theta[None, :]
+    z = (c[:d // 2] + 1j * c[d // 2:]) * np.exp(1j * ang)  # rotate-half pair (e, e + d/2) as a complex number
+    pk = np.concatenate([z.real, z.imag], axis=1)
+    pv = np.zeros((P, d))
+    pv[:, 0] = np.arange(P)
+    valid = np.zeros(P, bool)
+    valid[16:] = True                               # 48 valid keys at indices 16..63
+    valid[[20, 33, 40]] = False                     # and three holes: 45 valid
+    n_valid = int(valid.sum())
+    W = O.Weights(wb, cfg)
+    v = O.velocity(W, np.zeros((T, 4)), 1.0, pk[None], pv[None], valid)
+    for j in range(T):
+        assert valid[n_valid + j]
+        assert v[j, 0] == pytest.approx(1.0 + n_valid + j, abs=1e-9), (j, v[j, 0])
+
+
 # --------------------------------------------------------------------- pi0 variant
 TINY_PI0 = TINY.replace(variant=1)
 

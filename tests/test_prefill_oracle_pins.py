@@ -76,10 +76,12 @@ def _brute_prefill(wb, cfg, emb_bits, mask):
                     y[e + d // 2] = x[e + d // 2] * math.cos(a) + x[e] * math.sin(a)
                 return y
 
-            k = [rot(k[i], i) for i in range(P)]
+            # token i sits at the count of valid tokens before it
+            pos = [sum(1 for j in range(i) if mask[b][j]) for i in range(P)]
+            k = [rot(k[i], pos[i]) for i in range(P)]
             for hd in range(H):
                 for i in range(P):
-                    q[i][hd * d:(hd + 1) * d] = rot(q[i][hd * d:(hd + 1) * d], i)
+                    q[i][hd * d:(hd + 1) * d] = rot(q[i][hd * d:(hd + 1) * d], pos[i])
             K[l, b] = k
             V[l, b] = v
             if l == L - 1:
@@ -112,12 +114,23 @@ def _brute_prefill(wb, cfg, emb_bits, mask):
 def test_prefill_matches_brute_force():
     cfg = TINY.replace(width=8, mlp_dim=6, head_dim=4)
     w = inputs.make_prefill_weights(cfg, seed=11, std=0.3)
-    e = inputs.make_prefix_embeddings(cfg, 2, 4, seed=12)
-    m = inputs.make_pad_mask(2, 4, [4, 3])
+    e = inputs.make_prefix_embeddings(cfg, 3, 5, seed=12)
+    # trailing pads, a hole in the middle, a left-padded episode
+    m = np.array([[1, 1, 1, 1, 1], [1, 1, 0, 1, 0], [0, 0, 1, 1, 1]], np.uint8)
     K, V = PO.prefill(w, cfg, e, m)
     Kb, Vb = _brute_prefill(w, cfg, e, m)
     np.testing.assert_allclose(K, Kb, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(V, Vb, rtol=1e-11, atol=1e-12)
+
+
+def test_token_positions_count_valid_tokens_before():
+    """Valid tokens take positions 0 .. n_valid - 1 in order, wherever the pads are
+    (the expert's suffix continues them at n_valid + j)."""
+    assert PO.token_positions(np.ones(4, bool)).tolist() == [0, 1, 2, 3]
+    assert PO.token_positions(np.array([1, 1, 0, 0], bool)).tolist() == [0, 1, 2, 2]
+    assert PO.token_positions(np.array([0, 0, 1, 1], bool)).tolist() == [0, 0, 0, 1]
+    assert PO.token_positions(np.array([1, 0, 1, 0, 1], bool)).tolist() == [0, 1, 1, 2, 2]
+    assert PO.token_positions(np.zeros(0, bool)).tolist() == []
 
 
 def test_prefill_layer_is_the_pinned_pi0_layer_without_prefix():
@@ -136,7 +149,8 @@ def test_prefill_layer_is_the_pinned_pi0_layer_without_prefix():
 
 def test_pad_tokens_do_not_reach_valid_tokens():
     """Valid tokens' K/V equal those of the sequence with the pad tokens removed,
-    whatever the pad tokens hold."""
+    whatever the pad tokens hold and wherever they sit (trailing, in a hole, in
+    front)."""
     w, e, m = tiny_inputs()
     K, V = PO.prefill(w, TINY, e, m)
     e2 = e.copy()
@@ -147,6 +161,14 @@ def test_pad_tokens_do_not_reach_valid_tokens():
     Kc, Vc = PO.prefill(w, TINY, e[1:2, :5], None)
     np.testing.assert_allclose(K[:, 1, :5], Kc[:, 0], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(V[:, 1, :5], Vc[:, 0], rtol=1e-12, atol=1e-12)
+    # pads in front of and between the valid tokens
+    for keep in ([2, 3, 5, 6], [0, 3, 4, 6], [1, 2, 3, 4]):
+        mh = np.zeros((1, 7), np.uint8)
+        mh[0, keep] = 1
+        Kh, Vh = PO.prefill(w, TINY, e[0:1], mh)
+        Kr, Vr = PO.prefill(w, TINY, e[0:1, keep], None)
+        np.testing.assert_allclose(Kh[:, 0, keep], Kr[:, 0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(Vh[:, 0, keep], Vr[:, 0], rtol=1e-12, atol=1e-12)
 
 
 def test_episodes_are_independent():
@@ -199,4 +221,7 @@ def test_no_valid_token_gives_zero_attention():
     w0 = dict(w)
     w0["layers.0.o.w"] = np.zeros_like(w["layers.0.o.w"])
     K0, V0 = PO.prefill(w0, TINY, e, np.ones((1, 4), np.uint8))
-    np.testing.assert_allclose(K[1], K0[1], rtol=1e-12, atol=1e-12)
+    # values do not depend on positions; keys agree where the positions do (token 0:
+    # with no valid token every token sits at position 0)
+    np.testing.assert_allclose(V[1], V0[1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(K[1][:, 0], K0[1][:, 0], rtol=1e-12, atol=1e-12)
