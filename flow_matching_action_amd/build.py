@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpi_ae.so")
 SOURCES = [os.path.join(CSRC, "pi_ae_kernels.hip"), os.path.join(CSRC, "pi_ae_diag.hip"),
-           os.path.join(CSRC, "pi_ae_runtime.cpp")]
+           os.path.join(CSRC, "pi_ae_noalloc.hip"), os.path.join(CSRC, "pi_ae_runtime.cpp")]
 
 # Packed-fp32 VALU forms are kept out of generated code on purpose.  MFMA
 # results go to ordinary VGPRs: the attention kernels rescale their

@@ -271,6 +271,14 @@ hipError_t launch_vis_attn(const VisAttnParams& p, hipStream_t s, const KernelTi
 hipError_t launch_vis_gemm(int which, const GemmParams& p, int S, float* part, hipStream_t s,
                            const KernelTiming* t = nullptr);
 
+// The fixed device array of the allocation-free entry point (one copy per GPU,
+// defined in pi_ae_noalloc.hip): its capacity, the largest number of GEMM rows
+// a call through it may have (the weight-streaming kernels' row range), and
+// the lookup of its device address on the current GPU (once per device).
+constexpr size_t kNoallocScratchBytes = size_t(24) << 20;
+constexpr int kNoallocMaxRows = 64;
+hipError_t noalloc_scratch(void** ptr);
+
 // The thread-local message that pi_ae_last_error returns (set by every
 // translation unit of the library on failure).
 void set_last_error(const std::string& msg);

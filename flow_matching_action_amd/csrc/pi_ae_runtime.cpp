@@ -980,6 +980,64 @@ PI_AE_API pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, c
   return PI_AE_OK;
 }
 
+namespace {
+// Carves the working memory of one call with batch * chunk_len <= 64 rows out
+// of a byte range at `base` (256-byte aligned pieces); returns the bytes used.
+// With base == nullptr only the size is computed.
+size_t noalloc_layout(int L, int B, int T, int nkb, char* base, Workspace* ws) {
+  const size_t Mp = size_t(kNoallocMaxRows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  Workspace w;
+  w.h = reinterpret_cast<float*>(take(Mp * kD * 4));
+  w.q = reinterpret_cast<uint16_t*>(take(Mp * kH * kHd * 2));
+  w.o = reinterpret_cast<uint16_t*>(take(Mp * kH * kHd * 2));
+  w.o2 = reinterpret_cast<uint16_t*>(take(Mp * kH * kHd * 2 + Mp * kH * 4 * 4));
+  w.m = reinterpret_cast<uint16_t*>(take(Mp * kF * 2));
+  w.u = reinterpret_cast<uint16_t*>(take(Mp * kD * 2));
+  w.ssq = reinterpret_cast<float*>(take(Mp * (kD / 16) * 4));
+  w.rope_cs = reinterpret_cast<float2*>(take(Mp * kRopeHalf * 8));
+  w.kbias = reinterpret_cast<float*>(take(size_t(B) * nkb * 32 * 4));
+  w.n_valid = reinterpret_cast<int*>(take(size_t(B) * 4));
+  w.da = reinterpret_cast<DevArgs*>(take(sizeof(DevArgs)));
+  w.kp = reinterpret_cast<uint16_t*>(take(size_t(L) * B * nkb * 8192 * 2));
+  w.vp = reinterpret_cast<uint16_t*>(take(size_t(L) * B * nkb * 8192 * 2));
+  (void)T;
+  if (ws) *ws = w;
+  return off;
+}
+}  // namespace
+
+PI_AE_API pi_ae_status pi_ae_sample_noalloc(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise,
+                                            float* actions, int32_t batch, void* stream) {
+  pi_ae_status st = check_call(ctx, kv, noise, actions, batch);
+  if (st || batch == 0) return st;
+  const int T = ctx->cfg.chunk_len, L = ctx->cfg.num_layers, P = kv->prefix_len;
+  if (batch * T > kNoallocMaxRows)
+    return fail(PI_AE_EINVAL, "sample_noalloc: batch * chunk_len must be at most " + std::to_string(kNoallocMaxRows));
+  const int nkb = (P + T + 31) / 32;
+  const size_t need = noalloc_layout(L, batch, T, nkb, nullptr, nullptr);
+  if (need > kNoallocScratchBytes)
+    return fail(PI_AE_EINVAL, "sample_noalloc: this call needs " + std::to_string(need) +
+                                  " bytes of working memory; the fixed array holds " +
+                                  std::to_string(kNoallocScratchBytes) + " (fewer layers or a shorter prefix)");
+  DeviceGuard dg(ctx->device);
+  void* base = nullptr;
+  hipError_t e = noalloc_scratch(&base);
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("sample_noalloc: scratch address: ") + hipGetErrorString(e));
+  Workspace ws;
+  noalloc_layout(L, batch, T, nkb, static_cast<char*>(base), &ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = launch_args(args_for(ws, kv, noise, actions, batch), s);
+  if (e == hipSuccess) e = enqueue(ctx, ws, batch, P, s, StopAt{});
+  if (e != hipSuccess) return fail(PI_AE_EHIP, std::string("sample_noalloc: launch failed: ") + hipGetErrorString(e));
+  return PI_AE_OK;
+}
+
 PI_AE_API void pi_ae_destroy(pi_ae_ctx* ctx) {
   if (!ctx) return;
   {

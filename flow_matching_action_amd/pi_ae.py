@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("PI_AE_LIB") or os.path.join(HERE, "libpi_ae.so")
 PI_AE_OK, PI_AE_EINVAL, PI_AE_EUNSUPPORTED, PI_AE_ENOMEM, PI_AE_EHIP, PI_AE_ESTATE = range(6)
 
 # symbols declared in include/pi_ae.h
-EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_destroy", "pi_ae_status_string",
+EXPORTS = ("pi_ae_prepare_weights", "pi_ae_sample", "pi_ae_sample_noalloc", "pi_ae_destroy", "pi_ae_status_string",
            "pi_ae_last_error", "pi_ae_debug_table", "pi_ae_debug_host_table", "pi_ae_debug_probe",
            "pi_ae_debug_time_phase", "pi_ae_vlm_prepare", "pi_ae_vlm_prefill", "pi_ae_vlm_destroy",
            "pi_ae_vlm_debug_time_phase", "pi_ae_pipeline_create", "pi_ae_pipeline_run", "pi_ae_pipeline_destroy",
@@ -114,6 +114,9 @@ def load_library(path: str = LIB_PATH):
     lib.pi_ae_sample.argtypes = [ctypes.c_void_p, ctypes.POINTER(PrefixKV), ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_int32, ctypes.c_void_p]
     lib.pi_ae_sample.restype = ctypes.c_int
+    lib.pi_ae_sample_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(PrefixKV), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.pi_ae_sample_noalloc.restype = ctypes.c_int
     lib.pi_ae_destroy.argtypes = [ctypes.c_void_p]
     lib.pi_ae_destroy.restype = None
     lib.pi_ae_status_string.argtypes = [ctypes.c_int]
@@ -321,6 +324,13 @@ class Context:
         kv = self._kv(k, v, pad_mask, batch, prefix_len)
         _check(self._lib.pi_ae_sample(self._h, ctypes.byref(kv), self._xbuf(noise, "noise", batch),
                                       self._xbuf(actions, "actions", batch), int(batch), _stream_handle(stream)))
+
+    def sample_noalloc(self, k, v, pad_mask, noise, actions, batch: int, prefix_len: int, stream=None):
+        """Enqueue pi_ae_sample_noalloc (the library's fixed working memory, no graph)."""
+        kv = self._kv(k, v, pad_mask, batch, prefix_len)
+        _check(self._lib.pi_ae_sample_noalloc(self._h, ctypes.byref(kv), self._xbuf(noise, "noise", batch),
+                                              self._xbuf(actions, "actions", batch), int(batch),
+                                              _stream_handle(stream)))
 
     def time_phase(self, k, v, pad_mask, noise, actions, batch, prefix_len, phase, chunks, stream=None) -> float:
         """Mean duration (us) of one phase's kernel inside the loop: `chunks` whole

@@ -181,6 +181,26 @@ pi_ae_status pi_ae_prepare_weights(const pi_ae_config* cfg, const pi_ae_weights*
 pi_ae_status pi_ae_sample(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
                           int32_t batch, void* stream);
 
+/* Allocation-free variant of pi_ae_sample, for callers that cannot allocate
+ * device memory: code under stream capture (its launches are plain kernel
+ * launches on `stream`, no graph of the library's own), tight serving loops,
+ * harnesses that forbid it.  Same arguments, validation, results and stream
+ * semantics as pi_ae_sample (the same kernels in the same order), but the
+ * call's working memory (residual stream, GEMM operands, packed K/V, key
+ * bias, RoPE rows) is a fixed device array of the library (24 MiB, one copy
+ * per GPU, held until the process ends) instead of the context's workspace,
+ * and no graph is captured or instantiated.  Limits: batch * chunk_len <= 64
+ * and 2 * num_layers * batch * ceil((prefix_len + chunk_len) / 32) * 16 KiB
+ * of packed K/V plus about 2.1 MiB of activations within the 24 MiB (an
+ * 18-layer expert: prefix_len + chunk_len <= 1088 at batch 1); larger calls
+ * return PI_AE_EINVAL before anything is enqueued.  It calls no hipMalloc or
+ * hipFree.  Every call on one GPU uses that GPU's array and leaves its last
+ * contents there (every part a call reads is written earlier in the same
+ * call): calls that overlap on one GPU, on any streams or contexts, race and
+ * must be serialised by the caller. */
+pi_ae_status pi_ae_sample_noalloc(pi_ae_ctx* ctx, const pi_ae_prefix_kv* kv, const float* noise, float* actions,
+                                  int32_t batch, void* stream);
+
 /* Wait for the work this context has enqueued (the graphs it launched, on
  * whatever streams), then free everything it owns.  Other work on the device
  * is not waited for.  NULL is a no-op. */
