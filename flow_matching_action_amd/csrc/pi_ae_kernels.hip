@@ -959,20 +959,21 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
 // per k-block: each wave first waits for its own loads of that block
 // (vmcnt: the loads of the two later blocks may stay in flight), the barrier
 // then makes every wave's weight fragments visible and retires all reads of
-// the slot that the next copy overwrites.  The fused epilogue runs in
-// quarters of 64 rows through a 64 x 132 LDS tile, so two workgroups fit on
-// a CU (about 67 KB of LDS each) and one's epilogue overlaps the other's
-// MFMAs.
+// the slot that the next copy overwrites.  The MFMAs take the weights as
+// their first operand, so each accumulator holds the transposed 32x32 tile
+// (lane l: activation row l%32, 16 output columns); the fused GELU epilogue
+// then runs per wave from the registers (see there), with no LDS tile and
+// no barrier, and two workgroups share a CU.
 template <int EPI, int D, int F>
 __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
-  constexpr int TR = 2, TC = 4, BM = 256, BN = 128, FB = BN / 16, CS = BN + 4, QR = 64;
-  constexpr bool NORM = epi_norm(EPI);
+  constexpr int TR = 2, TC = 4, BM = 256, BN = 128, FB = BN / 16;
+  static_assert(EPI == E_GELU, "the register epilogue is the gate/up one");
   __shared__ __attribute__((aligned(16))) u32x4 ring0[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring1[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring2[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring3[FB][64];
-  __shared__ __attribute__((aligned(16))) float ct[QR * CS];
   __shared__ float srstd[BM];
+  __shared__ __attribute__((aligned(16))) float sbias[BN];
   kernarg_touch(p);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KB = K >> 5, NS = KB;  // one 32-wide k-block per stage; NS is a multiple of 4
@@ -1009,18 +1010,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   PI_AE_W_DMA(ring1, 1)
   PI_AE_W_LOADA(2, 2)
   PI_AE_W_DMA(ring2, 2)
-  if constexpr (NORM) tile_rstd<BM, 256, D>(p, srstd, mb0);
-  // the epilogue's bias chunk of this thread (the same in every quarter),
-  // loaded now so that its latency hides behind the main loop
-  float4 bpre[4];
-  if constexpr (NORM) {
-    const int c = threadIdx.x % FB, jp = nb0 / 2 + (c >> 1), hf = c & 1;
-    const int c0 = 16 * (2 * jp) + 8 * hf, c1 = 16 * (2 * jp + 1) + 8 * hf;
-    bpre[0] = *reinterpret_cast<const float4*>(p.bias + c0);
-    bpre[1] = *reinterpret_cast<const float4*>(p.bias + c0 + 4);
-    bpre[2] = *reinterpret_cast<const float4*>(p.bias + c1);
-    bpre[3] = *reinterpret_cast<const float4*>(p.bias + c1 + 4);
-  }
+  tile_rstd<BM, 256, D>(p, srstd, mb0);
+  // the tile's shift-fold bias (gate and up columns as the weights interleave
+  // them); the first barrier of the main loop publishes it with srstd
+  if (threadIdx.x < BN) sbias[threadIdx.x] = p.bias[nb0 * 16 + threadIdx.x];
 
   f32x16 acc[TR][TC];
 #pragma unroll
@@ -1046,7 +1039,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
     _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
       _Pragma("unroll") for (int r = 0; r < TR; ++r)                                  \
         _Pragma("unroll") for (int c = 0; c < TC; ++c)                                \
-          acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, av[SL][r][h]), __builtin_bit_cast(bf16x8, b[c][h]), acc[r][c]); \
+          acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, b[c][h]), __builtin_bit_cast(bf16x8, av[SL][r][h]), acc[r][c]); \
   }
   for (int sg = 0; sg < NS; sg += 4) {
     PI_AE_W_STEP(ring0, 0, sg, ring3)
@@ -1058,23 +1051,40 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
 #undef PI_AE_W_DMA
 #undef PI_AE_W_LOADA
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the re-reads past the last block have landed
-  __syncthreads();
-  // epilogue by quarters: wave q's 64 rows through the LDS tile
+  // Epilogue from the registers.  acc[r][c] is the transposed tile: lane l
+  // holds row 32r + l%32 of the wave's 64 and, in register i, column
+  // 8(i/4) + 4(l/32) + i%4 of the 32 of tile c, whose first 16 columns are
+  // gate and last 16 up for the same 16 product columns 16jp.., jp = nb0/2 + c.
+  // Swapping registers i+4 of the lower half-wave with registers i of the
+  // upper half (i%8 < 4; v_permlane32_swap, both lanes on the same row)
+  // leaves lane l with gate columns 8(l/32) + 0..7 in registers 0-7 and the
+  // same up columns in registers 8-15: one 16-byte chunk of the product row,
+  // stored straight into its fragment-major place.
+  const int hh = lane >> 5;
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    if (w == qt) {
+  for (int r = 0; r < TR; ++r) {
+    const int rl = 64 * w + 32 * r + (lane & 31), row = mb0 * 16 + rl;
+    const float rs = srstd[rl];
 #pragma unroll
-      for (int r = 0; r < TR; ++r)
+    for (int c = 0; c < TC; ++c) {
+      f32x16 v = acc[r][c];
 #pragma unroll
-        for (int c = 0; c < TC; ++c)
+      for (int g = 0; g < 16; g += 8)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            ct[(r * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
+        for (int i = 0; i < 4; ++i) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[g + i]), __float_as_uint(v[g + i + 4]),
+                                                           false, false);
+          v[g + i] = __uint_as_float(sw[0]);
+          v[g + i + 4] = __uint_as_float(sw[1]);
+        }
+      const float* bg = sbias + 32 * c + 8 * hh;
+      float mv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(v[e] * rs + bg[e]) * (v[8 + e] * rs + bg[16 + e]);
+      if (row < p.M)
+        *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * (nb0 / 2 + c) + 8 * hh, F / 32)) =
+            __builtin_bit_cast(uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
     }
-    __syncthreads();
-    tile_epilogue<QR, BN, CS, 256, EPI, D, F>(p, ct, srstd + qt * QR, mb0 + qt * (QR / 16), nb0,
-                                              NORM ? bpre : nullptr);
-    __syncthreads();
   }
 }
 
