@@ -48,6 +48,16 @@ __device__ __forceinline__ bf16x8 pack8(float4 lo, float4 hi) {
   f32x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   return __builtin_convertvector(v, bf16x8);
 }
+// max and sum across lanes l and l^32 (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -582,6 +592,63 @@ __device__ __forceinline__ void tile_rstd(const GemmParams& p, float* srstd, int
     srstd[r] = 1.f / sqrtf(sum * (1.f / D) + p.eps);
   }
 }
+// Output of the QKV epilogues for one row and one 8-column chunk: pair jp of
+// n-blocks (2jp: columns x, 2jp+1: their partners), half hf.  y0 / y1: the
+// normalised, biased values of the chunk's 8 columns of each block; cs: the
+// row's (cos, sin) of RoPE pairs ip .. ip+7 (unused for V).  Q heads and K_s
+// rotate pairs (ip, ip + 128), ip = (jp % 8) * 16 + 8hf; Q goes to
+// [M][8][256], suffix K into the packed per-layer buffer (and the natural
+// layout cache when present), V_s (head-dim (jp - 72) * 32 + 8hf + e and
+// + 16, no rotation) likewise.
+__device__ __forceinline__ void qkv_emit(const GemmParams& p, int row, int jp, int hf, const float (&y0)[8],
+                                         const float (&y1)[8], const float4 (&cs)[4]) {
+  const int b = row / p.T, t = row - b * p.T;
+  if (jp < 72) {
+    const int ip = (jp & 7) * 16 + 8 * hf;
+    float o0[8], o1[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float4 cs2 = cs[e2];
+      o0[2 * e2] = y0[2 * e2] * cs2.x - y1[2 * e2] * cs2.y;
+      o1[2 * e2] = y1[2 * e2] * cs2.x + y0[2 * e2] * cs2.y;
+      o0[2 * e2 + 1] = y0[2 * e2 + 1] * cs2.z - y1[2 * e2 + 1] * cs2.w;
+      o1[2 * e2 + 1] = y1[2 * e2 + 1] * cs2.z + y0[2 * e2 + 1] * cs2.w;
+    }
+    const uint4 w0 = __builtin_bit_cast(uint4, pack8(make_float4(o0[0], o0[1], o0[2], o0[3]), make_float4(o0[4], o0[5], o0[6], o0[7])));
+    const uint4 w1 = __builtin_bit_cast(uint4, pack8(make_float4(o1[0], o1[1], o1[2], o1[3]), make_float4(o1[4], o1[5], o1[6], o1[7])));
+    if (jp < 64) {
+      uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
+      *reinterpret_cast<uint4*>(dst + ip) = w0;
+      *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
+    } else {
+      const int key = p.P + t;
+      if (p.kp) {
+        *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
+        *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
+      }
+      if (p.k_cache) {
+        *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + ip) = w0;
+        *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + kRopeHalf + ip) = w1;
+      }
+    }
+  } else {
+    const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
+    if (p.vp) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
+        p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
+      }
+    }
+    if (p.v_cache) {
+      *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0) = __builtin_bit_cast(
+          uint4, pack8(make_float4(y0[0], y0[1], y0[2], y0[3]), make_float4(y0[4], y0[5], y0[6], y0[7])));
+      *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0 + 16) = __builtin_bit_cast(
+          uint4, pack8(make_float4(y1[0], y1[1], y1[2], y1[3]), make_float4(y1[4], y1[5], y1[6], y1[7])));
+    }
+  }
+}
+
 // Epilogue of the large-M GEMMs, after the BM x BN fp32 tile has been placed
 // in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
 // inputs): each of the NT threads takes 8 consecutive columns of one row per
@@ -737,54 +804,28 @@ __device__ __forceinline__ void tile_epilogue(const GemmParams& p, const float* 
           *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * jp + 8 * hf, F / 32)) = __builtin_bit_cast(
               uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
         } else {  // E_QKV, E_KV
-          const int b = row / p.T, t = row - b * p.T;
-          if (jp < 72) {  // Q heads and K_s: rotate pairs (ip, ip+128), ip = (jp%8)*16 + 8hf + e
-            float o0[8], o1[8];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const float4 cs2 = cs[q][e2];
-              o0[2 * e2] = y0[2 * e2] * cs2.x - y1[2 * e2] * cs2.y;
-              o1[2 * e2] = y1[2 * e2] * cs2.x + y0[2 * e2] * cs2.y;
-              o0[2 * e2 + 1] = y0[2 * e2 + 1] * cs2.z - y1[2 * e2 + 1] * cs2.w;
-              o1[2 * e2 + 1] = y1[2 * e2 + 1] * cs2.z + y0[2 * e2 + 1] * cs2.w;
-            }
-            const uint4 w0 = __builtin_bit_cast(uint4, pack8(make_float4(o0[0], o0[1], o0[2], o0[3]), make_float4(o0[4], o0[5], o0[6], o0[7])));
-            const uint4 w1 = __builtin_bit_cast(uint4, pack8(make_float4(o1[0], o1[1], o1[2], o1[3]), make_float4(o1[4], o1[5], o1[6], o1[7])));
-            if (jp < 64) {
-              uint16_t* dst = p.q_out + (size_t(row) * kH + (jp >> 3)) * kHd;
-              *reinterpret_cast<uint4*>(dst + ip) = w0;
-              *reinterpret_cast<uint4*>(dst + kRopeHalf + ip) = w1;
-            } else {
-              const int key = p.P + t;
-              if (p.kp) {
-                *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, ip, p.nkb)) = w0;
-                *reinterpret_cast<uint4*>(p.kp + kpack_index(b, key, kRopeHalf + ip, p.nkb)) = w1;
-              }
-              if (p.k_cache) {
-                *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + ip) = w0;
-                *reinterpret_cast<uint4*>(p.k_cache + size_t(row) * kHd + kRopeHalf + ip) = w1;
-              }
-            }
-          } else {  // V_s: head-dim (jp-72)*32 + 8hf + e and +16, no rotation
-            const int key = p.P + t, d0 = (jp - 72) * 32 + 8 * hf;
-            if (p.vp) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                p.vp[vpack_index(b, key, d0 + e, p.nkb)] = f2bf(y0[e]);
-                p.vp[vpack_index(b, key, d0 + 16 + e, p.nkb)] = f2bf(y1[e]);
-              }
-            }
-            if (p.v_cache) {
-              *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0) = __builtin_bit_cast(
-                  uint4, pack8(make_float4(y0[0], y0[1], y0[2], y0[3]), make_float4(y0[4], y0[5], y0[6], y0[7])));
-              *reinterpret_cast<uint4*>(p.v_cache + size_t(row) * kHd + d0 + 16) = __builtin_bit_cast(
-                  uint4, pack8(make_float4(y1[0], y1[1], y1[2], y1[3]), make_float4(y1[4], y1[5], y1[6], y1[7])));
-            }
-          }
+          qkv_emit(p, row, jp, hf, y0, y1, cs[q]);
         }
       }
     }
   }
+}
+
+// A transposed 32x32 accumulator tile (lane l: activation row l%32; register
+// i: output column 8(i/4) + 4(l/32) + i%4) regrouped so that lane l holds
+// columns 8(l/32) + 0..7 in registers 0-7 and 16 + 8(l/32) + 0..7 in
+// registers 8-15: registers i+4 of the lower half-wave trade places with
+// registers i of the upper half (i%8 < 4), both lanes being on the same row.
+__device__ __forceinline__ void acc_cols_to_lanes(f32x16& v) {
+#pragma unroll
+  for (int g = 0; g < 16; g += 8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[g + i]), __float_as_uint(v[g + i + 4]),
+                                                       false, false);
+      v[g + i] = __uint_as_float(sw[0]);
+      v[g + i + 4] = __uint_as_float(sw[1]);
+    }
 }
 
 // Large-M GEMM (many rows: the batched loop) on 32x32x16 MFMAs, the form that
@@ -1055,11 +1096,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   // holds row 32r + l%32 of the wave's 64 and, in register i, column
   // 8(i/4) + 4(l/32) + i%4 of the 32 of tile c, whose first 16 columns are
   // gate and last 16 up for the same 16 product columns 16jp.., jp = nb0/2 + c.
-  // Swapping registers i+4 of the lower half-wave with registers i of the
-  // upper half (i%8 < 4; v_permlane32_swap, both lanes on the same row)
-  // leaves lane l with gate columns 8(l/32) + 0..7 in registers 0-7 and the
-  // same up columns in registers 8-15: one 16-byte chunk of the product row,
-  // stored straight into its fragment-major place.
+  // Regrouped (acc_cols_to_lanes), lane l holds gate columns 8(l/32) + 0..7
+  // in registers 0-7 and the same up columns in registers 8-15: one 16-byte
+  // chunk of the product row, stored straight into its fragment-major place.
   const int hh = lane >> 5;
 #pragma unroll
   for (int r = 0; r < TR; ++r) {
@@ -1068,15 +1107,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
       f32x16 v = acc[r][c];
-#pragma unroll
-      for (int g = 0; g < 16; g += 8)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[g + i]), __float_as_uint(v[g + i + 4]),
-                                                           false, false);
-          v[g + i] = __uint_as_float(sw[0]);
-          v[g + i + 4] = __uint_as_float(sw[1]);
-        }
+      acc_cols_to_lanes(v);
       const float* bg = sbias + 32 * c + 8 * hh;
       float mv[8];
 #pragma unroll
@@ -1425,16 +1456,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 constexpr int kAttn32Groups = 2;  // 32-row query groups per workgroup (two waves each)
 // 16-row query blocks (all episodes) from which this kernel is used
 constexpr int kAttnRowsMinBlocks = 256;
-
-// max and sum across lanes l and l^32 (v_permlane32_swap exchanges the halves)
-__device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int NWQ, bool SPREAD>
 __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
