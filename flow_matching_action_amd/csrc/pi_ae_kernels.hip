@@ -1442,11 +1442,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 // halves), K through the 32x32 gather of the packed K fragments.  NWQ 32-row
 // query groups share a workgroup, and two waves work on each group: wave kh
 // takes block kh of every pair, and the two halves are merged through LDS at
-// the end.  Pairs of K/V blocks are copied straight from memory into LDS
-// (buffer loads that write LDS, no registers), one pair ahead of the math,
-// into two LDS buffers that are separate objects so that the compiler's
-// wait counting keeps the copy into one buffer in flight while the other is
-// read.  The running max moves only when a block's max exceeds it by more
+// the end.  K and V blocks are copied straight from memory into LDS (buffer
+// loads that write LDS, no registers).  A CU's load path takes about as long
+// for a pair's 64 KiB as the pair's math, and a wave cannot issue past a
+// copy the path has not yet accepted: so the copies are spread between the
+// MFMAs (two MFMAs, one 1 KiB copy) instead of being issued in a block.
+// Each pair step has two halves with a barrier each: the scores (K of the
+// pair, while the next pair's V is copied) and the softmax and PV products
+// (V of the pair, while the K of the pair after next is copied into the K
+// buffer the scores have just finished with).  K and V of even and odd pairs
+// sit in four separate LDS objects, so that the compiler's wait counting
+// keeps a copy into one in flight while another is read.  The running max moves only when a block's max exceeds it by more
 // than 8 (log2 units, i.e. probabilities up to 256; FlashAttention-4's
 // conditional rescaling): O / l is the same for any reference max, and the
 // wave skips the accumulator rescale in the common case.
@@ -1460,17 +1466,19 @@ constexpr int kAttnRowsMinBlocks = 256;
 template <int NWQ, bool SPREAD>
 __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   constexpr int NW = NWQ * 2;
-  constexpr int FPW = 64 / NW;  // fragments of a block pair copied per wave
-  static_assert(64 % NW == 0, "a pair's 64 fragments split evenly over the waves");
-  // one LDS buffer: [block of the pair][16 K + 16 V fragments][lane] (64 KiB)
-  // and the pair's 64 key biases.  After the key loop, buffer g holds query
-  // group g's merge area (the second half's accumulators, four per lane and 16-byte access,
-  // its max and sum: 130 x 64 floats) and then its output rows as bf16.
-  constexpr int kMrgFloats = 130 * 64, kORow = kHd + 8;  // bf16 per output row (16-byte aligned, staggered banks)
-  static_assert(NWQ <= 2, "one LDS buffer per query group after the loop");
-  static_assert(kMrgFloats * 4 + 32 * kORow * 2 <= 65536, "merge + output rows fit one buffer");
-  __shared__ __attribute__((aligned(16))) u32x4 kva[2][32][64];
-  __shared__ __attribute__((aligned(16))) u32x4 kvb[2][32][64];
+  static_assert(NW == 4, "each wave copies 4 of a block's 16 K (or V) fragments");
+  // LDS: K of even / odd pairs [block of the pair][16 fragments][lane] (32
+  // KiB each), V likewise, and the pair's 64 key biases (copied with V).
+  // After the key loop, query group g's merge area is K buffer g (the second
+  // half's accumulators, four per lane and 16-byte access: 128 x 64 floats)
+  // and V buffer g (its max and sum, then its output rows as bf16).
+  constexpr int kORow = kHd + 8;  // bf16 per output row (16-byte aligned, staggered banks)
+  static_assert(NWQ <= 2, "one K and one V buffer per query group after the loop");
+  static_assert(128 * 64 * 4 <= 32768 && 128 * 4 + 32 * kORow * 2 <= 32768, "merge areas fit the buffers");
+  __shared__ __attribute__((aligned(16))) u32x4 k0s[2][16][64];
+  __shared__ __attribute__((aligned(16))) u32x4 k1s[2][16][64];
+  __shared__ __attribute__((aligned(16))) u32x4 v0s[2][16][64];
+  __shared__ __attribute__((aligned(16))) u32x4 v1s[2][16][64];
   __shared__ __attribute__((aligned(16))) float kba[64];
   __shared__ __attribute__((aligned(16))) float kbb[64];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1498,20 +1506,21 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
   const rsrc_t br = make_rsrc(p.kbias + size_t(b) * nkb * 32, uint32_t(nkb) * 128u);
 
-  // fragment q*NW + w of pair PR (block f/32; K if f%32 < 16, else V) into
-  // buffer KV, and the pair's 64 biases into KB (every wave copies the same
-  // biases to the same place, which keeps the wait counts uniform).  A
-  // missing second block re-reads block 0 (in bounds; masked).
-#define PI_AE_KV32_COPY(KV, KB, PR)                                                   \
+  // copy Q (0 <= Q < 8) of pair PR's K (RS = kr) or V (RS = vr) into buffer
+  // BUF: fragment 4(Q%4) + w of block Q/4 of the pair.  A pair past the last
+  // re-copies pair 0 and a missing second block re-reads block 0 (in bounds;
+  // never read, or masked), so that every step issues the same copies and
+  // every wait count below is exact.
+#define PI_AE_KV32_DMA(RS, BUF, PR, Q)                                                \
   {                                                                                   \
-    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
-      const int f = q * NW + w, blk = 2 * (PR) + (f >> 5);                            \
-      const uint32_t kb_ = uint32_t(blk < nkb ? blk : 0);                             \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((f & 31) < 16 ? kr : vr, (lds_ptr_t)&KV[f >> 5][f & 31][0], 16, \
-                                               uint32_t(lane) * 16u, kb_ * 16384u + uint32_t(f & 15) * 1024u, 0, 0); \
-    }                                                                                 \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)&KB[0], 4, uint32_t(lane) * 4u, uint32_t(PR) * 256u, 0, 0); \
+    const int blk_ = 2 * ((PR) < npair ? (PR) : 0) + ((Q) >> 2), fi_ = ((Q) & 3) * NW + w; \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(RS, (lds_ptr_t)&BUF[(Q) >> 2][fi_][0], 16, uint32_t(lane) * 16u, \
+                                             uint32_t(blk_ < nkb ? blk_ : 0) * 16384u + uint32_t(fi_) * 1024u, 0, 0); \
   }
+  // the pair's 64 key biases (every wave copies the same ones to the same
+  // place, which keeps the wait counts uniform; past the end they read as 0)
+#define PI_AE_KV32_BIAS(KB, PR) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)&KB[0], 4, uint32_t(lane) * 4u, uint32_t((PR) < npair ? (PR) : 0) * 256u, 0, 0);
 
   f32x16 acc[8];
 #pragma unroll
@@ -1522,20 +1531,48 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const int kl0 = frag32_lane(lane, 0), kl1 = frag32_lane(lane, 1);
   const int vl0 = (lane & 15) + 16 * hh, vl1 = vl0 + 32;
 
-  // the math of block kh of the pair in buffer KV
-#define PI_AE_KV32_MATH(KV, KB, PR)                                                    \
+  // L2 warm-up of pair PR: one dword load per lane touches one 128-byte line;
+  // a workgroup's waves cover half of the pair's 512 lines (K: waves 0-1, V:
+  // waves 2-3; which half alternates with the workgroup), the episode's other
+  // workgroups the rest.  Past the last block the loads read as zeros.  The
+  // loaded words go to an LDS scratch word per lane that nothing reads (a
+  // load that writes LDS needs no register, so nothing waits for it).
+  __shared__ uint32_t warm_sink[64];
+  const uint32_t warm_off = uint32_t((qw & 1) * 128 + (w & 1) * 64 + lane) * 128u;
+#define PI_AE_KV32_WARM(PR) \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(w < 2 ? kr : vr, (lds_ptr_t)&warm_sink[0], 4, warm_off, uint32_t(PR) * 32768u, 0, 0);
+
+  // Pair step PR on block kh of the pair.  Copies per wave, in issue order:
+  // each step's first half issues the warm-up of pair PR+3, V of pair PR+1
+  // (8) and its biases, the second half K of pair PR+2 (8); before the
+  // loop: K of pair 0, the warm-up of pair 2, V and biases of pair 0, K of
+  // pair 1.  So 18 copies are issued after this wave's K of pair PR and 18
+  // after its biases of pair PR: vmcnt(18) at either barrier means that
+  // half's data has landed, and the barrier makes every wave's visible (and
+  // retires every read of the buffers the next copies overwrite).
+#define PI_AE_KV32_STEP(KS, VS, KB, VS2, KB2, PR)                                      \
   {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(0x4f72); /* vmcnt(18) */                                \
+    lds_barrier();                                                                     \
+    PI_AE_KV32_WARM((PR) + 3)                                                          \
     u32x4 fr[16];                                                                      \
-    _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KV[kh][sub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
+    _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KS[kh][sub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
     __builtin_amdgcn_sched_barrier(0);                                                 \
     f32x16 sc;                                                                         \
     _Pragma("unroll") for (int i = 0; i < 16; ++i) sc[i] = 0.f;                        \
-    _Pragma("unroll") for (int s = 0; s < 16; ++s) sc = mfma32(__builtin_bit_cast(bf16x8, fr[s]), qf[s], sc); \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
+    _Pragma("unroll") for (int c = 0; c < 8; ++c) {                                    \
+      sc = mfma32(__builtin_bit_cast(bf16x8, fr[2 * c]), qf[2 * c], sc);               \
+      sc = mfma32(__builtin_bit_cast(bf16x8, fr[2 * c + 1]), qf[2 * c + 1], sc);       \
+      PI_AE_KV32_DMA(vr, VS2, (PR) + 1, c)                                             \
+      __builtin_amdgcn_sched_barrier(0);                                               \
+    }                                                                                  \
+    PI_AE_KV32_BIAS(KB2, (PR) + 1)                                                     \
+    __builtin_amdgcn_s_waitcnt(0x4f72); /* vmcnt(18) */                                \
+    lds_barrier();                                                                     \
     /* V operands of d-tile dt (both halves of the block) and the biases */           \
     _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
-      fr[2 * dt] = KV[kh][16 + 2 * dt + sub][vl0];                                     \
-      fr[2 * dt + 1] = KV[kh][16 + 2 * dt + sub][vl1];                                 \
+      fr[2 * dt] = VS[kh][2 * dt + sub][vl0];                                          \
+      fr[2 * dt + 1] = VS[kh][2 * dt + sub][vl1];                                      \
     }                                                                                  \
     float4 bias[4];                                                                    \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                      \
@@ -1566,66 +1603,56 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
     }                                                                                  \
     const bf16x8 p0 = pack8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7])); \
     const bf16x8 p1 = pack8(make_float4(pv[8], pv[9], pv[10], pv[11]), make_float4(pv[12], pv[13], pv[14], pv[15])); \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
     _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
       const u32x4 a0 = fr[2 * dt], a1 = fr[2 * dt + 1];                                \
       acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), p0, acc[dt]); \
       acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.z, a0.w, a1.z, a1.w}), p1, acc[dt]); \
+      PI_AE_KV32_DMA(kr, KS, (PR) + 2, dt)                                             \
+      __builtin_amdgcn_sched_barrier(0);                                               \
     }                                                                                  \
   }
-  // L2 warm-up of pair PR: one dword load per lane touches one 128-byte line;
-  // a workgroup's waves cover half of the pair's 512 lines (K: waves 0-1, V:
-  // waves 2-3; which half alternates with the workgroup), the episode's other
-  // workgroups the rest.  Past the last block the loads read as zeros.  The
-  // loaded words go to an LDS scratch word per lane that nothing reads (a
-  // load that writes LDS needs no register, so nothing waits for it).
-  __shared__ uint32_t warm_sink[64];
-  const uint32_t warm_off = uint32_t((qw & 1) * 128 + (w & 1) * 64 + lane) * 128u;
-#define PI_AE_KV32_WARM(PR) \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(w < 2 ? kr : vr, (lds_ptr_t)&warm_sink[0], 4, warm_off, uint32_t(PR) * 32768u, 0, 0);
 
-  // step PR: this wave's copies of pair PR (into KV) have landed (only the
-  // warm-up load issued after them may be outstanding), the barrier makes
-  // every wave's visible and retires all reads of the other buffer, then pair
-  // PR+1 is copied there and pair PR+2 warmed up in L2 while pair PR is
-  // processed
-#define PI_AE_KV32_STEP(KV, KB, KV2, KB2, PR)                                          \
-  {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(0x0f71); /* vmcnt(1) */                                 \
-    lds_barrier();                                                                     \
-    if ((PR) + 1 < npair) PI_AE_KV32_COPY(KV2, KB2, (PR) + 1)                          \
-    PI_AE_KV32_WARM((PR) + 2)                                                          \
-    PI_AE_KV32_MATH(KV, KB, PR)                                                        \
+#pragma unroll
+  for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(kr, k0s, 0, c)
+  PI_AE_KV32_WARM(2)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(vr, v0s, 0, c)
+  PI_AE_KV32_BIAS(kba, 0)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(kr, k1s, 1, c)
+  // (the loop body always runs both steps, so that the wait counts the
+  // compiler derives for each step's LDS reads see the same copies in flight
+  // on every path; an odd last pair runs after it)
+  int pr = 0;
+  for (; pr + 1 < npair; pr += 2) {
+    PI_AE_KV32_STEP(k0s, v0s, kba, v1s, kbb, pr)
+    PI_AE_KV32_STEP(k1s, v1s, kbb, v0s, kba, pr + 1)
   }
-
-  PI_AE_KV32_COPY(kva, kba, 0)
-  PI_AE_KV32_WARM(1)
-  for (int pr = 0; pr < npair; pr += 2) {
-    PI_AE_KV32_STEP(kva, kba, kvb, kbb, pr)
-    if (pr + 1 < npair) PI_AE_KV32_STEP(kvb, kbb, kva, kba, pr + 1)
-  }
+  if (pr < npair) PI_AE_KV32_STEP(k0s, v0s, kba, v1s, kbb, pr)
 #undef PI_AE_KV32_STEP
 #undef PI_AE_KV32_WARM
-#undef PI_AE_KV32_MATH
-#undef PI_AE_KV32_COPY
+#undef PI_AE_KV32_BIAS
+#undef PI_AE_KV32_DMA
 
   // merge the key halves, normalise, and write O through LDS so that each
   // lane stores 8 consecutive head-dim values of one row (16 bytes)
   __syncthreads();  // every copy has landed and every read of the buffers is done
-  float* mg = reinterpret_cast<float*>(rg == 0 ? &kva[0][0][0] : &kvb[0][0][0]);
-  uint16_t* orow = reinterpret_cast<uint16_t*>(mg + kMrgFloats);  // [32][kORow]
-  float4* mg4 = reinterpret_cast<float4*>(mg);  // [dt][q][lane]: accumulator values 4q .. 4q+3
+  float4* mg4 = reinterpret_cast<float4*>(rg == 0 ? &k0s[0][0][0] : &k1s[0][0][0]);  // [dt][q][lane]: values 4q .. 4q+3
+  float* mst = reinterpret_cast<float*>(rg == 0 ? &v0s[0][0][0] : &v1s[0][0][0]);     // max, sum [2][lane]
+  uint16_t* orow = reinterpret_cast<uint16_t*>(mst + 128);                                 // [32][kORow]
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         mg4[(dt * 4 + q) * 64 + lane] = make_float4(acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]);
-    mg[128 * 64 + lane] = m_run;
-    mg[129 * 64 + lane] = xor32_sum(l_part);
+    mst[lane] = m_run;
+    mst[64 + lane] = xor32_sum(l_part);
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = mg[128 * 64 + lane], l1 = mg[129 * 64 + lane];
+    const float m1 = mst[lane], l1 = mst[64 + lane];
     // m is -inf only when no key of the row is valid (a VLM episode without
     // valid tokens); its output is then 0
     const float m = fmaxf(m_run, m1);
