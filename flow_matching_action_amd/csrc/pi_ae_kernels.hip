@@ -1635,24 +1635,32 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
 #undef PI_AE_KV32_BIAS
 #undef PI_AE_KV32_DMA
 
-  // merge the key halves, normalise, and write O through LDS so that each
-  // lane stores 8 consecutive head-dim values of one row (16 bytes)
+  // Merge the key halves and normalise.  Each wave of a group combines four
+  // of the eight d-tiles (kh = 0: 0-3, kh = 1: 4-7): it hands the other wave
+  // the accumulators of the four it does not combine, through the group's K
+  // buffer, and both leave their max and sum in its V buffer; the combined
+  // rows go to LDS as bf16 (after the sums, in the V buffer).
+  static_assert(NWQ == 2 && kH == 8, "a workgroup holds 8 tokens x 8 heads");
   __syncthreads();  // every copy has landed and every read of the buffers is done
-  float4* mg4 = reinterpret_cast<float4*>(rg == 0 ? &k0s[0][0][0] : &k1s[0][0][0]);  // [dt][q][lane]: values 4q .. 4q+3
-  float* mst = reinterpret_cast<float*>(rg == 0 ? &v0s[0][0][0] : &v1s[0][0][0]);     // max, sum [2][lane]
-  uint16_t* orow = reinterpret_cast<uint16_t*>(mst + 128);                                 // [32][kORow]
-  if (kh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        mg4[(dt * 4 + q) * 64 + lane] = make_float4(acc[dt][4 * q], acc[dt][4 * q + 1], acc[dt][4 * q + 2], acc[dt][4 * q + 3]);
-    mst[lane] = m_run;
-    mst[64 + lane] = xor32_sum(l_part);
-  }
-  __syncthreads();
+  float4* xch = reinterpret_cast<float4*>(rg == 0 ? &k0s[0][0][0] : &k1s[0][0][0]);  // [kh][dd][q][lane]
+  float* mst = reinterpret_cast<float*>(rg == 0 ? &v0s[0][0][0] : &v1s[0][0][0]);     // [kh][max, sum][lane]
+  uint16_t* orow = reinterpret_cast<uint16_t*>(mst + 256);                                 // [32][kORow]
+#define PI_AE_KV32_GIVE(DT0)                                                           \
+  _Pragma("unroll") for (int dd = 0; dd < 4; ++dd)                                     \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                      \
+      xch[((kh * 4 + dd) * 4 + q) * 64 + lane] =                                       \
+          make_float4(acc[(DT0) + dd][4 * q], acc[(DT0) + dd][4 * q + 1], acc[(DT0) + dd][4 * q + 2], acc[(DT0) + dd][4 * q + 3]);
   if (kh == 0) {
-    const float m1 = mst[lane], l1 = mst[64 + lane];
+    PI_AE_KV32_GIVE(4)
+  } else {
+    PI_AE_KV32_GIVE(0)
+  }
+#undef PI_AE_KV32_GIVE
+  mst[kh * 128 + lane] = m_run;
+  mst[kh * 128 + 64 + lane] = xor32_sum(l_part);
+  __syncthreads();
+  {
+    const float m1 = mst[(1 - kh) * 128 + lane], l1 = mst[(1 - kh) * 128 + 64 + lane];
     // m is -inf only when no key of the row is valid (a VLM episode without
     // valid tokens); its output is then 0
     const float m = fmaxf(m_run, m1);
@@ -1660,42 +1668,53 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
     const float den = a0 * xor32_sum(l_part) + a1 * l1;
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const float f0 = a0 * inv, f1 = a1 * inv;
-    // two batches of four d-tiles: all reads of a batch are issued before its
-    // writes (which the compiler may not reorder across, both being LDS)
+    // all reads of the other wave's tiles are issued before the writes
+    // (which the compiler may not reorder across, both being LDS)
+    float4 x[16];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float4 x[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) x[k] = mg4[(half * 16 + k) * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int dt = half * 4 + (k >> 2), q = k & 3;
-        const float o0 = acc[dt][4 * q] * f0 + x[k].x * f1, o1 = acc[dt][4 * q + 1] * f0 + x[k].y * f1;
-        const float o2 = acc[dt][4 * q + 2] * f0 + x[k].z * f1, o3 = acc[dt][4 * q + 3] * f0 + x[k].w * f1;
-        const uint32_t lo = uint32_t(f2bf(o0)) | (uint32_t(f2bf(o1)) << 16);
-        const uint32_t hi = uint32_t(f2bf(o2)) | (uint32_t(f2bf(o3)) << 16);
-        *reinterpret_cast<uint2*>(&orow[l32 * kORow + dt * 32 + 8 * q + 4 * hh]) = make_uint2(lo, hi);
-      }
+    for (int k = 0; k < 16; ++k) x[k] = xch[((1 - kh) * 16 + k) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+#define PI_AE_KV32_COMBINE(DT0)                                                        \
+    _Pragma("unroll") for (int k = 0; k < 16; ++k) {                                   \
+      const int dt = (DT0) + (k >> 2), q = k & 3;                                      \
+      const float o0 = acc[dt][4 * q] * f0 + x[k].x * f1, o1 = acc[dt][4 * q + 1] * f0 + x[k].y * f1; \
+      const float o2 = acc[dt][4 * q + 2] * f0 + x[k].z * f1, o3 = acc[dt][4 * q + 3] * f0 + x[k].w * f1; \
+      const uint32_t lo = uint32_t(f2bf(o0)) | (uint32_t(f2bf(o1)) << 16);            \
+      const uint32_t hi = uint32_t(f2bf(o2)) | (uint32_t(f2bf(o3)) << 16);            \
+      *reinterpret_cast<uint2*>(&orow[l32 * kORow + dt * 32 + 8 * q + 4 * hh]) = make_uint2(lo, hi); \
     }
+    if (kh == 0) {
+      PI_AE_KV32_COMBINE(0)
+    } else {
+      PI_AE_KV32_COMBINE(4)
+    }
+#undef PI_AE_KV32_COMBINE
   }
   __syncthreads();
-  // the two waves of a group store its 32 rows x 32 chunks of 8 values
-  const int tg = kh * 64 + lane;
-  uint4 ov[8];
+  // Store O in the O projection's fragment-major layout: a 16-byte piece of
+  // fragment (token row / 16, k-block) sits at lane (row % 16) + 16 j, so the
+  // workgroup's 8 consecutive token rows of one head and k-block are 4 runs
+  // of 8 consecutive pieces.  Lane t%8 of a run takes token 8qw + t%8, its
+  // group's row (token % 4) * 8 + head; each store instruction covers the two
+  // k-blocks of one head-dim slice of 64 (8 per wave, 32 per workgroup).
+  {
+    const int tk = lane & 7, jj = (lane >> 3) & 3, kbh = lane >> 5;
+    const int t = 8 * qw + tk;  // token in the episode
+    const uint16_t* og = reinterpret_cast<const uint16_t*>(
+        reinterpret_cast<const float*>(tk < 4 ? &v0s[0][0][0] : &v1s[0][0][0]) + 256);
+    uint4 ov[8];
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int idx = pass * 128 + tg, q = idx >> 5, d0 = (idx & 31) * 8;
-    ov[pass] = *reinterpret_cast<const uint4*>(&orow[q * kORow + d0]);
-  }
+    for (int i = 0; i < 8; ++i) {
+      const int c = w * 8 + i, head = c >> 2, kb = 2 * (c & 3) + kbh;  // kb: 32-wide block of the head's 256
+      ov[i] = *reinterpret_cast<const uint4*>(&og[((tk & 3) * 8 + head) * kORow + kb * 32 + jj * 8]);
+    }
+    if (t < p.T) {
+      const int trow = b * p.T + t;
 #pragma unroll
-  for (int pass = 0; pass < 8; ++pass) {
-    const int idx = pass * 128 + tg, q = idx >> 5, d0 = (idx & 31) * 8;
-    const int rq = (qw * NWQ + rg) * 32 + q;
-    const uint4 v = ov[pass];
-    if (rq < nq) {
-      const int trow = b * p.T + rq / kH, head = rq % kH;
-      *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + d0, (kH * kHd) / 32)) = v;
+      for (int i = 0; i < 8; ++i) {
+        const int c = w * 8 + i, head = c >> 2, kb = 2 * (c & 3) + kbh;
+        *reinterpret_cast<uint4*>(p.o + afrag_index(trow, head * kHd + kb * 32 + jj * 8, (kH * kHd) / 32)) = ov[i];
+      }
     }
   }
 }
