@@ -56,6 +56,9 @@ struct DevArgs {
 // From this many rows on the GEMMs are MFMA-bound and use 128 x 128 tiles
 // staged through LDS; below it they stream weights with one row tile.
 constexpr int kTiledMinRows = 129;
+// From this many rows (five 256-row tiles, 160 workgroups of 256 x 256 on
+// 256 CUs) the expert's gate/up uses the square-tile GEMM.
+constexpr int kSqMinRows = 1025;
 
 // L2 warm-up of a later kernel's operands by spare workgroups appended to a
 // launch.  A workgroup's XCD (and so its L2) follows its linear block index

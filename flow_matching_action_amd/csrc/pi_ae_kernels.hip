@@ -1119,6 +1119,128 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   }
 }
 
+// Square-tile GEMM for the gate/up projection when the rows alone give
+// about a CU's worth of 256 x 256 tiles (the batched loop): 8 waves, 2 along
+// M x 4 along N (128 x 64 each, 4 x 2 accumulator tiles of 32x32), one
+// workgroup per CU.  A 256 x 128 tile moves 24 KiB through its CU's load
+// path per 32-wide k-block for 1 MFLOP-clock of work on each SIMD, more than
+// the path delivers; 256 x 256 moves 32 KiB for twice the work.  Both
+// operands go from memory to LDS directly (buffer loads that write LDS) into
+// a 4-slot ring (4 LDS objects: the 16 A and the 16 weight fragments of a
+// k-block), 3 k-blocks ahead; each wave issues 4 of a k-block's 32 copies,
+// one after every 4 of its 16 MFMAs, so that a copy the load path has not
+// yet accepted stalls the wave while its MFMAs run.  One barrier per
+// k-block, after each wave's own copies of that block have landed (vmcnt:
+// the 8 copies of the two later blocks may stay in flight).  The MFMAs take
+// the weights as their first operand (transposed accumulators, one
+// activation row per lane), and the GELU product is formed from the
+// registers as in k_gemm_wide.
+template <int D, int F>
+__global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
+  constexpr int BM = 256, BN = 256, TR = 4, TC = 2;
+  __shared__ __attribute__((aligned(16))) u32x4 ring0[32][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring1[32][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring2[32][64];
+  __shared__ __attribute__((aligned(16))) u32x4 ring3[32][64];
+  __shared__ float srstd[BM];
+  __shared__ __attribute__((aligned(16))) float sbias[BN];
+  kernarg_touch(p);
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 2, wn = w & 3;  // rows 128 wm.., columns 64 wn..
+  const int KB = K >> 5, NS = KB;     // NS is a multiple of 4
+  const int nb0 = blockIdx.x * (BN / 16), mb0 = blockIdx.y * (BM / 16);
+  const int sub = frag32_sub(lane);
+  const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
+  // the tile's 16 A and 16 weight fragment rows: fragment (mb0 + f, kb) of A
+  // and (nb0 + f, kb) of the weights at (f KB + kb) KiB from their bases
+  const rsrc_t ar = make_rsrc(p.a_frag + size_t(mb0) * KB * 512, 16u * uint32_t(KB) * 1024u);
+  const rsrc_t wr = make_rsrc(p.w + size_t(nb0) * KB * 512, 16u * uint32_t(KB) * 1024u);
+  // copy Q (0..3) of k-block KBK into slot RING: ring fragment w + 8Q (0-15:
+  // A, 16-31: weights).  A block past the last re-reads block 0 (in bounds,
+  // never used).
+#define PI_AE_SQ_DMA(RING, KBK, Q)                                                    \
+  {                                                                                   \
+    const int f_ = w + 8 * (Q);                                                       \
+    const uint32_t kb_ = uint32_t((KBK) < NS ? (KBK) : 0);                            \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(f_ < 16 ? ar : wr, (lds_ptr_t)&RING[f_][0], 16, uint32_t(lane) * 16u, \
+                                             (uint32_t(f_ & 15) * uint32_t(KB) + kb_) * 1024u, 0, 0); \
+  }
+#define PI_AE_SQ_COPY(RING, KBK) \
+  _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) PI_AE_SQ_DMA(RING, KBK, q_)
+  PI_AE_SQ_COPY(ring0, 0)
+  PI_AE_SQ_COPY(ring1, 1)
+  PI_AE_SQ_COPY(ring2, 2)
+  tile_rstd<BM, 512, D>(p, srstd, mb0);
+  // the tile's shift-fold bias (gate and up columns as the weights interleave
+  // them); the first barrier of the main loop publishes it with srstd
+  if (threadIdx.x < BN) sbias[threadIdx.x] = p.bias[nb0 * 16 + threadIdx.x];
+
+  f32x16 acc[TR][TC];
+#pragma unroll
+  for (int r = 0; r < TR; ++r)
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
+
+  // k-block SG from slot RING: its copies have landed, barrier (which also
+  // retires every read of slot RING3, that of block SG-1), the wave's
+  // operands from LDS, then its 16 MFMAs with block SG+3's copies into
+  // RING3 between them
+#define PI_AE_SQ_STEP(RING, SG, RING3)                                                 \
+  {                                                                                   \
+    __builtin_amdgcn_s_waitcnt(0x0f78); /* vmcnt(8) */                                \
+    lds_barrier();                                                                    \
+    u32x4 a[TR][2], b[TC][2];                                                         \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
+      _Pragma("unroll") for (int r = 0; r < TR; ++r) a[r][h] = RING[8 * wm + 2 * r + sub][al[h]]; \
+      _Pragma("unroll") for (int c = 0; c < TC; ++c) b[c][h] = RING[16 + 4 * wn + 2 * c + sub][al[h]]; \
+    }                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
+      _Pragma("unroll") for (int r2 = 0; r2 < TR; r2 += 2) {                          \
+        _Pragma("unroll") for (int r = r2; r < r2 + 2; ++r)                           \
+          _Pragma("unroll") for (int c = 0; c < TC; ++c)                              \
+            acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, b[c][h]), __builtin_bit_cast(bf16x8, a[r][h]), acc[r][c]); \
+        PI_AE_SQ_DMA(RING3, (SG) + 3, h * 2 + r2 / 2)                                 \
+        __builtin_amdgcn_sched_barrier(0);                                            \
+      }                                                                               \
+  }
+  for (int sg = 0; sg < NS; sg += 4) {
+    PI_AE_SQ_STEP(ring0, sg, ring3)
+    PI_AE_SQ_STEP(ring1, sg + 1, ring0)
+    PI_AE_SQ_STEP(ring2, sg + 2, ring1)
+    PI_AE_SQ_STEP(ring3, sg + 3, ring2)
+  }
+#undef PI_AE_SQ_STEP
+#undef PI_AE_SQ_COPY
+#undef PI_AE_SQ_DMA
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the re-reads past the last block have landed
+  // Epilogue from the registers, as in k_gemm_wide: acc[r][c] is the
+  // transposed tile of rows 128 wm + 32 r.. and tile columns 32 (2 wn + c)..,
+  // whose first 16 columns are gate and last 16 up for the product columns
+  // 16 jp.., jp = nb0/2 + 2 wn + c.
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < TR; ++r) {
+    const int rl = 128 * wm + 32 * r + (lane & 31), row = mb0 * 16 + rl;
+    const float rs = srstd[rl];
+#pragma unroll
+    for (int c = 0; c < TC; ++c) {
+      const int tc = 2 * wn + c;
+      f32x16 v = acc[r][c];
+      acc_cols_to_lanes(v);
+      const float* bg = sbias + 32 * tc + 8 * hh;
+      float mv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mv[e] = gelu_tanh(v[e] * rs + bg[e]) * (v[8 + e] * rs + bg[16 + e]);
+      if (row < p.M)
+        *reinterpret_cast<uint4*>(p.m_out + afrag_index(row, 16 * (nb0 / 2 + tc) + 8 * hh, F / 32)) =
+            __builtin_bit_cast(uint4, pack8(make_float4(mv[0], mv[1], mv[2], mv[3]), make_float4(mv[4], mv[5], mv[6], mv[7])));
+    }
+  }
+}
+
 // The second half of a split-K GEMM: sum the S partial tiles of a BM x BN
 // output tile (fixed order z = 0 .. S-1) into LDS and run the GEMM's fused
 // epilogue on it.  Partials: [S][Mp][Np] fp32, columns local to the GEMM's
@@ -1749,6 +1871,8 @@ hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t)
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
+  if (p.M >= kSqMinRows)
+    return go(k_gemm_sq<kD, kF>, dim3(kNgu / 256, row_tiles(p.M, 256)), dim3(512), s, t, p, kD);
   if (p.M >= kTiledMinRows)
     return go(k_gemm_wide<E_GELU, kD, kF>, dim3(kNgu / 128, row_tiles(p.M, 256)), dim3(256), s, t, p, kD);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
