@@ -594,7 +594,7 @@ def pmc_summary(args):
                 return short
         if "k_attn" in kname:
             return "k_attn"
-        if "k_gemm_wide" in kname or "k_gemm<4, 2, 4, 8, 1," in kname:
+        if "k_gemm_sq" in kname or "k_gemm_wide" in kname or "k_gemm<4, 2, 4, 8, 1," in kname:
             return "k_gemm<gate_up>"
         if any(t in kname for t in ("k_gemm_big32<4, 1, 2, 0,", "k_gemm<2, 2, 4, 8, 0,", "k_gemm<4, 2, 4, 8, 0,")):
             return "k_gemm<qkv>"

@@ -866,7 +866,17 @@ __device__ __forceinline__ void acc_cols_to_lanes(f32x16& v) {
 // fp32 tile to part[z][row][col] ([z][gridDim.y * BM][gridDim.x * BN]) and
 // k_splitk_reduce sums them and runs the epilogue (for GEMMs whose tiles alone
 // would not fill the chip).
-template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF, bool SPLIT = false>
+// XG > 0 (unsplit launches): the tiles are dealt out XCD by XCD.  Workgroups
+// are dispatched round-robin over the 8 XCDs (linear id i on XCD i mod 8),
+// and each XCD's L2 serves only its own CUs, so a tile order in which
+// consecutive workgroups share operands makes every XCD fetch all of A and
+// all of the weights.  Instead XCD c takes the c-th eighth of the tiles in
+// an order that runs through the rows of one of XG column groups at a time:
+// for the residual GEMMs at 1600 rows (16 x 13 tiles, XG = 2) an XCD holds
+// about 3 row tiles of A and half the weight columns instead of all 13 and a
+// quarter.  Any mapping computes the same tiles; only the grids whose tile
+// count is a multiple of 8 are remapped.
+template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF, bool SPLIT = false, int XG = 0>
 __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, float* part) {
   constexpr int NW = WM, KS = 2;
   constexpr int NP = 4;                          // stages of loads in flight (register slots)
@@ -889,7 +899,17 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
   const int KBs = SPLIT ? KB / int(gridDim.z) : KB, kb0 = SPLIT ? int(blockIdx.z) * KBs : 0;
   const int NS = KBs / KS;
   // E_KV covers the K/V columns only: n-blocks from 2 * 64 on (Q is 64 pairs)
-  const int nb0 = blockIdx.x * FB + (EPI == E_KV ? 128 : 0), mb0 = blockIdx.y * FA;
+  int tx = int(blockIdx.x), ty = int(blockIdx.y);
+  if constexpr (XG > 0 && !SPLIT) {
+    const int GX = int(gridDim.x), GY = int(gridDim.y), n = GX * GY;
+    if ((n & 7) == 0 && GX % XG == 0) {
+      const int id = tx + GX * ty, t = (id & 7) * (n >> 3) + (id >> 3);
+      const int gw = GX / XG, g = t / (gw * GY), rem = t - g * gw * GY;
+      ty = rem / gw;
+      tx = g * gw + rem % gw;
+    }
+  }
+  const int nb0 = tx * FB + (EPI == E_KV ? 128 : 0), mb0 = ty * FA;
   const int sub = frag32_sub(lane);
   // this lane's A rows: fragments mb0 + 2(w*TR + r) + sub
   const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + (size_t(mb0 + 2 * w * TR + sub) * KB + kb0) * 64;
@@ -1882,7 +1902,7 @@ hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) 
 hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows) {
     if (p.a_frag2) return hipErrorInvalidValue;  // the key split is only taken at small M
-    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd, (float*)nullptr);
+    return go(k_gemm_big32<4, 1, 2, E_RES, kD, kF, false, 2>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kH * kHd, (float*)nullptr);
   }
   if (p.a_frag2) {
     if (p.M <= 64)
@@ -1895,7 +1915,7 @@ hipError_t launch_o(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
 }
 hipError_t launch_down(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 2, E_RES>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kF, (float*)nullptr);
+    return go(k_gemm_big32<4, 1, 2, E_RES, kD, kF, false, 2>, dim3(kD / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kF, (float*)nullptr);
   if (p.M <= 64)
     return go(k_gemm<1, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M, 16)), dim3(512), s, t, p);
   return go(k_gemm<4, 1, 8, 16, E_RES>, dim3(kD / 16 + p.pf.nwg, row_tiles(p.M)), dim3(512), s, t, p);
