@@ -1637,10 +1637,18 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const int r = (qw * NWQ + rg) * 32 + l32;
   const int rc = r < nq ? r : nq - 1;
 
+  // Q of the group's 32 rows (lane l: row l%32, head-dim 16s + 8(l/32) + j):
+  // the two waves of a group each load half (s < 8 or s >= 8) and trade
+  // halves through LDS below, which halves the Q bytes through the CU.
   bf16x8 qf[16];
   const uint16_t* qrow = p.q + (size_t(b) * nq + rc) * kHd + 8 * hh;
+  if (kh == 0) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) qf[s] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * s));
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * s));
+  } else {
+#pragma unroll
+    for (int s = 8; s < 16; ++s) qf[s] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * s));
+  }
 
   const int nkb = p.nkb, npair = (nkb + 1) / 2;
   const uint32_t ep_bytes = uint32_t(nkb) * 16384u;
@@ -1649,20 +1657,20 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const rsrc_t br = make_rsrc(p.kbias + size_t(b) * nkb * 32, uint32_t(nkb) * 128u);
 
   // copy Q (0 <= Q < 8) of pair PR's K (RS = kr) or V (RS = vr) into buffer
-  // BUF: fragment 4(Q%4) + w of block Q/4 of the pair.  A pair past the last
-  // re-copies pair 0 and a missing second block re-reads block 0 (in bounds;
-  // never read, or masked), so that every step issues the same copies and
-  // every wait count below is exact.
+  // BUF: fragment 4(Q%4) + w of block Q/4 of the pair.  Blocks past the last
+  // (a missing second block, pairs after the last) are read out of the
+  // buffer's range: zeros, no memory traffic, never read or masked.  So
+  // every step issues the same copies and every wait count below is exact.
 #define PI_AE_KV32_DMA(RS, BUF, PR, Q)                                                \
   {                                                                                   \
-    const int blk_ = 2 * ((PR) < npair ? (PR) : 0) + ((Q) >> 2), fi_ = ((Q) & 3) * NW + w; \
+    const int blk_ = 2 * (PR) + ((Q) >> 2), fi_ = ((Q) & 3) * NW + w;                 \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(RS, (lds_ptr_t)&BUF[(Q) >> 2][fi_][0], 16, uint32_t(lane) * 16u, \
-                                             uint32_t(blk_ < nkb ? blk_ : 0) * 16384u + uint32_t(fi_) * 1024u, 0, 0); \
+                                             blk_ < nkb ? uint32_t(blk_) * 16384u + uint32_t(fi_) * 1024u : ep_bytes, 0, 0); \
   }
   // the pair's 64 key biases (every wave copies the same ones to the same
   // place, which keeps the wait counts uniform; past the end they read as 0)
 #define PI_AE_KV32_BIAS(KB, PR) \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)&KB[0], 4, uint32_t(lane) * 4u, uint32_t((PR) < npair ? (PR) : 0) * 256u, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)&KB[0], 4, uint32_t(lane) * 4u, uint32_t(PR) * 256u, 0, 0);
 
   f32x16 acc[8];
 #pragma unroll
@@ -1763,6 +1771,24 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   PI_AE_KV32_BIAS(kba, 0)
 #pragma unroll
   for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(kr, k1s, 1, c)
+  // the two halves of Q: each wave parks its half in V buffer 1 (first
+  // written by the copies after the first barrier of the loop) and takes
+  // the other wave's
+  if (kh == 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v1s[rg][s][lane] = __builtin_bit_cast(u32x4, qf[s]);
+  } else {
+#pragma unroll
+    for (int s = 8; s < 16; ++s) v1s[rg][s][lane] = __builtin_bit_cast(u32x4, qf[s]);
+  }
+  lds_barrier();
+  if (kh == 0) {
+#pragma unroll
+    for (int s = 8; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, v1s[rg][s][lane]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, v1s[rg][s][lane]);
+  }
   // (the loop body always runs both steps, so that the wait counts the
   // compiler derives for each step's LDS reads see the same copies in flight
   // on every path; an odd last pair runs after it)
