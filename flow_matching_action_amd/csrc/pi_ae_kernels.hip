@@ -1139,6 +1139,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   }
 }
 
+constexpr int kSqWaves = 8;
 // Square-tile GEMM for the gate/up projection when the rows alone give
 // about a CU's worth of 256 x 256 tiles (the batched loop): 8 waves, 2 along
 // M x 4 along N (128 x 64 each, 4 x 2 accumulator tiles of 32x32), one
@@ -1155,9 +1156,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
 // the weights as their first operand (transposed accumulators, one
 // activation row per lane), and the GELU product is formed from the
 // registers as in k_gemm_wide.
-template <int D, int F>
-__global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
-  constexpr int BM = 256, BN = 256, TR = 4, TC = 2;
+template <int D, int F, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_gemm_sq(GemmParams p, int K) {
+  // NWV waves, 4 along N (64 columns each) and NWV/4 along M
+  constexpr int BM = 256, BN = 256, WR = BM / (NWV / 4), TR = WR / 32, TC = 2, CPW = 32 / NWV;
+  static_assert(NWV == 8 || NWV == 16, "8 waves (128 x 64 each) or 16 (64 x 64)");
   __shared__ __attribute__((aligned(16))) u32x4 ring0[32][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring1[32][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring2[32][64];
@@ -1166,7 +1169,7 @@ __global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
   __shared__ __attribute__((aligned(16))) float sbias[BN];
   kernarg_touch(p);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 2, wn = w & 3;  // rows 128 wm.., columns 64 wn..
+  const int wm = w >> 2, wn = w & 3;  // rows WR wm.., columns 64 wn..
   const int KB = K >> 5, NS = KB;     // NS is a multiple of 4
   const int nb0 = blockIdx.x * (BN / 16), mb0 = blockIdx.y * (BM / 16);
   const int sub = frag32_sub(lane);
@@ -1175,22 +1178,22 @@ __global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
   // and (nb0 + f, kb) of the weights at (f KB + kb) KiB from their bases
   const rsrc_t ar = make_rsrc(p.a_frag + size_t(mb0) * KB * 512, 16u * uint32_t(KB) * 1024u);
   const rsrc_t wr = make_rsrc(p.w + size_t(nb0) * KB * 512, 16u * uint32_t(KB) * 1024u);
-  // copy Q (0..3) of k-block KBK into slot RING: ring fragment w + 8Q (0-15:
-  // A, 16-31: weights).  A block past the last re-reads block 0 (in bounds,
-  // never used).
+  // copy Q (0 <= Q < CPW) of k-block KBK into slot RING: ring fragment
+  // w + NWV Q (0-15: A, 16-31: weights).  A block past the last re-reads
+  // block 0 (in bounds, never used).
 #define PI_AE_SQ_DMA(RING, KBK, Q)                                                    \
   {                                                                                   \
-    const int f_ = w + 8 * (Q);                                                       \
+    const int f_ = w + NWV * (Q);                                                     \
     const uint32_t kb_ = uint32_t((KBK) < NS ? (KBK) : 0);                            \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(f_ < 16 ? ar : wr, (lds_ptr_t)&RING[f_][0], 16, uint32_t(lane) * 16u, \
                                              (uint32_t(f_ & 15) * uint32_t(KB) + kb_) * 1024u, 0, 0); \
   }
 #define PI_AE_SQ_COPY(RING, KBK) \
-  _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) PI_AE_SQ_DMA(RING, KBK, q_)
+  _Pragma("unroll") for (int q_ = 0; q_ < CPW; ++q_) PI_AE_SQ_DMA(RING, KBK, q_)
   PI_AE_SQ_COPY(ring0, 0)
   PI_AE_SQ_COPY(ring1, 1)
   PI_AE_SQ_COPY(ring2, 2)
-  tile_rstd<BM, 512, D>(p, srstd, mb0);
+  tile_rstd<BM, NWV * 64, D>(p, srstd, mb0);
   // the tile's shift-fold bias (gate and up columns as the weights interleave
   // them); the first barrier of the main loop publishes it with srstd
   if (threadIdx.x < BN) sbias[threadIdx.x] = p.bias[nb0 * 16 + threadIdx.x];
@@ -1203,28 +1206,31 @@ __global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
 
-  // k-block SG from slot RING: its copies have landed, barrier (which also
-  // retires every read of slot RING3, that of block SG-1), the wave's
-  // operands from LDS, then its 16 MFMAs with block SG+3's copies into
-  // RING3 between them
+  // k-block SG from slot RING: its copies have landed (the 2 CPW copies of
+  // the two later blocks may be in flight), barrier (which also retires
+  // every read of slot RING3, that of block SG-1), the wave's operands from
+  // LDS, then its MFMAs with block SG+3's CPW copies into RING3 spread
+  // between them
+  constexpr int MPC = 2 * TR * TC / CPW;  // MFMAs per copy
 #define PI_AE_SQ_STEP(RING, SG, RING3)                                                 \
   {                                                                                   \
-    __builtin_amdgcn_s_waitcnt(0x0f78); /* vmcnt(8) */                                \
+    if constexpr (CPW == 4) __builtin_amdgcn_s_waitcnt(0x0f78); /* vmcnt(8) */        \
+    else __builtin_amdgcn_s_waitcnt(0x0f74);                    /* vmcnt(4) */        \
     lds_barrier();                                                                    \
     u32x4 a[TR][2], b[TC][2];                                                         \
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
-      _Pragma("unroll") for (int r = 0; r < TR; ++r) a[r][h] = RING[8 * wm + 2 * r + sub][al[h]]; \
+      _Pragma("unroll") for (int r = 0; r < TR; ++r) a[r][h] = RING[(WR / 16) * wm + 2 * r + sub][al[h]]; \
       _Pragma("unroll") for (int c = 0; c < TC; ++c) b[c][h] = RING[16 + 4 * wn + 2 * c + sub][al[h]]; \
     }                                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                     \
-      _Pragma("unroll") for (int r2 = 0; r2 < TR; r2 += 2) {                          \
-        _Pragma("unroll") for (int r = r2; r < r2 + 2; ++r)                           \
-          _Pragma("unroll") for (int c = 0; c < TC; ++c)                              \
-            acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, b[c][h]), __builtin_bit_cast(bf16x8, a[r][h]), acc[r][c]); \
-        PI_AE_SQ_DMA(RING3, (SG) + 3, h * 2 + r2 / 2)                                 \
+    _Pragma("unroll") for (int m = 0; m < 2 * TR * TC; ++m) {                         \
+      const int h = m / (TR * TC), r = (m / TC) % TR, c = m % TC;                     \
+      acc[r][c] = mfma32(__builtin_bit_cast(bf16x8, b[c][h]), __builtin_bit_cast(bf16x8, a[r][h]), acc[r][c]); \
+      if (m % MPC == MPC - 1) {                                                       \
+        PI_AE_SQ_DMA(RING3, (SG) + 3, m / MPC)                                        \
         __builtin_amdgcn_sched_barrier(0);                                            \
       }                                                                               \
+    }                                                                                 \
   }
   for (int sg = 0; sg < NS; sg += 4) {
     PI_AE_SQ_STEP(ring0, sg, ring3)
@@ -1237,13 +1243,13 @@ __global__ __launch_bounds__(512) void k_gemm_sq(GemmParams p, int K) {
 #undef PI_AE_SQ_DMA
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the re-reads past the last block have landed
   // Epilogue from the registers, as in k_gemm_wide: acc[r][c] is the
-  // transposed tile of rows 128 wm + 32 r.. and tile columns 32 (2 wn + c)..,
+  // transposed tile of rows WR wm + 32 r.. and tile columns 32 (2 wn + c)..,
   // whose first 16 columns are gate and last 16 up for the product columns
   // 16 jp.., jp = nb0/2 + 2 wn + c.
   const int hh = lane >> 5;
 #pragma unroll
   for (int r = 0; r < TR; ++r) {
-    const int rl = 128 * wm + 32 * r + (lane & 31), row = mb0 * 16 + rl;
+    const int rl = WR * wm + 32 * r + (lane & 31), row = mb0 * 16 + rl;
     const float rs = srstd[rl];
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
@@ -1918,7 +1924,7 @@ hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t)
 }
 hipError_t launch_gu(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
   if (p.M >= kSqMinRows)
-    return go(k_gemm_sq<kD, kF>, dim3(kNgu / 256, row_tiles(p.M, 256)), dim3(512), s, t, p, kD);
+    return go(k_gemm_sq<kD, kF, kSqWaves>, dim3(kNgu / 256, row_tiles(p.M, 256)), dim3(kSqWaves * 64), s, t, p, kD);
   if (p.M >= kTiledMinRows)
     return go(k_gemm_wide<E_GELU, kD, kF>, dim3(kNgu / 128, row_tiles(p.M, 256)), dim3(256), s, t, p, kD);
   return go(k_gemm<4, 2, 4, 8, E_GELU>, dim3(kNgu / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
