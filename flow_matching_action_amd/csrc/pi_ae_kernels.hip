@@ -137,16 +137,19 @@ __device__ __forceinline__ void kernarg_touch(const P& p) {
     return;                                                                                   \
   }
 
-// GELU, tanh approximation (the MLP activation of the Gemma-shaped expert).
-// tanh through one exp2 and one hardware reciprocal (v_rcp_f32, 1 ulp):
-// tanh(z) = 1 - 2 / (e^(2z) + 1), exact at both tails (e^(2z) -> inf gives 1,
-// -> 0 gives -1); relative error a few ulp, far below the bf16 rounding of its
-// result.  The reciprocal instead of an IEEE division trims the fused GELU
-// epilogues (the batched gate/up GEMM: 40.0 -> 38.3 us per launch).
+// GELU, tanh approximation (the MLP activation of the Gemma-shaped expert):
+// 0.5 x (1 + tanh z), z = sqrt(2/pi) (x + 0.044715 x^3), which is
+// x / (1 + e^(-2z)): one exp2 of a cubic in x (the constants folded:
+// -2 sqrt(2/pi) log2(e) and the same times 0.044715) and one hardware
+// reciprocal (v_rcp_f32, 1 ulp).  Exact at both tails (x -> -inf: the
+// reciprocal of inf is 0; x -> +inf: of 1); relative error a few ulp, far
+// below the bf16 rounding of its result.  The fused GELU epilogues are VALU
+// work that every workgroup reaches at once, so its count matters (the
+// batched gate/up GEMM: an IEEE division instead of the reciprocal took
+// 40.0 against 38.3 us per launch).
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float z = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  const float e = exp2f(z * 2.8853900817779268f);  // e^(2z)
-  return 0.5f * x * (2.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+  const float u = x * __builtin_fmaf(x * x, -0.1029432395800235f, -2.302208198144325f);  // -2 z log2(e)
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(u));
 }
 // Offset (in bf16 elements) of activation (row, k) in the fragment-major
 // layout [rows/16][K/32][64 lanes][8] that the GEMM A operand loads directly.
@@ -649,6 +652,30 @@ __device__ __forceinline__ void qkv_emit(const GemmParams& p, int row, int jp, i
   }
 }
 
+// The same 1/rms split in two, for kernels whose first operand loads would
+// otherwise sit in front of the h^2 partials in the load queue (waiting for
+// the partials then waits for those loads too): load() before them (thread
+// i < BM: row mb0*16 + i, into registers), finish() after them (the sum in
+// tile_rstd's order, into srstd).
+template <int BM, int D>
+struct RstdPre {
+  float4 v[D / 64];
+  __device__ __forceinline__ void load(const GemmParams& p, int mb0) {
+    if (threadIdx.x < BM) {
+      const float4* sp = reinterpret_cast<const float4*>(p.ssq + size_t(mb0 * 16 + threadIdx.x) * (D / 16));
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) v[i] = sp[i];
+    }
+  }
+  __device__ __forceinline__ void finish(const GemmParams& p, float* srstd) const {
+    if (threadIdx.x < BM) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+      srstd[threadIdx.x] = 1.f / sqrtf(sum * (1.f / D) + p.eps);
+    }
+  }
+};
 // Epilogue of the large-M GEMMs, after the BM x BN fp32 tile has been placed
 // in LDS (ct, CS floats per row; row scale 1/rms in srstd for the normalised
 // inputs): each of the NT threads takes 8 consecutive columns of one row per
@@ -935,9 +962,16 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
 #define PI_AE_B32_STORE_B(SL, BUF) \
   _Pragma("unroll") for (int q = 0; q < BPW; ++q) st[BUF][q * NW + w][lane] = pb[SL][q];
 
+  // 1/rms: the partials loaded ahead of the operands where their registers
+  // fit beside the loads in flight (D = 1024: 64 VGPRs), else after them
+  static_assert(NW * 64 >= BM, "one row of 1/rms per thread");
+  constexpr bool PRE = NORM && !SPLIT && D <= 1024;
+  RstdPre<BM, D> rp;
+  if constexpr (PRE) rp.load(p, mb0);
 #pragma unroll
   for (int sl = 0; sl < NP - 1; ++sl) PI_AE_B32_LOAD(sl, sl)
-  if constexpr (NORM && !SPLIT) tile_rstd<BM, NW * 64, D>(p, srstd, mb0);
+  if constexpr (PRE) rp.finish(p, srstd);
+  else if constexpr (NORM && !SPLIT) tile_rstd<BM, NW * 64, D>(p, srstd, mb0);
   PI_AE_B32_STORE_B(0, 0)
   lds_barrier();
 
@@ -1065,16 +1099,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
                                                (uint32_t(f) * uint32_t(KB) + kb_) * 1024u, 0, 0);    \
     }                                                                                 \
   }
+  // the tile's shift-fold bias (gate and up columns as the weights interleave
+  // them) and 1/rms of its rows, loaded ahead of the operands; the first
+  // barrier of the main loop publishes them
+  RstdPre<BM, D> rp;
+  rp.load(p, mb0);
+  const float bv = threadIdx.x < BN ? p.bias[nb0 * 16 + threadIdx.x] : 0.f;
   PI_AE_W_LOADA(0, 0)
   PI_AE_W_DMA(ring0, 0)
   PI_AE_W_LOADA(1, 1)
   PI_AE_W_DMA(ring1, 1)
   PI_AE_W_LOADA(2, 2)
   PI_AE_W_DMA(ring2, 2)
-  tile_rstd<BM, 256, D>(p, srstd, mb0);
-  // the tile's shift-fold bias (gate and up columns as the weights interleave
-  // them); the first barrier of the main loop publishes it with srstd
-  if (threadIdx.x < BN) sbias[threadIdx.x] = p.bias[nb0 * 16 + threadIdx.x];
+  rp.finish(p, srstd);
+  if (threadIdx.x < BN) sbias[threadIdx.x] = bv;
 
   f32x16 acc[TR][TC];
 #pragma unroll
@@ -1126,8 +1164,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
     const float rs = srstd[rl];
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
-      f32x16 v = acc[r][c];
-      acc_cols_to_lanes(v);
+      acc_cols_to_lanes(acc[r][c]);
+      const f32x16& v = acc[r][c];
       const float* bg = sbias + 32 * c + 8 * hh;
       float mv[8];
 #pragma unroll
@@ -1190,13 +1228,18 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm_sq(GemmParams p, int K) {
   }
 #define PI_AE_SQ_COPY(RING, KBK) \
   _Pragma("unroll") for (int q_ = 0; q_ < CPW; ++q_) PI_AE_SQ_DMA(RING, KBK, q_)
+  // the tile's shift-fold bias (gate and up columns as the weights interleave
+  // them) and 1/rms of its rows, loaded ahead of the copies; the first
+  // barrier of the main loop publishes them
+  static_assert(BM == BN && NWV * 64 >= BM, "one row and one bias column per thread");
+  RstdPre<BM, D> rp;
+  rp.load(p, mb0);
+  const float bv = threadIdx.x < BN ? p.bias[nb0 * 16 + threadIdx.x] : 0.f;
   PI_AE_SQ_COPY(ring0, 0)
   PI_AE_SQ_COPY(ring1, 1)
   PI_AE_SQ_COPY(ring2, 2)
-  tile_rstd<BM, NWV * 64, D>(p, srstd, mb0);
-  // the tile's shift-fold bias (gate and up columns as the weights interleave
-  // them); the first barrier of the main loop publishes it with srstd
-  if (threadIdx.x < BN) sbias[threadIdx.x] = p.bias[nb0 * 16 + threadIdx.x];
+  rp.finish(p, srstd);
+  if (threadIdx.x < BN) sbias[threadIdx.x] = bv;
 
   f32x16 acc[TR][TC];
 #pragma unroll
@@ -1254,8 +1297,8 @@ __global__ __launch_bounds__(NWV * 64) void k_gemm_sq(GemmParams p, int K) {
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
       const int tc = 2 * wn + c;
-      f32x16 v = acc[r][c];
-      acc_cols_to_lanes(v);
+      acc_cols_to_lanes(acc[r][c]);
+      const f32x16& v = acc[r][c];
       const float* bg = sbias + 32 * tc + 8 * hh;
       float mv[8];
 #pragma unroll
