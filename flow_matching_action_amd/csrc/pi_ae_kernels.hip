@@ -1059,10 +1059,14 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
 // (lane l: activation row l%32, 16 output columns); the fused GELU epilogue
 // then runs per wave from the registers (see there), with no LDS tile and
 // no barrier, and two workgroups share a CU.
-template <int EPI, int D, int F>
-__global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
-  constexpr int TR = 2, TC = 4, BM = 256, BN = 128, FB = BN / 16;
+// NWV waves stacked along M, each TR row tiles of 32 x all TC column tiles of
+// 32 (the 256 x 128 default: 4 waves of 64 x 128, two workgroups per CU;
+// 8 waves of 32 x 256 make a 256 x 256 tile at one workgroup per CU).
+template <int EPI, int D, int F, int NWV = 4, int TR = 2, int TC = 4>
+__global__ __launch_bounds__(NWV * 64, 8 / NWV) void k_gemm_wide(GemmParams p, int K) {
+  constexpr int BM = NWV * 32 * TR, BN = 32 * TC, FB = BN / 16, FPW = FB / NWV;
   static_assert(EPI == E_GELU, "the register epilogue is the gate/up one");
+  static_assert(FB % NWV == 0 && NWV * 64 >= BM && NWV * 64 >= BN, "copies split evenly, a row / column per thread");
   __shared__ __attribute__((aligned(16))) u32x4 ring0[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring1[FB][64];
   __shared__ __attribute__((aligned(16))) u32x4 ring2[FB][64];
@@ -1075,9 +1079,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   const int nb0 = blockIdx.x * FB, mb0 = blockIdx.y * (BM / 16);
   const int sub = frag32_sub(lane);
   const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
-  // wave w: rows 64w.., fragments mb0 + 4w + 2r + sub (row tile r)
-  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 4 * w + sub) * KB * 64;
-  // the tile's 8 weight fragment columns: fragment (nb0 + f, kb) at (f KB + kb) KiB
+  // wave w: rows 32 TR w.., fragments mb0 + 2 TR w + 2r + sub (row tile r)
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + size_t(mb0 + 2 * TR * w + sub) * KB * 64;
+  // the tile's FB weight fragment columns: fragment (nb0 + f, kb) at (f KB + kb) KiB
   const rsrc_t wr = make_rsrc(p.w + size_t(nb0) * KB * 512, uint32_t(FB) * uint32_t(KB) * 1024u);
 
   u32x4 av[4][TR][2];
@@ -1088,13 +1092,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
       _Pragma("unroll") for (int h = 0; h < 2; ++h)                                   \
         av[SL][r][h] = ap[(size_t(2 * r) * KB + kb_) * 64 + al[h]];                   \
   }
-  // fragments w and w + 4 of k-block KBK into slot RING (a missing block
-  // re-reads block 0: in bounds, never used)
+  // fragments w + NWV q (q < FPW) of k-block KBK into slot RING (a missing
+  // block re-reads block 0: in bounds, never used)
 #define PI_AE_W_DMA(RING, KBK)                                                        \
   {                                                                                   \
     const uint32_t kb_ = uint32_t((KBK) < NS ? (KBK) : 0);                            \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                   \
-      const int f = q * 4 + w;                                                        \
+    _Pragma("unroll") for (int q = 0; q < FPW; ++q) {                                 \
+      const int f = q * NWV + w;                                                      \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)&RING[f][0], 16, uint32_t(lane) * 16u, \
                                                (uint32_t(f) * uint32_t(KB) + kb_) * 1024u, 0, 0);    \
     }                                                                                 \
@@ -1123,12 +1127,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
 
   // stage SG (register slot SL = SG mod 4, weights in RING): its loads have
-  // landed (6 per wave per stage; the two later stages' 12 may be pending),
-  // barrier, then k-block SG+3 is issued into slot SL+3 / RING3 (= the slot
-  // of stage SG-1, read by every wave before the barrier), and the 16 MFMAs.
+  // landed (2 TR + FPW per wave per stage; the two later stages' may be
+  // pending), barrier, then k-block SG+3 is issued into slot SL+3 / RING3
+  // (= the slot of stage SG-1, read by every wave before the barrier), and
+  // the MFMAs.
+  constexpr int VPS = 2 * TR + FPW;  // loads per wave and stage
+  static_assert(2 * VPS <= 15, "the wait count fits the low vmcnt bits");
 #define PI_AE_W_STEP(RING, SL, SG, RING3)                                             \
   {                                                                                   \
-    __builtin_amdgcn_s_waitcnt(0x0f7c); /* vmcnt(12) */                               \
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * VPS)); /* vmcnt(2 VPS) */                \
     lds_barrier();                                                                    \
     PI_AE_W_LOADA(((SL) + 3) & 3, (SG) + 3)                                           \
     PI_AE_W_DMA(RING3, (SG) + 3)                                                      \
@@ -1151,7 +1158,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
 #undef PI_AE_W_LOADA
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the re-reads past the last block have landed
   // Epilogue from the registers.  acc[r][c] is the transposed tile: lane l
-  // holds row 32r + l%32 of the wave's 64 and, in register i, column
+  // holds row 32r + l%32 of the wave's 32 TR and, in register i, column
   // 8(i/4) + 4(l/32) + i%4 of the 32 of tile c, whose first 16 columns are
   // gate and last 16 up for the same 16 product columns 16jp.., jp = nb0/2 + c.
   // Regrouped (acc_cols_to_lanes), lane l holds gate columns 8(l/32) + 0..7
@@ -1160,7 +1167,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(GemmParams p, int K) {
   const int hh = lane >> 5;
 #pragma unroll
   for (int r = 0; r < TR; ++r) {
-    const int rl = 64 * w + 32 * r + (lane & 31), row = mb0 * 16 + rl;
+    const int rl = 32 * TR * w + 32 * r + (lane & 31), row = mb0 * 16 + rl;
     const float rs = srstd[rl];
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
