@@ -72,35 +72,55 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 // Body of an appended prefetching workgroup (see Prefetch).  The `per`
-// prefetchers that share XCD residue `res` split that XCD's bytes evenly;
-// this one is number `sub` of them.  Loads are batched 8 deep per thread.
+// prefetchers that share XCD residue `res` split that XCD's bytes of each
+// region evenly; this one is number `sub` of them.  Its shares of the (up to
+// three) regions are walked as one run of 16-byte units, kPfDepth loads per
+// thread in flight before any is consumed, so that a share of up to
+// kPfDepth * 16 bytes per thread costs one round trip to memory (a loop per
+// region and slice made one round trip each).
 // Written only if the XOR of everything a prefetcher loaded hits a magic
 // value: keeps the loads from being removed.
 __device__ uint32_t g_pf_sink;
+constexpr int kPfDepth = 16;
+struct PfShare {
+  const u32x4* base;
+  uint32_t lo, len, n16;  // units [lo, lo + len) of the region's units, n16 per slice
+  bool sliced;
+};
+__device__ __forceinline__ PfShare pf_share(const Prefetch& r, int sub, int per, int res) {
+  PfShare z{nullptr, 0u, 0u, 1u, false};
+  if (!r.base || r.bytes < 16) return z;
+  z.base = static_cast<const u32x4*>(r.base);
+  z.n16 = r.bytes >> 4;
+  z.sliced = r.count > 0;
+  // broadcast: one "slice", the whole region; slices: j = res, res+8, ...
+  const uint32_t nsl = r.count > 0 ? (r.count > res ? uint32_t(r.count - res + 7) / 8u : 0u) : 1u;
+  const uint64_t total = uint64_t(nsl) * z.n16;
+  z.lo = uint32_t(total * sub / per);
+  z.len = uint32_t(total * (sub + 1) / per) - z.lo;
+  return z;
+}
 __device__ __forceinline__ void prefetch_body(const PrefetchSet& pf, int sub, int per, int res) {
+  const PfShare z0 = pf_share(pf.r[0], sub, per, res), z1 = pf_share(pf.r[1], sub, per, res),
+                z2 = pf_share(pf.r[2], sub, per, res);
+  const uint32_t c1 = z0.len, c2 = c1 + z1.len, n = c2 + z2.len;
   uint32_t acc = 0;
-  for (int d = 0; d < 3; ++d) {
-    const Prefetch& r = pf.r[d];
-    if (!r.base || r.bytes < 16) continue;
-    const u32x4* base = static_cast<const u32x4*>(r.base);
-    const uint32_t n16 = r.bytes >> 4;
-    // broadcast: one "slice", the whole region; slices: j = res, res+8, ...
-    const uint32_t nsl = r.count > 0 ? (r.count > res ? uint32_t(r.count - res + 7) / 8u : 0u) : 1u;
-    const uint64_t total = uint64_t(nsl) * n16;
-    uint32_t u = uint32_t(total * sub / per);
-    const uint32_t hi = uint32_t(total * (sub + 1) / per);
-    while (u < hi) {  // this prefetcher's units, one slice at a time
-      const uint32_t sl = u / n16, off = u - sl * n16, n = min(hi, (sl + 1) * n16) - u;
-      const u32x4* src = base + (r.count > 0 ? size_t(res + 8 * sl) * n16 : size_t(0)) + off;
-      for (uint32_t i = threadIdx.x; i < n; i += 8 * blockDim.x) {
-        u32x4 v[8];
+  for (uint32_t j0 = threadIdx.x; j0 < n; j0 += kPfDepth * blockDim.x) {
+    u32x4 v[kPfDepth];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = (i + k * blockDim.x < n) ? src[i + k * blockDim.x] : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].w;
-      }
-      u += n;
+    for (int k = 0; k < kPfDepth; ++k) {
+      // unit j of the run: region by selects (no branches), then its slice
+      const uint32_t j = j0 + k * blockDim.x;
+      const bool r1 = j >= c1, r2 = j >= c2;
+      const PfShare& z = r2 ? z2 : r1 ? z1 : z0;
+      const uint32_t u = z.lo + j - (r2 ? c2 : r1 ? c1 : 0u), sl = u / z.n16;
+      const u32x4* src = z.base + (z.sliced ? size_t(res + 8 * sl) * z.n16 : size_t(0)) + (u - sl * z.n16);
+      v[k] = u32x4{0, 0, 0, 0};
+      if (j < n) v[k] = *src;
     }
+    // every word is used, so no load's registers are reused while it is in flight
+#pragma unroll
+    for (int k = 0; k < kPfDepth; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   if (acc == 0x9E3779B9u && threadIdx.x == 0) g_pf_sink = acc;  // keeps the loads
 }
