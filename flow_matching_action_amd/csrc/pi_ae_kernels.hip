@@ -1536,7 +1536,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 
   const int nkb = p.nkb;
   const int kbs = split * nkb / KS, nks = (split + 1) * nkb / KS - kbs;
-  const int kb0 = kbs + w * nks / kAttnWaves, kb1 = kbs + (w + 1) * nks / kAttnWaves;
+  // nks / 8 blocks per wave and one more for the first nks % 8 waves: their
+  // loads are the first the CU serves, so their further blocks start earliest
+  const int nbw = nks / kAttnWaves, nex = nks % kAttnWaves;
+  const int kb0 = kbs + w * nbw + min(w, nex), kb1 = kb0 + nbw + (w < nex ? 1 : 0);
   const uint32_t ep_bytes = uint32_t(nkb) * 16384u;  // one episode's packed K (or V)
   const rsrc_t kr = make_rsrc(p.kp + size_t(b) * nkb * 8192, ep_bytes);
   const rsrc_t vr = make_rsrc(p.vp + size_t(b) * nkb * 8192, ep_bytes);
@@ -1550,8 +1553,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 
   // one K / V register set per wave: block kb+1's K is issued as soon as the
   // scores of block kb have consumed K, its V as soon as O^T has consumed V
-  // (unconditional, so that every wait count is exact: a wave without a
-  // block reads block 0, in bounds and unused)
+  // (a wave without a block reads block 0, in bounds and unused, so that
+  // every wave issues the same first loads)
   uint4 kf[16], vf[16];
   float4 bias[2];
   {
@@ -1569,35 +1572,42 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf(qs[c * 33 + ks * 4 + g]);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const bool more = kb + 1 < kb1;
-    const uint32_t nxt = uint32_t(kb + 1) * 16384u;
-    f32x4 s[2];
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk) {
-      s[mk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[mk] = mfma(as_bf(kf[mk * 8 + ks]), qf[ks], s[mk]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, nxt + f * 1024u);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float alpha;
-    const bf16x8 pf = attn_softmax(s, bias, m_run, l_run, alpha);
-#pragma unroll
-    for (int md = 0; md < 16; ++md) acc[md] = mfma(as_bf(vf[md]), pf, acc[md] * alpha);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-#pragma unroll
-      for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, nxt + f * 1024u);
-      bias[0] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb + 1) * 128u));
-      bias[1] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t(kb + 1) * 128u + 64u));
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  // one block: scores from kf, then (NEXT) block kb+1's K into kf, the
+  // softmax and O^T += V^T P^T from vf, then (NEXT) block kb+1's V and biases
+#define PI_AE_ATTN_BLOCK(NEXT, KB)                                                     \
+  {                                                                                    \
+    f32x4 s[2];                                                                        \
+    _Pragma("unroll") for (int mk = 0; mk < 2; ++mk) {                                 \
+      s[mk] = f32x4{0.f, 0.f, 0.f, 0.f};                                               \
+      _Pragma("unroll") for (int ks = 0; ks < 8; ++ks) s[mk] = mfma(as_bf(kf[mk * 8 + ks]), qf[ks], s[mk]); \
+    }                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    const uint32_t nxt = uint32_t((KB) + 1) * 16384u;                                  \
+    if (NEXT) {                                                                        \
+      _Pragma("unroll") for (int f = 0; f < 16; ++f) kf[f] = bload16(kr, lo16, nxt + f * 1024u); \
+    }                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    float alpha;                                                                       \
+    const bf16x8 pf = attn_softmax(s, bias, m_run, l_run, alpha);                      \
+    _Pragma("unroll") for (int md = 0; md < 16; ++md) acc[md] = mfma(as_bf(vf[md]), pf, acc[md] * alpha); \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    if (NEXT) {                                                                        \
+      _Pragma("unroll") for (int f = 0; f < 16; ++f) vf[f] = bload16(vr, lo16, nxt + f * 1024u); \
+      bias[0] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t((KB) + 1) * 128u)); \
+      bias[1] = __builtin_bit_cast(float4, bload16(br, go16, uint32_t((KB) + 1) * 128u + 64u)); \
+    }                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
   }
+  // every block but the wave's last issues the next block's loads, the last
+  // none: no load sits behind a branch (so the compiler's wait counts are
+  // exact; a branch around the next block's loads made the products of a
+  // block wait for the next block's K) and no wave issues loads it does not
+  // use (loads read out of range move no data, but each still takes its
+  // turn in the CU's address path that the K/V stream is queued in)
+  int kb = kb0;
+  for (; kb + 1 < kb1; ++kb) PI_AE_ATTN_BLOCK(true, kb)
+  if (kb < kb1) PI_AE_ATTN_BLOCK(false, kb)
+#undef PI_AE_ATTN_BLOCK
 
   // merge the key ranges of the waves
   float* sml = ored + kAttnWaves * 16 * kOStride;  // [waves][16][2]
