@@ -923,43 +923,51 @@ __device__ __forceinline__ void acc_cols_to_lanes(f32x16& v) {
 // about 3 row tiles of A and half the weight columns instead of all 13 and a
 // quarter.  Any mapping computes the same tiles; only the grids whose tile
 // count is a multiple of 8 are remapped.
-template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF, bool SPLIT = false, int XG = 0>
-__global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, float* part) {
+// LDS of one big32 workgroup (floats): the B staging of a stage pair or the
+// output tile, whichever is larger, for a tile of WNC column tiles
+template <int WM, int TR, int TC, int WNC>
+constexpr int big32_lds_floats() {
+  constexpr int FB = 2 * TC, BM = 32 * TR * WM / WNC, BN = 32 * TC * WNC, FBS = FB * WNC * 2;
+  return 2 * FBS * 64 * 4 > BM * (BN + 4) ? 2 * FBS * 64 * 4 : BM * (BN + 4);
+}
+// TAIL: a tile of half the rows and two column tiles (the WM waves as 2 along
+// the columns x WM/2 along the rows; each wave still computes TR x TC 32x32
+// tiles), for a last row tile with at most half its rows valid: it halves that
+// row's workgroups (at 1600 rows, the QKV GEMM's 13 x 40 = 520 tiles of
+// 128 x 64 exceed the 512 that fit on the chip at two per CU, and the 8 left
+// over ran as a second round: 22.3 us per launch; as 12 x 40 + 20 double-width
+// tiles, all in one round: 19.4 us).
+template <int WM, int TR, int TC, int EPI, int D, int F, bool SPLIT, int XG, bool TAIL>
+__device__ __forceinline__ void big32_body(const GemmParams& p, int K, float* part, float* lds_raw, float* srstd,
+                                           int tx, int ty) {
   constexpr int NW = WM, KS = 2;
   constexpr int NP = 4;                          // stages of loads in flight (register slots)
-  constexpr int FA = 2 * TR * WM, FB = 2 * TC;  // 16-row / 16-column fragments of the tile
-  constexpr int BM = 16 * FA, BN = 16 * FB;
-  constexpr int FBS = FB * KS;                  // B fragments per stage
+  constexpr int WNC = TAIL ? 2 : 1;              // column tiles of the workgroup
+  static_assert(!TAIL || (!SPLIT && WM % 2 == 0), "tail tiles: unsplit, waves in pairs");
+  constexpr int FA = 2 * TR * WM / WNC, FB = 2 * TC;  // 16-row fragments of the tile / 16-column ones of a column tile
+  constexpr int FBW = FB * WNC;                 // 16-column fragments of the tile
+  constexpr int BM = 16 * FA, BN = 16 * FBW;
+  constexpr int FBS = FBW * KS;                 // B fragments per stage
   constexpr int BPW = FBS / NW;                 // B fragments copied per wave and stage
   constexpr bool NORM = epi_norm(EPI);
   static_assert(FBS % NW == 0, "stage B fragments split evenly over the waves");
   constexpr int CS = BN + 4;
-  constexpr int kStFloats = 2 * FBS * 64 * 4, kCtFloats = BM * CS;
-  __shared__ __attribute__((aligned(16))) float lds_raw[kStFloats > kCtFloats ? kStFloats : kCtFloats];
   u32x4 (*st)[FBS][64] = reinterpret_cast<u32x4 (*)[FBS][64]>(lds_raw);
-  __shared__ float srstd[BM];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // this wave's 32-row slice and column tile
+  const int wr = TAIL ? (w & (WM / 2 - 1)) : w, wc = TAIL ? w / (WM / 2) : 0;
   // KB: k-blocks of the whole K (the operands' row stride); this workgroup
   // takes KBs of them from kb0 on.  NS is a multiple of NP: each K range is a
   // multiple of 256 for every GEMM here.
   const int KB = K >> 5;
   const int KBs = SPLIT ? KB / int(gridDim.z) : KB, kb0 = SPLIT ? int(blockIdx.z) * KBs : 0;
   const int NS = KBs / KS;
-  // E_KV covers the K/V columns only: n-blocks from 2 * 64 on (Q is 64 pairs)
-  int tx = int(blockIdx.x), ty = int(blockIdx.y);
-  if constexpr (XG > 0 && !SPLIT) {
-    const int GX = int(gridDim.x), GY = int(gridDim.y), n = GX * GY;
-    if ((n & 7) == 0 && GX % XG == 0) {
-      const int id = tx + GX * ty, t = (id & 7) * (n >> 3) + (id >> 3);
-      const int gw = GX / XG, g = t / (gw * GY), rem = t - g * gw * GY;
-      ty = rem / gw;
-      tx = g * gw + rem % gw;
-    }
-  }
-  const int nb0 = tx * FB + (EPI == E_KV ? 128 : 0), mb0 = ty * FA;
+  // E_KV covers the K/V columns only: n-blocks from 2 * 64 on (Q is 64 pairs);
+  // a tail tile starts at the row its row tile of full height would
+  const int nb0 = tx * FBW + (EPI == E_KV ? 128 : 0), mb0 = ty * FA * WNC;
   const int sub = frag32_sub(lane);
-  // this lane's A rows: fragments mb0 + 2(w*TR + r) + sub
-  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + (size_t(mb0 + 2 * w * TR + sub) * KB + kb0) * 64;
+  // this lane's A rows: fragments mb0 + 2(wr*TR + r) + sub
+  const u32x4* ap = reinterpret_cast<const u32x4*>(p.a_frag) + (size_t(mb0 + 2 * wr * TR + sub) * KB + kb0) * 64;
   const u32x4* wp = reinterpret_cast<const u32x4*>(p.w) + (size_t(nb0) * KB + kb0) * 64 + lane;
   const int al[2] = {frag32_lane(lane, 0), frag32_lane(lane, 1)};
 
@@ -975,7 +983,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
         _Pragma("unroll") for (int h = 0; h < 2; ++h)                                  \
           av[SL][kk][r][h] = ap[(size_t(2 * r) * KB + sg_ * KS + kk) * 64 + al[h]];   \
     _Pragma("unroll") for (int q = 0; q < BPW; ++q) {                                  \
-      const int fi = q * NW + w, kk = fi / FB, j = fi % FB;                            \
+      const int fi = q * NW + w, kk = fi / FBW, j = fi % FBW;                          \
       pb[SL][q] = wp[(size_t(j) * KB + sg_ * KS + kk) * 64];                           \
     }                                                                                  \
   }
@@ -1012,7 +1020,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
     _Pragma("unroll") for (int kk = 0; kk < KS; ++kk)                                  \
       _Pragma("unroll") for (int h = 0; h < 2; ++h)                                    \
         _Pragma("unroll") for (int c = 0; c < TC; ++c)                                 \
-          b[kk][c][h] = st[(SG) & 1][kk * FB + 2 * c + sub][al[h]];                    \
+          b[kk][c][h] = st[(SG) & 1][kk * FBW + wc * FB + 2 * c + sub][al[h]];         \
     _Pragma("unroll") for (int kk = 0; kk < KS; ++kk)                                  \
       _Pragma("unroll") for (int h = 0; h < 2; ++h)                                    \
         _Pragma("unroll") for (int r = 0; r < TR; ++r)                                 \
@@ -1043,7 +1051,7 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
       for (int c = 0; c < TC; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          dst[size_t((w * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * Np + c * 32 + (lane & 31)] =
+          dst[size_t((wr * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * Np + c * 32 + (lane & 31)] =
               acc[r][c][i];
     return;
   }
@@ -1056,9 +1064,34 @@ __global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, flo
     for (int c = 0; c < TC; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        ct[((w * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + c * 32 + (lane & 31)] = acc[r][c][i];
+        ct[((wr * TR + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * CS + wc * (32 * TC) + c * 32 + (lane & 31)] =
+            acc[r][c][i];
   __syncthreads();
   tile_epilogue<BM, BN, CS, NW * 64, EPI, D, F>(p, ct, srstd, mb0, nb0);
+}
+
+template <int WM, int TR, int TC, int EPI, int D = kD, int F = kF, bool SPLIT = false, int XG = 0, bool TAILW = false>
+__global__ __launch_bounds__(WM * 64) void k_gemm_big32(GemmParams p, int K, float* part) {
+  constexpr int kMain = big32_lds_floats<WM, TR, TC, 1>(), kTail = TAILW ? big32_lds_floats<WM, TR, TC, 2>() : 0;
+  __shared__ __attribute__((aligned(16))) float lds_raw[kMain > kTail ? kMain : kTail];
+  __shared__ float srstd[32 * TR * WM];
+  int tx = int(blockIdx.x), ty = int(blockIdx.y);
+  if constexpr (XG > 0 && !SPLIT) {
+    const int GX = int(gridDim.x), GY = int(gridDim.y), n = GX * GY;
+    if ((n & 7) == 0 && GX % XG == 0) {
+      const int id = tx + GX * ty, t = (id & 7) * (n >> 3) + (id >> 3);
+      const int gw = GX / XG, g = t / (gw * GY), rem = t - g * gw * GY;
+      ty = rem / gw;
+      tx = g * gw + rem % gw;
+    }
+  }
+  if constexpr (TAILW) {  // the grid's last row: tail tiles in its first half, nothing in the second
+    if (ty == int(gridDim.y) - 1) {
+      if (tx < int(gridDim.x) / 2) big32_body<WM, TR, TC, EPI, D, F, SPLIT, XG, true>(p, K, part, lds_raw, srstd, tx, ty);
+      return;
+    }
+  }
+  big32_body<WM, TR, TC, EPI, D, F, SPLIT, XG, false>(p, K, part, lds_raw, srstd, tx, ty);
 }
 #undef PI_AE_B32_SCHED
 
@@ -1996,8 +2029,14 @@ hipError_t launch_io(const IoParams& p, hipStream_t s, const KernelTiming* t) {
   return go(k_io, dim3(p.M + p.pf.nwg), dim3(256), s, t, p);
 }
 hipError_t launch_qkv(const GemmParams& p, hipStream_t s, const KernelTiming* t) {
-  if (p.M >= kTiledMinRows)
-    return go(k_gemm_big32<4, 1, 2, E_QKV>, dim3(kNqkv / 64, row_tiles(p.M, 128)), dim3(256), s, t, p, kD, (float*)nullptr);
+  if (p.M >= kTiledMinRows) {
+    // a last row tile with at most 64 valid rows runs as double-width tail tiles
+    const unsigned rt = row_tiles(p.M, 128);
+    if (p.M - 128 * int(rt - 1) <= 64)
+      return go(k_gemm_big32<4, 1, 2, E_QKV, kD, kF, false, 0, true>, dim3(kNqkv / 64, rt), dim3(256), s, t, p, kD,
+                (float*)nullptr);
+    return go(k_gemm_big32<4, 1, 2, E_QKV>, dim3(kNqkv / 64, rt), dim3(256), s, t, p, kD, (float*)nullptr);
+  }
   if (p.M <= 64)  // 32-row tiles: half the activation bytes per workgroup, twice the CUs
     return go(k_gemm<2, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M, 32)), dim3(256), s, t, p);
   return go(k_gemm<4, 2, 4, 8, E_QKV>, dim3(kNqkv / 32 + p.pf.nwg, row_tiles(p.M)), dim3(256), s, t, p);
