@@ -1800,30 +1800,20 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   const int kl0 = frag32_lane(lane, 0), kl1 = frag32_lane(lane, 1);
   const int vl0 = (lane & 15) + 16 * hh, vl1 = vl0 + 32;
 
-  // L2 warm-up of pair PR: one dword load per lane touches one 128-byte line;
-  // a workgroup's waves cover half of the pair's 512 lines (K: waves 0-1, V:
-  // waves 2-3; which half alternates with the workgroup), the episode's other
-  // workgroups the rest.  Past the last block the loads read as zeros.  The
-  // loaded words go to an LDS scratch word per lane that nothing reads (a
-  // load that writes LDS needs no register, so nothing waits for it).
-  __shared__ uint32_t warm_sink[64];
-  const uint32_t warm_off = uint32_t((qw & 1) * 128 + (w & 1) * 64 + lane) * 128u;
-#define PI_AE_KV32_WARM(PR) \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(w < 2 ? kr : vr, (lds_ptr_t)&warm_sink[0], 4, warm_off, uint32_t(PR) * 32768u, 0, 0);
-
   // Pair step PR on block kh of the pair.  Copies per wave, in issue order:
-  // each step's first half issues the warm-up of pair PR+3, V of pair PR+1
-  // (8) and its biases, the second half K of pair PR+2 (8); before the
-  // loop: K of pair 0, the warm-up of pair 2, V and biases of pair 0, K of
-  // pair 1.  So 18 copies are issued after this wave's K of pair PR and 18
-  // after its biases of pair PR: vmcnt(18) at either barrier means that
-  // half's data has landed, and the barrier makes every wave's visible (and
-  // retires every read of the buffers the next copies overwrite).
+  // each step's first half issues V of pair PR+1 (8) and its biases, the
+  // second half K of pair PR+2 (8); before the loop: K of pair 0, V and
+  // biases of pair 0, K of pair 1.  So 17 copies are issued after this wave's
+  // K of pair PR and 17 after its biases of pair PR: vmcnt(17) at either
+  // barrier means that half's data has landed, and the barrier makes every
+  // wave's visible (and retires every read of the buffers the next copies
+  // overwrite).  (No L2 warm-up loads ride along: one dword per lane over the
+  // pair three steps ahead cost 3 us per launch at 32 episodes, their turns
+  // in the CU's address path taken from the copies.)
 #define PI_AE_KV32_STEP(KS, VS, KB, VS2, KB2, PR)                                      \
   {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(0x4f72); /* vmcnt(18) */                                \
+    __builtin_amdgcn_s_waitcnt(0x4f71); /* vmcnt(17) */                                \
     lds_barrier();                                                                     \
-    PI_AE_KV32_WARM((PR) + 3)                                                          \
     u32x4 fr[16];                                                                      \
     _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KS[kh][sub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
     __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -1836,7 +1826,7 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);                                               \
     }                                                                                  \
     PI_AE_KV32_BIAS(KB2, (PR) + 1)                                                     \
-    __builtin_amdgcn_s_waitcnt(0x4f72); /* vmcnt(18) */                                \
+    __builtin_amdgcn_s_waitcnt(0x4f71); /* vmcnt(17) */                                \
     lds_barrier();                                                                     \
     /* V operands of d-tile dt (both halves of the block) and the biases */           \
     _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
@@ -1884,7 +1874,6 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
 
 #pragma unroll
   for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(kr, k0s, 0, c)
-  PI_AE_KV32_WARM(2)
 #pragma unroll
   for (int c = 0; c < 8; ++c) PI_AE_KV32_DMA(vr, v0s, 0, c)
   PI_AE_KV32_BIAS(kba, 0)
@@ -1918,7 +1907,6 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
   }
   if (pr < npair) PI_AE_KV32_STEP(k0s, v0s, kba, v1s, kbb, pr)
 #undef PI_AE_KV32_STEP
-#undef PI_AE_KV32_WARM
 #undef PI_AE_KV32_BIAS
 #undef PI_AE_KV32_DMA
 
