@@ -1797,7 +1797,13 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;  // l_part: this lane's keys only
-  const int kl0 = frag32_lane(lane, 0), kl1 = frag32_lane(lane, 1);
+  // Key order of the scores.  Row r of S^T (accumulator element i of lane l:
+  // r = 8(i/4) + 4(l/32) + i%4) holds key r with bits 3 and 4 swapped, so that
+  // the 8 probabilities of p0 (i < 8) are keys 4g..4g+3 and 16+4g..16+4g+3 of
+  // the block with g = l/32, and those of p1 the same with g = l/32 + 2: the
+  // key order of the packed V entries (vpack_index), so each V entry is a PV
+  // operand as loaded.  Lane l reads K row (l & 7) + 8 sub + 16 ((l >> 3) & 1).
+  const int ksub = (lane >> 3) & 1, kl0 = (lane & 7) + 8 * sub + 16 * hh, kl1 = kl0 + 32;
   const int vl0 = (lane & 15) + 16 * hh, vl1 = vl0 + 32;
 
   // Pair step PR on block kh of the pair.  Copies per wave, in issue order:
@@ -1815,7 +1821,7 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0x4f71); /* vmcnt(17) */                                \
     lds_barrier();                                                                     \
     u32x4 fr[16];                                                                      \
-    _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KS[kh][sub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
+    _Pragma("unroll") for (int s = 0; s < 16; ++s) fr[s] = KS[kh][ksub * 8 + (s >> 1)][(s & 1) ? kl1 : kl0]; \
     __builtin_amdgcn_sched_barrier(0);                                                 \
     f32x16 sc;                                                                         \
     _Pragma("unroll") for (int i = 0; i < 16; ++i) sc[i] = 0.f;                        \
@@ -1826,49 +1832,68 @@ __global__ __launch_bounds__(NWQ * 2 * 64) void k_attn_rows32(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);                                               \
     }                                                                                  \
     PI_AE_KV32_BIAS(KB2, (PR) + 1)                                                     \
+    /* the scores are consumed here, so their MFMAs stay ahead of the barrier (pure   \
+       instructions otherwise sink past it to their first use in the softmax) */      \
+    asm volatile("" : "+v"(sc));                                                       \
     __builtin_amdgcn_s_waitcnt(0x4f71); /* vmcnt(17) */                                \
     lds_barrier();                                                                     \
-    /* V operands of d-tile dt (both halves of the block) and the biases */           \
+    /* the biases, then the V operands of d-tile dt (both halves of the block): LDS  \
+       reads return in order, so the softmax waits for the biases only */              \
+    float4 bias[4];                                                                    \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) /* keys 8 q' + 4 hh.., q' = q with bits swapped */ \
+      bias[q] = *reinterpret_cast<const float4*>(&KB[kh * 32 + 8 * (((q & 1) << 1) | (q >> 1)) + 4 * hh]); \
     _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
       fr[2 * dt] = VS[kh][2 * dt + sub][vl0];                                          \
       fr[2 * dt + 1] = VS[kh][2 * dt + sub][vl1];                                      \
     }                                                                                  \
-    float4 bias[4];                                                                    \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                      \
-      bias[q] = *reinterpret_cast<const float4*>(&KB[kh * 32 + 8 * q + 4 * hh]);       \
     __builtin_amdgcn_sched_barrier(0);                                                 \
-    const bool valid = 2 * (PR) + kh < nkb;                                            \
     const float scl = 0.0625f * 1.4426950408889634f; /* 1/sqrt(256) * log2(e) */       \
     float mloc = -INFINITY;                                                            \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                   \
-      const float4 bq = bias[i >> 2];                                                  \
-      const float bv = (i & 3) == 0 ? bq.x : (i & 3) == 1 ? bq.y : (i & 3) == 2 ? bq.z : bq.w; \
-      sc[i] = valid ? sc[i] * scl + bv : -INFINITY;                                    \
-      mloc = fmaxf(mloc, sc[i]);                                                       \
+    if (2 * (PR) + kh < nkb) { /* a block past the last: every score -inf */           \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                 \
+        const float4 bq = bias[i >> 2];                                                \
+        const float bv = (i & 3) == 0 ? bq.x : (i & 3) == 1 ? bq.y : (i & 3) == 2 ? bq.z : bq.w; \
+        sc[i] = sc[i] * scl + bv;                                                      \
+        mloc = fmaxf(mloc, sc[i]);                                                     \
+      }                                                                                \
+    } else {                                                                           \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) sc[i] = -INFINITY;                \
     }                                                                                  \
     mloc = xor32_max(mloc);                                                            \
     if (__builtin_amdgcn_ballot_w64(mloc > m_run + 8.f)) {                             \
       const float m_new = fmaxf(m_run, mloc);                                          \
-      const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);             \
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new); \
       l_part *= alpha;                                                                 \
       _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;               \
       m_run = m_new;                                                                   \
     }                                                                                  \
-    const bool none = m_run == -INFINITY;                                              \
+    /* a row with no valid key yet (m_run = -inf) takes exp2(-inf - 0) = 0; the raw \
+       hardware exp2 (no denormal rescaling: a probability below 2^-126 of the      \
+       running max is negligible) */                                                   \
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;                              \
     float pv[16];                                                                      \
     _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                   \
-      pv[i] = none ? 0.f : exp2f(sc[i] - m_run);                                       \
+      pv[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);                                   \
       l_part += pv[i];                                                                 \
     }                                                                                  \
     const bf16x8 p0 = pack8(make_float4(pv[0], pv[1], pv[2], pv[3]), make_float4(pv[4], pv[5], pv[6], pv[7])); \
     const bf16x8 p1 = pack8(make_float4(pv[8], pv[9], pv[10], pv[11]), make_float4(pv[12], pv[13], pv[14], pv[15])); \
     __builtin_amdgcn_sched_barrier(0);                                                 \
+    /* the first key half of every d-tile, then the second: eight MFMAs apart, no  \
+       product waits for the one before it on the same accumulator */                  \
     _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
-      const u32x4 a0 = fr[2 * dt], a1 = fr[2 * dt + 1];                                \
-      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), p0, acc[dt]); \
-      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, u32x4{a0.z, a0.w, a1.z, a1.w}), p1, acc[dt]); \
-      PI_AE_KV32_DMA(kr, KS, (PR) + 2, dt)                                             \
-      __builtin_amdgcn_sched_barrier(0);                                               \
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, fr[2 * dt]), p0, acc[dt]);           \
+      if (dt & 1) {                                                                    \
+        PI_AE_KV32_DMA(kr, KS, (PR) + 2, dt - 1)                                       \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+      }                                                                                \
+    }                                                                                  \
+    _Pragma("unroll") for (int dt = 0; dt < 8; ++dt) {                                 \
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, fr[2 * dt + 1]), p1, acc[dt]);       \
+      if (dt & 1) {                                                                    \
+        PI_AE_KV32_DMA(kr, KS, (PR) + 2, dt)                                           \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+      }                                                                                \
     }                                                                                  \
   }
 
