@@ -1695,12 +1695,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn(AttnParams p) {
 // K/V blocks is read once per workgroup into LDS and shared by its waves.  A
 // wave owns 32 query rows: their Q is the B operand of S^T = K Q^T (lane l:
 // row l%32, head-dim 16s + 8(l/32) + j), so S^T of a 32-key block is one 32x32
-// accumulator in which lane l holds 16 keys of row l%32.  Those 16
-// probabilities are, unchanged, the lane's B operand of O^T += V^T P^T when
-// the block's keys are contracted in the order k -> 16t + 8((k%8)/4) +
-// 4(k/8) + k%4 (t: which half of the block); V^T is read in that order from
-// the packed V (two 16-byte LDS reads give a d-tile's operands for both
-// halves), K through the 32x32 gather of the packed K fragments.  NWQ 32-row
+// accumulator in which lane l holds 16 keys of row l%32.  The K rows of a
+// block are read in a permuted order (accumulator row r holds key r with
+// bits 3 and 4 swapped), which makes each half of those 16 probabilities,
+// unchanged, the lane's B operand of O^T += V^T P^T over exactly the 8 keys
+// of one packed V entry (keys 4g..4g+3 and 16+4g..16+4g+3): V^T is read
+// from the packed V one 16-byte LDS read per d-tile and half, with no
+// register regrouping.  NWQ 32-row
 // query groups share a workgroup, and two waves work on each group: wave kh
 // takes block kh of every pair, and the two halves are merged through LDS at
 // the end.  K and V blocks are copied straight from memory into LDS (buffer
