@@ -2445,7 +2445,16 @@ template <int EPI>
 static hipError_t vis_gemm(const GemmParams& p, int ncols, int K, int S, float* part, hipStream_t s,
                            const KernelTiming* t) {
   const dim3 grid(ncols / 64, row_tiles(p.M, 128), S);
-  if (S <= 1) return go(k_gemm_big32<4, 1, 2, EPI, kSD, kSFk>, grid, dim3(256), s, t, p, K, (float*)nullptr);
+  if (S <= 1) {
+    // 64-row tiles (two waves) when they still fit one workgroup per CU: at
+    // one view (256 rows) twice the workgroups, each re-reading half the
+    // activation rows (QKV 12.3 -> 10.2 us, projector 11.8 -> 10.3 us);
+    // fc1's 272 such tiles would not, and stay 128-row
+    const unsigned rt64 = row_tiles(p.M, 64);
+    if (unsigned(ncols / 64) * rt64 <= 256u)
+      return go(k_gemm_big32<2, 1, 2, EPI, kSD, kSFk>, dim3(ncols / 64, rt64), dim3(128), s, t, p, K, (float*)nullptr);
+    return go(k_gemm_big32<4, 1, 2, EPI, kSD, kSFk>, grid, dim3(256), s, t, p, K, (float*)nullptr);
+  }
   const KernelTiming t0{t ? t->start : nullptr, nullptr}, t1{nullptr, t ? t->stop : nullptr};
   hipError_t e = go(k_gemm_big32<4, 1, 2, EPI, kSD, kSFk, true>, grid, dim3(256), s, t ? &t0 : nullptr, p, K, part);
   if (e != hipSuccess) return e;
